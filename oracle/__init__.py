@@ -1,0 +1,199 @@
+"""CPU oracle (fp64) for the block-quantized-weight batched GEMM.
+
+TEST INFRASTRUCTURE ONLY: it is loaded by ``tests/``, by the smoke check and
+by the benchmark's CPU-baseline leg, never by the library.  It reads the
+logical arrays produced by ``synth`` (one code per byte, scales in their own
+arrays) and shares no code with the HIP library.
+
+What it computes (plain definitions, see qgemm_oracle.c for the decoders):
+
+* ``y[b][n] = g(n) * sum_k x[b][k] * w[n][k]`` in fp64, k increasing, with
+  ``w`` decoded per format: Q8_0 ``d*q``; MXFP4 ``E2M1(c) * 2**(e-127)``;
+  NVFP4 ``E2M1(c) * E4M3(s)`` and ``g(n)`` the fp32 tensor scale of row n's
+  tensor, applied after the sum (Atlas issue "[job] Qwen3.8-27B on Strix
+  Halo: prefill 2.4x gap + DP4A verify tiers for K=5..9", section
+  "Kernel-level root cause of the gfx1151 NVFP4 prefill gap", Fix).
+* fused gate+up: ``out[b][j] = SiLU(G) * U`` with G from row j and U from row
+  Nh + j (Atlas issue, "What's the job?" asks for the fused gate+up
+  dual-accumulator GEMM; the workload names SiLU(gate)*up).
+
+Every function here is pinned by ``tests/test_oracle_pins.py`` against
+library decoders (numpy float16, torch float8, transformers' FP4 table),
+closed forms, exact rational brute force and invariants.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qgemm_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+FMT = {"q8_0": 0, "mxfp4": 1, "nvfp4": 2}
+ACT = {"f32": 0, "bf16": 1}
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (plain C, OpenMP, no fp contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+                               "-ffp-contract=off", "-fno-fast-math", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        d, i64, vp, u8, u16, i32 = (ctypes.c_double, ctypes.c_int64, ctypes.c_void_p,
+                                    ctypes.c_uint8, ctypes.c_uint16, ctypes.c_int)
+        for name, arg in (("oracle_fp16", u16), ("oracle_bf16", u16), ("oracle_e2m1", u8),
+                          ("oracle_e8m0", u8), ("oracle_e4m3", u8), ("oracle_silu", d)):
+            f = getattr(lib, name)
+            f.restype = d
+            f.argtypes = [arg]
+        lib.oracle_dequant.restype = None
+        lib.oracle_dequant.argtypes = [i32, vp, vp, vp, i64, i32, i64, i64, vp]
+        lib.oracle_gemm.restype = None
+        lib.oracle_gemm.argtypes = [i32, vp, vp, vp, i64, i32, vp, i64, i64, i64, vp]
+        lib.oracle_swiglu.restype = None
+        lib.oracle_swiglu.argtypes = [i32, vp, vp, vp, i64, i32, vp, i64, i64, i64, vp]
+        for name in ("oracle_gemm_at", "oracle_swiglu_at"):
+            f = getattr(lib, name)
+            f.restype = None
+            f.argtypes = [i32, vp, vp, vp, i64, i32, vp, i64, i64, vp, vp, i64, vp]
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _prep(w: dict):
+    codes = np.ascontiguousarray(w["codes"])
+    scales = np.ascontiguousarray(w["scales"])
+    g = w.get("g")
+    g = None if g is None else np.ascontiguousarray(g, dtype=np.float32)
+    nt = 0 if g is None else len(g)
+    return FMT[w["fmt"]], codes, scales, g, nt
+
+
+def _act(x):
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float32:
+        return ACT["f32"], x
+    if x.dtype == np.uint16:
+        return ACT["bf16"], x
+    raise TypeError("activations must be float32 or bf16 bits (uint16)")
+
+
+# ---- scalar decoders (exposed for the pins) ----
+
+def fp16(h):
+    return _load().oracle_fp16(int(h))
+
+
+def bf16(h):
+    return _load().oracle_bf16(int(h))
+
+
+def e2m1(c):
+    return _load().oracle_e2m1(int(c))
+
+
+def e8m0(b):
+    return _load().oracle_e8m0(int(b))
+
+
+def e4m3(b):
+    return _load().oracle_e4m3(int(b))
+
+
+def silu(t):
+    return _load().oracle_silu(float(t))
+
+
+# ---- array entry points ----
+
+def dequant(w: dict, apply_g: bool = False) -> np.ndarray:
+    """Dense fp64 [N][K] decoded weights (times the tensor scale if apply_g)."""
+    fmt, codes, scales, g, nt = _prep(w)
+    n, k = codes.shape
+    out = np.empty((n, k), dtype=np.float64)
+    _load().oracle_dequant(fmt, _ptr(codes), _ptr(scales), _ptr(g), nt, int(apply_g), n, k,
+                           _ptr(out))
+    return out
+
+
+def gemm(w: dict, x: np.ndarray) -> np.ndarray:
+    """y[B][N] in fp64."""
+    fmt, codes, scales, g, nt = _prep(w)
+    a, x = _act(x)
+    n, k = codes.shape
+    b = x.shape[0]
+    assert x.shape[1] == k
+    y = np.empty((b, n), dtype=np.float64)
+    _load().oracle_gemm(fmt, _ptr(codes), _ptr(scales), _ptr(g), nt, a, _ptr(x), b, n, k, _ptr(y))
+    return y
+
+
+def gemm_at(w: dict, x: np.ndarray, bidx, nidx) -> np.ndarray:
+    """y[bidx[i]][nidx[i]] in fp64."""
+    fmt, codes, scales, g, nt = _prep(w)
+    a, x = _act(x)
+    n, k = codes.shape
+    bi = np.ascontiguousarray(bidx, dtype=np.int64)
+    ni = np.ascontiguousarray(nidx, dtype=np.int64)
+    assert bi.shape == ni.shape
+    assert bi.size == 0 or (bi.max() < x.shape[0] and ni.max() < n and bi.min() >= 0
+                            and ni.min() >= 0)
+    y = np.empty(bi.size, dtype=np.float64)
+    _load().oracle_gemm_at(fmt, _ptr(codes), _ptr(scales), _ptr(g), nt, a, _ptr(x), n, k,
+                           _ptr(bi), _ptr(ni), bi.size, _ptr(y))
+    return y
+
+
+def swiglu(w: dict, x: np.ndarray) -> np.ndarray:
+    """out[B][N/2] = SiLU(gate) * up, fp64."""
+    fmt, codes, scales, g, nt = _prep(w)
+    a, x = _act(x)
+    n, k = codes.shape
+    assert n % 2 == 0
+    b = x.shape[0]
+    out = np.empty((b, n // 2), dtype=np.float64)
+    _load().oracle_swiglu(fmt, _ptr(codes), _ptr(scales), _ptr(g), nt, a, _ptr(x), b, n, k,
+                          _ptr(out))
+    return out
+
+
+def swiglu_at(w: dict, x: np.ndarray, bidx, jidx) -> np.ndarray:
+    fmt, codes, scales, g, nt = _prep(w)
+    a, x = _act(x)
+    n, k = codes.shape
+    bi = np.ascontiguousarray(bidx, dtype=np.int64)
+    ji = np.ascontiguousarray(jidx, dtype=np.int64)
+    assert bi.size == 0 or (bi.max() < x.shape[0] and ji.max() < n // 2)
+    out = np.empty(bi.size, dtype=np.float64)
+    _load().oracle_swiglu_at(fmt, _ptr(codes), _ptr(scales), _ptr(g), nt, a, _ptr(x), n, k,
+                             _ptr(bi), _ptr(ji), bi.size, _ptr(out))
+    return out
+
+
+def rel_fro(y, ref) -> float:
+    """||y - ref||_F / ||ref||_F in fp64."""
+    y = np.asarray(y, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref.ravel())
+    num = np.linalg.norm((y - ref).ravel())
+    return float(num / den) if den > 0 else float(num)
