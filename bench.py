@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Throughput of the block-quantized-weight batched GEMM on one MI355X.
+
+Headline (one JSON line on stdout): the Q8_0 attention-projection GEMM,
+K = N = 5120, B = 16 fp32 activation rows, fp32 output, fp32-faithful math:
+weight-stream GB/s = packed weight bytes per call / time per call.  One step
+is one qgemm_run.  The packed weights rotate over enough copies (> 1 GiB in
+total) that every call streams them from HBM, not from the 256 MB Infinity
+Cache.  Steps are replayed from a HIP graph so host launch cost is not timed.
+
+Extra keys carry the rest of the B sweep of that shape and the prefill
+workloads (Q8_0 FFN B = 2048, MXFP4 down projection, NVFP4 fused gate+up),
+plus the roofline of the dominant kernel and the CPU oracle baseline.
+
+    python bench.py [--steps K] [--warmup W] [--headline-only] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2516.6       # MI355X dense bf16 MFMA
+ROTATE_BYTES = 1 << 30          # weight bytes to rotate over (> Infinity Cache)
+METRIC = "weight-stream GB/s (B≤16) and TFLOP/s (B≥256) vs MI355X roofline"
+SRC_FILES = ("prefill_q8_mxfp4_amd/csrc/kernels.hip", "prefill_q8_mxfp4_amd/csrc/api.hip",
+             "prefill_q8_mxfp4_amd/csrc/layout.h")
+
+
+def kernel_src_sha() -> str:
+    h = hashlib.sha256()
+    for f in SRC_FILES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def log(msg):
+    sys.stderr.write(msg + "\n")
+    sys.stderr.flush()
+
+
+class Workload:
+    """Packed weights (rotating copies), activations and output on the GPU."""
+
+    def __init__(self, name, B, copies=1, math_mode=None):
+        import numpy as np
+        import torch
+
+        import prefill_q8_mxfp4_amd as q
+        import synth
+
+        c = synth.CONFIGS[name]
+        self.name, self.B, self.c = name, B, c
+        self.N, self.K = c["N"], c["K"]
+        self.plan = q.Plan(c["fmt"], c["N"], c["K"], act=c["act"], out=c["out"],
+                           epilogue="swiglu" if c["epi"] == "swiglu" else "none",
+                           math=math_mode or c["math"])
+        t0 = time.time()
+        self.w_logical = synth.gen_config_weights(name)
+        self.x_host = synth.gen_config_x(name, B)
+        packed = torch.from_numpy(q.pack_logical(self.w_logical))
+        dev = torch.device("cuda:0")
+        self.wbytes = packed.numel()
+        self.ws = [packed.to(dev) for _ in range(copies)]
+        if c["act"] == "f32":
+            self.x = torch.from_numpy(self.x_host).to(dev)
+        else:
+            self.x = torch.from_numpy(self.x_host.view(np.int16)).view(torch.bfloat16).to(dev)
+        odt = torch.float32 if c["out"] == "f32" else torch.bfloat16
+        self.y = torch.empty((B, self.plan.out_cols), dtype=odt, device=dev)
+        torch.cuda.synchronize()
+        log(f"[bench] {name} B={B} copies={copies} ready in {time.time() - t0:.1f}s "
+            f"tier={self.plan.tier(B)}")
+
+    def flops(self):
+        return 2.0 * self.B * self.N * self.K
+
+    def io_bytes(self):
+        xb = self.x.numel() * self.x.element_size()
+        yb = self.y.numel() * self.y.element_size()
+        return self.wbytes + xb + yb
+
+    def time_ms(self, steps, warmup):
+        """Average ms per call over `steps` calls replayed from a HIP graph
+        holding one call per weight copy, bracketed by events on the stream
+        the calls run on."""
+        import torch
+
+        n = len(self.ws)
+        reps = max(1, math.ceil(steps / n))
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            for i in range(max(warmup, n)):
+                self.plan.run(self.x, self.ws[i % n], self.y)
+        stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n):
+                self.plan.run(self.x, self.ws[i], self.y)
+        with torch.cuda.stream(stream):
+            g.replay()
+        stream.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):  # replays and events on one stream
+            start.record(stream)
+            for _ in range(reps):
+                g.replay()
+            end.record(stream)
+        end.synchronize()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / (reps * n), reps * n
+
+    def free(self):
+        self.ws = self.x = self.y = None
+
+
+def copies_for(wbytes):
+    return max(1, math.ceil(ROTATE_BYTES / wbytes))
+
+
+def traffic_record(sha):
+    p = os.path.join(ROOT, "profiles", "traffic_q8_0_5120x5120_b16.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p))
+    if rec.get("kernel_src_sha") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl):
+    import oracle
+
+    t0 = time.time()
+    oracle.gemm(wl.w_logical, wl.x_host)
+    dt = time.time() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", 0) or os.cpu_count() or 1)
+    return {"value": round(wl.wbytes / dt / 1e9, 6), "unit": "GB/s", "cores": cores,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"the whole headline call: fp64 oracle, q8_0 K=N=5120, B={wl.B}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--headline-only", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the library has no multi-GPU path; "
+              "run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import prefill_q8_mxfp4_amd as q
+    import synth
+
+    q.lib()  # fails loudly without the HIP library
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    sha = kernel_src_sha()
+
+    # ---- headline: q8_0 5120x5120, B = 16, fp32 activations
+    B = 16
+    probe = q.weight_bytes("q8_0", 5120, 5120)
+    wl = Workload("cfg2", B, copies=copies_for(probe))
+    ms, steps_done = wl.time_ms(args.steps, args.warmup)
+    value = wl.wbytes / (ms * 1e-3) / 1e9
+    achieved = wl.io_bytes() / (ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps_done,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "Q8_0 batched GEMM K=5120 N=5120 B=16, fp32 activations "
+                               "~N(0,1), weights ~N(0,0.02), fp32 out, fp32-faithful math",
+                   "B": B, "N": 5120, "K": 5120, "weight_copies": len(wl.ws),
+                   "tier": wl.plan.tier(B)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_record(sha), "algorithmic_bytes": wl.io_bytes(),
+                     "kernel_src_sha": sha},
+    }
+    log(f"[bench] headline {ms * 1e3:.2f} us/call  {value:.1f} GB/s weights")
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl)
+    wl.free()
+
+    if not args.headline_only:
+        sweep = {}
+        for b in (1, 4, 8, 16, 64, 65, 70, 76, 256):
+            w = Workload("cfg2", b, copies=copies_for(probe) if b <= 16 else 4)
+            t, _ = w.time_ms(max(40, args.steps // 4), 5)
+            sweep[str(b)] = {"us": round(t * 1e3, 2),
+                             "weight_GBs": round(w.wbytes / (t * 1e-3) / 1e9, 1),
+                             "hbm_frac": round(w.io_bytes() / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                             "TFLOPs": round(w.flops() / (t * 1e-3) / 1e12, 2),
+                             "tier": w.plan.tier(b)}
+            w.free()
+        line["sweep_q8_0_5120x5120_fp32"] = sweep
+        pre = {}
+        for name, bs in (("cfg3", (2048,)), ("cfg4", (1, 16, 256, 2048)), ("cfg5", (2048,))):
+            for b in bs:
+                c = synth.CONFIGS[name]
+                nb = q.weight_bytes(c["fmt"], c["N"], c["K"])
+                w = Workload(name, b, copies=copies_for(nb) if b <= 16 else 1)
+                t, _ = w.time_ms(max(20, args.steps // 10) if b > 16 else max(40, args.steps // 4),
+                                 3)
+                c = w.c
+                key = f"{name}:{c['fmt']}:{c['N']}x{c['K']}:B={b}"
+                rec = {"us": round(t * 1e3, 2), "TFLOPs": round(w.flops() / (t * 1e-3) / 1e12, 2),
+                       "mfma_frac": round(w.flops() / (t * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                       "weight_GBs": round(w.wbytes / (t * 1e-3) / 1e9, 1),
+                       "hbm_frac": round(w.io_bytes() / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                       "tier": w.plan.tier(b)}
+                pre[key] = rec
+                log(f"[bench] {key} {rec}")
+                w.free()
+                torch.cuda.empty_cache()
+        line["prefill"] = pre
+
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,205 @@
+/*
+ * qgemm.h - block-quantized-weight batched GEMM for AMD Instinct MI355X (gfx950)
+ *
+ *     y[b][n] = sum_k x[b][k] * dequant(W)[n][k],   0 <= b < B, 0 <= n < N
+ *
+ * The operation is the Q8_0 batched GEMM that speculative-decoding verify and
+ * prefill call with any batch width (hipfire issue "Qwen3.8-27B native MTP
+ * crashes when Q8 batched GEMM exceeds MAX_BATCH=64", Summary and Expected
+ * behavior: widths 70, 76, 256 must run, not abort), and its 4-bit siblings
+ * MXFP4 (HF model card "Qwen3.8-27B - MXFP4 (AMD Quark) for RDNA4", "What's
+ * 4-bit") and NVFP4 (Atlas issue "[job] Qwen3.8-27B on Strix Halo: prefill
+ * 2.4x gap + DP4A verify tiers for K=5..9", section "Kernel-level root cause
+ * of the gfx1151 NVFP4 prefill gap", Fix), plus the fused gate+up
+ * dual-accumulator GEMM with a SiLU*mul epilogue that the same Atlas issue
+ * asks for in "What's the job?".
+ *
+ * There is no batch limit: every B >= 0 runs in one call, with no host loop
+ * over batch chunks (B = 0 is a no-op).
+ *
+ * Conventions for every entry point
+ *  - Return value: QGEMM_OK (0) or a positive qgemm_status.  On failure,
+ *    qgemm_last_error() returns a message for the calling thread.  The library
+ *    never aborts, asserts, prints or exits.
+ *  - "device pointer": memory the caller allocated on the current HIP device
+ *    (hipMalloc or a framework allocator).  The caller owns every buffer.
+ *  - stream: a hipStream_t passed as void* (NULL = the default stream).  GPU
+ *    work is enqueued asynchronously on it; errors raised while a kernel runs
+ *    surface at the caller's next synchronisation, as in HIP.
+ *
+ * Weight formats (the logical arrays; N rows of K weights, blocks along K)
+ *  - QGEMM_Q8_0:  int8 q[N][K] and fp16 d[N][K/32];   w = d * q.
+ *  - QGEMM_MXFP4: E2M1 codes c[N][K] (4 bits) and E8M0 e[N][K/32];
+ *                 w = E2M1(c) * 2^(e-127)  (e = 255 is NaN).
+ *  - QGEMM_NVFP4: E2M1 codes c[N][K] and FP8-E4M3 s[N][K/16], plus an fp32
+ *                 tensor scale g per tensor;  w = g * E2M1(c) * E4M3(s), with
+ *                 g applied to the finished sum.
+ *  E2M1 code bits: sign (bit 3), exponent (bits 2-1, bias 1), mantissa (bit 0):
+ *  magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qgemm_status {
+    QGEMM_OK = 0,
+    QGEMM_EINVAL = 1,  /* bad argument: null/misaligned pointer, B < 0, N or K <= 0,
+                          K not a multiple of the block, odd N with SwiGLU, ... */
+    QGEMM_ENOTSUP = 2, /* combination of format / dtypes / epilogue / tier not built */
+    QGEMM_EHIP = 3,    /* a HIP call failed; qgemm_last_error() holds its message */
+    QGEMM_ENOMEM = 4   /* host allocation failed */
+} qgemm_status;
+
+typedef enum qgemm_format {
+    QGEMM_Q8_0 = 0,
+    QGEMM_MXFP4 = 1,
+    QGEMM_NVFP4 = 2
+} qgemm_format;
+
+typedef enum qgemm_dtype {
+    QGEMM_F32 = 0,  /* IEEE binary32 */
+    QGEMM_BF16 = 1  /* bfloat16, passed as its 16-bit pattern */
+} qgemm_dtype;
+
+typedef enum qgemm_epilogue {
+    QGEMM_EPI_NONE = 0,
+    /* Fused gate+up: W has N = 2*Nh rows, rows [0, Nh) the gate projection and
+     * rows [Nh, 2Nh) the up projection.  y is [B][Nh]:
+     *     y[b][j] = SiLU(G) * U,  G = sum_k x w[j],  U = sum_k x w[Nh + j],
+     * SiLU(t) = t / (1 + exp(-t)).  G and U never reach memory. */
+    QGEMM_EPI_SWIGLU = 1
+} qgemm_epilogue;
+
+typedef enum qgemm_math {
+    /* fp32-faithful: used with fp32 activations.  Weights enter exactly and
+     * activations are split into bf16 terms that together hold their full fp32
+     * value; relative Frobenius error against an exact product <= 1e-5. */
+    QGEMM_MATH_FP32 = 0,
+    /* bf16 operands: fp32 activations are rounded to bf16 (nearest even) in the
+     * kernel; bf16 activations enter as they are.  Decoded MXFP4 and NVFP4
+     * weights are exact in bf16; a Q8_0 weight d*q is rounded once to bf16 in
+     * the large-batch tier.  Relative Frobenius error <= 1e-2. */
+    QGEMM_MATH_BF16 = 1
+} qgemm_math;
+
+/* Tiers (how a call maps onto kernels); qgemm_create flags may force one. */
+typedef enum qgemm_tier {
+    QGEMM_TIER_SKINNY = 1, /* weights streamed once per 16..64 batch rows straight
+                              into matrix-core operands; for small B */
+    QGEMM_TIER_TILED = 2   /* batch x weight tiles staged through LDS; for large B */
+} qgemm_tier;
+
+#define QGEMM_FLAG_FORCE_SKINNY 0x1u
+#define QGEMM_FLAG_FORCE_TILED 0x2u
+
+/* ---------------------------------------------------------------- layout
+ * The packed device buffer that qgemm_pack writes and every kernel reads.
+ *
+ * Rows are grouped in row tiles of 16 (Np = N rounded up to 16) and K is cut
+ * into slabs of KS = 64 (Q8_0) or 128 (MXFP4, NVFP4) weights (Kp = K rounded
+ * up to KS; S = Kp / KS).  Padding rows and columns hold zero codes and zero
+ * scale bytes.
+ *
+ * 1. Codes: slab (rt, s) is 1024 bytes at ((rt * S) + s) * 1024.  Its 16-byte
+ *    chunk L (0..63) belongs to row r = L % 16 of the tile and k-group
+ *    g = L / 16, and holds, for each 32-wide unit u of the slab, the eight
+ *    weights k = s*KS + 32u + 8g + 0..7 of that row:
+ *      Q8_0 : byte 8u + j is q (int8) for j = 0..7, u = 0..1;
+ *      FP4  : byte 4u + j holds the codes of k = ... + 2j (low nibble) and
+ *             ... + 2j + 1 (high nibble), u = 0..3.
+ * 2. Scales: at QGEMM_ALIGN-rounded offset, Np rows of SP bytes (row-major):
+ *      Q8_0 : fp16 d[n][K/32 blocks], SP = round16(2 * Kp/32);
+ *      MXFP4: u8 e[n][K/32],          SP = round16(Kp/32);
+ *      NVFP4: u8 s[n][K/16],          SP = round16(Kp/16).
+ * 3. NVFP4 only, at the next QGEMM_ALIGN offset, 256 bytes:
+ *      int32 ntensors, int32 rows_per_tensor, int32 0, int32 0,
+ *      float g[QGEMM_MAX_TENSORS];  row n uses g[n / rows_per_tensor].
+ */
+#define QGEMM_ALIGN 256
+#define QGEMM_MAX_TENSORS 60
+
+/* Size in bytes of the packed buffer for an N x K weight.  0 on bad input. */
+size_t qgemm_weight_bytes(qgemm_format fmt, int64_t N, int64_t K);
+
+/* Host-side packer: logical arrays (host pointers) -> packed buffer (host
+ * pointer, out_bytes >= qgemm_weight_bytes).  codes: Q8_0 int8 [N][K]; FP4
+ * uint8 [N][K], one code (0..15) per byte.  scales: Q8_0 uint16 fp16 bits
+ * [N][K/32]; MXFP4 uint8 [N][K/32]; NVFP4 uint8 [N][K/16].  tensor_scales:
+ * NVFP4 only, ntensors (1..QGEMM_MAX_TENSORS, dividing N) fp32 values; NULL
+ * and 0 for the other formats.  Pure host code, callable without a GPU. */
+int qgemm_pack(qgemm_format fmt, int64_t N, int64_t K, const void *codes, const void *scales,
+               const float *tensor_scales, int64_t ntensors, void *out, size_t out_bytes);
+
+/* ------------------------------------------------------------------ plan */
+typedef struct qgemm_plan qgemm_plan;
+
+/* Validate and record a problem shape.  act: activation dtype; out: output
+ * dtype; math: see qgemm_math (QGEMM_MATH_FP32 needs act = QGEMM_F32); flags:
+ * 0 or one QGEMM_FLAG_FORCE_* bit (also settable with the environment
+ * variable QGEMM_FORCE_TIER=skinny|tiled).  Host only: allocates the small
+ * plan object, no device memory and no HIP call.  *plan receives the handle. */
+int qgemm_create(qgemm_plan **plan, qgemm_format fmt, qgemm_dtype act, qgemm_dtype out,
+                 qgemm_epilogue epi, qgemm_math math, int64_t N, int64_t K, uint32_t flags);
+
+/* y = x * W^T (or the SwiGLU of the two halves) for B rows.
+ *   w: packed weights (device, 16-byte aligned), laid out as above for the
+ *      plan's N and K;
+ *   x: activations [B][K] row-major (device, 16-byte aligned, act dtype);
+ *   y: output [B][N] (or [B][N/2] for SwiGLU) row-major (device, out dtype);
+ *      must not overlap x or w.
+ * Any B >= 0; B = 0 returns QGEMM_OK and enqueues nothing.  No allocation,
+ * no synchronisation.  Plans are immutable, so several threads may run one
+ * plan at once.  Results are deterministic: no atomics, fixed summation order
+ * for a given plan, tier and B. */
+int qgemm_run(const qgemm_plan *plan, int64_t B, const void *w, const void *x, void *y,
+              void *stream);
+
+/* Bytes of device workspace with which qgemm_run_ws may split K across
+ * workgroups for this plan and B (0 when the chosen tier does not use one). */
+size_t qgemm_workspace_bytes(const qgemm_plan *plan, int64_t B);
+
+/* qgemm_run with a caller-owned workspace (device memory, 256-byte aligned).
+ * With at least qgemm_workspace_bytes(plan, B) bytes, the small-batch tier
+ * splits K over several workgroups per output tile; the last workgroup of a
+ * tile to finish adds the partial tiles in a fixed order, so results stay
+ * deterministic (they can differ in rounding from the unsplit route).
+ * Contract: the workspace must be all zero before its first use; every call
+ * returns its counter words to zero, so it can be reused by later calls on
+ * the same stream (any plan).  Calls that may overlap in time need distinct
+ * workspaces.  A NULL or smaller workspace selects the unsplit route. */
+int qgemm_run_ws(const qgemm_plan *plan, int64_t B, const void *w, const void *x, void *y,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* The tier qgemm_run would use for B (QGEMM_TIER_*), or 0 for a bad plan. */
+int qgemm_plan_tier(const qgemm_plan *plan, int64_t B);
+
+/* Release a plan (NULL is accepted). */
+int qgemm_destroy(qgemm_plan *plan);
+
+/* Device decode of a packed buffer to fp32 w_out[N][K] (device pointer),
+ * using the kernels' own decoders: Q8_0 d*q; MXFP4 E2M1 * 2^(e-127); NVFP4
+ * g * (E2M1 * E4M3) rounded once to fp32.  Every value except the NVFP4
+ * product with g is exact. */
+int qgemm_dequantize(qgemm_format fmt, const void *w, float *w_out, int64_t N, int64_t K,
+                     void *stream);
+
+/* Text for a status code (static storage). */
+const char *qgemm_strerror(int status);
+
+/* Message of the last failure on the calling thread ("" if none). */
+const char *qgemm_last_error(void);
+
+/* Library version, (major << 16) | minor. */
+int qgemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMM_H */

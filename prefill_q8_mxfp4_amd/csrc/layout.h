@@ -1,0 +1,63 @@
+// Packed weight layout of the library (host and device side).
+//
+// Row tiles of 16 rows; slabs of KS weights along K (64 for Q8_0, 128 for the
+// FP4 formats), 1024 bytes each, laid out so that 16-byte chunk L of a slab is
+// exactly the operand that lane L of a wave feeds to a 16x16x32 bf16 MFMA for
+// each 32-wide unit of the slab (row L % 16, k-group L / 16).  Scales follow
+// in a row-major region; NVFP4 adds a 256-byte tensor-scale record.
+#pragma once
+#include <stdint.h>
+
+#include "../../include/qgemm.h"
+
+namespace qg {
+
+enum { FMT_Q8 = 0, FMT_MX = 1, FMT_NV = 2 };
+
+struct Layout {
+    int64_t N, K;
+    int64_t Np, Kp;      // padded rows (x16) and K (xKS)
+    int64_t KS;          // weights per slab along K
+    int64_t S;           // slabs per row tile
+    int64_t RT;          // row tiles
+    int64_t SP;          // scale row pitch in bytes
+    int64_t scale_off;   // byte offset of the scale region
+    int64_t meta_off;    // byte offset of the NVFP4 tensor-scale record (or -1)
+    int64_t total;       // total bytes
+    int64_t blk;         // weights per scale
+};
+
+static inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+static inline int64_t block_of(int fmt) { return fmt == FMT_NV ? 16 : 32; }
+
+static inline bool make_layout(int fmt, int64_t N, int64_t K, Layout *L)
+{
+    if (fmt < FMT_Q8 || fmt > FMT_NV || N <= 0 || K <= 0)
+        return false;
+    if (K % block_of(fmt))
+        return false;
+    L->N = N;
+    L->K = K;
+    L->blk = block_of(fmt);
+    L->KS = fmt == FMT_Q8 ? 64 : 128;
+    L->Np = round_up(N, 16);
+    L->Kp = round_up(K, L->KS);
+    L->S = L->Kp / L->KS;
+    L->RT = L->Np / 16;
+    int64_t per_row = fmt == FMT_Q8 ? 2 * (L->Kp / 32) : (fmt == FMT_MX ? L->Kp / 32 : L->Kp / 16);
+    L->SP = round_up(per_row, 16);
+    int64_t codes = L->RT * L->S * 1024;
+    L->scale_off = round_up(codes, QGEMM_ALIGN);
+    int64_t end = L->scale_off + L->Np * L->SP;
+    if (fmt == FMT_NV) {
+        L->meta_off = round_up(end, QGEMM_ALIGN);
+        L->total = L->meta_off + 256;
+    } else {
+        L->meta_off = -1;
+        L->total = round_up(end, QGEMM_ALIGN);
+    }
+    return true;
+}
+
+}  // namespace qg

@@ -1,0 +1,200 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+symbol, validates arguments before any HIP call, and packs the documented
+layout.  No compute call is made here."""
+
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import prefill_q8_mxfp4_amd as q
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qgemm.h")
+FACTS = json.load(open(os.path.join(ROOT, "tests", "golden", "page_facts.json")))
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qgemm_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = q.lib()
+    names = _declared()
+    assert set(names) == set(q.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+    assert q.version() == (1, 0)
+
+
+def _create(*args):
+    h = ctypes.c_void_p()
+    st = q.lib().qgemm_create(ctypes.byref(h), *args)
+    return st, h
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 0, 0, 0, 0, 256, 512, 0), q.OK),
+    ((0, 0, 0, 0, 0, 0, 512, 0), q.EINVAL),          # N = 0
+    ((0, 0, 0, 0, 0, 256, -32, 0), q.EINVAL),        # K < 0
+    ((0, 0, 0, 0, 0, 256, 48, 0), q.EINVAL),         # K % 32
+    ((2, 1, 0, 0, 1, 256, 48, 0), q.OK),             # NVFP4: 16-wide blocks
+    ((1, 1, 0, 0, 1, 256, 48, 0), q.EINVAL),         # MXFP4: K % 32
+    ((3, 0, 0, 0, 0, 256, 512, 0), q.EINVAL),        # unknown format
+    ((0, 2, 0, 0, 0, 256, 512, 0), q.EINVAL),        # unknown dtype
+    ((0, 0, 0, 2, 0, 256, 512, 0), q.EINVAL),        # unknown epilogue
+    ((0, 0, 0, 0, 2, 256, 512, 0), q.EINVAL),        # unknown math
+    ((0, 1, 0, 0, 0, 256, 512, 0), q.EINVAL),        # fp32 math with bf16 activations
+    ((2, 1, 1, 1, 1, 255, 512, 0), q.EINVAL),        # SwiGLU with odd N
+    ((2, 1, 1, 1, 1, 40, 512, 0), q.ENOTSUP),        # SwiGLU with N/2 % 16
+    ((0, 0, 0, 0, 0, 256, 512, 3), q.EINVAL),        # both tiers forced
+    ((0, 0, 0, 0, 0, 256, 512, 0x10), q.EINVAL),     # unknown flag
+    ((0, 0, 0, 0, 0, 256, 512, 2), q.ENOTSUP),       # fp32 math in the tiled tier
+    ((2, 1, 1, 1, 1, 64, 512, 1), q.ENOTSUP),        # SwiGLU in the skinny tier
+])
+def test_create_validation(args, status):
+    st, h = _create(*args)
+    assert st == status, q.lib().qgemm_last_error()
+    if st == q.OK:
+        assert h.value
+        assert q.lib().qgemm_destroy(h) == q.OK
+    else:
+        assert not h.value
+        assert q.lib().qgemm_last_error()
+
+
+def test_destroy_null_and_strerror():
+    assert q.lib().qgemm_destroy(None) == q.OK
+    for s in (q.OK, q.EINVAL, q.ENOTSUP, q.EHIP, q.ENOMEM):
+        assert q.lib().qgemm_strerror(s)
+    assert q.lib().qgemm_create(None, 0, 0, 0, 0, 0, 16, 32, 0) == q.EINVAL
+
+
+def test_run_validation_before_any_hip_call():
+    L = q.lib()
+    st, h = _create(0, 0, 0, 0, 0, 256, 512, 0)
+    assert st == q.OK
+    buf = ctypes.create_string_buffer(64)
+    p16 = ctypes.addressof(buf) + (-ctypes.addressof(buf)) % 16
+    assert L.qgemm_run(h, 0, None, None, None, None) == q.OK          # B = 0: no-op
+    assert L.qgemm_run(h, -1, p16, p16, p16, None) == q.EINVAL
+    assert L.qgemm_run(h, 4, None, p16, p16, None) == q.EINVAL
+    assert L.qgemm_run(h, 4, p16 + 4, p16, p16, None) == q.EINVAL       # misaligned
+    assert L.qgemm_run(None, 4, p16, p16, p16, None) == q.EINVAL
+    assert L.qgemm_run(h, 1 << 31, p16, p16, p16, None) == q.EINVAL
+    assert L.qgemm_plan_tier(h, 16) == 1
+    assert L.qgemm_plan_tier(h, 2048) == 1    # fp32 math stays in the skinny tier
+    assert L.qgemm_plan_tier(h, -1) == 0
+    assert L.qgemm_destroy(h) == q.OK
+
+
+def test_tier_choice():
+    p = q.Plan("mxfp4", 5120, 17408, act="bf16")
+    assert p.tier(1) == "skinny" and p.tier(16) == "skinny" and p.tier(2048) == "tiled"
+    p = q.Plan("nvfp4", 2 * 17408, 5120, act="bf16", out="bf16", epilogue="swiglu")
+    assert p.tier(2048) == "tiled" and p.tier(1) == "tiled"
+    p = q.Plan("q8_0", 5120, 5120, act="f32", tier="skinny")
+    assert p.tier(256) == "skinny"
+
+
+def test_weight_bytes_match_format_density():
+    # N, K multiples of the tile: exactly the algorithmic bytes per weight
+    assert q.weight_bytes("q8_0", 5120, 5120) == 5120 * 5120 * 17 // 16
+    assert q.weight_bytes("mxfp4", 5120, 17408) == 5120 * 17408 * 17 // 32
+    assert q.weight_bytes("nvfp4", 34816, 5120) == 34816 * 5120 * 9 // 16 + 256
+    assert q.weight_bytes("q8_0", 16, 48) == 0
+    assert q.weight_bytes("nvfp4", 0, 16) == 0
+
+
+def test_mxfp4_density_matches_page():
+    """HF model card, 'What's 4-bit': 22.7B MXFP4 parameters in 12.05B bytes."""
+    f = FACTS["mxfp4_density"]
+    per_weight = q.weight_bytes("mxfp4", 5120, 17408) / (5120 * 17408)
+    assert abs(per_weight - f["packed_bytes"] / f["params"]) < 0.002
+
+
+def _unpack(fmt, buf, n, k):
+    """Read logical arrays back out of a packed buffer, following the layout
+    the header documents (row tiles of 16, slabs, lane chunks, scale rows)."""
+    ks = 64 if fmt == "q8_0" else 128
+    kp = -(-k // ks) * ks
+    np_ = -(-n // 16) * 16
+    S = kp // ks
+    codes = np.zeros((n, k), dtype=np.int16)
+    for row in range(n):
+        rt, r = divmod(row, 16)
+        for kk in range(k):
+            s, o = divmod(kk, ks)
+            u, rem = divmod(o, 32)
+            g, j = divmod(rem, 8)
+            base = (rt * S + s) * 1024 + (g * 16 + r) * 16
+            if fmt == "q8_0":
+                codes[row, kk] = np.int8(buf[base + 8 * u + j].view(np.int8))
+            else:
+                byte = int(buf[base + 4 * u + j // 2])
+                codes[row, kk] = (byte >> (4 * (j & 1))) & 15
+    per = {"q8_0": 2 * kp // 32, "mxfp4": kp // 32, "nvfp4": kp // 16}[fmt]
+    sp = -(-per // 16) * 16
+    soff = -(-(np_ // 16) * S * 1024 // 256) * 256
+    nsc = k // (16 if fmt == "nvfp4" else 32)
+    esz = 2 if fmt == "q8_0" else 1
+    sc = np.stack([buf[soff + row * sp: soff + row * sp + nsc * esz] for row in range(n)])
+    if fmt == "q8_0":
+        sc = sc.view(np.uint16)
+    return codes, sc, soff + np_ * sp
+
+
+@pytest.mark.parametrize("fmt,n,k", [("q8_0", 37, 96), ("mxfp4", 21, 160), ("nvfp4", 18, 144)])
+def test_pack_layout_roundtrip(fmt, n, k):
+    rng = np.random.default_rng(0)
+    if fmt == "q8_0":
+        codes = rng.integers(-128, 128, (n, k)).astype(np.int8)
+        scales = rng.integers(0, 65536, (n, k // 32)).astype(np.uint16)
+        g = None
+    else:
+        codes = rng.integers(0, 16, (n, k)).astype(np.uint8)
+        scales = rng.integers(0, 256, (n, k // (16 if fmt == "nvfp4" else 32))).astype(np.uint8)
+        g = np.array([0.5, 2.0], dtype=np.float32) if fmt == "nvfp4" else None
+    buf = q.pack(fmt, n, k, codes, scales, g)
+    assert buf.size == q.weight_bytes(fmt, n, k)
+    c2, s2, meta = _unpack(fmt, buf, n, k)
+    assert np.array_equal(c2, codes.astype(np.int16))
+    assert np.array_equal(s2, scales)
+    if fmt == "nvfp4":
+        meta = -(-meta // 256) * 256
+        hdr = buf[meta:meta + 16].view(np.int32)
+        assert list(hdr) == [2, n // 2, 0, 0]
+        assert np.array_equal(buf[meta + 16:meta + 24].view(np.float32), g)
+
+
+def test_pack_rejects_bad_input():
+    codes = np.zeros((16, 32), dtype=np.uint8)
+    codes[3, 4] = 16
+    with pytest.raises(q.QgemmError):
+        q.pack("mxfp4", 16, 32, codes, np.zeros((16, 1), np.uint8))
+    with pytest.raises(q.QgemmError):   # NVFP4 without tensor scales
+        q.pack("nvfp4", 16, 32, np.zeros((16, 32), np.uint8), np.zeros((16, 2), np.uint8))
+    with pytest.raises(q.QgemmError):   # tensor count must divide N
+        q.pack("nvfp4", 16, 32, np.zeros((16, 32), np.uint8), np.zeros((16, 2), np.uint8),
+               np.ones(3, np.float32))
+
+
+def test_plan_errors_raise():
+    with pytest.raises(q.QgemmError) as e:
+        q.Plan("q8_0", 256, 48, act="f32")
+    assert e.value.status == q.EINVAL
+    with pytest.raises(q.QgemmError) as e:
+        q.Plan("q8_0", 256, 512, act="f32", math="fp32", tier="tiled")
+    assert e.value.status == q.ENOTSUP
+
+
+def test_synth_configs_pack():
+    w = synth.gen_config_weights("cfg1")
+    buf = q.pack_logical(w)
+    assert buf.size == q.weight_bytes("q8_0", 256, 512)

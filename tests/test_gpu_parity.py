@@ -1,0 +1,332 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs.  Tolerances (relative Frobenius error against the
+unrounded fp64 oracle): 1e-5 for fp32 math, 1e-2 for bf16 math.  Decoded
+weights, exact closed forms, one-hot read-outs and batch chunking are
+compared bit for bit."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import prefill_q8_mxfp4_amd as q
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL_FP32 = 1e-5
+TOL_BF16 = 1e-2
+
+
+def _dev():
+    return torch.device("cuda:0")
+
+
+def w_dev(w):
+    return torch.from_numpy(q.pack_logical(w)).to(_dev())
+
+
+def x_dev(x):
+    if x.dtype == np.float32:
+        return torch.from_numpy(np.ascontiguousarray(x)).to(_dev())
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(_dev())
+
+
+def y_new(plan, B, fill=float("nan")):
+    dt = torch.float32 if plan.out == "f32" else torch.bfloat16
+    return torch.full((B, plan.out_cols), fill, dtype=dt, device=_dev())
+
+
+def host(y):
+    return y.float().cpu().numpy().astype(np.float64)
+
+
+def run(plan, x, wd, B=None, workspace="auto"):
+    B = x.shape[0] if B is None else B
+    xd = x_dev(x)
+    y = y_new(plan, B)
+    plan.run(xd, wd, y, B=B, workspace=workspace)
+    torch.cuda.synchronize()
+    return host(y)
+
+
+# ----------------------------------------------------------- dequantize
+
+def _edge_weights(fmt, n, k, rng):
+    if fmt == "q8_0":
+        codes = rng.integers(-128, 128, (n, k)).astype(np.int8)
+        d = rng.standard_normal((n, k // 32)).astype(np.float16).view(np.uint16)
+        d.flat[:6] = [0x0001, 0x03FF, 0x7BFF, 0xFBFF, 0x8000, 0x0400]  # subnormal, max, -0
+        return {"fmt": fmt, "codes": codes, "scales": d, "g": None}
+    codes = rng.integers(0, 16, (n, k)).astype(np.uint8)
+    if fmt == "mxfp4":
+        e = rng.integers(100, 150, (n, k // 32)).astype(np.uint8)
+        e.flat[:6] = [0, 1, 2, 127, 253, 255]
+        return {"fmt": fmt, "codes": codes, "scales": e, "g": None}
+    s = rng.integers(0, 256, (n, k // 16)).astype(np.uint8)
+    s.flat[:6] = [0x00, 0x01, 0x07, 0x7E, 0x7F, 0xFF]
+    return {"fmt": fmt, "codes": codes, "scales": s,
+            "g": np.array([0.75, 3.0e-5], dtype=np.float32)}
+
+
+@pytest.mark.parametrize("fmt,n,k", [("q8_0", 100, 96), ("mxfp4", 98, 160), ("nvfp4", 98, 144),
+                                     ("q8_0", 256, 512), ("mxfp4", 64, 17408 // 8)])
+def test_dequantize_bit_exact(fmt, n, k):
+    rng = np.random.default_rng(n + k)
+    w = _edge_weights(fmt, n, k, rng)
+    got = q.dequantize(fmt, w_dev(w), n, k).cpu().numpy()
+    with np.errstate(over="ignore", invalid="ignore"):
+        ref = oracle.dequant(w, apply_g=True).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+# ------------------------------------------------ small workload (cfg1)
+
+def test_q8_0_256x512_b70_fp32():
+    c = synth.CONFIGS["cfg1"]
+    w = synth.gen_config_weights("cfg1")
+    x = synth.gen_config_x("cfg1", 70)
+    plan = q.Plan("q8_0", c["N"], c["K"], act="f32", out="f32", math="fp32")
+    y = run(plan, x, w_dev(w))
+    err = oracle.rel_fro(y, oracle.gemm(w, x))
+    print(f"cfg1 B=70 rel_fro={err:.3e}")
+    assert err <= TOL_FP32
+
+
+# ------------------------------------------- attention projection sweep
+
+@pytest.fixture(scope="module")
+def cfg2():
+    w = synth.gen_config_weights("cfg2")
+    x = synth.gen_config_x("cfg2", 256)
+    ref = oracle.gemm(w, x)  # rows are independent: prefixes serve every B
+    return w, x, ref, w_dev(w)
+
+
+@pytest.mark.parametrize("B", synth.CONFIGS["cfg2"]["Bs"])
+def test_q8_0_5120_sweep_fp32(cfg2, B):
+    w, x, ref, wd = cfg2
+    plan = q.Plan("q8_0", 5120, 5120, act="f32", out="f32", math="fp32")
+    y = run(plan, x[:B], wd)
+    err = oracle.rel_fro(y, ref[:B])
+    print(f"cfg2 B={B} tier={plan.tier(B)} rel_fro={err:.3e}")
+    assert err <= TOL_FP32
+
+
+@pytest.mark.parametrize("tier", ["skinny", "tiled"])
+def test_boundary_matrix_chunked_is_bitwise(cfg2, tier):
+    """hipfire PR 'fix(mtp): chunk scalar Q8 batched GEMM above 64 rows',
+    Scalar-Q8 boundary matrix: one call at B = 64/65/70/76/256 equals the
+    same rows computed in contiguous chunks of 64, bit for bit."""
+    w, x, ref, wd = cfg2
+    math = "fp32" if tier == "skinny" else "bf16"
+    plan = q.Plan("q8_0", 5120, 5120, act="f32", out="f32", math=math, tier=tier)
+    for B in (64, 65, 70, 76, 256):
+        whole = run(plan, x[:B], wd, workspace=None)
+        parts = [run(plan, x[r0:min(B, r0 + 64)], wd, workspace=None) for r0 in range(0, B, 64)]
+        assert np.array_equal(whole, np.concatenate(parts, axis=0)), B
+        tol = TOL_FP32 if math == "fp32" else TOL_BF16
+        assert oracle.rel_fro(whole, ref[:B]) <= tol
+
+
+def test_deterministic(cfg2):
+    w, x, ref, wd = cfg2
+    plan = q.Plan("q8_0", 5120, 5120, act="f32", out="f32", math="fp32")
+    for B in (1, 16, 70):
+        assert plan.workspace_bytes(B) > 0
+        assert np.array_equal(run(plan, x[:B], wd), run(plan, x[:B], wd))
+
+
+@pytest.mark.parametrize("B", (1, 16, 65, 256))
+def test_split_k_and_unsplit_agree(cfg2, B):
+    """The K-split route (workspace) and the unsplit route agree with the
+    oracle at every width; counters re-arm so a shared workspace serves calls
+    of several plans in a row."""
+    w, x, ref, wd = cfg2
+    plan = q.Plan("q8_0", 5120, 5120, act="f32", out="f32", math="fp32")
+    ws = torch.zeros(plan.workspace_bytes(256) + (1 << 20), dtype=torch.uint8, device=_dev())
+    for _ in range(3):
+        ysplit = run(plan, x[:B], wd, workspace=ws)
+        assert oracle.rel_fro(ysplit, ref[:B]) <= TOL_FP32
+    yflat = run(plan, x[:B], wd, workspace=None)
+    assert oracle.rel_fro(yflat, ref[:B]) <= TOL_FP32
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(ws[:128]) == 0  # tile counters re-armed
+    # another plan through the same workspace
+    w2 = synth.gen_weights("q8_0", 96, 640, seed=7)
+    x2 = synth.gen_x_f32(B, 640, seed=8)
+    p2 = q.Plan("q8_0", 96, 640, act="f32", out="f32", math="fp32")
+    assert p2.workspace_bytes(B) <= ws.numel()
+    y2 = run(p2, x2, w_dev(w2), workspace=ws)
+    assert oracle.rel_fro(y2, oracle.gemm(w2, x2)) <= TOL_FP32
+
+
+# ------------------------------------------------- exact read-outs
+
+@pytest.mark.parametrize("fmt,act,tier", [("q8_0", "f32", "skinny"), ("mxfp4", "bf16", "skinny"),
+                                          ("nvfp4", "bf16", "skinny"), ("mxfp4", "bf16", "tiled"),
+                                          ("nvfp4", "bf16", "tiled")])
+def test_one_hot_reads_out_decoded_weights(fmt, act, tier):
+    """x = e_j makes y[b][n] = w[n][j]: the decoded weights, read through the
+    whole GEMM path, must be exact."""
+    n, k = 80, 512
+    rng = np.random.default_rng(9)
+    w = _edge_weights(fmt, n, k, rng)
+    # keep scales in a normal range so every product stays exact
+    if fmt == "q8_0":
+        w["scales"] = rng.standard_normal((n, k // 32)).astype(np.float16).view(np.uint16)
+    elif fmt == "mxfp4":
+        w["scales"] = rng.integers(110, 140, (n, k // 32)).astype(np.uint8)
+    else:
+        w["scales"] = rng.integers(1, 0x7E, (n, k // 16)).astype(np.uint8)
+        w["g"] = np.array([1.0, 1.0], dtype=np.float32)
+    cols = [0, 1, 7, 8, 31, 32, 63, 64, 100, 127, 128, 255, 300, 511]
+    xf = np.zeros((len(cols), k), dtype=np.float32)
+    for i, j in enumerate(cols):
+        xf[i, j] = 1.0
+    x = xf if act == "f32" else synth.f32_to_bf16_bits(xf)
+    plan = q.Plan(fmt, n, k, act=act, out="f32", tier=tier)
+    y = run(plan, x, w_dev(w))
+    dq = oracle.dequant(w, apply_g=True)
+    assert np.array_equal(y, dq[:, cols].T.astype(np.float32).astype(np.float64))
+
+
+@pytest.mark.parametrize("tier,math", [("skinny", "fp32"), ("tiled", "bf16")])
+def test_closed_form_constant_is_exact(tier, math):
+    """Constant q = 3, d = 2^-7, x = 0.5 over K = 5120: every output is
+    K*d*q*x = 60 exactly and each row sums to N*K*d*q*x."""
+    n, k, b = 96, 5120, 20
+    w = {"fmt": "q8_0", "codes": np.full((n, k), 3, np.int8),
+         "scales": np.full((n, k // 32), np.float16(2.0 ** -7).view(np.uint16), np.uint16),
+         "g": None}
+    x = np.full((b, k), 0.5, np.float32)
+    plan = q.Plan("q8_0", n, k, act="f32", out="f32", math=math, tier=tier)
+    y = run(plan, x, w_dev(w))
+    assert np.all(y == 60.0)
+    assert np.all(y.sum(axis=1) == n * k * 2.0 ** -7 * 3 * 0.5)
+
+
+# ------------------------------------------------------ ragged shapes
+
+@pytest.mark.parametrize("fmt,act,math,out", [
+    ("q8_0", "f32", "fp32", "f32"), ("q8_0", "f32", "bf16", "f32"), ("q8_0", "bf16", "bf16", "bf16"),
+    ("mxfp4", "bf16", "bf16", "f32"), ("mxfp4", "f32", "fp32", "f32"),
+    ("nvfp4", "bf16", "bf16", "f32"), ("nvfp4", "f32", "fp32", "bf16")])
+@pytest.mark.parametrize("tier", ["skinny", "tiled"])
+def test_ragged_shapes(fmt, act, math, out, tier):
+    if tier == "tiled" and math == "fp32":
+        pytest.skip("fp32 math runs in the skinny tier only")
+    n = 100
+    k = {"q8_0": 96, "mxfp4": 160, "nvfp4": 144}[fmt]
+    w = synth.gen_weights(fmt, n, k, seed=1)
+    for B in (1, 3, 17, 33, 65, 130):
+        xf = synth.gen_x_f32(B, k, seed=2)
+        x = xf if act == "f32" else synth.f32_to_bf16_bits(xf)
+        plan = q.Plan(fmt, n, k, act=act, out=out, math=math, tier=tier)
+        y = run(plan, x, w_dev(w))
+        tol = TOL_FP32 if (math == "fp32" and out == "f32") else TOL_BF16
+        err = oracle.rel_fro(y, oracle.gemm(w, x))
+        assert err <= tol, (B, err)
+
+
+def test_b_zero_is_a_noop():
+    w = synth.gen_weights("q8_0", 32, 64, seed=1)
+    plan = q.Plan("q8_0", 32, 64, act="f32")
+    y = torch.full((1, 32), 7.0, device=_dev())
+    plan.run(torch.zeros((1, 64), device=_dev()), w_dev(w), y, B=0)
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
+
+
+# ------------------------------------- prefill workloads, sampled outputs
+
+def _samples(B, ncols, count, seed):
+    rng = np.random.default_rng(seed)
+    bi = rng.integers(0, B, count)
+    ni = rng.integers(0, ncols, count)
+    # always include the corners and the ragged edges
+    bi[:4] = [0, B - 1, 0, B - 1]
+    ni[:4] = [0, 0, ncols - 1, ncols - 1]
+    return bi, ni
+
+
+def test_q8_0_ffn_prefill_2048_bf16():
+    c = synth.CONFIGS["cfg3"]
+    w = synth.gen_config_weights("cfg3")
+    x = synth.gen_config_x("cfg3", 2048)
+    plan = q.Plan("q8_0", c["N"], c["K"], act="f32", out="f32", math="bf16")
+    assert plan.tier(2048) == "tiled"
+    y = run(plan, x, w_dev(w))
+    assert np.all(np.isfinite(y))
+    bi, ni = _samples(2048, c["N"], 6000, 3)
+    err = oracle.rel_fro(y[bi, ni], oracle.gemm_at(w, x, bi, ni))
+    print(f"cfg3 rel_fro(sampled)={err:.3e}")
+    assert err <= TOL_BF16
+
+
+@pytest.fixture(scope="module")
+def cfg4():
+    w = synth.gen_config_weights("cfg4")
+    x = synth.gen_config_x("cfg4", 2048)
+    return w, x, w_dev(w)
+
+
+@pytest.mark.parametrize("B", synth.CONFIGS["cfg4"]["Bs"])
+def test_mxfp4_down_projection(cfg4, B):
+    w, x, wd = cfg4
+    plan = q.Plan("mxfp4", 5120, 17408, act="bf16", out="f32")
+    y = run(plan, x[:B], wd)
+    assert np.all(np.isfinite(y))
+    bi, ni = _samples(B, 5120, 3000, B)
+    err = oracle.rel_fro(y[bi, ni], oracle.gemm_at(w, x[:B], bi, ni))
+    print(f"cfg4 B={B} tier={plan.tier(B)} rel_fro(sampled)={err:.3e}")
+    assert err <= TOL_BF16
+
+
+def test_nvfp4_fused_gate_up_swiglu_2048():
+    c = synth.CONFIGS["cfg5"]
+    w = synth.gen_config_weights("cfg5")
+    x = synth.gen_config_x("cfg5", 2048)
+    plan = q.Plan("nvfp4", c["N"], c["K"], act="bf16", out="bf16", epilogue="swiglu")
+    y = run(plan, x, w_dev(w))
+    assert y.shape == (2048, c["N"] // 2)
+    assert np.all(np.isfinite(y))
+    bi, ji = _samples(2048, c["N"] // 2, 4000, 5)
+    err = oracle.rel_fro(y[bi, ji], oracle.swiglu_at(w, x, bi, ji))
+    print(f"cfg5 rel_fro(sampled)={err:.3e}")
+    assert err <= TOL_BF16
+
+
+def test_swiglu_small_exhaustive():
+    rng = np.random.default_rng(12)
+    nh, k = 48, 160
+    w = _edge_weights("nvfp4", 2 * nh, k, rng)
+    w["scales"] = rng.integers(0x20, 0x50, (2 * nh, k // 16)).astype(np.uint8)
+    w["g"] = np.array([0.01, 0.02], dtype=np.float32)
+    for B in (1, 5, 130):
+        x = synth.gen_x_bf16(B, k, seed=B)
+        plan = q.Plan("nvfp4", 2 * nh, k, act="bf16", out="f32", epilogue="swiglu")
+        y = run(plan, x, w_dev(w))
+        assert oracle.rel_fro(y, oracle.swiglu(w, x)) <= 1e-3
+
+
+@pytest.mark.parametrize("tier", ["skinny", "tiled"])
+def test_mxfp4_extreme_scales_one_hot(tier):
+    """E8M0 scale bytes at both ends of the range (subnormal and near-overflow
+    products) read out exactly through the GEMM path."""
+    n, k = 32, 256
+    rng = np.random.default_rng(21)
+    codes = rng.integers(0, 16, (n, k)).astype(np.uint8)
+    e = rng.choice(np.array([1, 2, 3, 4, 126, 127, 250, 251, 252], dtype=np.uint8), (n, k // 32))
+    w = {"fmt": "mxfp4", "codes": codes, "scales": e, "g": None}
+    cols = [0, 9, 33, 70, 127, 128, 200, 255]
+    xf = np.zeros((len(cols), k), dtype=np.float32)
+    for i, j in enumerate(cols):
+        xf[i, j] = 1.0
+    plan = q.Plan("mxfp4", n, k, act="bf16", out="f32", tier=tier)
+    y = run(plan, synth.f32_to_bf16_bits(xf), w_dev(w))
+    ref = oracle.dequant(w)[:, cols].T.astype(np.float32).astype(np.float64)
+    bad = np.argwhere(y != ref)
+    assert bad.size == 0, [(int(i), int(j), y[i, j], ref[i, j]) for i, j in bad[:8]]
