@@ -169,10 +169,12 @@ size_t qgemm_workspace_bytes(const qgemm_plan *plan, int64_t B);
  * splits K over several workgroups per output tile; the last workgroup of a
  * tile to finish adds the partial tiles in a fixed order, so results stay
  * deterministic (they can differ in rounding from the unsplit route).
- * Contract: the workspace must be all zero before its first use; every call
- * returns its counter words to zero, so it can be reused by later calls on
- * the same stream (any plan).  Calls that may overlap in time need distinct
- * workspaces.  A NULL or smaller workspace selects the unsplit route. */
+ * Contract: the workspace must be all zero before its first use with a plan;
+ * every call returns its counter words to zero, so it can be reused by later
+ * calls of that plan on the same stream, at any B.  A workspace moved to
+ * another plan must be zeroed again.  Calls that may overlap in time need
+ * distinct workspaces.  A NULL or smaller workspace selects the unsplit
+ * route. */
 int qgemm_run_ws(const qgemm_plan *plan, int64_t B, const void *w, const void *x, void *y,
                  void *workspace, size_t workspace_bytes, void *stream);
 

@@ -1,5 +1,7 @@
 """Build libqgemm.so (HIP, gfx950) in-tree with hipcc.
 
+Each tier is its own translation unit, compiled in parallel, then linked:
+
     python -m prefill_q8_mxfp4_amd.build
 """
 
@@ -8,19 +10,22 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
+OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqgemm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+UNITS = ("api.hip", "skinny.hip", "tiled.hip", "dequant.hip")
+HEADERS = ("common.h", "layout.h")
 
 FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Wall",
     "-Wno-unused-function",
     "-Wno-unused-variable",
@@ -31,23 +36,32 @@ FLAGS = [
 
 
 def sources():
-    return [os.path.join(CSRC, f) for f in ("api.hip", "kernels.hip", "layout.h")] + [
-        os.path.join(ROOT, "include", "qgemm.h")]
+    return ([os.path.join(CSRC, f) for f in UNITS + HEADERS]
+            + [os.path.join(ROOT, "include", "qgemm.h")])
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + list(extra) + [os.path.join(CSRC, "api.hip"), "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libqgemm.so")
     noise = [ln for ln in (res.stdout + res.stderr).splitlines()
              if "packed-fp32-ops" not in ln and ln.strip()]
+    if res.returncode != 0:
+        sys.stderr.write("\n".join(noise) + "\n")
+        raise RuntimeError("hipcc failed: " + " ".join(cmd[-3:]))
     if verbose and noise:
         print("\n".join(noise))
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    objs = [os.path.join(OBJ, u.replace(".hip", ".o")) for u in UNITS]
+    cmds = [[HIPCC] + FLAGS + list(extra) + ["-c", os.path.join(CSRC, u), "-o", o]
+            for u, o in zip(UNITS, objs)]
+    with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    tmp = LIB + ".tmp%d" % os.getpid()
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -8,7 +8,7 @@
 
 #include <new>
 
-#include "kernels.hip"
+#include "common.h"
 
 namespace qg {
 
@@ -34,29 +34,13 @@ static const uint32_t PLAN_MAGIC = 0x51474D31u;  // "QGM1"
 
 struct qgemm_plan {
     uint32_t magic;
-    int fmt, act, out, epi, math;
-    int64_t N, K;
     int forced_tier;  // 0 = automatic
-    qg::Layout L;
+    qg::Problem p;
 };
 
 namespace qg {
 
-static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
-
-// ------------------------------------------------------------ dispatch
-
-// ---- skinny tier configuration
-//
-// MB: 16-row batch groups per workgroup; NT: row tiles per wave (a workgroup
-// covers 4*NT); D: weight slabs in flight per wave; ksplit / kc: workgroups
-// per output tile along K and slabs per workgroup.
-
-struct SkCfg {
-    int MB, NT, D;
-    int ngroups, nby, ksplit, kc;
-    int64_t cnt_bytes, part_bytes;
-};
+static bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
 static int env_int(const char *name, int dflt)
 {
@@ -64,33 +48,52 @@ static int env_int(const char *name, int dflt)
     return (v && *v) ? atoi(v) : dflt;
 }
 
-static SkCfg skinny_cfg(const qgemm_plan *p, int64_t B, bool split)
+// ---- small-batch tier shape
+//
+// About SK_WGS workgroups per batch group (enough waves to keep HBM busy):
+// ngroups row groups, and K is split ksplit ways to reach the target when a
+// workspace is available.  The activation stage (kch slabs)
+// is bounded by SK_LDS_MAX; larger ranges are walked in chunks.
+static const int SK_LDS_MAX = 96 * 1024;
+static const int SK_SPLIT_NBY = 8;  // batch groups up to which K is split
+
+static SkCfg skinny_cfg(const Problem &p, int64_t B, bool split)
 {
     SkCfg c;
+    const int nta = p.act == QGEMM_F32 && p.math == QGEMM_MATH_FP32 ? 3 : 1;
     c.MB = B <= 16 ? 1 : (B <= 32 ? 2 : 4);
-    const int U = p->fmt == FMT_Q8 ? 2 : 4;
-    const int nta = p->act == QGEMM_F32 && p->math == QGEMM_MATH_FP32 ? 3 : 1;
-    while (c.MB > 1 && 2 * nta * c.MB * U > 96)  // activation LDS (KB) per workgroup
+    while (c.MB > 1 && skinny_lds_per_slab(p.fmt, nta, c.MB) * SK_RING > SK_LDS_MAX)
         c.MB /= 2;
+    const int per_slab = skinny_lds_per_slab(p.fmt, nta, c.MB);
+    const int kch_max = SK_LDS_MAX / per_slab / SK_RING * SK_RING;  // >= SK_RING by the MB choice
     c.NT = env_int("QGEMM_SK_NT", 2) == 1 ? 1 : 2;
-    c.D = 4;
-    c.ngroups = (int)((p->L.RT + 4 * c.NT - 1) / (4 * c.NT));
+    c.ngroups = (int)((p.L.RT + 4 * c.NT - 1) / (4 * c.NT));
     c.nby = (int)((B + 16 * c.MB - 1) / (16 * c.MB));
-    const int S = (int)p->L.S;
-    c.ksplit = 1;
-    if (split) {
-        const int64_t target = env_int("QGEMM_SK_WGS", 512);
-        const int64_t cols = (int64_t)c.ngroups * c.nby;
-        int64_t ks = (target + cols - 1) / cols;
-        ks = ks < 1 ? 1 : (ks > S ? S : ks);
-        c.ksplit = (int)ks;
+    const int S = (int)p.L.S;
+    // The split depends on N and K only (not on B), so each batch row is
+    // summed in the same order whatever B is, up to SK_SPLIT_NBY batch
+    // groups; larger batches are not split (they have enough tiles).
+    int ks = 1;
+    if (split && c.nby <= SK_SPLIT_NBY) {
+        const int64_t target = env_int("QGEMM_SK_WGS", 256);
+        const int64_t k = (target + c.ngroups - 1) / c.ngroups;
+        ks = (int)(k < 1 ? 1 : (k > S ? S : k));
     }
-    c.kc = (S + c.ksplit - 1) / c.ksplit;
-    c.kc = (c.kc + c.D - 1) / c.D * c.D;  // the kernel walks whole rings of D slabs
+    c.kc = (S + ks - 1) / ks;
+    c.kc = (c.kc + SK_RING - 1) / SK_RING * SK_RING;
+    if (c.kc <= kch_max) {
+        c.kch = c.kc;
+    } else {
+        c.kch = kch_max;
+        c.kc = (c.kc + c.kch - 1) / c.kch * c.kch;
+    }
     c.ksplit = (S + c.kc - 1) / c.kc;
+    c.lds = c.kch * per_slab;
     if (c.ksplit > 1) {
         const int64_t tiles = (int64_t)c.nby * c.ngroups * 4 * c.MB * c.NT;
-        c.cnt_bytes = round_up((int64_t)c.nby * c.ngroups * 4, 256);
+        // The counter region has the same size for every B, so no call's
+        // partial tiles can land on another call's counters.
+        c.cnt_bytes = round_up((int64_t)SK_SPLIT_NBY * c.ngroups * 4, 256);
         c.part_bytes = (int64_t)c.ksplit * tiles * 1024;
     } else {
         c.cnt_bytes = c.part_bytes = 0;
@@ -98,101 +101,32 @@ static SkCfg skinny_cfg(const qgemm_plan *p, int64_t B, bool split)
     return c;
 }
 
-template <int FMT, int ACT, int NTERM, int MB, int NT, int OUTT>
-static void launch_skinny_k(const KArgs &a, const SkCfg &c, const SkinnyWs &ws, hipStream_t st)
+static int choose_tier(const qgemm_plan *plan, int64_t B)
 {
-    dim3 grid(c.ngroups, c.ksplit, c.nby);
-    hipLaunchKernelGGL((skinny_kernel<FMT, ACT, NTERM, MB, NT, 4, OUTT>), grid, dim3(256), 0, st, a, ws);
+    const Problem &p = plan->p;
+    if (plan->forced_tier)
+        return plan->forced_tier;
+    if (p.math == QGEMM_MATH_FP32)
+        return QGEMM_TIER_SKINNY;  // the only tier with the fp32-faithful split
+    if (p.epi == QGEMM_EPI_SWIGLU)
+        return QGEMM_TIER_TILED;   // the fused gate+up epilogue
+    return B <= 64 ? QGEMM_TIER_SKINNY : QGEMM_TIER_TILED;
 }
 
-template <int FMT, int ACT, int NTERM, int OUTT>
-static void launch_skinny_t(const KArgs &a, const SkCfg &c, const SkinnyWs &ws, hipStream_t st)
-{
-#define QG_S(MB, NT) launch_skinny_k<FMT, ACT, NTERM, MB, NT, OUTT>(a, c, ws, st)
-    if (c.NT == 1) {
-        if (c.MB == 1) QG_S(1, 1); else if (c.MB == 2) QG_S(2, 1); else QG_S(4, 1);
-    } else {
-        if (c.MB == 1) QG_S(1, 2); else if (c.MB == 2) QG_S(2, 2); else QG_S(4, 2);
-    }
-#undef QG_S
-}
-
-template <int FMT>
-static void launch_skinny_f(const qgemm_plan *p, const KArgs &a, const SkCfg &c, const SkinnyWs &ws,
-                            hipStream_t st, int nterm)
-{
-    const bool f32 = p->act == QGEMM_F32, o32 = p->out == QGEMM_F32;
-    if (!f32) {
-        if (o32) launch_skinny_t<FMT, ACT_BF16, 1, OUT_F32>(a, c, ws, st);
-        else launch_skinny_t<FMT, ACT_BF16, 1, OUT_BF16>(a, c, ws, st);
-    } else if (nterm == 1) {
-        if (o32) launch_skinny_t<FMT, ACT_F32, 1, OUT_F32>(a, c, ws, st);
-        else launch_skinny_t<FMT, ACT_F32, 1, OUT_BF16>(a, c, ws, st);
-    } else if (nterm == 2) {
-        if (o32) launch_skinny_t<FMT, ACT_F32, 2, OUT_F32>(a, c, ws, st);
-        else launch_skinny_t<FMT, ACT_F32, 2, OUT_BF16>(a, c, ws, st);
-    } else {
-        if (o32) launch_skinny_t<FMT, ACT_F32, 3, OUT_F32>(a, c, ws, st);
-        else launch_skinny_t<FMT, ACT_F32, 3, OUT_BF16>(a, c, ws, st);
-    }
-}
-
-constexpr int TBM = 128, TBN = 128, TWM = 2, TWN = 2;
-
-template <int FMT, int ACT, int OUTT, bool DUAL>
-static void launch_tiled_t(const KArgs &a, hipStream_t st, int Nh)
-{
-    const int mtiles = (a.B + TBM - 1) / TBM;
-    const int nrows = DUAL ? Nh : a.N;
-    const int ntiles = (nrows + TBN - 1) / TBN;
-    dim3 grid(mtiles * ntiles);
-    hipLaunchKernelGGL((tiled_kernel<FMT, ACT, OUTT, DUAL, TBM, TBN, TWM, TWN>), grid,
-                       dim3(TWM * TWN * 64), 0, st, a, Nh, mtiles, ntiles);
-}
-
-template <int FMT>
-static void launch_tiled_f(const qgemm_plan *p, const KArgs &a, hipStream_t st)
-{
-    const bool f32 = p->act == QGEMM_F32, o32 = p->out == QGEMM_F32;
-    const bool dual = p->epi == QGEMM_EPI_SWIGLU;
-    const int Nh = (int)(p->N / 2);
-#define QG_T(A, O, D) launch_tiled_t<FMT, A, O, D>(a, st, Nh)
-    if (f32) {
-        if (o32) { if (dual) QG_T(ACT_F32, OUT_F32, true); else QG_T(ACT_F32, OUT_F32, false); }
-        else { if (dual) QG_T(ACT_F32, OUT_BF16, true); else QG_T(ACT_F32, OUT_BF16, false); }
-    } else {
-        if (o32) { if (dual) QG_T(ACT_BF16, OUT_F32, true); else QG_T(ACT_BF16, OUT_F32, false); }
-        else { if (dual) QG_T(ACT_BF16, OUT_BF16, true); else QG_T(ACT_BF16, OUT_BF16, false); }
-    }
-#undef QG_T
-}
-
-static int choose_tier(const qgemm_plan *p, int64_t B)
-{
-    if (p->forced_tier)
-        return p->forced_tier;
-    if (p->math == QGEMM_MATH_FP32 || p->epi == QGEMM_EPI_NONE) {
-        if (p->math == QGEMM_MATH_FP32)
-            return QGEMM_TIER_SKINNY;
-        return B <= 64 ? QGEMM_TIER_SKINNY : QGEMM_TIER_TILED;
-    }
-    return QGEMM_TIER_TILED;  // fused gate+up
-}
-
-static KArgs make_args(const qgemm_plan *p, int64_t B, const void *w, const void *x, void *y)
+static KArgs make_args(const Problem &p, int64_t B, const void *w, const void *x, void *y)
 {
     KArgs a;
     a.w = (const uint8_t *)w;
     a.x = x;
     a.y = y;
     a.B = (int)B;
-    a.N = (int)p->N;
-    a.K = (int)p->K;
-    a.S = (int)p->L.S;
-    a.RT = (int)p->L.RT;
-    a.SP = (int)p->L.SP;
-    a.scale_off = p->L.scale_off;
-    a.meta_off = p->L.meta_off;
+    a.N = (int)p.N;
+    a.K = (int)p.K;
+    a.S = (int)p.L.S;
+    a.RT = (int)p.L.RT;
+    a.SP = (int)p.L.SP;
+    a.scale_off = p.L.scale_off;
+    a.meta_off = p.L.meta_off;
     return a;
 }
 
@@ -332,15 +266,15 @@ int qgemm_create(qgemm_plan **plan, qgemm_format fmt, qgemm_dtype act, qgemm_dty
     if (!p)
         return fail(QGEMM_ENOMEM, "qgemm_create: out of host memory");
     p->magic = PLAN_MAGIC;
-    p->fmt = (int)fmt;
-    p->act = (int)act;
-    p->out = (int)out;
-    p->epi = (int)epi;
-    p->math = (int)math;
-    p->N = N;
-    p->K = K;
     p->forced_tier = forced;
-    make_layout((int)fmt, N, K, &p->L);
+    p->p.fmt = (int)fmt;
+    p->p.act = (int)act;
+    p->p.out = (int)out;
+    p->p.epi = (int)epi;
+    p->p.math = (int)math;
+    p->p.N = N;
+    p->p.K = K;
+    make_layout((int)fmt, N, K, &p->p.L);
     *plan = p;
     return QGEMM_OK;
 }
@@ -369,7 +303,7 @@ size_t qgemm_workspace_bytes(const qgemm_plan *plan, int64_t B)
         return 0;
     if (choose_tier(plan, B) != QGEMM_TIER_SKINNY)
         return 0;
-    const SkCfg c = skinny_cfg(plan, B, true);
+    const SkCfg c = skinny_cfg(plan->p, B, true);
     return (size_t)(c.cnt_bytes + c.part_bytes);
 }
 
@@ -378,6 +312,7 @@ int qgemm_run_ws(const qgemm_plan *plan, int64_t B, const void *w, const void *x
 {
     if (!plan || plan->magic != PLAN_MAGIC)
         return fail(QGEMM_EINVAL, "qgemm_run: not a live plan");
+    const Problem &p = plan->p;
     if (B < 0)
         return fail(QGEMM_EINVAL, "qgemm_run: B=%lld < 0", (long long)B);
     if (B > (1ll << 30))
@@ -390,40 +325,32 @@ int qgemm_run_ws(const qgemm_plan *plan, int64_t B, const void *w, const void *x
         return fail(QGEMM_EINVAL, "qgemm_run: w, x and y must be 16-byte aligned");
     if (workspace && ((uintptr_t)workspace & 255u))
         return fail(QGEMM_EINVAL, "qgemm_run: workspace must be 256-byte aligned");
-    const int64_t ncols = plan->epi == QGEMM_EPI_SWIGLU ? plan->N / 2 : plan->N;
-    if (B * plan->K > (1ll << 31) - 1 || B * ncols > (1ll << 31) - 1)
+    const int64_t ncols = p.epi == QGEMM_EPI_SWIGLU ? p.N / 2 : p.N;
+    if (B * p.K > (1ll << 31) - 1 || B * ncols > (1ll << 31) - 1)
         return fail(QGEMM_EINVAL, "qgemm_run: B*K or B*N above 2^31 elements");
-    const KArgs a = make_args(plan, B, w, x, y);
+    const KArgs a = make_args(p, B, w, x, y);
     hipStream_t st = (hipStream_t)stream;
-    const int tier = choose_tier(plan, B);
-    if (tier == QGEMM_TIER_SKINNY) {
-        SkCfg c = skinny_cfg(plan, B, workspace != nullptr);
+    hipError_t e;
+    if (choose_tier(plan, B) == QGEMM_TIER_SKINNY) {
+        SkCfg c = skinny_cfg(p, B, workspace != nullptr);
         if (c.ksplit > 1 && (size_t)(c.cnt_bytes + c.part_bytes) > ws_bytes)
-            c = skinny_cfg(plan, B, false);  // workspace too small: no K split
+            c = skinny_cfg(p, B, false);  // workspace too small: no K split
         if (c.nby > 65535)
-            return fail(QGEMM_EINVAL, "qgemm_run: B=%lld exceeds the skinny tier's grid",
+            return fail(QGEMM_EINVAL, "qgemm_run: B=%lld exceeds the small-batch tier's grid",
                         (long long)B);
         SkinnyWs ws;
         ws.cnt = c.ksplit > 1 ? (uint32_t *)workspace : nullptr;
         ws.part = c.ksplit > 1 ? (float *)((uint8_t *)workspace + c.cnt_bytes) : nullptr;
         ws.ksplit = c.ksplit;
         ws.kc = c.kc;
-        const int nterm = plan->math == QGEMM_MATH_BF16 ? 1 : env_int("QGEMM_FP32_TERMS", 3);
+        ws.kch = c.kch;
+        const int nterm = p.math == QGEMM_MATH_BF16 ? 1 : env_int("QGEMM_FP32_TERMS", 3);
         if (nterm < 1 || nterm > 3)
             return fail(QGEMM_EINVAL, "qgemm_run: QGEMM_FP32_TERMS must be 1..3");
-        switch (plan->fmt) {
-        case FMT_Q8: launch_skinny_f<FMT_Q8>(plan, a, c, ws, st, nterm); break;
-        case FMT_MX: launch_skinny_f<FMT_MX>(plan, a, c, ws, st, nterm); break;
-        default: launch_skinny_f<FMT_NV>(plan, a, c, ws, st, nterm); break;
-        }
+        e = launch_skinny(p, a, c, ws, nterm, st);
     } else {
-        switch (plan->fmt) {
-        case FMT_Q8: launch_tiled_f<FMT_Q8>(plan, a, st); break;
-        case FMT_MX: launch_tiled_f<FMT_MX>(plan, a, st); break;
-        default: launch_tiled_f<FMT_NV>(plan, a, st); break;
-        }
+        e = launch_tiled(p, a, st);
     }
-    hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return hip_fail(e, "qgemm_run: kernel launch");
     return QGEMM_OK;
@@ -457,17 +384,9 @@ int qgemm_dequantize(qgemm_format fmt, const void *w, float *w_out, int64_t N, i
     a.SP = (int)L.SP;
     a.scale_off = L.scale_off;
     a.meta_off = L.meta_off;
-    const int64_t threads = N * (K / 8);
-    dim3 grid((unsigned)((threads + 255) / 256));
-    hipStream_t st = (hipStream_t)stream;
-    switch ((int)fmt) {
-    case FMT_Q8: hipLaunchKernelGGL(dequant_kernel<FMT_Q8>, grid, dim3(256), 0, st, a, w_out); break;
-    case FMT_MX: hipLaunchKernelGGL(dequant_kernel<FMT_MX>, grid, dim3(256), 0, st, a, w_out); break;
-    default: hipLaunchKernelGGL(dequant_kernel<FMT_NV>, grid, dim3(256), 0, st, a, w_out); break;
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return hip_fail(e, "qgemm_dequantize: kernel launch");
+    hipError_t e0 = launch_dequant((int)fmt, a, w_out, (hipStream_t)stream);
+    if (e0 != hipSuccess)
+        return hip_fail(e0, "qgemm_dequantize: kernel launch");
     return QGEMM_OK;
 }
 

@@ -1,0 +1,246 @@
+// Shared device code of the block-quantized-weight batched GEMM on gfx950
+// (CDNA4),
+//
+//   y[b][n] = sum_k x[b][k] * w[n][k],
+//
+// used by every tier: operand types, the per-format decoders, the split of
+// fp32 activations into bf16 terms, the MFMA wrapper, epilogue helpers and the
+// launch interface the host side (api.hip) calls.
+//
+// Block scales.  Where a tier keeps weights exact in its MFMA operand, int8 q
+// and E2M1 codes are exact in bf16 and the fp32 block scale multiplies the
+// fp32 partial of each 32-wide block.  NVFP4 (16-wide blocks) folds its E4M3
+// scale into the operand (E2M1 x E4M3 is exact in bf16); the large-batch tier
+// folds every format's scale into the bf16 operand (exact for the FP4
+// formats; a Q8_0 weight d*q is rounded once to bf16 there).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "layout.h"
+
+namespace qg {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+enum { ACT_F32 = 0, ACT_BF16 = 1 };
+enum { OUT_F32 = 0, OUT_BF16 = 1 };
+
+struct KArgs {
+    const uint8_t *w;
+    const void *x;
+    void *y;
+    int B, N, K;
+    int S;              // slabs per row tile
+    int RT;             // row tiles
+    int SP;             // scale pitch (bytes)
+    int64_t scale_off;  // scale region offset
+    int64_t meta_off;   // NVFP4 tensor-scale record offset (or -1)
+};
+
+// ------------------------------------------------------------ decoders
+
+__device__ __forceinline__ float fp16_bits_to_f32(uint32_t h)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// E8M0 byte -> fp32 2^(e-127); 0 -> 2^-127 (subnormal), 255 -> NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e)
+{
+    uint32_t bits = e == 0 ? 0x00400000u : (e == 255 ? 0x7FC00000u : (e << 23));
+    return __uint_as_float(bits);
+}
+
+// FP8 E4M3 byte -> fp32 (exact).  Subnormals 2^-9 * M; 0x7F / 0xFF -> NaN.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b)
+{
+    uint32_t s = (b & 0x80u) << 24;
+    uint32_t em = b & 0x7Fu;
+    float v;
+    if ((em >> 3) == 0)
+        v = (float)em * 0.001953125f;  // M * 2^-9, exact
+    else
+        v = __uint_as_float(((em >> 3) + 120u) << 23 | (em & 7u) << 20);
+    v = __uint_as_float(__float_as_uint(v) | s);
+    return em == 0x7Fu ? __uint_as_float(0x7FC00000u) : v;
+}
+
+// E2M1 code -> fp32 (exact).
+__device__ __forceinline__ float e2m1_to_f32(uint32_t c)
+{
+    uint32_t m = c & 7u;
+    // magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 as fp32 bit patterns
+    uint32_t bits = m == 0 ? 0u
+                  : m == 1 ? 0x3F000000u
+                  : (((m >> 1) + 126u) << 23) | ((m & 1u) << 22);
+    return __uint_as_float(bits | ((c & 8u) << 28));
+}
+
+// Eight int8 (two dwords) -> bf16x8, exact.
+__device__ __forceinline__ bf16x8 q8_to_bf16(uint32_t lo, uint32_t hi)
+{
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        r[i] = (__bf16)(float)(int8_t)(lo >> (8 * i));
+        r[4 + i] = (__bf16)(float)(int8_t)(hi >> (8 * i));
+    }
+    return r;
+}
+
+// Eight int8 times an fp32 scale -> bf16x8 (one rounding each).
+__device__ __forceinline__ bf16x8 q8_scaled_to_bf16(uint32_t lo, uint32_t hi, float d)
+{
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        r[i] = (__bf16)((float)(int8_t)(lo >> (8 * i)) * d);
+        r[4 + i] = (__bf16)((float)(int8_t)(hi >> (8 * i)) * d);
+    }
+    return r;
+}
+
+// Eight E2M1 codes (one dword, element 2j in the low nibble of byte j) times
+// a power-of-two fp32 scale -> bf16x8, through the gfx950 scaled FP4
+// conversion.  The conversion applies only the exponent of its scale operand
+// (it is built for E8M0 scales), so it serves MXFP4 and unscaled E2M1 only.
+__device__ __forceinline__ bf16x8 fp4_to_bf16(uint32_t v, float scale)
+{
+    bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 0);
+    bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 1);
+    bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 2);
+    bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 3);
+    bf16x8 r;
+    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+    return r;
+}
+
+// Eight E2M1 codes times an arbitrary fp32 scale (an E4M3 block scale) ->
+// bf16x8: codes to fp32 exactly, one fp32 multiply (exact: at most 6
+// significant bits), then a conversion that does not round.
+__device__ __forceinline__ bf16x8 fp4_to_bf16_mul(uint32_t v, float scale)
+{
+    auto f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 0);
+    auto f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 1);
+    auto f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 2);
+    auto f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 3);
+    bf16x8 r;
+    r[0] = (__bf16)(f0[0] * scale); r[1] = (__bf16)(f0[1] * scale);
+    r[2] = (__bf16)(f1[0] * scale); r[3] = (__bf16)(f1[1] * scale);
+    r[4] = (__bf16)(f2[0] * scale); r[5] = (__bf16)(f2[1] * scale);
+    r[6] = (__bf16)(f3[0] * scale); r[7] = (__bf16)(f3[1] * scale);
+    return r;
+}
+
+// ------------------------------------------------ activation operands
+
+// CNT fp32 values -> NT bf16 terms each, whose sum is the fp32 value:
+// NT = 1: nearest bf16; NT = 2: hi + lo, |residual| <= 2^-17 |x|;
+// NT = 3: exact (truncated hi and mid carry 16 bits, the 8-bit rest is exact).
+template <int NT>
+struct Split {
+    bf16x8 t[NT];
+};
+
+template <int NT, int CNT = 8>
+__device__ __forceinline__ Split<NT> split_f32(const float *v)
+{
+    Split<NT> s;
+#pragma unroll
+    for (int i = 0; i < CNT; i++) {
+        float f = v[i];
+        if constexpr (NT == 1) {
+            s.t[0][i] = (__bf16)f;
+        } else if constexpr (NT == 2) {
+            __bf16 h = (__bf16)f;
+            float r = f - (float)h;
+            s.t[0][i] = h;
+            s.t[1][i] = (__bf16)r;
+        } else {
+            float h = __uint_as_float(__float_as_uint(f) & 0xFFFF0000u);
+            float r1 = f - h;
+            float m = __uint_as_float(__float_as_uint(r1) & 0xFFFF0000u);
+            float r2 = r1 - m;
+            s.t[0][i] = (__bf16)h;
+            s.t[1][i] = (__bf16)m;
+            s.t[2][i] = (__bf16)r2;
+        }
+    }
+    return s;
+}
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float silu(float t)
+{
+    return t / (1.0f + __expf(-t));
+}
+
+__device__ __forceinline__ float tensor_scale(const KArgs &a, int n)
+{
+    const int *meta = (const int *)(a.w + a.meta_off);
+    const float *g = (const float *)(a.w + a.meta_off + 16);
+    int rpt = meta[1];
+    return g[n / rpt];
+}
+
+template <int OUTT>
+__device__ __forceinline__ void store_out(void *y, int64_t idx, float v)
+{
+    if constexpr (OUTT == OUT_F32)
+        ((float *)y)[idx] = v;
+    else
+        ((__bf16 *)y)[idx] = (__bf16)v;
+}
+
+// ------------------------------------------------------------ launch API
+// (host side; one translation unit per tier)
+
+struct Problem {
+    int fmt, act, out, epi, math;
+    int64_t N, K;
+    Layout L;
+};
+
+// Small-batch tier shape: MB 16-row batch groups and 4*NT row tiles per
+// workgroup, kc slabs of K per workgroup staged kch at a time, ksplit
+// workgroups per output tile along K; grid ngroups x ksplit x nby.
+constexpr int SK_RING = 8;  // weight slabs in flight per wave
+
+struct SkCfg {
+    int MB, NT;
+    int ngroups, nby, ksplit, kc, kch;
+    int lds;                        // dynamic LDS bytes (activation stage)
+    int64_t cnt_bytes, part_bytes;  // workspace regions (0 without a K split)
+};
+
+// Workspace of the K split: tile counters, then partial tiles.
+struct SkinnyWs {
+    float *part;      // [ksplit][tiles][64 lanes][4]
+    uint32_t *cnt;    // [nby][ngroups], zero between calls
+    int ksplit;
+    int kc;           // a multiple of kch
+    int kch;          // a multiple of SK_RING
+};
+
+// LDS bytes of one staged slab: NTA terms x MB x units x 64 lanes x 16 B.
+__host__ __device__ constexpr int skinny_lds_per_slab(int fmt, int nta, int mb)
+{
+    return nta * mb * (fmt == FMT_Q8 ? 2 : 4) * 64 * 16;
+}
+
+hipError_t launch_skinny(const Problem &p, const KArgs &a, const SkCfg &c, const SkinnyWs &ws,
+                         int nterm, hipStream_t st);
+hipError_t launch_tiled(const Problem &p, const KArgs &a, hipStream_t st);
+hipError_t launch_dequant(int fmt, const KArgs &a, float *out, hipStream_t st);
+
+}  // namespace qg
