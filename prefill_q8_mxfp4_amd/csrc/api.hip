@@ -124,7 +124,7 @@ static KArgs make_args(const Problem &p, int64_t B, const void *w, const void *x
     a.K = (int)p.K;
     a.S = (int)p.L.S;
     a.RT = (int)p.L.RT;
-    a.SP = (int)p.L.SP;
+    a.SG = (int)p.L.SG;
     a.scale_off = p.L.scale_off;
     a.meta_off = p.L.meta_off;
     return a;
@@ -202,11 +202,20 @@ int qgemm_pack(qgemm_format fmt, int64_t N, int64_t K, const void *codes, const 
             }
         }
     }
-    // scales
-    const int64_t nsc = K / L.blk;
-    const int64_t esz = fmt == QGEMM_Q8_0 ? 2 : 1;
-    for (int64_t n = 0; n < N; n++)
-        memcpy(o + L.scale_off + n * L.SP, (const uint8_t *)scales + n * nsc * esz, (size_t)(nsc * esz));
+    // scales: per row and slab, the slab's blocks in k order (blocks past K stay 0)
+    const int64_t nsc = K / L.blk;                       // scales per row
+    const int64_t esz = fmt == QGEMM_Q8_0 ? 2 : 1;        // bytes per scale
+    const int64_t per_slab = L.KS / L.blk;               // scales per row per slab
+    for (int64_t n = 0; n < N; n++) {
+        const uint8_t *src = (const uint8_t *)scales + n * nsc * esz;
+        for (int64_t s = 0; s < L.S; s++) {
+            const int64_t first = s * per_slab;
+            const int64_t cnt = first >= nsc ? 0 : (nsc - first < per_slab ? nsc - first : per_slab);
+            if (cnt > 0)
+                memcpy(o + scale_offset(L.scale_off, L.SG, (int)fmt, n / 16, (int)(n % 16), (int)s),
+                       src + first * esz, (size_t)(cnt * esz));
+        }
+    }
     // tensor scales
     if (fmt == QGEMM_NVFP4) {
         int32_t hdr[4] = {(int32_t)ntensors, (int32_t)(N / ntensors), 0, 0};
@@ -381,7 +390,7 @@ int qgemm_dequantize(qgemm_format fmt, const void *w, float *w_out, int64_t N, i
     a.K = (int)K;
     a.S = (int)L.S;
     a.RT = (int)L.RT;
-    a.SP = (int)L.SP;
+    a.SG = (int)L.SG;
     a.scale_off = L.scale_off;
     a.meta_off = L.meta_off;
     hipError_t e0 = launch_dequant((int)fmt, a, w_out, (hipStream_t)stream);

@@ -37,7 +37,7 @@ struct KArgs {
     int B, N, K;
     int S;              // slabs per row tile
     int RT;             // row tiles
-    int SP;             // scale pitch (bytes)
+    int SG;             // 256-byte scale records per row tile
     int64_t scale_off;  // scale region offset
     int64_t meta_off;   // NVFP4 tensor-scale record offset (or -1)
 };
@@ -183,6 +183,13 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c)
 __device__ __forceinline__ float silu(float t)
 {
     return t / (1.0f + __expf(-t));
+}
+
+// Scales of row r of row tile rt for slab s (see layout.h).
+template <int FMT>
+__device__ __forceinline__ const uint8_t *slab_scales(const KArgs &a, int64_t rt, int r, int s)
+{
+    return a.w + scale_offset(a.scale_off, a.SG, FMT, rt, r, s);
 }
 
 __device__ __forceinline__ float tensor_scale(const KArgs &a, int n)

@@ -20,10 +20,10 @@ __global__ __launch_bounds__(256) void dequant_kernel(KArgs a, float *out)
     const int rt = n / 16, r = n % 16;
     const int L = g * 16 + r;
     const uint8_t *chunk = a.w + (((int64_t)rt * a.S + s) << 10) + (L << 4);
-    const uint8_t *sp = a.w + a.scale_off + (int64_t)n * a.SP;
+    const uint8_t *sp = slab_scales<FMT>(a, rt, r, s);  // this row's scales of slab s
     float v[8];
     if constexpr (FMT == FMT_Q8) {
-        const float d = fp16_bits_to_f32(((const uint16_t *)sp)[k0 / 32]);
+        const float d = fp16_bits_to_f32(((const uint16_t *)sp)[u]);
 #pragma unroll
         for (int j = 0; j < 8; j++)
             v[j] = (float)(int8_t)chunk[8 * u + j] * d;
@@ -31,9 +31,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(KArgs a, float *out)
         const uint32_t codes = *(const uint32_t *)(chunk + 4 * u);
         float sc;
         if constexpr (FMT == FMT_MX)
-            sc = e8m0_to_f32(sp[k0 / 32]);
+            sc = e8m0_to_f32(sp[u]);
         else
-            sc = e4m3_to_f32(sp[k0 / 16]);
+            sc = e4m3_to_f32(sp[(k0 % KS) / 16]);
         float gs = 1.f;
         if constexpr (FMT == FMT_NV)
             gs = tensor_scale(a, n);

@@ -58,7 +58,6 @@ __global__ __launch_bounds__(256) void skinny_kernel(KArgs a, SkinnyWs ws)
     const int s_beg = ks * ws.kc;
     const int s_end = min(a.S, s_beg + ws.kc);
     const int s_last = s_end - 1;
-    const uint8_t *scl = a.w + a.scale_off;
 
     f32x4 acc[MB][NT];
 #pragma unroll
@@ -75,13 +74,13 @@ __global__ __launch_bounds__(256) void skinny_kernel(KArgs a, SkinnyWs ws)
         for (int nt = 0; nt < NT; nt++) {
             const int64_t rt = min(rt0 + nt, a.RT - 1);
             wr[j][nt] = *(const u32x4 *)(a.w + ((rt * a.S + s) << 10) + (lane << 4));
-            const uint8_t *sp = scl + (rt * 16 + r) * (int64_t)a.SP;
+            const uint8_t *sp = slab_scales<FMT>(a, rt, r, s);
             if constexpr (FMT == FMT_NV) {
-                const u32x2 v = *(const u32x2 *)(sp + s * 8);
+                const u32x2 v = *(const u32x2 *)sp;
                 sr[j][nt][0] = v[0];
                 sr[j][nt][1] = v[1];
             } else {
-                sr[j][nt][0] = *(const uint32_t *)(sp + s * 4);
+                sr[j][nt][0] = *(const uint32_t *)sp;
                 sr[j][nt][1] = 0;
             }
         }

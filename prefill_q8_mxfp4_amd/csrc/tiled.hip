@@ -54,7 +54,6 @@ __global__ __launch_bounds__(WM * WN * 64) void tiled_kernel(KArgs a, int Nh, in
     const int n0 = ntl * BN;                       // first row (gate row for DUAL)
     const int rt_base = n0 / 16;
 
-    const uint8_t *scl = a.w + a.scale_off;
 
     // register stage for the next K step.  Loads are unconditional (addresses
     // clamped in bounds); out-of-range activations are zeroed when staged, and
@@ -92,13 +91,13 @@ __global__ __launch_bounds__(WM * WN * 64) void tiled_kernel(KArgs a, int Nh, in
                 rt = rt_base + tr;
             rt = min(rt, a.RT - 1);
             wr[i] = *(const u32x4 *)(a.w + (((int64_t)rt * a.S + s) << 10) + (L << 4));
-            const uint8_t *sp = scl + ((int64_t)rt * 16 + (L & 15)) * a.SP;
+            const uint8_t *sp = slab_scales<FMT>(a, rt, L & 15, s);
             if constexpr (FMT == FMT_NV) {
-                u32x2 v = *(const u32x2 *)(sp + s * 8);
+                const u32x2 v = *(const u32x2 *)sp;
                 sr[i][0] = v[0];
                 sr[i][1] = v[1];
             } else {
-                sr[i][0] = *(const uint32_t *)(sp + s * 4);
+                sr[i][0] = *(const uint32_t *)sp;
                 sr[i][1] = 0;
             }
         }

@@ -139,15 +139,24 @@ def _unpack(fmt, buf, n, k):
             else:
                 byte = int(buf[base + 4 * u + j // 2])
                 codes[row, kk] = (byte >> (4 * (j & 1))) & 15
-    per = {"q8_0": 2 * kp // 32, "mxfp4": kp // 32, "nvfp4": kp // 16}[fmt]
-    sp = -(-per // 16) * 16
+    g = 2 if fmt == "nvfp4" else 4                  # slabs per scale record
+    sg = -(-S // g)                                  # records per row tile
     soff = -(-(np_ // 16) * S * 1024 // 256) * 256
-    nsc = k // (16 if fmt == "nvfp4" else 32)
+    blk = 16 if fmt == "nvfp4" else 32
     esz = 2 if fmt == "q8_0" else 1
-    sc = np.stack([buf[soff + row * sp: soff + row * sp + nsc * esz] for row in range(n)])
+    per_slab = ks // blk
+    nsc = k // blk
+    sc = np.zeros((n, nsc * esz), dtype=np.uint8)
+    for row in range(n):
+        rt, r = divmod(row, 16)
+        for j in range(nsc):
+            s, i = divmod(j, per_slab)
+            q, p = divmod(s, g)
+            off = soff + (rt * sg + q) * 256 + r * 16 + p * per_slab * esz + i * esz
+            sc[row, j * esz:(j + 1) * esz] = buf[off:off + esz]
     if fmt == "q8_0":
         sc = sc.view(np.uint16)
-    return codes, sc, soff + np_ * sp
+    return codes, sc, soff + (np_ // 16) * sg * 256
 
 
 @pytest.mark.parametrize("fmt,n,k", [("q8_0", 37, 96), ("mxfp4", 21, 160), ("nvfp4", 18, 144)])
