@@ -1,96 +1,108 @@
-// Large-batch tier: a BM x BN output tile per workgroup, activation and
-// decoded-weight tiles staged through LDS as bf16 MFMA fragments.
+// Large-batch tier: one BM x BN output tile per workgroup, bf16 MFMA from
+// LDS-staged fragments.
+//
+// 8 waves (two per SIMD, so one wave's MFMAs overlap the other's decode)
+// arranged 2 (batch) x 4 (weight rows); each wave owns BM/2 x 64 outputs as
+// (BM/32) x 4 tiles of v_mfma_f32_16x16x32_bf16.  K advances 64 per step:
+//
+//  * activations: BM x 64 (fp32 input rounded to bf16 on the way);
+//  * weights: BN rows x 64, i.e. one Q8_0 slab or half an FP4 slab of each of
+//    the BN/16 row tiles; a thread's 16-byte (Q8_0) or 8-byte (FP4) piece of a
+//    slab chunk is decoded with its block scale folded in (exact for the FP4
+//    formats, one rounding for Q8_0) into the two bf16 fragments it feeds.
+//
+// LDS holds both operands as 16-byte fragment entries [k-group][row], rows
+// padded by one entry so neither the stage writes nor the fragment reads
+// collide in banks; it is double-buffered, and the next step's global loads
+// are in registers while the current step computes, so each K step needs one
+// barrier.  SwiGLU: the staged rows are BN/2 gate rows j and the BN/2 up rows
+// Nh + j, and every wave owns matching gate and up columns, so G and U of an
+// output sit in the same lane for the epilogue.
 #include "common.h"
 
 namespace qg {
 
-// ================================================================= tiled
-//
-// Workgroup tile BM (batch) x BN (weight rows; for SwiGLU BN gate rows plus
-// the matching BN up rows).  WM x WN waves, each owning (BM/WM) x (BN/WN).
-// K advances one slab (KS) per step.  LDS holds fragments as 16-byte entries
-// [k-group][row] with one spare row per k-group against bank conflicts.
-
-template <int FMT, int ACT, int OUTT, bool DUAL, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(WM * WN * 64) void tiled_kernel(KArgs a, int Nh, int mtiles, int ntiles)
+template <int FMT, int ACT, int OUTT, bool DUAL, int BM>
+__global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles, int ntiles)
 {
-    constexpr int KS = FMT == FMT_Q8 ? 64 : 128;
-    constexpr int U = KS / 32;
-    constexpr int KG = KS / 8;                     // k-groups of 8 per step
-    constexpr int NTHR = WM * WN * 64;
-    constexpr int BNT = DUAL ? 2 * BN : BN;        // weight rows staged
-    constexpr int XS = BM + 1;                     // LDS row pitch (entries)
-    constexpr int WS = BNT + 1;
-    constexpr int TM = BM / WM / 16;               // 16-row MFMA tiles per wave (batch)
-    constexpr int TN = BN / WN / 16;               // 16-col MFMA tiles per wave (rows n)
-    constexpr int XCH = BM * KG / NTHR;            // activation chunks per thread
-    constexpr int WCH = (BNT / 16) * 64 / NTHR;    // weight chunks per thread
-    static_assert(BM * KG % NTHR == 0, "x chunks");
-    static_assert((BNT / 16) * 64 % NTHR == 0, "w chunks");
+    constexpr int BN = 256;                    // staged weight rows
+    constexpr int KT = 64;                     // K per step
+    constexpr int KG = KT / 8;                 // 16-byte k-groups per step
+    constexpr int NTHR = 512;
+    constexpr int XP = BM + 1, WP = BN + 1;    // padded LDS row counts
+    constexpr int TM = BM / 2 / 16;            // 16-row MFMA tiles per wave (batch)
+    constexpr int TN = 4;                      // 16-col MFMA tiles per wave (weights)
+    constexpr int CE = ACT == ACT_F32 ? 4 : 8; // activations per 16-byte load
+    constexpr int XCH = BM * KT / CE / NTHR;   // activation loads per thread per step
+    constexpr int WCH = (BN / 16) * 64 / NTHR; // weight chunks per thread per step (2)
+    constexpr bool FP4 = FMT != FMT_Q8;
+    static_assert(XCH * NTHR * CE == BM * KT, "activation staging");
 
-    __shared__ u32x4 xs[KG * XS];
-    __shared__ u32x4 ws[KG * WS];
+    __shared__ u32x4 xs[2][KG * XP];
+    __shared__ u32x4 ws[2][KG * WP];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wid = tid >> 6;
-    const int wm = wid % WM;
-    const int wn = wid / WM;
+    const int lane = tid & 63, wid = tid >> 6;
+    const int wm = wid & 1, wn = wid >> 1;
 
-    // XCD-aware order: consecutive workgroup ids go to different XCDs, so
-    // give each XCD a contiguous range of tiles; batch tiles vary fastest so
-    // neighbours share a weight tile.
-    const int nwg = gridDim.x;
+    // XCD-aware order: hardware hands consecutive workgroup ids to different
+    // XCDs (id mod 8); give each XCD a contiguous range of tiles, batch tiles
+    // fastest, so the workgroups sharing an XCD's L2 share weight tiles and
+    // the same activation rows.
     int t = blockIdx.x;
     {
+        const int nwg = gridDim.x;
         const int per = (nwg + 7) / 8;
         const int xcd = t % 8, loc = t / 8;
         const int full = nwg % 8 == 0 ? 8 : nwg % 8;  // XCDs that own 'per' tiles
         t = xcd < full ? xcd * per + loc : full * per + (xcd - full) * (per - 1) + loc;
     }
-    const int mt = t % mtiles;
-    const int ntl = t / mtiles;
+    const int mt = t % mtiles, ntl = t / mtiles;
     const int b0 = mt * BM;
-    const int n0 = ntl * BN;                       // first row (gate row for DUAL)
-    const int rt_base = n0 / 16;
+    const int n0 = ntl * (DUAL ? BN / 2 : BN);  // first output column
+    const int nsteps = (a.K + KT - 1) / KT;
 
-
-    // register stage for the next K step.  Loads are unconditional (addresses
-    // clamped in bounds); out-of-range activations are zeroed when staged, and
-    // weight tiles past the last row tile feed columns that are never stored.
-    u32x4 xr[XCH][ACT == ACT_F32 ? 2 : 1];
+    // ---- register stage of one K step (loads clamped in bounds, masked at store)
+    u32x4 xr[XCH];
     bool xin[XCH];
-    u32x4 wr[WCH];
+    uint32_t wr[WCH][FP4 ? 2 : 4];
     uint32_t sr[WCH][2];
 
-    auto load_stage = [&](int s) {
+    auto load_stage = [&](int step) {
+        const int kb = step * KT;
 #pragma unroll
         for (int i = 0; i < XCH; i++) {
             const int c = tid + i * NTHR;
-            const int row = c / KG, kg = c % KG;
+            const int row = c / (KT / CE), k = kb + (c % (KT / CE)) * CE;
             const int b = b0 + row;
-            const int k = s * KS + kg * 8;
-            xin[i] = b < a.B && k < a.K;
-            const int bc = min(b, a.B - 1), kc = min(k, a.K - 8);
-            if constexpr (ACT == ACT_F32) {
-                const float *xp = (const float *)a.x + (int64_t)bc * a.K + kc;
-                xr[i][0] = *(const u32x4 *)xp;
-                xr[i][1] = *(const u32x4 *)(xp + 4);
-            } else {
-                xr[i][0] = *(const u32x4 *)((const uint16_t *)a.x + (int64_t)bc * a.K + kc);
-            }
+            xin[i] = b < a.B && k < a.K;  // K % 16 == 0: a load is all in or all out
+            const int bc = min(b, a.B - 1), kc = min(k, a.K - CE);
+            if constexpr (ACT == ACT_F32)
+                xr[i] = *(const u32x4 *)((const float *)a.x + (int64_t)bc * a.K + kc);
+            else
+                xr[i] = *(const u32x4 *)((const uint16_t *)a.x + (int64_t)bc * a.K + kc);
         }
+        const int s = FP4 ? step >> 1 : step;   // slab
+        const int half = FP4 ? step & 1 : 0;    // which 64 k of an FP4 slab
 #pragma unroll
         for (int i = 0; i < WCH; i++) {
             const int c = tid + i * NTHR;
-            const int tr = c >> 6, L = c & 63;     // staged row tile, lane chunk
+            const int tr = c >> 6, L = c & 63;  // staged row tile, lane chunk
             int rt;
             if constexpr (DUAL)
-                rt = tr < BN / 16 ? rt_base + tr : (Nh / 16) + rt_base + (tr - BN / 16);
+                rt = tr < BN / 32 ? n0 / 16 + tr : (Nh / 16) + n0 / 16 + (tr - BN / 32);
             else
-                rt = rt_base + tr;
+                rt = n0 / 16 + tr;
             rt = min(rt, a.RT - 1);
-            wr[i] = *(const u32x4 *)(a.w + (((int64_t)rt * a.S + s) << 10) + (L << 4));
+            const uint8_t *chunk = a.w + (((int64_t)rt * a.S + s) << 10) + (L << 4);
+            if constexpr (FP4) {
+                const u32x2 v = *(const u32x2 *)(chunk + 8 * half);
+                wr[i][0] = v[0];
+                wr[i][1] = v[1];
+            } else {
+                const u32x4 v = *(const u32x4 *)chunk;
+                wr[i][0] = v[0]; wr[i][1] = v[1]; wr[i][2] = v[2]; wr[i][3] = v[3];
+            }
             const uint8_t *sp = slab_scales<FMT>(a, rt, L & 15, s);
             if constexpr (FMT == FMT_NV) {
                 const u32x2 v = *(const u32x2 *)sp;
@@ -103,158 +115,151 @@ __global__ __launch_bounds__(WM * WN * 64) void tiled_kernel(KArgs a, int Nh, in
         }
     };
 
-    auto store_stage = [&]() {
+    auto store_stage = [&](int buf, int step) {
 #pragma unroll
         for (int i = 0; i < XCH; i++) {
             const int c = tid + i * NTHR;
-            const int row = c / KG, kg = c % KG;
-            u32x4 v;
+            const int row = c / (KT / CE), kk = (c % (KT / CE)) * CE;
+            const u32x4 v = xin[i] ? xr[i] : u32x4{0u, 0u, 0u, 0u};
             if constexpr (ACT == ACT_F32) {
-                float f[8];
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    f[j] = xin[i] ? __uint_as_float(xr[i][0][j]) : 0.f;
-                    f[4 + j] = xin[i] ? __uint_as_float(xr[i][1][j]) : 0.f;
-                }
-                bf16x8 h;
-#pragma unroll
-                for (int j = 0; j < 8; j++)
-                    h[j] = (__bf16)f[j];
-                v = __builtin_bit_cast(u32x4, h);
+                bf16x2 p0, p1;
+                p0[0] = (__bf16)__uint_as_float(v[0]);
+                p0[1] = (__bf16)__uint_as_float(v[1]);
+                p1[0] = (__bf16)__uint_as_float(v[2]);
+                p1[1] = (__bf16)__uint_as_float(v[3]);
+                u32x2 *dst = (u32x2 *)&xs[buf][(kk >> 3) * XP + row] + ((kk & 7) >> 2);
+                *dst = u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
             } else {
-                v = xin[i] ? xr[i][0] : u32x4{0u, 0u, 0u, 0u};
+                xs[buf][(kk >> 3) * XP + row] = v;
             }
-            xs[kg * XS + row] = v;
         }
+        const int half = FP4 ? step & 1 : 0;
 #pragma unroll
         for (int i = 0; i < WCH; i++) {
             const int c = tid + i * NTHR;
             const int tr = c >> 6, L = c & 63;
-            const int row = tr * 16 + (L & 15);
+            const int col = tr * 16 + (L & 15);
             const int g = L >> 4;
 #pragma unroll
-            for (int u = 0; u < U; u++) {
+            for (int ul = 0; ul < 2; ul++) {      // the two 32-wide units of this step
                 bf16x8 h;
                 if constexpr (FMT == FMT_Q8) {
-                    const float d = fp16_bits_to_f32((sr[i][0] >> (16 * u)) & 0xFFFFu);
-                    h = q8_scaled_to_bf16(wr[i][2 * u], wr[i][2 * u + 1], d);
+                    const float d = fp16_bits_to_f32((sr[i][0] >> (16 * ul)) & 0xFFFFu);
+                    h = q8_scaled_to_bf16(wr[i][2 * ul], wr[i][2 * ul + 1], d);
                 } else if constexpr (FMT == FMT_MX) {
-                    h = fp4_to_bf16(wr[i][u], e8m0_to_f32((sr[i][0] >> (8 * u)) & 0xFFu));
+                    const int u = 2 * half + ul;
+                    h = fp4_to_bf16(wr[i][ul], e8m0_to_f32((sr[i][0] >> (8 * u)) & 0xFFu));
                 } else {
+                    const int u = 2 * half + ul;
                     const int si = 2 * u + (g >> 1);
                     const uint32_t sb = (si < 4 ? sr[i][0] >> (8 * si) : sr[i][1] >> (8 * (si - 4))) & 0xFFu;
-                    h = fp4_to_bf16_mul(wr[i][u], e4m3_to_f32(sb));
+                    h = fp4_to_bf16_mul(wr[i][ul], e4m3_to_f32(sb));
                 }
-                ws[(4 * u + g) * WS + row] = __builtin_bit_cast(u32x4, h);
+                ws[buf][(4 * ul + g) * WP + col] = __builtin_bit_cast(u32x4, h);
             }
         }
     };
 
+    // staged column of the wave's n-tile j (SwiGLU: tiles 0,1 gate, 2,3 the
+    // matching up columns)
+    auto wcol = [&](int j) {
+        if constexpr (DUAL)
+            return j < 2 ? wn * 32 + 16 * j : BN / 2 + wn * 32 + 16 * (j - 2);
+        else
+            return wn * 64 + 16 * j;
+    };
+
     f32x4 acc[TM][TN];
-    f32x4 acc2[DUAL ? TM : 1][DUAL ? TN : 1];
 #pragma unroll
     for (int i = 0; i < TM; i++)
 #pragma unroll
-        for (int j = 0; j < TN; j++) {
+        for (int j = 0; j < TN; j++)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if constexpr (DUAL)
-                acc2[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
 
-    const int nsteps = a.S;
     load_stage(0);
-    for (int s = 0; s < nsteps; s++) {
-        __syncthreads();  // previous step's fragment reads are done
-        store_stage();
-        __syncthreads();
-        if (s + 1 < nsteps)
-            load_stage(s + 1);
+    store_stage(0, 0);
+    if (nsteps > 1)
+        load_stage(1);
+    __syncthreads();
+
+    for (int step = 0; step < nsteps; step++) {
+        const int buf = step & 1;
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-            if (s * KS + 32 * u >= a.K)
-                break;
-            const int kg = 4 * u + (lane >> 4);
-            bf16x8 af[TM];
+        for (int kk = 0; kk < 2; kk++) {        // two 32-wide MFMA k-steps
+            const int kg = 4 * kk + (lane >> 4);
+            bf16x8 af[TM], bw[TN];
 #pragma unroll
             for (int i = 0; i < TM; i++)
-                af[i] = __builtin_bit_cast(bf16x8, xs[kg * XS + wm * (BM / WM) + 16 * i + (lane & 15)]);
+                af[i] = __builtin_bit_cast(bf16x8, xs[buf][kg * XP + wm * (BM / 2) + 16 * i + (lane & 15)]);
 #pragma unroll
-            for (int j = 0; j < TN; j++) {
-                const int col = wn * (BN / WN) + 16 * j + (lane & 15);
-                bf16x8 bw = __builtin_bit_cast(bf16x8, ws[kg * WS + col]);
+            for (int j = 0; j < TN; j++)
+                bw[j] = __builtin_bit_cast(bf16x8, ws[buf][kg * WP + wcol(j) + (lane & 15)]);
 #pragma unroll
-                for (int i = 0; i < TM; i++)
-                    acc[i][j] = mfma(af[i], bw, acc[i][j]);
-                if constexpr (DUAL) {
-                    bf16x8 bu = __builtin_bit_cast(bf16x8, ws[kg * WS + BN + col]);
+            for (int i = 0; i < TM; i++)
 #pragma unroll
-                    for (int i = 0; i < TM; i++)
-                        acc2[i][j] = mfma(af[i], bu, acc2[i][j]);
-                }
-            }
+                for (int j = 0; j < TN; j++)
+                    acc[i][j] = mfma(af[i], bw[j], acc[i][j]);
         }
+        if (step + 1 < nsteps)
+            store_stage(buf ^ 1, step + 1);
+        if (step + 2 < nsteps)
+            load_stage(step + 2);
+        __syncthreads();
     }
 
-    // ---- epilogue
+    // ---- epilogue (lane holds rows 4*(lane/16)+e of each 16x16 tile, column lane%16)
 #pragma unroll
-    for (int j = 0; j < TN; j++) {
-        const int col = n0 + wn * (BN / WN) + 16 * j + (lane & 15);
-        if constexpr (DUAL) {
-            if (col >= Nh)
-                continue;
-            float gg = 1.f, gu = 1.f;
-            if constexpr (FMT == FMT_NV) {
-                gg = tensor_scale(a, col);
-                gu = tensor_scale(a, Nh + col);
-            }
-#pragma unroll
-            for (int i = 0; i < TM; i++)
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int b = b0 + wm * (BM / WM) + 16 * i + 4 * (lane >> 4) + e;
-                    if (b < a.B) {
-                        const float G = gg * acc[i][j][e];
-                        const float Uv = gu * acc2[i][j][e];
-                        store_out<OUTT>(a.y, (int64_t)b * Nh + col, silu(G) * Uv);
-                    }
-                }
-        } else {
-            if (col >= a.N)
-                continue;
-            float g = 1.f;
-            if constexpr (FMT == FMT_NV)
-                g = tensor_scale(a, col);
-#pragma unroll
-            for (int i = 0; i < TM; i++)
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int b = b0 + wm * (BM / WM) + 16 * i + 4 * (lane >> 4) + e;
-                    if (b < a.B)
-                        store_out<OUTT>(a.y, (int64_t)b * a.N + col, g * acc[i][j][e]);
-                }
+    for (int j = 0; j < (DUAL ? TN / 2 : TN); j++) {
+        const int col = n0 + (DUAL ? wn * 32 + 16 * j : wn * 64 + 16 * j) + (lane & 15);
+        if (col >= (DUAL ? Nh : a.N))
+            continue;
+        float g0 = 1.f, g1 = 1.f;
+        if constexpr (FMT == FMT_NV) {
+            g0 = tensor_scale(a, col);
+            if constexpr (DUAL)
+                g1 = tensor_scale(a, Nh + col);
         }
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int b = b0 + wm * (BM / 2) + 16 * i + 4 * (lane >> 4) + e;
+                if (b >= a.B)
+                    continue;
+                if constexpr (DUAL) {
+                    const float G = g0 * acc[i][j][e];
+                    const float U = g1 * acc[i][j + 2][e];
+                    store_out<OUTT>(a.y, (int64_t)b * Nh + col, silu(G) * U);
+                } else {
+                    store_out<OUTT>(a.y, (int64_t)b * a.N + col, g0 * acc[i][j][e]);
+                }
+            }
     }
 }
 
-constexpr int TBM = 128, TBN = 128, TWM = 2, TWN = 2;
+// ------------------------------------------------------------------ host
 
 template <int FMT, int ACT, int OUTT, bool DUAL>
 static void launch_tiled_t(const KArgs &a, hipStream_t st, int Nh)
 {
-    const int mtiles = (a.B + TBM - 1) / TBM;
-    const int nrows = DUAL ? Nh : a.N;
-    const int ntiles = (nrows + TBN - 1) / TBN;
-    dim3 grid(mtiles * ntiles);
-    hipLaunchKernelGGL((tiled_kernel<FMT, ACT, OUTT, DUAL, TBM, TBN, TWM, TWN>), grid,
-                       dim3(TWM * TWN * 64), 0, st, a, Nh, mtiles, ntiles);
+    const int bm = a.B <= 128 ? 128 : 256;
+    const int mtiles = (a.B + bm - 1) / bm;
+    const int ntiles = ((DUAL ? Nh : a.N) + (DUAL ? 127 : 255)) / (DUAL ? 128 : 256);
+    const dim3 grid((unsigned)(mtiles * ntiles));
+    if (bm == 128)
+        hipLaunchKernelGGL((tiled_kernel<FMT, ACT, OUTT, DUAL, 128>), grid, dim3(512), 0, st, a, Nh, mtiles,
+                           ntiles);
+    else
+        hipLaunchKernelGGL((tiled_kernel<FMT, ACT, OUTT, DUAL, 256>), grid, dim3(512), 0, st, a, Nh, mtiles,
+                           ntiles);
 }
 
 template <int FMT>
-static void launch_tiled_f(const Problem *p, const KArgs &a, hipStream_t st)
+static void launch_tiled_f(const Problem &p, const KArgs &a, hipStream_t st)
 {
-    const bool f32 = p->act == QGEMM_F32, o32 = p->out == QGEMM_F32;
-    const bool dual = p->epi == QGEMM_EPI_SWIGLU;
-    const int Nh = (int)(p->N / 2);
+    const bool f32 = p.act == QGEMM_F32, o32 = p.out == QGEMM_F32;
+    const bool dual = p.epi == QGEMM_EPI_SWIGLU;
+    const int Nh = (int)(p.N / 2);
 #define QG_T(A, O, D) launch_tiled_t<FMT, A, O, D>(a, st, Nh)
     if (f32) {
         if (o32) { if (dual) QG_T(ACT_F32, OUT_F32, true); else QG_T(ACT_F32, OUT_F32, false); }
@@ -269,9 +274,9 @@ static void launch_tiled_f(const Problem *p, const KArgs &a, hipStream_t st)
 hipError_t launch_tiled(const Problem &p, const KArgs &a, hipStream_t st)
 {
     switch (p.fmt) {
-    case FMT_Q8: launch_tiled_f<FMT_Q8>(&p, a, st); break;
-    case FMT_MX: launch_tiled_f<FMT_MX>(&p, a, st); break;
-    default: launch_tiled_f<FMT_NV>(&p, a, st); break;
+    case FMT_Q8: launch_tiled_f<FMT_Q8>(p, a, st); break;
+    case FMT_MX: launch_tiled_f<FMT_MX>(p, a, st); break;
+    default: launch_tiled_f<FMT_NV>(p, a, st); break;
     }
     return hipGetLastError();
 }
