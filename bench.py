@@ -32,14 +32,18 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2516.6       # MI355X dense bf16 MFMA
 ROTATE_BYTES = 1 << 30          # weight bytes to rotate over (> Infinity Cache)
 METRIC = "weight-stream GB/s (B≤16) and TFLOP/s (B≥256) vs MI355X roofline"
-SRC_FILES = ("prefill_q8_mxfp4_amd/csrc/kernels.hip", "prefill_q8_mxfp4_amd/csrc/api.hip",
-             "prefill_q8_mxfp4_amd/csrc/layout.h")
+CSRC = os.path.join(ROOT, "prefill_q8_mxfp4_amd", "csrc")
 
 
 def kernel_src_sha() -> str:
+    """Hash of every library source: a stored counter record is used only
+    while the kernels it was taken on are unchanged."""
     h = hashlib.sha256()
-    for f in SRC_FILES:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(CSRC, f), "rb").read())
+    h.update(open(os.path.join(ROOT, "include", "qgemm.h"), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -89,10 +93,10 @@ class Workload:
         yb = self.y.numel() * self.y.element_size()
         return self.wbytes + xb + yb
 
-    def time_ms(self, steps, warmup):
+    def time_ms(self, steps, warmup, eager=False):
         """Average ms per call over `steps` calls replayed from a HIP graph
-        holding one call per weight copy, bracketed by events on the stream
-        the calls run on."""
+        holding one call per weight copy (or launched one by one when
+        `eager`), bracketed by events on the stream the calls run on."""
         import torch
 
         n = len(self.ws)
@@ -102,6 +106,16 @@ class Workload:
             for i in range(max(warmup, n)):
                 self.plan.run(self.x, self.ws[i % n], self.y)
         stream.synchronize()
+        if eager:
+            start = torch.cuda.Event(enable_timing=True)
+            end = torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                start.record(stream)
+                for i in range(reps * n):
+                    self.plan.run(self.x, self.ws[i % n], self.y)
+                end.record(stream)
+            end.synchronize()
+            return start.elapsed_time(end) / (reps * n), reps * n
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             for i in range(n):
@@ -139,16 +153,36 @@ def traffic_record(sha):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl):
+def cpu_baseline(wl, budget_s=10.0):
+    """The fp64 oracle on the host cores, on whole headline calls repeated
+    until about `budget_s` seconds have passed (at least one call)."""
     import oracle
 
-    t0 = time.time()
-    oracle.gemm(wl.w_logical, wl.x_host)
-    dt = time.time() - t0
-    cores = int(os.environ.get("OMP_NUM_THREADS", 0) or os.cpu_count() or 1)
-    return {"value": round(wl.wbytes / dt / 1e9, 6), "unit": "GB/s", "cores": cores,
-            "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"the whole headline call: fp64 oracle, q8_0 K=N=5120, B={wl.B}"}
+    calls, t0 = 0, time.time()
+    while True:
+        oracle.gemm(wl.w_logical, wl.x_host)
+        calls += 1
+        dt = time.time() - t0
+        if dt >= budget_s or dt / calls * (calls + 1) > 3 * budget_s:
+            break
+    per = dt / calls
+    return {"value": round(wl.wbytes / per / 1e9, 6), "unit": "GB/s", "cores": oracle.threads(),
+            "kind": "oracle", "seconds_per_call": round(per, 3),
+            "sample": f"{calls} whole headline call(s) of the fp64 oracle: q8_0 K=N=5120, "
+                      f"B={wl.B}, fp32 activations"}
+
+
+def copy_calibration(mib=512, reps=5):
+    """A plain device copy of known size, for scaling the HBM byte counters
+    of a profiled run (FETCH_SIZE / WRITE_SIZE of this copy read mib MiB)."""
+    import torch
+
+    src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: {reps} copies of {mib} MiB")
 
 
 def main():
@@ -158,6 +192,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch calls one by one instead of replaying a HIP graph (profiling)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 512 MiB copy (scales profiler byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path; "
@@ -172,12 +210,14 @@ def main():
     q.lib()  # fails loudly without the HIP library
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     sha = kernel_src_sha()
+    if args.copy_calibration:
+        copy_calibration()
 
     # ---- headline: q8_0 5120x5120, B = 16, fp32 activations
     B = 16
     probe = q.weight_bytes("q8_0", 5120, 5120)
     wl = Workload("cfg2", B, copies=copies_for(probe))
-    ms, steps_done = wl.time_ms(args.steps, args.warmup)
+    ms, steps_done = wl.time_ms(args.steps, args.warmup, eager=args.eager)
     value = wl.wbytes / (ms * 1e-3) / 1e9
     achieved = wl.io_bytes() / (ms * 1e-3) / 1e9
     line = {

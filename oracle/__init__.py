@@ -62,6 +62,8 @@ def _load():
             f = getattr(lib, name)
             f.restype = d
             f.argtypes = [arg]
+        lib.oracle_threads.restype = i32
+        lib.oracle_threads.argtypes = []
         lib.oracle_dequant.restype = None
         lib.oracle_dequant.argtypes = [i32, vp, vp, vp, i64, i32, i64, i64, vp]
         lib.oracle_gemm.restype = None
@@ -118,6 +120,11 @@ def e8m0(b):
 
 def e4m3(b):
     return _load().oracle_e4m3(int(b))
+
+
+def threads() -> int:
+    """Threads the oracle's parallel loops use."""
+    return int(_load().oracle_threads())
 
 
 def silu(t):

@@ -33,6 +33,7 @@
  * increasing k.  Compile with -ffp-contract=off.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -185,6 +186,18 @@ void oracle_gemm_at(int fmt, const void *codes, const void *scales, const float 
 }
 
 /* SiLU(t) = t * sigmoid(t) = t / (1 + e^-t). */
+/* Threads an OpenMP region of this library runs on (for reporting only). */
+int oracle_threads(void)
+{
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        n = omp_get_num_threads();
+    }
+    return n;
+}
+
 double oracle_silu(double t)
 {
     return t / (1.0 + exp(-t));

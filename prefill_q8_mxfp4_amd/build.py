@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqgemm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-UNITS = ("api.hip", "skinny.hip", "tiled.hip", "dequant.hip")
+UNITS = ("api.hip", "skinny.hip", "stream.hip", "tiled.hip", "dequant.hip")
 HEADERS = ("common.h", "layout.h")
 
 FLAGS = [

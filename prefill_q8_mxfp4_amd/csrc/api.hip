@@ -50,17 +50,79 @@ static int env_int(const char *name, int dflt)
 
 // ---- small-batch tier shape
 //
-// About SK_WGS workgroups per batch group (enough waves to keep HBM busy):
-// ngroups row groups, and K is split ksplit ways to reach the target when a
-// workspace is available.  The activation stage (kch slabs)
-// is bounded by SK_LDS_MAX; larger ranges are walked in chunks.
+// With a workspace, K is split into ranges of split_kc() slabs, a choice that
+// depends on the problem (format, activation terms, N, K) and not on B: every
+// batch row is then summed in the same order by both small-batch kernels, up
+// to SK_SPLIT_NBY batch groups (larger batches have enough tiles unsplit).
+// The counter region has one size for every B, so no call's partial tiles
+// land on another call's counters.
 static const int SK_LDS_MAX = 96 * 1024;
 static const int SK_SPLIT_NBY = 8;  // batch groups up to which K is split
+static const int ST_MAX_B = 16;     // the streaming kernel's batch limit
+
+static int act_terms(const Problem &p)
+{
+    return p.act == QGEMM_F32 && p.math == QGEMM_MATH_FP32 ? 3 : 1;
+}
+
+static int split_kc(const Problem &p)
+{
+    const int forced = env_int("QGEMM_ST_KC", 0);
+    if (forced == 8 || forced == 16)
+        return forced;
+    const int64_t groups = (p.L.RT + 7) / 8;
+    const int64_t S = p.L.S;
+    const int per_slab = skinny_lds_per_slab(p.fmt, act_terms(p), 1);
+    if (16 * per_slab <= SK_LDS_MAX && groups * ((S + 15) / 16) >= 256)
+        return 16;
+    return 8;
+}
+
+static int64_t split_cnt_bytes(const Problem &p)
+{
+    return round_up((int64_t)SK_SPLIT_NBY * ((p.L.RT + 3) / 4) * 4, 256);
+}
+
+static bool use_stream(const Problem &p, int64_t B)
+{
+    return B <= ST_MAX_B && env_int("QGEMM_SK_STREAM", 1) != 0;
+}
+
+// The streaming kernel's shape: KC-slab splits (as split_kc), and as many
+// waves per workgroup (8..ST_MAX_WAVES) as make groups x splits about two
+// workgroups per CU (measured faster than one larger workgroup per CU).
+// Depends on the problem only, not on B.
+static StCfg stream_cfg(const Problem &p, bool split)
+{
+    StCfg c;
+    const int S = (int)p.L.S;
+    const int RT = (int)p.L.RT;
+    c.KC = split_kc(p);
+    c.kc = split ? c.KC : (S + c.KC - 1) / c.KC * c.KC;
+    c.ksplit = (S + c.kc - 1) / c.kc;
+    const int cus = env_int("QGEMM_ST_WGS", 512);
+    const int groups_target = cus / c.ksplit > 0 ? cus / c.ksplit : 1;
+    int R = (RT + groups_target - 1) / groups_target;
+    const int forced = env_int("QGEMM_ST_WAVES", 0);
+    if (forced)
+        R = forced;
+    R = R < 8 ? 8 : (R > ST_MAX_WAVES(c.KC) ? ST_MAX_WAVES(c.KC) : R);
+    c.R = R;
+    c.ngroups = (RT + R - 1) / R;
+    c.lds = c.KC * skinny_lds_per_slab(p.fmt, act_terms(p), 1);
+    if (c.ksplit > 1) {
+        c.cnt_bytes = split_cnt_bytes(p);
+        c.part_bytes = (int64_t)c.ksplit * c.ngroups * c.R * 1024;
+    } else {
+        c.cnt_bytes = c.part_bytes = 0;
+    }
+    return c;
+}
 
 static SkCfg skinny_cfg(const Problem &p, int64_t B, bool split)
 {
     SkCfg c;
-    const int nta = p.act == QGEMM_F32 && p.math == QGEMM_MATH_FP32 ? 3 : 1;
+    const int nta = act_terms(p);
     c.MB = B <= 16 ? 1 : (B <= 32 ? 2 : 4);
     while (c.MB > 1 && skinny_lds_per_slab(p.fmt, nta, c.MB) * SK_RING > SK_LDS_MAX)
         c.MB /= 2;
@@ -70,17 +132,7 @@ static SkCfg skinny_cfg(const Problem &p, int64_t B, bool split)
     c.ngroups = (int)((p.L.RT + 4 * c.NT - 1) / (4 * c.NT));
     c.nby = (int)((B + 16 * c.MB - 1) / (16 * c.MB));
     const int S = (int)p.L.S;
-    // The split depends on N and K only (not on B), so each batch row is
-    // summed in the same order whatever B is, up to SK_SPLIT_NBY batch
-    // groups; larger batches are not split (they have enough tiles).
-    int ks = 1;
-    if (split && c.nby <= SK_SPLIT_NBY) {
-        const int64_t target = env_int("QGEMM_SK_WGS", 256);
-        const int64_t k = (target + c.ngroups - 1) / c.ngroups;
-        ks = (int)(k < 1 ? 1 : (k > S ? S : k));
-    }
-    c.kc = (S + ks - 1) / ks;
-    c.kc = (c.kc + SK_RING - 1) / SK_RING * SK_RING;
+    c.kc = split && c.nby <= SK_SPLIT_NBY ? split_kc(p) : (S + SK_RING - 1) / SK_RING * SK_RING;
     if (c.kc <= kch_max) {
         c.kch = c.kc;
     } else {
@@ -91,14 +143,23 @@ static SkCfg skinny_cfg(const Problem &p, int64_t B, bool split)
     c.lds = c.kch * per_slab;
     if (c.ksplit > 1) {
         const int64_t tiles = (int64_t)c.nby * c.ngroups * 4 * c.MB * c.NT;
-        // The counter region has the same size for every B, so no call's
-        // partial tiles can land on another call's counters.
-        c.cnt_bytes = round_up((int64_t)SK_SPLIT_NBY * c.ngroups * 4, 256);
+        c.cnt_bytes = split_cnt_bytes(p);
         c.part_bytes = (int64_t)c.ksplit * tiles * 1024;
     } else {
         c.cnt_bytes = c.part_bytes = 0;
     }
     return c;
+}
+
+// Workspace bytes the small-batch tier uses for B (0: no K split).
+static int64_t skinny_ws_bytes(const Problem &p, int64_t B)
+{
+    if (use_stream(p, B)) {
+        const StCfg c = stream_cfg(p, true);
+        return c.cnt_bytes + c.part_bytes;
+    }
+    const SkCfg c = skinny_cfg(p, B, true);
+    return c.cnt_bytes + c.part_bytes;
 }
 
 static int choose_tier(const qgemm_plan *plan, int64_t B)
@@ -312,8 +373,7 @@ size_t qgemm_workspace_bytes(const qgemm_plan *plan, int64_t B)
         return 0;
     if (choose_tier(plan, B) != QGEMM_TIER_SKINNY)
         return 0;
-    const SkCfg c = skinny_cfg(plan->p, B, true);
-    return (size_t)(c.cnt_bytes + c.part_bytes);
+    return (size_t)skinny_ws_bytes(plan->p, B);
 }
 
 int qgemm_run_ws(const qgemm_plan *plan, int64_t B, const void *w, const void *x, void *y,
@@ -341,7 +401,24 @@ int qgemm_run_ws(const qgemm_plan *plan, int64_t B, const void *w, const void *x
     hipStream_t st = (hipStream_t)stream;
     hipError_t e;
     if (choose_tier(plan, B) == QGEMM_TIER_SKINNY) {
-        SkCfg c = skinny_cfg(p, B, workspace != nullptr);
+        const int nterm = p.math == QGEMM_MATH_BF16 ? 1 : env_int("QGEMM_FP32_TERMS", 3);
+        if (nterm < 1 || nterm > 3)
+            return fail(QGEMM_EINVAL, "qgemm_run: QGEMM_FP32_TERMS must be 1..3");
+        const bool split = workspace != nullptr && (size_t)skinny_ws_bytes(p, B) <= ws_bytes;
+        if (use_stream(p, B)) {
+            const StCfg c = stream_cfg(p, split);
+            SkinnyWs ws;
+            ws.cnt = c.ksplit > 1 ? (uint32_t *)workspace : nullptr;
+            ws.part = c.ksplit > 1 ? (float *)((uint8_t *)workspace + c.cnt_bytes) : nullptr;
+            ws.ksplit = c.ksplit;
+            ws.kc = c.kc;
+            ws.kch = c.KC;
+            e = launch_stream(p, a, c, ws, nterm, st);
+            if (e != hipSuccess)
+                return hip_fail(e, "qgemm_run: kernel launch");
+            return QGEMM_OK;
+        }
+        SkCfg c = skinny_cfg(p, B, split);
         if (c.ksplit > 1 && (size_t)(c.cnt_bytes + c.part_bytes) > ws_bytes)
             c = skinny_cfg(p, B, false);  // workspace too small: no K split
         if (c.nby > 65535)
@@ -353,9 +430,6 @@ int qgemm_run_ws(const qgemm_plan *plan, int64_t B, const void *w, const void *x
         ws.ksplit = c.ksplit;
         ws.kc = c.kc;
         ws.kch = c.kch;
-        const int nterm = p.math == QGEMM_MATH_BF16 ? 1 : env_int("QGEMM_FP32_TERMS", 3);
-        if (nterm < 1 || nterm > 3)
-            return fail(QGEMM_EINVAL, "qgemm_run: QGEMM_FP32_TERMS must be 1..3");
         e = launch_skinny(p, a, c, ws, nterm, st);
     } else {
         e = launch_tiled(p, a, st);

@@ -175,6 +175,22 @@ __device__ __forceinline__ Split<NT> split_f32(const float *v)
     return s;
 }
 
+// All-ones when `keep`, else zero, opaque to the optimiser.  Masking a loaded
+// value with it (instead of `keep ? v : 0`) stops the compiler from turning the
+// load into a conditional one issued late, which would make later waits drain
+// every load in flight.
+__device__ __forceinline__ uint32_t keep_mask(bool keep)
+{
+    uint32_t m = keep ? 0xFFFFFFFFu : 0u;
+    asm volatile("" : "+v"(m));
+    return m;
+}
+
+__device__ __forceinline__ u32x4 masked(u32x4 v, uint32_t m)
+{
+    return u32x4{v[0] & m, v[1] & m, v[2] & m, v[3] & m};
+}
+
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -245,7 +261,51 @@ __host__ __device__ constexpr int skinny_lds_per_slab(int fmt, int nta, int mb)
     return nta * mb * (fmt == FMT_Q8 ? 2 : 4) * 64 * 16;
 }
 
+// Small-batch streaming kernel for B <= 16: R waves (8..ST_MAX_WAVES) of one
+// row tile each, chunks of KC slabs (8 or 16) with every load of a chunk
+// issued at once; grid ngroups * ksplit.
+__host__ __device__ constexpr int ST_MAX_WAVES(int kc) { return kc == 16 ? 12 : 16; }
+
+struct StCfg {
+    int KC, R;
+    int ngroups, ksplit, kc;
+    int lds;
+    int64_t cnt_bytes, part_bytes;
+};
+
+// Last workgroup of a K split: sum the ksplit partial tiles of `tile` in
+// split order (its own partial `own` in place ks), loading up to 8 partials
+// at a time so their latencies overlap.
+__device__ __forceinline__ f32x4 reduce_partials(const uint64_t *part, int ksplit, int ks, int64_t tiles,
+                                                 int64_t tile, int lane, f32x4 own)
+{
+    f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < ksplit; k0 += 8) {
+        uint64_t lo[8], hi[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const int kk = min(k0 + j, ksplit - 1);
+            const uint64_t *src = part + (((int64_t)kk * tiles + tile) * 64 + lane) * 2;
+            lo[j] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            hi[j] = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const int kk = k0 + j;
+            if (kk >= ksplit)
+                break;
+            const f32x4 v = kk == ks ? own
+                                     : __builtin_bit_cast(f32x4, u32x4{(uint32_t)lo[j], (uint32_t)(lo[j] >> 32),
+                                                                       (uint32_t)hi[j], (uint32_t)(hi[j] >> 32)});
+            sum[0] += v[0]; sum[1] += v[1]; sum[2] += v[2]; sum[3] += v[3];
+        }
+    }
+    return sum;
+}
+
 hipError_t launch_skinny(const Problem &p, const KArgs &a, const SkCfg &c, const SkinnyWs &ws,
+                         int nterm, hipStream_t st);
+hipError_t launch_stream(const Problem &p, const KArgs &a, const StCfg &c, const SkinnyWs &ws,
                          int nterm, hipStream_t st);
 hipError_t launch_tiled(const Problem &p, const KArgs &a, hipStream_t st);
 hipError_t launch_dequant(int fmt, const KArgs &a, float *out, hipStream_t st);

@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(KArgs a, SkinnyWs ws)
             const int row = cc / (KS / CE), kk = (cc % (KS / CE)) * CE;
             const int mb = row >> 4, b = row & 15;
             const int u = kk >> 5, g8 = (kk & 31) >> 3;
-            const u32x4 xv = xin[i] ? xr[i] : u32x4{0u, 0u, 0u, 0u};
+            const u32x4 xv = masked(xr[i], keep_mask(xin[i]));
             u32x4 *slab = xs + sl * SLAB_E;
             if constexpr (ACT == ACT_F32) {
                 float v[4];
@@ -260,24 +260,8 @@ __global__ __launch_bounds__(256) void skinny_kernel(KArgs a, SkinnyWs ws)
 #pragma unroll
         for (int mb = 0; mb < MB; mb++)
 #pragma unroll
-            for (int nt = 0; nt < NT; nt++) {
-                f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
-                for (int kk = 0; kk < ws.ksplit; kk++) {
-                    f32x4 v;
-                    if (kk == ks) {
-                        v = acc[mb][nt];
-                    } else {
-                        const uint64_t *src =
-                            part + (((int64_t)kk * tiles + tbase + mb * NT + nt) * 64 + lane) * 2;
-                        const uint64_t lo = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        const uint64_t hi = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        v = __builtin_bit_cast(f32x4, u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi,
-                                                            (uint32_t)(hi >> 32)});
-                    }
-                    sum[0] += v[0]; sum[1] += v[1]; sum[2] += v[2]; sum[3] += v[3];
-                }
-                acc[mb][nt] = sum;
-            }
+            for (int nt = 0; nt < NT; nt++)
+                acc[mb][nt] = reduce_partials(part, ws.ksplit, ks, tiles, tbase + mb * NT + nt, lane, acc[mb][nt]);
         if (tid == 0)
             __hip_atomic_store(&ws.cnt[by * ngroups + grp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }

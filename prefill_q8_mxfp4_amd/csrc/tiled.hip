@@ -120,7 +120,7 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
         for (int i = 0; i < XCH; i++) {
             const int c = tid + i * NTHR;
             const int row = c / (KT / CE), kk = (c % (KT / CE)) * CE;
-            const u32x4 v = xin[i] ? xr[i] : u32x4{0u, 0u, 0u, 0u};
+            const u32x4 v = masked(xr[i], keep_mask(xin[i]));
             if constexpr (ACT == ACT_F32) {
                 bf16x2 p0, p1;
                 p0[0] = (__bf16)__uint_as_float(v[0]);
