@@ -65,17 +65,47 @@ static int act_terms(const Problem &p)
     return p.act == QGEMM_F32 && p.math == QGEMM_MATH_FP32 ? 3 : 1;
 }
 
+// Shape of the streaming kernel (B <= 16): W waves per workgroup, NPH slabs
+// per wave, so KC = W * NPH slabs per K split.  The search minimises the work
+// (row tiles x slabs) of the busiest CU, assuming one workgroup per CU and
+// rounds of 256; ties go to fewer splits (less partial-tile traffic), then to
+// fewer waves.  It depends on N and K only.
+struct StShape {
+    int W, NPH;
+};
+
+static StShape stream_shape(const Problem &p)
+{
+    const int64_t groups = (p.L.RT + ST_RG - 1) / ST_RG;
+    const int64_t S = p.L.S;
+    const int fw = env_int("QGEMM_ST_WAVES", 0), fp = env_int("QGEMM_ST_NPH", 0);
+    StShape best = {8, 1};
+    int64_t best_cost = -1, best_splits = 0;
+    for (int nph = 1; nph <= 2; nph++) {
+        if (fp && nph != fp)
+            continue;
+        for (int w = 8; w <= st_max_waves(nph); w++) {
+            if (fw && w != fw)
+                continue;
+            const int64_t kc = (int64_t)w * nph;
+            const int64_t splits = (S + kc - 1) / kc;
+            const int64_t rounds = (groups * splits + 255) / 256;
+            const int64_t cost = rounds * ST_RG * (kc < S ? kc : S);
+            if (best_cost < 0 || cost < best_cost || (cost == best_cost && splits < best_splits)) {
+                best = {w, nph};
+                best_cost = cost;
+                best_splits = splits;
+            }
+        }
+    }
+    return best;
+}
+
+// Slabs per K split (with a workspace), shared by both small-batch kernels.
 static int split_kc(const Problem &p)
 {
-    const int forced = env_int("QGEMM_ST_KC", 0);
-    if (forced == 8 || forced == 16)
-        return forced;
-    const int64_t groups = (p.L.RT + 7) / 8;
-    const int64_t S = p.L.S;
-    const int per_slab = skinny_lds_per_slab(p.fmt, act_terms(p), 1);
-    if (16 * per_slab <= SK_LDS_MAX && groups * ((S + 15) / 16) >= 256)
-        return 16;
-    return 8;
+    const StShape sh = stream_shape(p);
+    return sh.W * sh.NPH;
 }
 
 static int64_t split_cnt_bytes(const Problem &p)
@@ -88,31 +118,22 @@ static bool use_stream(const Problem &p, int64_t B)
     return B <= ST_MAX_B && env_int("QGEMM_SK_STREAM", 1) != 0;
 }
 
-// The streaming kernel's shape: KC-slab splits (as split_kc), and as many
-// waves per workgroup (8..ST_MAX_WAVES) as make groups x splits about two
-// workgroups per CU (measured faster than one larger workgroup per CU).
-// Depends on the problem only, not on B.
+// The streaming kernel's shape: 8 row tiles per workgroup and KC-slab splits
+// (split_kc).  Depends on the problem only, not on B.
 static StCfg stream_cfg(const Problem &p, bool split)
 {
     StCfg c;
     const int S = (int)p.L.S;
-    const int RT = (int)p.L.RT;
-    c.KC = split_kc(p);
+    const StShape sh = stream_shape(p);
+    c.W = sh.W;
+    c.NPH = sh.NPH;
+    c.KC = sh.W * sh.NPH;
     c.kc = split ? c.KC : (S + c.KC - 1) / c.KC * c.KC;
     c.ksplit = (S + c.kc - 1) / c.kc;
-    const int cus = env_int("QGEMM_ST_WGS", 512);
-    const int groups_target = cus / c.ksplit > 0 ? cus / c.ksplit : 1;
-    int R = (RT + groups_target - 1) / groups_target;
-    const int forced = env_int("QGEMM_ST_WAVES", 0);
-    if (forced)
-        R = forced;
-    R = R < 8 ? 8 : (R > ST_MAX_WAVES(c.KC) ? ST_MAX_WAVES(c.KC) : R);
-    c.R = R;
-    c.ngroups = (RT + R - 1) / R;
-    c.lds = c.KC * skinny_lds_per_slab(p.fmt, act_terms(p), 1);
+    c.ngroups = (int)((p.L.RT + 7) / 8);
     if (c.ksplit > 1) {
         c.cnt_bytes = split_cnt_bytes(p);
-        c.part_bytes = (int64_t)c.ksplit * c.ngroups * c.R * 1024;
+        c.part_bytes = (int64_t)c.ksplit * c.ngroups * 8 * 1024;
     } else {
         c.cnt_bytes = c.part_bytes = 0;
     }
@@ -132,13 +153,8 @@ static SkCfg skinny_cfg(const Problem &p, int64_t B, bool split)
     c.ngroups = (int)((p.L.RT + 4 * c.NT - 1) / (4 * c.NT));
     c.nby = (int)((B + 16 * c.MB - 1) / (16 * c.MB));
     const int S = (int)p.L.S;
-    c.kc = split && c.nby <= SK_SPLIT_NBY ? split_kc(p) : (S + SK_RING - 1) / SK_RING * SK_RING;
-    if (c.kc <= kch_max) {
-        c.kch = c.kc;
-    } else {
-        c.kch = kch_max;
-        c.kc = (c.kc + c.kch - 1) / c.kch * c.kch;
-    }
+    c.kc = split && c.nby <= SK_SPLIT_NBY ? split_kc(p) : S;
+    c.kch = c.kc <= kch_max ? c.kc : kch_max;  // the last chunk of a range may be shorter
     c.ksplit = (S + c.kc - 1) / c.kc;
     c.lds = c.kch * per_slab;
     if (c.ksplit > 1) {

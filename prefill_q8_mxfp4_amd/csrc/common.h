@@ -261,15 +261,16 @@ __host__ __device__ constexpr int skinny_lds_per_slab(int fmt, int nta, int mb)
     return nta * mb * (fmt == FMT_Q8 ? 2 : 4) * 64 * 16;
 }
 
-// Small-batch streaming kernel for B <= 16: R waves (8..ST_MAX_WAVES) of one
-// row tile each, chunks of KC slabs (8 or 16) with every load of a chunk
-// issued at once; grid ngroups * ksplit.
-__host__ __device__ constexpr int ST_MAX_WAVES(int kc) { return kc == 16 ? 12 : 16; }
+// Small-batch streaming kernel for B <= 16: workgroups of W waves (8..16)
+// over ST_RG row tiles, chunks of KC = W * NPH slabs with every load of a
+// chunk issued at once; grid ngroups * ksplit.
+constexpr int ST_RG = 8;
+// wave limit per phase count: two phases hold twice the weight registers
+__host__ __device__ constexpr int st_max_waves(int nph) { return nph == 2 ? 12 : 16; }
 
 struct StCfg {
-    int KC, R;
+    int W, NPH, KC;
     int ngroups, ksplit, kc;
-    int lds;
     int64_t cnt_bytes, part_bytes;
 };
 

@@ -14,6 +14,9 @@
 //    also exact).  Waves keep a ring of D slabs in flight with no barrier.
 //  * Q8_0 and MXFP4 block scales multiply the fp32 partial of each 32-wide
 //    block, so a block's sum is exact before it is scaled.
+//  * Summation order, shared with the B <= 16 streaming kernel so a batch
+//    row's result does not depend on B: per slab, its units in order into a
+//    partial from zero, partials added to the running tile in slab order.
 //
 // Loads are unconditional (slab, row and column indices clamped in bounds;
 // out-of-range activations zeroed when staged), so no register is written on
@@ -176,6 +179,12 @@ __global__ __launch_bounds__(256) void skinny_kernel(KArgs a, SkinnyWs ws)
                 if (s >= s_end)
                     continue;  // padding slab (uniform)
                 const u32x4 *slab = xs + (s - c_beg) * SLAB_E;
+                f32x4 part[MB][NT];  // this slab's partial tiles, from zero
+#pragma unroll
+                for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+                    for (int nt = 0; nt < NT; nt++)
+                        part[mb][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
                 for (int u = 0; u < U; u++) {
@@ -212,15 +221,24 @@ __global__ __launch_bounds__(256) void skinny_kernel(KArgs a, SkinnyWs ws)
                                     t = mfma(A[mb][tt], Bw, t);
 #pragma unroll
                                 for (int i = 0; i < 4; i++)
-                                    acc[mb][nt][i] = __builtin_fmaf(ps, t[i], acc[mb][nt][i]);
+                                    part[mb][nt][i] = __builtin_fmaf(ps, t[i], part[mb][nt][i]);
                             } else {
 #pragma unroll
                                 for (int tt = 0; tt < NTA; tt++)
-                                    acc[mb][nt] = mfma(A[mb][tt], Bw, acc[mb][nt]);
+                                    part[mb][nt] = mfma(A[mb][tt], Bw, part[mb][nt]);
                             }
                         }
                     }
                 }
+#pragma unroll
+                for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+                    for (int nt = 0; nt < NT; nt++) {
+                        acc[mb][nt][0] += part[mb][nt][0];
+                        acc[mb][nt][1] += part[mb][nt][1];
+                        acc[mb][nt][2] += part[mb][nt][2];
+                        acc[mb][nt][3] += part[mb][nt][3];
+                    }
             }
         }
         c_beg += ws.kch;
