@@ -175,6 +175,31 @@ __device__ __forceinline__ Split<NT> split_f32(const float *v)
     return s;
 }
 
+// Raw buffer resource over [base, base + bytes) (clamped to 4 GiB); loads
+// through it take a 32-bit per-lane offset plus a uniform (scalar) offset,
+// and bytes past the end read as zero.  Descriptor word 3 is the gfx9-family
+// raw-buffer setting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes)
+{
+    const int64_t n = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)(uint32_t)n, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+__device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+{
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+
+__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
 // All-ones when `keep`, else zero, opaque to the optimiser.  Masking a loaded
 // value with it (instead of `keep ? v : 0`) stops the compiler from turning the
 // load into a conditional one issued late, which would make later waits drain

@@ -18,6 +18,8 @@
 // barrier.  SwiGLU: the staged rows are BN/2 gate rows j and the BN/2 up rows
 // Nh + j, and every wave owns matching gate and up columns, so G and U of an
 // output sit in the same lane for the epilogue.
+#include <type_traits>
+
 #include "common.h"
 
 namespace qg {
@@ -62,102 +64,125 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
     const int n0 = ntl * (DUAL ? BN / 2 : BN);  // first output column
     const int nsteps = (a.K + KT - 1) / KT;
 
-    // ---- register stage of one K step (loads clamped in bounds, masked at store)
+    // ---- register stage of one K step.  Loads go through buffer resources:
+    // per-lane offsets are fixed, the step only moves the scalar offset, and
+    // rows or tiles past the end of the data read as zero.
+    constexpr int ESZ = ACT == ACT_F32 ? 4 : 2;
+    const int gate_rt0 = n0 / 16;                          // first (gate) row tile
+    const int up_rt0 = DUAL ? (Nh + n0) / 16 : gate_rt0 + BN / 32;
+    const int64_t code_bytes = (int64_t)a.RT * a.S * 1024;
+    const int64_t sc_bytes = (int64_t)a.RT * a.SG * 256;
+    const __amdgpu_buffer_rsrc_t xres =
+        make_rsrc((const uint8_t *)a.x + (int64_t)b0 * a.K * ESZ, (int64_t)(a.B - b0) * a.K * ESZ);
+    // weight chunk i of a thread covers staged row tile c >> 6 with c = tid + 512 i:
+    // i = 0 the first BN/32 tiles, i = 1 the second (SwiGLU: gate, then up)
+    const int64_t wb0 = (int64_t)gate_rt0 * a.S * 1024, wb1 = (int64_t)up_rt0 * a.S * 1024;
+    const int64_t sb0 = (int64_t)gate_rt0 * a.SG * 256, sb1 = (int64_t)up_rt0 * a.SG * 256;
+    const __amdgpu_buffer_rsrc_t wres[2] = {make_rsrc(a.w + wb0, code_bytes - wb0),
+                                            make_rsrc(a.w + wb1, code_bytes - wb1)};
+    const __amdgpu_buffer_rsrc_t sres[2] = {make_rsrc(a.w + a.scale_off + sb0, sc_bytes - sb0),
+                                            make_rsrc(a.w + a.scale_off + sb1, sc_bytes - sb1)};
+    int xoff[XCH];
+#pragma unroll
+    for (int i = 0; i < XCH; i++) {
+        const int c = tid + i * NTHR;
+        xoff[i] = ((c / (KT / CE)) * a.K + (c % (KT / CE)) * CE) * ESZ;
+    }
+    const int woff = ((((tid >> 6) & (BN / 32 - 1)) * a.S) << 10) + (lane << 4);
+    const int soff = (((tid >> 6) & (BN / 32 - 1)) * a.SG << 8) + ((lane & 15) << 4);
+    const bool ktail = a.K % KT != 0;  // the last step has columns past K
+
     u32x4 xr[XCH];
-    bool xin[XCH];
     uint32_t wr[WCH][FP4 ? 2 : 4];
     uint32_t sr[WCH][2];
 
-    auto load_stage = [&](int step) {
-        const int kb = step * KT;
-#pragma unroll
-        for (int i = 0; i < XCH; i++) {
-            const int c = tid + i * NTHR;
-            const int row = c / (KT / CE), k = kb + (c % (KT / CE)) * CE;
-            const int b = b0 + row;
-            xin[i] = b < a.B && k < a.K;  // K % 16 == 0: a load is all in or all out
-            const int bc = min(b, a.B - 1), kc = min(k, a.K - CE);
-            if constexpr (ACT == ACT_F32)
-                xr[i] = *(const u32x4 *)((const float *)a.x + (int64_t)bc * a.K + kc);
-            else
-                xr[i] = *(const u32x4 *)((const uint16_t *)a.x + (int64_t)bc * a.K + kc);
-        }
+    auto load_wstage = [&](int step) {
         const int s = FP4 ? step >> 1 : step;   // slab
         const int half = FP4 ? step & 1 : 0;    // which 64 k of an FP4 slab
+        constexpr int G = FMT == FMT_NV ? 2 : 4;
+        const int ssc = ((s / G) << 8) + (s % G) * scale_bytes_per_slab(FMT);
 #pragma unroll
         for (int i = 0; i < WCH; i++) {
-            const int c = tid + i * NTHR;
-            const int tr = c >> 6, L = c & 63;  // staged row tile, lane chunk
-            int rt;
-            if constexpr (DUAL)
-                rt = tr < BN / 32 ? n0 / 16 + tr : (Nh / 16) + n0 / 16 + (tr - BN / 32);
-            else
-                rt = n0 / 16 + tr;
-            rt = min(rt, a.RT - 1);
-            const uint8_t *chunk = a.w + (((int64_t)rt * a.S + s) << 10) + (L << 4);
             if constexpr (FP4) {
-                const u32x2 v = *(const u32x2 *)(chunk + 8 * half);
+                const u32x2 v = bload8(wres[i], woff, (s << 10) + 8 * half);
                 wr[i][0] = v[0];
                 wr[i][1] = v[1];
             } else {
-                const u32x4 v = *(const u32x4 *)chunk;
+                const u32x4 v = bload16(wres[i], woff, s << 10);
                 wr[i][0] = v[0]; wr[i][1] = v[1]; wr[i][2] = v[2]; wr[i][3] = v[3];
             }
-            const uint8_t *sp = slab_scales<FMT>(a, rt, L & 15, s);
             if constexpr (FMT == FMT_NV) {
-                const u32x2 v = *(const u32x2 *)sp;
+                const u32x2 v = bload8(sres[i], soff, ssc);
                 sr[i][0] = v[0];
                 sr[i][1] = v[1];
             } else {
-                sr[i][0] = *(const uint32_t *)sp;
+                sr[i][0] = bload4(sres[i], soff, ssc);
                 sr[i][1] = 0;
             }
         }
     };
 
+    // The last step of a K that is not a multiple of the step reads the next
+    // row's first columns: zero them (rare; a branch of its own so the common
+    // steps carry no masking work).
+    auto tail_mask = [&](int step) {
+        if (ktail && step == nsteps - 1) {
+#pragma unroll
+            for (int i = 0; i < XCH; i++) {
+                const int c = tid + i * NTHR;
+                if (step * KT + (c % (KT / CE)) * CE >= a.K)
+                    xr[i] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    // One activation chunk (i < XCH) of the next stage into LDS buffer buf.
+    auto xpiece = [&](int buf, int i) {
+        const int c = tid + i * NTHR;
+        const int row = c / (KT / CE), kk = (c % (KT / CE)) * CE;
+        const u32x4 v = xr[i];
+        if constexpr (ACT == ACT_F32) {
+            bf16x2 p0, p1;
+            p0[0] = (__bf16)__uint_as_float(v[0]);
+            p0[1] = (__bf16)__uint_as_float(v[1]);
+            p1[0] = (__bf16)__uint_as_float(v[2]);
+            p1[1] = (__bf16)__uint_as_float(v[3]);
+            u32x2 *dst = (u32x2 *)&xs[buf][(kk >> 3) * XP + row] + ((kk & 7) >> 2);
+            *dst = u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
+        } else {
+            xs[buf][(kk >> 3) * XP + row] = v;
+        }
+    };
+    // One decoded weight unit (p < 2 * WCH: chunk p / 2, unit p % 2) of the
+    // next stage (step `step`) into LDS buffer buf, block scale folded in.
+    auto wpiece = [&](int buf, int step, int p) {
+        const int i = p >> 1, ul = p & 1;
+        const int half = FP4 ? step & 1 : 0;
+        const int c = tid + i * NTHR;
+        const int tr = c >> 6, L = c & 63;
+        const int col = tr * 16 + (L & 15);
+        const int g = L >> 4;
+        bf16x8 h;
+        if constexpr (FMT == FMT_Q8) {
+            const float d = fp16_bits_to_f32((sr[i][0] >> (16 * ul)) & 0xFFFFu);
+            h = q8_scaled_to_bf16(wr[i][2 * ul], wr[i][2 * ul + 1], d);
+        } else if constexpr (FMT == FMT_MX) {
+            const int u = 2 * half + ul;
+            h = fp4_to_bf16(wr[i][ul], e8m0_to_f32((sr[i][0] >> (8 * u)) & 0xFFu));
+        } else {
+            const int u = 2 * half + ul;
+            const int si = 2 * u + (g >> 1);
+            const uint32_t sb = (si < 4 ? sr[i][0] >> (8 * si) : sr[i][1] >> (8 * (si - 4))) & 0xFFu;
+            h = fp4_to_bf16_mul(wr[i][ul], e4m3_to_f32(sb));
+        }
+        ws[buf][(4 * ul + g) * WP + col] = __builtin_bit_cast(u32x4, h);
+    };
     auto store_stage = [&](int buf, int step) {
 #pragma unroll
-        for (int i = 0; i < XCH; i++) {
-            const int c = tid + i * NTHR;
-            const int row = c / (KT / CE), kk = (c % (KT / CE)) * CE;
-            const u32x4 v = masked(xr[i], keep_mask(xin[i]));
-            if constexpr (ACT == ACT_F32) {
-                bf16x2 p0, p1;
-                p0[0] = (__bf16)__uint_as_float(v[0]);
-                p0[1] = (__bf16)__uint_as_float(v[1]);
-                p1[0] = (__bf16)__uint_as_float(v[2]);
-                p1[1] = (__bf16)__uint_as_float(v[3]);
-                u32x2 *dst = (u32x2 *)&xs[buf][(kk >> 3) * XP + row] + ((kk & 7) >> 2);
-                *dst = u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
-            } else {
-                xs[buf][(kk >> 3) * XP + row] = v;
-            }
-        }
-        const int half = FP4 ? step & 1 : 0;
+        for (int i = 0; i < XCH; i++)
+            xpiece(buf, i);
 #pragma unroll
-        for (int i = 0; i < WCH; i++) {
-            const int c = tid + i * NTHR;
-            const int tr = c >> 6, L = c & 63;
-            const int col = tr * 16 + (L & 15);
-            const int g = L >> 4;
-#pragma unroll
-            for (int ul = 0; ul < 2; ul++) {      // the two 32-wide units of this step
-                bf16x8 h;
-                if constexpr (FMT == FMT_Q8) {
-                    const float d = fp16_bits_to_f32((sr[i][0] >> (16 * ul)) & 0xFFFFu);
-                    h = q8_scaled_to_bf16(wr[i][2 * ul], wr[i][2 * ul + 1], d);
-                } else if constexpr (FMT == FMT_MX) {
-                    const int u = 2 * half + ul;
-                    h = fp4_to_bf16(wr[i][ul], e8m0_to_f32((sr[i][0] >> (8 * u)) & 0xFFu));
-                } else {
-                    const int u = 2 * half + ul;
-                    const int si = 2 * u + (g >> 1);
-                    const uint32_t sb = (si < 4 ? sr[i][0] >> (8 * si) : sr[i][1] >> (8 * (si - 4))) & 0xFFu;
-                    h = fp4_to_bf16_mul(wr[i][ul], e4m3_to_f32(sb));
-                }
-                ws[buf][(4 * ul + g) * WP + col] = __builtin_bit_cast(u32x4, h);
-            }
-        }
+        for (int p = 0; p < 2 * WCH; p++)
+            wpiece(buf, step, p);
     };
 
     // staged column of the wave's n-tile j (SwiGLU: tiles 0,1 gate, 2,3 the
@@ -176,36 +201,74 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
         for (int j = 0; j < TN; j++)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    auto load_stage = [&](int step) {
+#pragma unroll
+        for (int i = 0; i < XCH; i++)
+            xr[i] = bload16(xres, xoff[i], step * KT * ESZ);
+        load_wstage(step);
+    };
+
     load_stage(0);
+    tail_mask(0);
     store_stage(0, 0);
-    if (nsteps > 1)
-        load_stage(1);
+    load_stage(min(1, nsteps - 1));
     __syncthreads();
 
+    // One step: the MFMAs of step s from LDS buffer s & 1, interleaved by
+    // hand (fences keep the order) with the next stage: after each group of
+    // TN MFMAs one piece of work on step s + 1 (a weight unit during the
+    // first k-step, an activation chunk during the second), whose registers
+    // are then refilled by the global loads of step s + 2.  Past the last step
+    // the pieces repeat the last step's data into a buffer no one reads.
+    static_assert(XCH <= TM && 2 * WCH <= TM, "one piece per MFMA group");
+    // The loop exists twice: with the K-tail masking (K not a multiple of the
+    // step) and without it, so the common case carries no masking work.
+    auto main_loop = [&](auto masking) {
     for (int step = 0; step < nsteps; step++) {
         const int buf = step & 1;
+        const int nst = min(step + 1, nsteps - 1);
+        if constexpr (decltype(masking)::value)
+            tail_mask(nst);
 #pragma unroll
         for (int kk = 0; kk < 2; kk++) {        // two 32-wide MFMA k-steps
             const int kg = 4 * kk + (lane >> 4);
-            bf16x8 af[TM], bw[TN];
-#pragma unroll
-            for (int i = 0; i < TM; i++)
-                af[i] = __builtin_bit_cast(bf16x8, xs[buf][kg * XP + wm * (BM / 2) + 16 * i + (lane & 15)]);
+            const u32x4 *xrow = &xs[buf][kg * XP + wm * (BM / 2) + (lane & 15)];
+            bf16x8 bw[TN];
 #pragma unroll
             for (int j = 0; j < TN; j++)
                 bw[j] = __builtin_bit_cast(bf16x8, ws[buf][kg * WP + wcol(j) + (lane & 15)]);
+            bf16x8 af = __builtin_bit_cast(bf16x8, xrow[0]);
 #pragma unroll
-            for (int i = 0; i < TM; i++)
+            for (int i = 0; i < TM; i++) {
+                bf16x8 afn = af;
+                if (i + 1 < TM)
+                    afn = __builtin_bit_cast(bf16x8, xrow[16 * (i + 1)]);
 #pragma unroll
                 for (int j = 0; j < TN; j++)
-                    acc[i][j] = mfma(af[i], bw[j], acc[i][j]);
+                    acc[i][j] = mfma(af, bw[j], acc[i][j]);
+                if (kk == 0 && i < 2 * WCH)
+                    wpiece(buf ^ 1, nst, i);
+                if (kk == 1 && i < XCH)
+                    xpiece(buf ^ 1, i);
+                __builtin_amdgcn_sched_barrier(0);
+                af = afn;
+            }
+            // refill what this half consumed: a full step ahead of its use
+            if (kk == 0) {
+                load_wstage(min(step + 2, nsteps - 1));
+            } else {
+#pragma unroll
+                for (int i = 0; i < XCH; i++)
+                    xr[i] = bload16(xres, xoff[i], min(step + 2, nsteps - 1) * KT * ESZ);
+            }
         }
-        if (step + 1 < nsteps)
-            store_stage(buf ^ 1, step + 1);
-        if (step + 2 < nsteps)
-            load_stage(step + 2);
         __syncthreads();
     }
+    };
+    if (ktail)
+        main_loop(std::true_type{});
+    else
+        main_loop(std::false_type{});
 
     // ---- epilogue (lane holds rows 4*(lane/16)+e of each 16x16 tile, column lane%16)
 #pragma unroll
