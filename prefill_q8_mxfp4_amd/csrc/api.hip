@@ -113,6 +113,16 @@ static int64_t split_cnt_bytes(const Problem &p)
     return round_up((int64_t)SK_SPLIT_NBY * ((p.L.RT + 3) / 4) * 4, 256);
 }
 
+// Workspace layout of a plan: the small-batch tiers' counters, then the
+// large-batch tier's counters (at most 255 split tiles), then partial tiles
+// (whichever tier the call used).  Counters are zero between calls.
+static const int64_t TI_CNT_BYTES = 1024;
+
+static int64_t ws_data_off(const Problem &p)
+{
+    return split_cnt_bytes(p) + TI_CNT_BYTES;
+}
+
 static bool use_stream(const Problem &p, int64_t B)
 {
     return B <= ST_MAX_B && env_int("QGEMM_SK_STREAM", 1) != 0;
@@ -132,7 +142,7 @@ static StCfg stream_cfg(const Problem &p, bool split)
     c.ksplit = (S + c.kc - 1) / c.kc;
     c.ngroups = (int)((p.L.RT + 7) / 8);
     if (c.ksplit > 1) {
-        c.cnt_bytes = split_cnt_bytes(p);
+        c.cnt_bytes = ws_data_off(p);
         c.part_bytes = (int64_t)c.ksplit * c.ngroups * 8 * 1024;
     } else {
         c.cnt_bytes = c.part_bytes = 0;
@@ -159,11 +169,54 @@ static SkCfg skinny_cfg(const Problem &p, int64_t B, bool split)
     c.lds = c.kch * per_slab;
     if (c.ksplit > 1) {
         const int64_t tiles = (int64_t)c.nby * c.ngroups * 4 * c.MB * c.NT;
-        c.cnt_bytes = split_cnt_bytes(p);
+        c.cnt_bytes = ws_data_off(p);
         c.part_bytes = (int64_t)c.ksplit * tiles * 1024;
     } else {
         c.cnt_bytes = c.part_bytes = 0;
     }
+    return c;
+}
+
+// Large-batch tier shape.  Whole rounds of 256 tiles (one per CU) run
+// unsplit; the tiles of a last, partial round are split along K into S
+// pieces, S chosen by a small cost model: rounds of work plus a charge for
+// the partial tiles' traffic.  Without a large enough workspace nothing is
+// split.
+static TiCfg tiled_cfg(const Problem &p, int64_t B, bool split)
+{
+    TiCfg c;
+    c.BM = B <= 128 ? 128 : 256;
+    const bool dual = p.epi == QGEMM_EPI_SWIGLU;
+    const int64_t cols = dual ? p.N / 2 : p.N;
+    c.mtiles = (int)((B + c.BM - 1) / c.BM);
+    c.ntiles = (int)((cols + (dual ? 127 : 255)) / (dual ? 128 : 256));
+    c.tiles = c.mtiles * c.ntiles;
+    const int nsteps = (int)((p.K + 63) / 64);
+    const int full = c.tiles / 256 * 256, rem = c.tiles - full;
+    int S = 1;
+    if (split && rem > 0) {
+        double best = 1e30;
+        const int forced = env_int("QGEMM_TI_SPLIT", 0);
+        for (int s = 1; s <= 16; s++) {
+            const int spp = (nsteps + s - 1) / s;
+            if (s > 1 && (s - 1) * spp >= nsteps)
+                continue;  // a piece would be empty
+            if (forced && s != forced)
+                continue;
+            const int64_t rounds = ((int64_t)rem * s + 255) / 256;
+            const double t = (double)rounds / s + 0.04 * (s - 1) * rem / 256.0;
+            if (t < best - 1e-9) {
+                best = t;
+                S = s;
+            }
+        }
+    }
+    c.sp.S = S;
+    c.sp.full = S > 1 ? full : c.tiles;
+    c.wgs = S > 1 ? full + rem * S : c.tiles;
+    c.sp.cnt = nullptr;
+    c.sp.part = nullptr;
+    c.part_bytes = S > 1 ? (int64_t)rem * S * c.BM * 256 * 4 : 0;
     return c;
 }
 
@@ -387,8 +440,10 @@ size_t qgemm_workspace_bytes(const qgemm_plan *plan, int64_t B)
 {
     if (!plan || plan->magic != PLAN_MAGIC || B <= 0 || B > (1ll << 30))
         return 0;
-    if (choose_tier(plan, B) != QGEMM_TIER_SKINNY)
-        return 0;
+    if (choose_tier(plan, B) != QGEMM_TIER_SKINNY) {
+        const TiCfg c = tiled_cfg(plan->p, B, true);
+        return c.part_bytes ? (size_t)(ws_data_off(plan->p) + c.part_bytes) : 0;
+    }
     return (size_t)skinny_ws_bytes(plan->p, B);
 }
 
@@ -448,7 +503,14 @@ int qgemm_run_ws(const qgemm_plan *plan, int64_t B, const void *w, const void *x
         ws.kch = c.kch;
         e = launch_skinny(p, a, c, ws, nterm, st);
     } else {
-        e = launch_tiled(p, a, st);
+        TiCfg c = tiled_cfg(p, B, workspace != nullptr);
+        if (c.part_bytes && (size_t)(ws_data_off(p) + c.part_bytes) > ws_bytes)
+            c = tiled_cfg(p, B, false);  // workspace too small: no K split
+        if (c.part_bytes) {
+            c.sp.cnt = (uint32_t *)((uint8_t *)workspace + split_cnt_bytes(p));
+            c.sp.part = (float *)((uint8_t *)workspace + ws_data_off(p));
+        }
+        e = launch_tiled(p, a, c, st);
     }
     if (e != hipSuccess)
         return hip_fail(e, "qgemm_run: kernel launch");

@@ -333,7 +333,22 @@ hipError_t launch_skinny(const Problem &p, const KArgs &a, const SkCfg &c, const
                          int nterm, hipStream_t st);
 hipError_t launch_stream(const Problem &p, const KArgs &a, const StCfg &c, const SkinnyWs &ws,
                          int nterm, hipStream_t st);
-hipError_t launch_tiled(const Problem &p, const KArgs &a, hipStream_t st);
+// Large-batch tier shape: BM x 256 tiles; the first `full` tiles run whole,
+// the rest are split along K into S pieces each (one workgroup per piece),
+// with partial tiles in `part` and one counter per split tile in `cnt`.
+struct TiSplit {
+    int full, S;
+    uint32_t *cnt;
+    float *part;
+};
+
+struct TiCfg {
+    int BM, mtiles, ntiles, tiles, wgs;
+    TiSplit sp;
+    int64_t part_bytes;  // workspace the split needs (0 without a split)
+};
+
+hipError_t launch_tiled(const Problem &p, const KArgs &a, const TiCfg &c, hipStream_t st);
 hipError_t launch_dequant(int fmt, const KArgs &a, float *out, hipStream_t st);
 
 }  // namespace qg

@@ -1,9 +1,9 @@
 // Large-batch tier: one BM x BN output tile per workgroup, bf16 MFMA from
 // LDS-staged fragments.
 //
-// 8 waves (two per SIMD, so one wave's MFMAs overlap the other's decode)
-// arranged 2 (batch) x 4 (weight rows); each wave owns BM/2 x 64 outputs as
-// (BM/32) x 4 tiles of v_mfma_f32_16x16x32_bf16.  K advances 64 per step:
+// 8 waves (two per SIMD) arranged 2 (batch) x 4 (weight rows); each wave owns
+// BM/2 x 64 outputs as (BM/32) x 4 tiles of v_mfma_f32_16x16x32_bf16.  K
+// advances 64 per step:
 //
 //  * activations: BM x 64 (fp32 input rounded to bf16 on the way);
 //  * weights: BN rows x 64, i.e. one Q8_0 slab or half an FP4 slab of each of
@@ -13,11 +13,19 @@
 //
 // LDS holds both operands as 16-byte fragment entries [k-group][row], rows
 // padded by one entry so neither the stage writes nor the fragment reads
-// collide in banks; it is double-buffered, and the next step's global loads
-// are in registers while the current step computes, so each K step needs one
-// barrier.  SwiGLU: the staged rows are BN/2 gate rows j and the BN/2 up rows
-// Nh + j, and every wave owns matching gate and up columns, so G and U of an
-// output sit in the same lane for the epilogue.
+// collide in banks; it is double-buffered.  Global loads go through buffer
+// resources (fixed per-lane offsets, the step in the scalar offset, zero
+// past the data) two steps ahead, and the conversion and LDS stores of the
+// next step are interleaved by hand with the MFMA groups of the current one,
+// so each step ends in one barrier.
+//
+// Tile counts: whole rounds of 256 tiles (one per CU) run unsplit; the tiles
+// of a last, partial round may be split along K into pieces, one workgroup
+// each, whose partial tiles tiled_reduce adds in piece order.
+//
+// SwiGLU: the staged rows are BN/2 gate rows j and the BN/2 up rows Nh + j,
+// and every wave owns matching gate and up columns, so G and U of an output
+// sit in the same lane for the epilogue.
 #include <type_traits>
 
 #include "common.h"
@@ -25,7 +33,7 @@
 namespace qg {
 
 template <int FMT, int ACT, int OUTT, bool DUAL, int BM>
-__global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles, int ntiles)
+__global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles, TiSplit sp)
 {
     constexpr int BN = 256;                    // staged weight rows
     constexpr int KT = 64;                     // K per step
@@ -50,19 +58,36 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
     // XCD-aware order: hardware hands consecutive workgroup ids to different
     // XCDs (id mod 8); give each XCD a contiguous range of tiles, batch tiles
     // fastest, so the workgroups sharing an XCD's L2 share weight tiles and
-    // the same activation rows.
-    int t = blockIdx.x;
+    // the same activation rows.  Whole tiles and split pieces are remapped as
+    // two separate groups (ids below and from sp.full), so both spread evenly
+    // over the XCDs.
+    const bool piece = (int)blockIdx.x >= sp.full;
+    const int g0 = piece ? sp.full : 0;
+    const int ng = piece ? (int)gridDim.x - sp.full : sp.full;
+    int t = (int)blockIdx.x - g0;
     {
-        const int nwg = gridDim.x;
-        const int per = (nwg + 7) / 8;
+        const int per = (ng + 7) / 8;
         const int xcd = t % 8, loc = t / 8;
-        const int full = nwg % 8 == 0 ? 8 : nwg % 8;  // XCDs that own 'per' tiles
+        const int full = ng % 8 == 0 ? 8 : ng % 8;  // XCDs that own 'per' tiles
         t = xcd < full ? xcd * per + loc : full * per + (xcd - full) * (per - 1) + loc;
     }
-    const int mt = t % mtiles, ntl = t / mtiles;
+    t += g0;
+    // Tiles below sp.full run whole; each later tile is split along K into
+    // sp.S pieces (workgroups).
+    int tile = t, ks = 0;
+    if (piece) {
+        tile = sp.full + (t - sp.full) / sp.S;
+        ks = (t - sp.full) % sp.S;
+    }
+    const bool split = piece && sp.S > 1;
+    const int mt = tile % mtiles, ntl = tile / mtiles;
     const int b0 = mt * BM;
     const int n0 = ntl * (DUAL ? BN / 2 : BN);  // first output column
     const int nsteps = (a.K + KT - 1) / KT;
+    // this workgroup's K steps [sb, se)
+    const int spp = split ? (nsteps + sp.S - 1) / sp.S : nsteps;
+    const int sb = split ? min(nsteps, ks * spp) : 0;
+    const int se = split ? min(nsteps, sb + spp) : nsteps;
 
     // ---- register stage of one K step.  Loads go through buffer resources:
     // per-lane offsets are fixed, the step only moves the scalar offset, and
@@ -208,10 +233,10 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
         load_wstage(step);
     };
 
-    load_stage(0);
-    tail_mask(0);
-    store_stage(0, 0);
-    load_stage(min(1, nsteps - 1));
+    load_stage(sb);
+    tail_mask(sb);
+    store_stage(sb & 1, sb);
+    load_stage(min(sb + 1, se - 1));
     __syncthreads();
 
     // One step: the MFMAs of step s from LDS buffer s & 1, interleaved by
@@ -224,9 +249,9 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
     // The loop exists twice: with the K-tail masking (K not a multiple of the
     // step) and without it, so the common case carries no masking work.
     auto main_loop = [&](auto masking) {
-    for (int step = 0; step < nsteps; step++) {
+    for (int step = sb; step < se; step++) {
         const int buf = step & 1;
-        const int nst = min(step + 1, nsteps - 1);
+        const int nst = min(step + 1, se - 1);
         if constexpr (decltype(masking)::value)
             tail_mask(nst);
 #pragma unroll
@@ -255,11 +280,11 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
             }
             // refill what this half consumed: a full step ahead of its use
             if (kk == 0) {
-                load_wstage(min(step + 2, nsteps - 1));
+                load_wstage(min(step + 2, se - 1));
             } else {
 #pragma unroll
                 for (int i = 0; i < XCH; i++)
-                    xr[i] = bload16(xres, xoff[i], min(step + 2, nsteps - 1) * KT * ESZ);
+                    xr[i] = bload16(xres, xoff[i], min(step + 2, se - 1) * KT * ESZ);
             }
         }
         __syncthreads();
@@ -269,6 +294,19 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
         main_loop(std::true_type{});
     else
         main_loop(std::false_type{});
+
+    // ---- K split: this piece's tile goes to the workspace; tiled_reduce (the
+    // next kernel on the stream) adds the pieces in order and stores y
+    if (split) {
+        const int r = tile - sp.full;               // split tile index
+        f32x4 *dst = (f32x4 *)sp.part + ((int64_t)r * sp.S + ks) * (NTHR * TM * TN) + tid;
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+            for (int j = 0; j < TN; j++)
+                dst[(i * TN + j) * NTHR] = acc[i][j];
+        return;
+    }
 
     // ---- epilogue (lane holds rows 4*(lane/16)+e of each 16x16 tile, column lane%16)
 #pragma unroll
@@ -300,30 +338,92 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
     }
 }
 
+// Sum of the K-split pieces of the split tiles, in piece order, then the
+// tiled_kernel epilogue.  The partial layout is the one tiled_kernel writes:
+// [split tile][piece][MFMA tile i * TN + j][thread][4], one thread of this
+// kernel per (split tile, i, j-pair, thread of the tiled workgroup).
+template <int FMT, int OUTT, bool DUAL, int BM>
+__global__ __launch_bounds__(256) void tiled_reduce(KArgs a, int Nh, int mtiles, TiSplit sp, int nsplit)
+{
+    constexpr int NTHR = 512, TM = BM / 2 / 16, TN = 4;
+    constexpr int JN = DUAL ? TN / 2 : TN;      // output column tiles per wave
+    const int64_t per_piece = (int64_t)NTHR * TM * TN;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (int64_t)nsplit * TM * JN * NTHR)
+        return;
+    const int th = (int)(idx % NTHR);
+    const int64_t q = idx / NTHR;
+    const int jj = (int)(q % JN);
+    const int i = (int)(q / JN % TM);
+    const int r = (int)(q / JN / TM);
+    const int tile = sp.full + r;
+    const int mt = tile % mtiles, ntl = tile / mtiles;
+    const int lane = th & 63, wid = th >> 6, wm = wid & 1, wn = wid >> 1;
+    const int b0 = mt * BM, n0 = ntl * (DUAL ? 128 : 256);
+    const f32x4 *src = (const f32x4 *)sp.part + (int64_t)r * sp.S * per_piece + th;
+    f32x4 v0 = f32x4{0.f, 0.f, 0.f, 0.f}, v1 = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < sp.S; k++) {
+        const f32x4 t0 = src[k * per_piece + (i * TN + jj) * NTHR];
+        v0[0] += t0[0]; v0[1] += t0[1]; v0[2] += t0[2]; v0[3] += t0[3];
+        if constexpr (DUAL) {
+            const f32x4 t1 = src[k * per_piece + (i * TN + jj + 2) * NTHR];
+            v1[0] += t1[0]; v1[1] += t1[1]; v1[2] += t1[2]; v1[3] += t1[3];
+        }
+    }
+    const int col = n0 + (DUAL ? wn * 32 + 16 * jj : wn * 64 + 16 * jj) + (lane & 15);
+    if (col >= (DUAL ? Nh : a.N))
+        return;
+    float g0 = 1.f, g1 = 1.f;
+    if constexpr (FMT == FMT_NV) {
+        g0 = tensor_scale(a, col);
+        if constexpr (DUAL)
+            g1 = tensor_scale(a, Nh + col);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        const int b = b0 + wm * (BM / 2) + 16 * i + 4 * (lane >> 4) + e;
+        if (b >= a.B)
+            continue;
+        if constexpr (DUAL)
+            store_out<OUTT>(a.y, (int64_t)b * Nh + col, silu(g0 * v0[e]) * (g1 * v1[e]));
+        else
+            store_out<OUTT>(a.y, (int64_t)b * a.N + col, g0 * v0[e]);
+    }
+}
+
 // ------------------------------------------------------------------ host
 
 template <int FMT, int ACT, int OUTT, bool DUAL>
-static void launch_tiled_t(const KArgs &a, hipStream_t st, int Nh)
+static void launch_tiled_t(const KArgs &a, const TiCfg &c, hipStream_t st, int Nh)
 {
-    const int bm = a.B <= 128 ? 128 : 256;
-    const int mtiles = (a.B + bm - 1) / bm;
-    const int ntiles = ((DUAL ? Nh : a.N) + (DUAL ? 127 : 255)) / (DUAL ? 128 : 256);
-    const dim3 grid((unsigned)(mtiles * ntiles));
-    if (bm == 128)
-        hipLaunchKernelGGL((tiled_kernel<FMT, ACT, OUTT, DUAL, 128>), grid, dim3(512), 0, st, a, Nh, mtiles,
-                           ntiles);
-    else
-        hipLaunchKernelGGL((tiled_kernel<FMT, ACT, OUTT, DUAL, 256>), grid, dim3(512), 0, st, a, Nh, mtiles,
-                           ntiles);
+    const dim3 grid((unsigned)c.wgs);
+    const int nsplit = c.tiles - c.sp.full;
+    if (c.BM == 128) {
+        hipLaunchKernelGGL((tiled_kernel<FMT, ACT, OUTT, DUAL, 128>), grid, dim3(512), 0, st, a, Nh, c.mtiles,
+                           c.sp);
+        if (c.sp.S > 1) {
+            const int64_t n = (int64_t)nsplit * (128 / 32) * (DUAL ? 2 : 4) * 512;
+            hipLaunchKernelGGL((tiled_reduce<FMT, OUTT, DUAL, 128>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                               st, a, Nh, c.mtiles, c.sp, nsplit);
+        }
+    } else {
+        hipLaunchKernelGGL((tiled_kernel<FMT, ACT, OUTT, DUAL, 256>), grid, dim3(512), 0, st, a, Nh, c.mtiles,
+                           c.sp);
+        if (c.sp.S > 1) {
+            const int64_t n = (int64_t)nsplit * (256 / 32) * (DUAL ? 2 : 4) * 512;
+            hipLaunchKernelGGL((tiled_reduce<FMT, OUTT, DUAL, 256>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                               st, a, Nh, c.mtiles, c.sp, nsplit);
+        }
+    }
 }
 
 template <int FMT>
-static void launch_tiled_f(const Problem &p, const KArgs &a, hipStream_t st)
+static void launch_tiled_f(const Problem &p, const KArgs &a, const TiCfg &c, hipStream_t st)
 {
     const bool f32 = p.act == QGEMM_F32, o32 = p.out == QGEMM_F32;
     const bool dual = p.epi == QGEMM_EPI_SWIGLU;
     const int Nh = (int)(p.N / 2);
-#define QG_T(A, O, D) launch_tiled_t<FMT, A, O, D>(a, st, Nh)
+#define QG_T(A, O, D) launch_tiled_t<FMT, A, O, D>(a, c, st, Nh)
     if (f32) {
         if (o32) { if (dual) QG_T(ACT_F32, OUT_F32, true); else QG_T(ACT_F32, OUT_F32, false); }
         else { if (dual) QG_T(ACT_F32, OUT_BF16, true); else QG_T(ACT_F32, OUT_BF16, false); }
@@ -334,12 +434,12 @@ static void launch_tiled_f(const Problem &p, const KArgs &a, hipStream_t st)
 #undef QG_T
 }
 
-hipError_t launch_tiled(const Problem &p, const KArgs &a, hipStream_t st)
+hipError_t launch_tiled(const Problem &p, const KArgs &a, const TiCfg &c, hipStream_t st)
 {
     switch (p.fmt) {
-    case FMT_Q8: launch_tiled_f<FMT_Q8>(p, a, st); break;
-    case FMT_MX: launch_tiled_f<FMT_MX>(p, a, st); break;
-    default: launch_tiled_f<FMT_NV>(p, a, st); break;
+    case FMT_Q8: launch_tiled_f<FMT_Q8>(p, a, c, st); break;
+    case FMT_MX: launch_tiled_f<FMT_MX>(p, a, c, st); break;
+    default: launch_tiled_f<FMT_NV>(p, a, c, st); break;
     }
     return hipGetLastError();
 }
