@@ -144,14 +144,17 @@ int qgemm_pack(qgemm_format fmt, int64_t N, int64_t K, const void *codes, const 
 typedef struct qgemm_plan qgemm_plan;
 
 /* Validate and record a problem shape.  act: activation dtype; out: output
- * dtype; math: see qgemm_math (QGEMM_MATH_FP32 needs act = QGEMM_F32); flags:
+ * dtype; math: see qgemm_math (QGEMM_MATH_FP32 needs act = QGEMM_F32; the
+ * SwiGLU epilogue needs QGEMM_MATH_BF16, else QGEMM_ENOTSUP); flags:
  * 0 or one QGEMM_FLAG_FORCE_* bit (also settable with the environment
  * variable QGEMM_FORCE_TIER=skinny|tiled).  Host only: allocates the small
  * plan object, no device memory and no HIP call.  *plan receives the handle. */
 int qgemm_create(qgemm_plan **plan, qgemm_format fmt, qgemm_dtype act, qgemm_dtype out,
                  qgemm_epilogue epi, qgemm_math math, int64_t N, int64_t K, uint32_t flags);
 
-/* y = x * W^T (or the SwiGLU of the two halves) for B rows.
+/* y = x * W^T (or the SwiGLU of the two halves) for B rows.  SwiGLU runs in
+ * the small-batch tier for B <= 16 and in the large-batch tier otherwise (a
+ * plan forced to the small-batch tier returns QGEMM_ENOTSUP for B > 16).
  *   w: packed weights (device, 16-byte aligned), laid out as above for the
  *      plan's N and K;
  *   x: activations [B][K] row-major (device, 16-byte aligned, act dtype);
@@ -170,9 +173,12 @@ size_t qgemm_workspace_bytes(const qgemm_plan *plan, int64_t B);
 
 /* qgemm_run with a caller-owned workspace (device memory, 256-byte aligned).
  * With at least qgemm_workspace_bytes(plan, B) bytes, the small-batch tier
- * splits K over several workgroups per output tile; the last workgroup of a
- * tile to finish adds the partial tiles in a fixed order, so results stay
- * deterministic (they can differ in rounding from the unsplit route).
+ * splits K over several workgroups per output tile (the last workgroup of a
+ * tile to finish adds the partial tiles in a fixed order), and the
+ * large-batch tier splits the tiles of a last, partial round of tiles along K
+ * (a second kernel on the stream adds the pieces in order).  Results stay
+ * deterministic; they can differ in rounding from the unsplit route, and in
+ * the large-batch tier from one B to another.
  * Contract: the workspace must be all zero before its first use with a plan;
  * every call returns its counter words to zero, so it can be reused by later
  * calls of that plan on the same stream, at any B.  A workspace moved to

@@ -137,6 +137,7 @@ static StCfg stream_cfg(const Problem &p, bool split)
     const StShape sh = stream_shape(p);
     c.W = sh.W;
     c.NPH = sh.NPH;
+    c.Nh = p.epi == QGEMM_EPI_SWIGLU ? (int)(p.N / 2) : 0;
     c.KC = sh.W * sh.NPH;
     c.kc = split ? c.KC : (S + c.KC - 1) / c.KC * c.KC;
     c.ksplit = (S + c.kc - 1) / c.kc;
@@ -238,8 +239,8 @@ static int choose_tier(const qgemm_plan *plan, int64_t B)
         return plan->forced_tier;
     if (p.math == QGEMM_MATH_FP32)
         return QGEMM_TIER_SKINNY;  // the only tier with the fp32-faithful split
-    if (p.epi == QGEMM_EPI_SWIGLU)
-        return QGEMM_TIER_TILED;   // the fused gate+up epilogue
+    if (p.epi == QGEMM_EPI_SWIGLU)  // fused gate+up: the streaming kernel or the tiled tier
+        return B <= ST_MAX_B ? QGEMM_TIER_SKINNY : QGEMM_TIER_TILED;
     return B <= 64 ? QGEMM_TIER_SKINNY : QGEMM_TIER_TILED;
 }
 
@@ -384,6 +385,9 @@ int qgemm_create(qgemm_plan **plan, qgemm_format fmt, qgemm_dtype act, qgemm_dty
         return fail(QGEMM_ENOTSUP, "qgemm_create: SwiGLU needs N/2 to be a multiple of 16");
     if (math == QGEMM_MATH_FP32 && act != QGEMM_F32)
         return fail(QGEMM_EINVAL, "qgemm_create: fp32 math needs fp32 activations");
+    if (math == QGEMM_MATH_FP32 && epi == QGEMM_EPI_SWIGLU)
+        return fail(QGEMM_ENOTSUP, "qgemm_create: the fused gate+up epilogue computes in bf16 "
+                                   "(QGEMM_MATH_BF16)");
     if ((flags & ~(QGEMM_FLAG_FORCE_SKINNY | QGEMM_FLAG_FORCE_TILED)) ||
         ((flags & QGEMM_FLAG_FORCE_SKINNY) && (flags & QGEMM_FLAG_FORCE_TILED)))
         return fail(QGEMM_EINVAL, "qgemm_create: bad flags 0x%x", flags);
@@ -399,8 +403,6 @@ int qgemm_create(qgemm_plan **plan, qgemm_format fmt, qgemm_dtype act, qgemm_dty
     if (forced == QGEMM_TIER_TILED && math == QGEMM_MATH_FP32)
         return fail(QGEMM_ENOTSUP, "qgemm_create: the tiled tier computes in bf16; fp32 math runs "
                                    "in the skinny tier");
-    if (forced == QGEMM_TIER_SKINNY && epi == QGEMM_EPI_SWIGLU)
-        return fail(QGEMM_ENOTSUP, "qgemm_create: the fused gate+up epilogue runs in the tiled tier");
     qgemm_plan *p = new (std::nothrow) qgemm_plan;
     if (!p)
         return fail(QGEMM_ENOMEM, "qgemm_create: out of host memory");
@@ -472,6 +474,9 @@ int qgemm_run_ws(const qgemm_plan *plan, int64_t B, const void *w, const void *x
     hipStream_t st = (hipStream_t)stream;
     hipError_t e;
     if (choose_tier(plan, B) == QGEMM_TIER_SKINNY) {
+        if (p.epi == QGEMM_EPI_SWIGLU && !use_stream(p, B))
+            return fail(QGEMM_ENOTSUP, "qgemm_run: the small-batch tier runs the fused gate+up epilogue "
+                                       "for B <= %d only (B=%lld)", ST_MAX_B, (long long)B);
         const int nterm = p.math == QGEMM_MATH_BF16 ? 1 : env_int("QGEMM_FP32_TERMS", 3);
         if (nterm < 1 || nterm > 3)
             return fail(QGEMM_EINVAL, "qgemm_run: QGEMM_FP32_TERMS must be 1..3");

@@ -295,6 +295,7 @@ __host__ __device__ constexpr int st_max_waves(int nph) { return nph == 2 ? 12 :
 
 struct StCfg {
     int W, NPH, KC;
+    int Nh;  // SwiGLU: gate rows (N / 2), else 0
     int ngroups, ksplit, kc;
     int64_t cnt_bytes, part_bytes;
 };

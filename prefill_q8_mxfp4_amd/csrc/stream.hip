@@ -26,6 +26,10 @@
 // Because each activation fragment is read by one wave only, LDS carries
 // just the partial tiles, not eight copies of the activations.
 //
+// Fused gate+up (SwiGLU): a workgroup's 8 row tiles are 4 gate tiles and the
+// 4 matching up tiles, so after the reduction G and U of an output column are
+// exchanged through LDS and the workgroup stores SiLU(G) * U.
+//
 // Summation order (also used by the B > 16 kernel, so a batch row's result
 // does not depend on B): per slab, its units in order into a partial from
 // zero; partials added to the running tile in slab order; K splits added in
@@ -36,7 +40,7 @@
 namespace qg {
 
 template <int FMT, int ACT, int NTERM, int NPH, int OUTT>
-__global__ __launch_bounds__(64 * st_max_waves(NPH)) void stream_kernel(KArgs a, SkinnyWs ws, int ngroups)
+__global__ __launch_bounds__(64 * st_max_waves(NPH)) void stream_kernel(KArgs a, SkinnyWs ws, int ngroups, int Nh)
 {
     constexpr int KS = FMT == FMT_Q8 ? 64 : 128;
     constexpr int U = KS / 32;                 // 32-wide units per slab
@@ -63,7 +67,12 @@ __global__ __launch_bounds__(64 * st_max_waves(NPH)) void stream_kernel(KArgs a,
         t = xcd < full ? xcd * per + loc : full * per + (xcd - full) * (per - 1) + loc;
     }
     const int ks = t / ngroups, grp = t % ngroups;
-    const int rt0 = grp * ST_RG;
+    // the group's row tiles g = 0..7: 8 consecutive ones, or with SwiGLU
+    // (Nh > 0) 4 gate tiles and the 4 matching up tiles Nh/16 further on
+    const int rt0 = Nh ? grp * (ST_RG / 2) : grp * ST_RG;
+    auto tile_of = [&](int g) -> int {
+        return Nh ? (g < ST_RG / 2 ? rt0 + g : Nh / 16 + rt0 + g - ST_RG / 2) : rt0 + g;
+    };
     const int s_beg = ks * ws.kc;
     const int s_end = min(a.S, s_beg + ws.kc);
     // activation row of this lane: rows past B read row B-1 (they only feed
@@ -105,7 +114,7 @@ __global__ __launch_bounds__(64 * st_max_waves(NPH)) void stream_kernel(KArgs a,
             const int sc = min(c_beg + ph * W + wid, a.S - 1);
 #pragma unroll
             for (int g = 0; g < ST_RG; g++) {
-                const int64_t rt = min(rt0 + g, a.RT - 1);  // tiles past the end: a copy, never stored
+                const int64_t rt = min(tile_of(g), a.RT - 1);  // tiles past the end: a copy, never stored
                 wr[ph][g] = *(const u32x4 *)(a.w + ((rt * a.S + sc) << 10) + (lane << 4));
                 const uint8_t *sp = slab_scales<FMT>(a, rt, r, sc);
                 if constexpr (FMT == FMT_NV) {
@@ -226,14 +235,38 @@ __global__ __launch_bounds__(64 * st_max_waves(NPH)) void stream_kernel(KArgs a,
             s_is_last = old == (uint32_t)(ws.ksplit - 1);
         }
         __syncthreads();
-        if (!s_is_last || wid >= ST_RG)
-            return;
-        acc = reduce_partials(part, ws.ksplit, ks, tiles, tile, lane, acc);
+        if (!s_is_last)
+            return;  // uniform over the workgroup
+        if (wid < ST_RG)
+            acc = reduce_partials(part, ws.ksplit, ks, tiles, tile, lane, acc);
         if (tid == 0)
             __hip_atomic_store(&ws.cnt[grp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
-    // ---- epilogue: tensor scale, store (lane holds batch rows 4*(lane/16)+i of column r)
+    // ---- epilogue (lane holds batch rows 4*(lane/16)+i of column r)
+    if (Nh) {
+        // SwiGLU: waves 4..7 hold the up tiles matching the gate tiles of
+        // waves 0..3; out = SiLU(g_gate G) * (g_up U), stored [B][Nh]
+        if (wid >= ST_RG / 2 && wid < ST_RG)
+            red[(wid - ST_RG / 2) * 64 + lane] = acc;
+        __syncthreads();
+        const int col = (rt0 + wid) * 16 + r;
+        if (wid >= ST_RG / 2 || col >= Nh)
+            return;
+        const f32x4 up = red[wid * 64 + lane];
+        float g0 = 1.f, g1 = 1.f;
+        if constexpr (FMT == FMT_NV) {
+            g0 = tensor_scale(a, col);
+            g1 = tensor_scale(a, Nh + col);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int b = 4 * gq + i;
+            if (b < a.B)
+                store_out<OUTT>(a.y, (int64_t)b * Nh + col, silu(g0 * acc[i]) * (g1 * up[i]));
+        }
+        return;
+    }
     const int n = (rt0 + wid) * 16 + r;
     if (wid >= ST_RG || n >= a.N)
         return;
@@ -257,9 +290,11 @@ static void launch_kc(const KArgs &a, const StCfg &c, const SkinnyWs &ws, hipStr
     const dim3 block((unsigned)(64 * c.W));
     const size_t lds = (size_t)c.W * ST_RG * 1024;
     if (c.NPH == 2)
-        hipLaunchKernelGGL((stream_kernel<FMT, ACT, NTERM, 2, OUTT>), grid, block, lds, st, a, ws, c.ngroups);
+        hipLaunchKernelGGL((stream_kernel<FMT, ACT, NTERM, 2, OUTT>), grid, block, lds, st, a, ws, c.ngroups,
+                           c.Nh);
     else
-        hipLaunchKernelGGL((stream_kernel<FMT, ACT, NTERM, 1, OUTT>), grid, block, lds, st, a, ws, c.ngroups);
+        hipLaunchKernelGGL((stream_kernel<FMT, ACT, NTERM, 1, OUTT>), grid, block, lds, st, a, ws, c.ngroups,
+                           c.Nh);
 }
 
 template <int FMT>

@@ -56,7 +56,8 @@ def _create(*args):
     ((0, 0, 0, 0, 0, 256, 512, 3), q.EINVAL),        # both tiers forced
     ((0, 0, 0, 0, 0, 256, 512, 0x10), q.EINVAL),     # unknown flag
     ((0, 0, 0, 0, 0, 256, 512, 2), q.ENOTSUP),       # fp32 math in the tiled tier
-    ((2, 1, 1, 1, 1, 64, 512, 1), q.ENOTSUP),        # SwiGLU in the skinny tier
+    ((2, 1, 1, 1, 1, 64, 512, 1), q.OK),             # SwiGLU in the skinny tier (B <= 16)
+    ((2, 0, 0, 1, 0, 64, 512, 0), q.ENOTSUP),        # SwiGLU with fp32 math
 ])
 def test_create_validation(args, status):
     st, h = _create(*args)
@@ -98,7 +99,8 @@ def test_tier_choice():
     p = q.Plan("mxfp4", 5120, 17408, act="bf16")
     assert p.tier(1) == "skinny" and p.tier(16) == "skinny" and p.tier(2048) == "tiled"
     p = q.Plan("nvfp4", 2 * 17408, 5120, act="bf16", out="bf16", epilogue="swiglu")
-    assert p.tier(2048) == "tiled" and p.tier(1) == "tiled"
+    assert p.tier(2048) == "tiled" and p.tier(17) == "tiled"
+    assert p.tier(1) == "skinny" and p.tier(16) == "skinny"
     p = q.Plan("q8_0", 5120, 5120, act="f32", tier="skinny")
     assert p.tier(256) == "skinny"
 

@@ -340,3 +340,56 @@ def test_mxfp4_extreme_scales_one_hot(tier):
     ref = oracle.dequant(w)[:, cols].T.astype(np.float32).astype(np.float64)
     bad = np.argwhere(y != ref)
     assert bad.size == 0, [(int(i), int(j), y[i, j], ref[i, j]) for i, j in bad[:8]]
+
+
+# ------------------------------------------- fused gate+up, small batch
+
+def _gate_up(fmt, nh, k, seed):
+    """Gate and up halves quantized as two tensors (own tensor scale each)."""
+    parts = [synth.quantize(fmt, synth.normal_f32(seed, synth.SID_W + h, nh, k, 0.02)) for h in (0, 1)]
+    w = {"fmt": fmt, "codes": np.concatenate([p["codes"] for p in parts]),
+         "scales": np.concatenate([p["scales"] for p in parts]), "g": None}
+    if fmt == "nvfp4":
+        w["g"] = np.concatenate([p["g"] for p in parts]).astype(np.float32)
+    return w
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "mxfp4", "nvfp4"])
+def test_swiglu_streaming_small_batch(fmt):
+    """B <= 16 SwiGLU runs in the streaming kernel (gate and up tiles of a
+    column in one workgroup, K split or not) and matches the fp64 oracle."""
+    nh, k = 320, 1024
+    w = _gate_up(fmt, nh, k, 31)
+    wd = w_dev(w)
+    plan = q.Plan(fmt, 2 * nh, k, act="bf16", out="f32", epilogue="swiglu")
+    for B in (1, 7, 16):
+        assert plan.tier(B) == "skinny"
+        x = synth.gen_x_bf16(B, k, seed=B)
+        ref = oracle.swiglu(w, x)
+        for ws in ("auto", None):
+            y = run(plan, x, wd, workspace=ws)
+            err = oracle.rel_fro(y, ref)
+            assert err <= 1e-4, (B, ws, err)
+
+
+def test_swiglu_streaming_cfg5_shape_b16():
+    """The NVFP4 fused gate+up shape (K = 5120, N = 2 x 17408) at B = 16,
+    bf16 output, checked on sampled outputs."""
+    c = synth.CONFIGS["cfg5"]
+    w = synth.gen_config_weights("cfg5")
+    x = synth.gen_config_x("cfg5", 16)
+    plan = q.Plan("nvfp4", c["N"], c["K"], act="bf16", out="bf16", epilogue="swiglu")
+    assert plan.tier(16) == "skinny"
+    y = run(plan, x, w_dev(w))
+    bi, ji = _samples(16, c["N"] // 2, 4000, 6)
+    err = oracle.rel_fro(y[bi, ji], oracle.swiglu_at(w, x, bi, ji))
+    assert err <= TOL_BF16, err
+
+
+def test_swiglu_forced_skinny_above_16_is_not_supported():
+    plan = q.Plan("nvfp4", 128, 256, act="bf16", out="f32", epilogue="swiglu", tier="skinny")
+    x = synth.gen_x_bf16(17, 256)
+    w = _gate_up("nvfp4", 64, 256, 3)
+    with pytest.raises(q.QgemmError) as e:
+        run(plan, x, w_dev(w))
+    assert e.value.status == q.ENOTSUP
