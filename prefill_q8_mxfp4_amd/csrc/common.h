@@ -81,15 +81,31 @@ __device__ __forceinline__ float e2m1_to_f32(uint32_t c)
     return __uint_as_float(bits | ((c & 8u) << 28));
 }
 
-// Eight int8 (two dwords) -> bf16x8, exact.
+// Signed byte BYTE of v -> fp32 (exact) in one SDWA conversion; written out
+// because the compiler shifts bytes 1 and 3 down first.
+template <int BYTE>
+__device__ __forceinline__ float sbyte_to_f32(uint32_t v)
+{
+    float r;
+    if constexpr (BYTE == 0)
+        asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(r) : "v"(v));
+    else if constexpr (BYTE == 1)
+        asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(v));
+    else if constexpr (BYTE == 2)
+        asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(v));
+    else
+        asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(v));
+    return r;
+}
+
+// Eight int8 (two dwords) -> bf16x8, exact: 8 conversions and 4 packs.
 __device__ __forceinline__ bf16x8 q8_to_bf16(uint32_t lo, uint32_t hi)
 {
     bf16x8 r;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        r[i] = (__bf16)(float)(int8_t)(lo >> (8 * i));
-        r[4 + i] = (__bf16)(float)(int8_t)(hi >> (8 * i));
-    }
+    r[0] = (__bf16)sbyte_to_f32<0>(lo); r[1] = (__bf16)sbyte_to_f32<1>(lo);
+    r[2] = (__bf16)sbyte_to_f32<2>(lo); r[3] = (__bf16)sbyte_to_f32<3>(lo);
+    r[4] = (__bf16)sbyte_to_f32<0>(hi); r[5] = (__bf16)sbyte_to_f32<1>(hi);
+    r[6] = (__bf16)sbyte_to_f32<2>(hi); r[7] = (__bf16)sbyte_to_f32<3>(hi);
     return r;
 }
 

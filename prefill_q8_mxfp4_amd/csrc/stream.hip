@@ -39,18 +39,24 @@
 
 namespace qg {
 
-template <int FMT, int ACT, int NTERM, int NPH, int OUTT>
+template <int FMT, int ACT, int NTERM, int NPH, int OUTT, bool FULLK>
 __global__ __launch_bounds__(64 * st_max_waves(NPH)) void stream_kernel(KArgs a, SkinnyWs ws, int ngroups, int Nh)
 {
     constexpr int KS = FMT == FMT_Q8 ? 64 : 128;
     constexpr int U = KS / 32;                 // 32-wide units per slab
     constexpr int NTA = ACT == ACT_F32 ? NTERM : 1;
     constexpr int XPU = ACT == ACT_F32 ? 2 : 1;  // 16-byte activation loads per unit
+    constexpr int XB = ACT == ACT_F32 ? 4 : 2;   // bytes per activation
+    constexpr int SG_SLABS = FMT == FMT_NV ? 2 : 4;  // slabs per 256-byte scale record
+    constexpr int SBYTES = FMT == FMT_NV ? 8 : 4;    // scale bytes per row and slab
 
     extern __shared__ f32x4 red[];             // [W][ST_RG][64]: one phase's partial tiles
     __shared__ int s_is_last;
 
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave index as a scalar: everything derived from it (slab, offsets, the
+    // idle-slab test) stays in scalar registers and branches
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int W = blockDim.x >> 6;             // waves = slabs per phase
     const int KC = W * NPH;                    // slabs per chunk
     const int r = lane & 15, gq = lane >> 4;
@@ -70,19 +76,33 @@ __global__ __launch_bounds__(64 * st_max_waves(NPH)) void stream_kernel(KArgs a,
     // the group's row tiles g = 0..7: 8 consecutive ones, or with SwiGLU
     // (Nh > 0) 4 gate tiles and the 4 matching up tiles Nh/16 further on
     const int rt0 = Nh ? grp * (ST_RG / 2) : grp * ST_RG;
-    auto tile_of = [&](int g) -> int {
-        return Nh ? (g < ST_RG / 2 ? rt0 + g : Nh / 16 + rt0 + g - ST_RG / 2) : rt0 + g;
-    };
     const int s_beg = ks * ws.kc;
     const int s_end = min(a.S, s_beg + ws.kc);
     // activation row of this lane: rows past B read row B-1 (they only feed
     // output rows that are never stored)
     const int xb = min(r, a.B - 1);
 
+    // Per-lane byte offsets.  Every per-tile and per-slab part of an address
+    // goes into a scalar buffer resource (or scalar offset), so no load needs
+    // vector address arithmetic.
+    const int xvoff = (xb * a.K + 8 * gq) * XB;
+    const int wvoff = lane << 4, svoff = r << 4;
+    const __amdgpu_buffer_rsrc_t xres = make_rsrc(a.x, (int64_t)a.B * a.K * XB);
+    // row tile of the group's tile g (tiles past the last read a copy of it;
+    // their outputs are never stored)
+    auto tile_of = [&](int g) -> int64_t {
+        const int rt = Nh ? (g < ST_RG / 2 ? rt0 + g : Nh / 16 + rt0 + g - ST_RG / 2) : rt0 + g;
+        return min(rt, a.RT - 1);
+    };
+
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};     // running sum of row tile `wid`
 
     for (int c_beg = s_beg; c_beg < s_end; c_beg += KC) {
-        // ---- 1. activations of this wave's slabs, then their weights and scales
+        // ---- 1. activations of this wave's slabs, then their weights and
+        // scales.  A wave with no slab in a phase (the end of the last split)
+        // reads activations of a valid slab, and its weight and scale loads
+        // go through empty resources: zeros, no memory traffic.  (Branching
+        // around them instead costs registers the compiler then spills.)
         u32x4 xr[NPH][U][XPU];
         uint32_t xm[NPH][U];
 #pragma unroll
@@ -90,16 +110,20 @@ __global__ __launch_bounds__(64 * st_max_waves(NPH)) void stream_kernel(KArgs a,
             const int sc = min(c_beg + ph * W + wid, a.S - 1);
 #pragma unroll
             for (int u = 0; u < U; u++) {
-                const int k = sc * KS + 32 * u + 8 * gq;
-                xm[ph][u] = keep_mask(k < a.K);  // K % 16 == 0: 8 columns all in or all out
-                const int kc = min(k, a.K - 8);
-                if constexpr (ACT == ACT_F32) {
-                    const float *src = (const float *)a.x + (int64_t)xb * a.K + kc;
-                    xr[ph][u][0] = *(const u32x4 *)src;
-                    xr[ph][u][XPU - 1] = *(const u32x4 *)(src + 4);
+                const int k0 = sc * KS + 32 * u;  // first column of the unit
+                int vo = xvoff, so = k0 * XB;
+                if constexpr (FULLK) {
+                    xm[ph][u] = 0xFFFFFFFFu;
                 } else {
-                    xr[ph][u][0] = *(const u32x4 *)((const uint16_t *)a.x + (int64_t)xb * a.K + kc);
+                    // K % 16 == 0: a lane's 8 columns are all in or all out
+                    const int k = k0 + 8 * gq;
+                    xm[ph][u] = keep_mask(k < a.K);
+                    vo = (xb * a.K + min(k, a.K - 8)) * XB;
+                    so = 0;
                 }
+                xr[ph][u][0] = bload16(xres, vo, so);
+                if constexpr (XPU == 2)
+                    xr[ph][u][1] = bload16(xres, vo, so + 16);
             }
         }
         // Keep the activation loads ahead of the weight loads: a wave's loads
@@ -111,18 +135,22 @@ __global__ __launch_bounds__(64 * st_max_waves(NPH)) void stream_kernel(KArgs a,
         uint32_t sr[NPH][ST_RG][2];
 #pragma unroll
         for (int ph = 0; ph < NPH; ph++) {
-            const int sc = min(c_beg + ph * W + wid, a.S - 1);
+            const int s = c_beg + ph * W + wid;
+            const int sc = min(s, a.S - 1);
+            const bool live = s < s_end;
 #pragma unroll
             for (int g = 0; g < ST_RG; g++) {
-                const int64_t rt = min(tile_of(g), a.RT - 1);  // tiles past the end: a copy, never stored
-                wr[ph][g] = *(const u32x4 *)(a.w + ((rt * a.S + sc) << 10) + (lane << 4));
-                const uint8_t *sp = slab_scales<FMT>(a, rt, r, sc);
+                const int64_t rt = tile_of(g);
+                wr[ph][g] = bload16(make_rsrc(a.w + ((rt * a.S + sc) << 10), live ? 1024 : 0), wvoff, 0);
+                const __amdgpu_buffer_rsrc_t srs =
+                    make_rsrc(a.w + a.scale_off + ((rt * a.SG + sc / SG_SLABS) << 8), live ? 256 : 0);
+                const int so = (sc % SG_SLABS) * SBYTES;
                 if constexpr (FMT == FMT_NV) {
-                    const u32x2 v = *(const u32x2 *)sp;
+                    const u32x2 v = bload8(srs, svoff, so);
                     sr[ph][g][0] = v[0];
                     sr[ph][g][1] = v[1];
                 } else {
-                    sr[ph][g][0] = *(const uint32_t *)sp;
+                    sr[ph][g][0] = bload4(srs, svoff, so);
                     sr[ph][g][1] = 0u;
                 }
             }
@@ -132,67 +160,69 @@ __global__ __launch_bounds__(64 * st_max_waves(NPH)) void stream_kernel(KArgs a,
 #pragma unroll
         for (int ph = 0; ph < NPH; ph++) {
             const int s = c_beg + ph * W + wid;  // this wave's slab
-            // units past K (padding of the last slab) are left out
-            const int nu = s < s_end ? min(U, (a.K - s * KS + 31) / 32) : 0;
+            if (s < s_end) {                     // uniform
+                // units past K (padding of the last slab) are left out
+                const int nu = FULLK ? U : min(U, (a.K - s * KS + 31) / 32);
 
-            // ---- 2. activation operands, then one partial tile per row tile
-            bf16x8 A[U][NTA];
-#pragma unroll
-            for (int u = 0; u < U; u++) {
-                if constexpr (ACT == ACT_F32) {
-                    float v[8];
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        v[e] = __uint_as_float(xr[ph][u][0][e] & xm[ph][u]);
-                        v[4 + e] = __uint_as_float(xr[ph][u][XPU - 1][e] & xm[ph][u]);
-                    }
-                    const Split<NTA> sp = split_f32<NTA, 8>(v);
-#pragma unroll
-                    for (int tt = 0; tt < NTA; tt++)
-                        A[u][tt] = sp.t[tt];
-                } else {
-                    A[u][0] = __builtin_bit_cast(bf16x8, masked(xr[ph][u][0], xm[ph][u]));
-                }
-            }
-#pragma unroll
-            for (int g = 0; g < ST_RG; g++) {
-                const u32x4 wc = wr[ph][g];
-                const uint32_t s0 = sr[ph][g][0], s1 = sr[ph][g][1];
-                f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
+                // ---- 2. activation operands, then one partial tile per row tile
+                bf16x8 A[U][NTA];
 #pragma unroll
                 for (int u = 0; u < U; u++) {
-                    if (u >= nu)
-                        continue;  // uniform
-                    if constexpr (FMT == FMT_Q8) {
-                        const bf16x8 Bw = q8_to_bf16(wc[2 * u], wc[2 * u + 1]);
-                        f32x4 tacc = mfma(A[u][0], Bw, f32x4{0.f, 0.f, 0.f, 0.f});
+                    if constexpr (ACT == ACT_F32) {
+                        float v[8];
 #pragma unroll
-                        for (int tt = 1; tt < NTA; tt++)
-                            tacc = mfma(A[u][tt], Bw, tacc);
-                        const float ps = fp16_bits_to_f32((s0 >> (16 * u)) & 0xFFFFu);
-#pragma unroll
-                        for (int i = 0; i < 4; i++)
-                            part[i] = __builtin_fmaf(ps, tacc[i], part[i]);
-                    } else if constexpr (FMT == FMT_MX) {
-                        const bf16x8 Bw = fp4_to_bf16(wc[u], 1.0f);
-                        f32x4 tacc = mfma(A[u][0], Bw, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-                        for (int tt = 1; tt < NTA; tt++)
-                            tacc = mfma(A[u][tt], Bw, tacc);
-                        const float ps = e8m0_to_f32((s0 >> (8 * u)) & 0xFFu);
-#pragma unroll
-                        for (int i = 0; i < 4; i++)
-                            part[i] = __builtin_fmaf(ps, tacc[i], part[i]);
-                    } else {
-                        const int si = 2 * u + (gq >> 1);
-                        const uint32_t sb = (si < 4 ? s0 >> (8 * si) : s1 >> (8 * (si - 4))) & 0xFFu;
-                        const bf16x8 Bw = fp4_to_bf16_mul(wc[u], e4m3_to_f32(sb));
+                        for (int e = 0; e < 4; e++) {
+                            v[e] = __uint_as_float(xr[ph][u][0][e] & xm[ph][u]);
+                            v[4 + e] = __uint_as_float(xr[ph][u][XPU - 1][e] & xm[ph][u]);
+                        }
+                        const Split<NTA> sp = split_f32<NTA, 8>(v);
 #pragma unroll
                         for (int tt = 0; tt < NTA; tt++)
-                            part = mfma(A[u][tt], Bw, part);
+                            A[u][tt] = sp.t[tt];
+                    } else {
+                        A[u][0] = __builtin_bit_cast(bf16x8, masked(xr[ph][u][0], xm[ph][u]));
                     }
                 }
-                red[(wid * ST_RG + g) * 64 + lane] = part;
+#pragma unroll
+                for (int g = 0; g < ST_RG; g++) {
+                    const u32x4 wc = wr[ph][g];
+                    const uint32_t s0 = sr[ph][g][0], s1 = sr[ph][g][1];
+                    f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int u = 0; u < U; u++) {
+                        if (!FULLK && u >= nu)
+                            continue;  // uniform
+                        if constexpr (FMT == FMT_Q8) {
+                            const bf16x8 Bw = q8_to_bf16(wc[2 * u], wc[2 * u + 1]);
+                            f32x4 tacc = mfma(A[u][0], Bw, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                            for (int tt = 1; tt < NTA; tt++)
+                                tacc = mfma(A[u][tt], Bw, tacc);
+                            const float ps = fp16_bits_to_f32((s0 >> (16 * u)) & 0xFFFFu);
+#pragma unroll
+                            for (int i = 0; i < 4; i++)
+                                part[i] = __builtin_fmaf(ps, tacc[i], part[i]);
+                        } else if constexpr (FMT == FMT_MX) {
+                            const bf16x8 Bw = fp4_to_bf16(wc[u], 1.0f);
+                            f32x4 tacc = mfma(A[u][0], Bw, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                            for (int tt = 1; tt < NTA; tt++)
+                                tacc = mfma(A[u][tt], Bw, tacc);
+                            const float ps = e8m0_to_f32((s0 >> (8 * u)) & 0xFFu);
+#pragma unroll
+                            for (int i = 0; i < 4; i++)
+                                part[i] = __builtin_fmaf(ps, tacc[i], part[i]);
+                        } else {
+                            const int si = 2 * u + (gq >> 1);
+                            const uint32_t sb = (si < 4 ? s0 >> (8 * si) : s1 >> (8 * (si - 4))) & 0xFFu;
+                            const bf16x8 Bw = fp4_to_bf16_mul(wc[u], e4m3_to_f32(sb));
+#pragma unroll
+                            for (int tt = 0; tt < NTA; tt++)
+                                part = mfma(A[u][tt], Bw, part);
+                        }
+                    }
+                    red[(wid * ST_RG + g) * 64 + lane] = part;
+                }
             }
             __syncthreads();
 
@@ -203,9 +233,11 @@ __global__ __launch_bounds__(64 * st_max_waves(NPH)) void stream_kernel(KArgs a,
 #pragma unroll
                 for (int w2 = 0; w2 < st_max_waves(NPH); w2++)
                     v[w2] = red[(min(w2, W - 1) * ST_RG + wid) * 64 + lane];
+                const int nv = min(W, s_end - (c_beg + ph * W));  // waves with a slab
 #pragma unroll
                 for (int w2 = 0; w2 < st_max_waves(NPH); w2++) {
-                    if (w2 < W && c_beg + ph * W + w2 < s_end) {  // uniform
+                    if (w2 < nv) {  // uniform: a scalar branch, not a select per add
+                        asm volatile("");
                         acc[0] += v[w2][0]; acc[1] += v[w2][1]; acc[2] += v[w2][2]; acc[3] += v[w2][3];
                     }
                 }
@@ -283,18 +315,29 @@ __global__ __launch_bounds__(64 * st_max_waves(NPH)) void stream_kernel(KArgs a,
 
 // ------------------------------------------------------------------ host
 
-template <int FMT, int ACT, int NTERM, int OUTT>
-static void launch_kc(const KArgs &a, const StCfg &c, const SkinnyWs &ws, hipStream_t st)
+template <int FMT, int ACT, int NTERM, int OUTT, bool FULLK>
+static void launch_kf(const KArgs &a, const StCfg &c, const SkinnyWs &ws, hipStream_t st)
 {
     const dim3 grid((unsigned)(c.ngroups * c.ksplit));
     const dim3 block((unsigned)(64 * c.W));
     const size_t lds = (size_t)c.W * ST_RG * 1024;
     if (c.NPH == 2)
-        hipLaunchKernelGGL((stream_kernel<FMT, ACT, NTERM, 2, OUTT>), grid, block, lds, st, a, ws, c.ngroups,
-                           c.Nh);
+        hipLaunchKernelGGL((stream_kernel<FMT, ACT, NTERM, 2, OUTT, FULLK>), grid, block, lds, st, a, ws,
+                           c.ngroups, c.Nh);
     else
-        hipLaunchKernelGGL((stream_kernel<FMT, ACT, NTERM, 1, OUTT>), grid, block, lds, st, a, ws, c.ngroups,
-                           c.Nh);
+        hipLaunchKernelGGL((stream_kernel<FMT, ACT, NTERM, 1, OUTT, FULLK>), grid, block, lds, st, a, ws,
+                           c.ngroups, c.Nh);
+}
+
+// K a whole number of slabs: no unit or activation masking at all
+template <int FMT, int ACT, int NTERM, int OUTT>
+static void launch_kc(const KArgs &a, const StCfg &c, const SkinnyWs &ws, hipStream_t st)
+{
+    constexpr int KS = FMT == FMT_Q8 ? 64 : 128;
+    if (a.K % KS == 0)
+        launch_kf<FMT, ACT, NTERM, OUTT, true>(a, c, ws, st);
+    else
+        launch_kf<FMT, ACT, NTERM, OUTT, false>(a, c, ws, st);
 }
 
 template <int FMT>
