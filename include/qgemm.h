@@ -113,14 +113,12 @@ typedef enum qgemm_tier {
  *      Q8_0 : byte 8u + j is q (int8) for j = 0..7, u = 0..1;
  *      FP4  : byte 4u + j holds the codes of k = ... + 2j (low nibble) and
  *             ... + 2j + 1 (high nibble), u = 0..3.
- * 2. Scales: at a QGEMM_ALIGN-rounded offset, 256-byte records, G slabs each
- *    (G = 4 for Q8_0 and MXFP4, 2 for NVFP4; SG = ceil(S / G) records per row
- *    tile); record (rt, q) is at (rt * SG + q) * 256 and its bytes
- *    16r .. 16r+15 hold row r's scales for slabs qG .. qG+G-1, slab by slab,
- *    blocks in k order:
- *      Q8_0 : 2 fp16 d per slab (4 bytes);
- *      MXFP4: 4 E8M0 bytes per slab;
- *      NVFP4: 8 E4M3 bytes per slab (one per 16 weights).
+ * 2. Scales: at a QGEMM_ALIGN-rounded offset, one record per slab, in the
+ *    codes' order: record (rt, s) is at ((rt * S) + s) * 16 * E and its bytes
+ *    E*r .. E*r+E-1 hold row r's scales of the slab, blocks in k order:
+ *      Q8_0 : E = 4, 2 fp16 d;
+ *      MXFP4: E = 4, 4 E8M0 bytes;
+ *      NVFP4: E = 8, 8 E4M3 bytes (one per 16 weights).
  * 3. NVFP4 only, at the next QGEMM_ALIGN offset, 256 bytes:
  *      int32 ntensors, int32 rows_per_tensor, int32 0, int32 0,
  *      float g[QGEMM_MAX_TENSORS];  row n uses g[n / rows_per_tensor].

@@ -255,7 +255,6 @@ static KArgs make_args(const Problem &p, int64_t B, const void *w, const void *x
     a.K = (int)p.K;
     a.S = (int)p.L.S;
     a.RT = (int)p.L.RT;
-    a.SG = (int)p.L.SG;
     a.scale_off = p.L.scale_off;
     a.meta_off = p.L.meta_off;
     return a;
@@ -343,7 +342,7 @@ int qgemm_pack(qgemm_format fmt, int64_t N, int64_t K, const void *codes, const 
             const int64_t first = s * per_slab;
             const int64_t cnt = first >= nsc ? 0 : (nsc - first < per_slab ? nsc - first : per_slab);
             if (cnt > 0)
-                memcpy(o + scale_offset(L.scale_off, L.SG, (int)fmt, n / 16, (int)(n % 16), (int)s),
+                memcpy(o + scale_offset(L.scale_off, L.S, (int)fmt, n / 16, (int)(n % 16), (int)s),
                        src + first * esz, (size_t)(cnt * esz));
         }
     }
@@ -547,7 +546,6 @@ int qgemm_dequantize(qgemm_format fmt, const void *w, float *w_out, int64_t N, i
     a.K = (int)K;
     a.S = (int)L.S;
     a.RT = (int)L.RT;
-    a.SG = (int)L.SG;
     a.scale_off = L.scale_off;
     a.meta_off = L.meta_off;
     hipError_t e0 = launch_dequant((int)fmt, a, w_out, (hipStream_t)stream);

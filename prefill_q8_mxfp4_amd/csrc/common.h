@@ -37,7 +37,6 @@ struct KArgs {
     int B, N, K;
     int S;              // slabs per row tile
     int RT;             // row tiles
-    int SG;             // 256-byte scale records per row tile
     int64_t scale_off;  // scale region offset
     int64_t meta_off;   // NVFP4 tensor-scale record offset (or -1)
 };
@@ -246,7 +245,7 @@ __device__ __forceinline__ float silu(float t)
 template <int FMT>
 __device__ __forceinline__ const uint8_t *slab_scales(const KArgs &a, int64_t rt, int r, int s)
 {
-    return a.w + scale_offset(a.scale_off, a.SG, FMT, rt, r, s);
+    return a.w + scale_offset(a.scale_off, a.S, FMT, rt, r, s);
 }
 
 __device__ __forceinline__ float tensor_scale(const KArgs &a, int n)

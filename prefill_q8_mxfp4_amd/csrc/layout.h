@@ -3,10 +3,10 @@
 // Row tiles of 16 rows; slabs of KS weights along K (64 for Q8_0, 128 for the
 // FP4 formats), 1024 bytes each, laid out so that 16-byte chunk L of a slab is
 // exactly the operand that lane L of a wave feeds to a 16x16x32 bf16 MFMA for
-// each 32-wide unit of the slab (row L % 16, k-group L / 16).  Scales follow
-// in 256-byte records per row tile (16 bytes per row covering G consecutive
-// slabs), so the scales a wave needs for a slab sit in two cache lines; NVFP4
-// adds a 256-byte tensor-scale record.
+// each 32-wide unit of the slab (row L % 16, k-group L / 16).  Scales follow,
+// one contiguous record of the 16 rows per (row tile, slab) in the codes'
+// order, so the scales of a slab are one 64-byte (128-byte for NVFP4) piece
+// of a cache line; NVFP4 adds a 256-byte tensor-scale record.
 #pragma once
 #include <stdint.h>
 
@@ -22,8 +22,6 @@ struct Layout {
     int64_t KS;          // weights per slab along K
     int64_t S;           // slabs per row tile
     int64_t RT;          // row tiles
-    int64_t G;           // slabs per 256-byte scale record of a row tile
-    int64_t SG;          // scale records per row tile
     int64_t scale_off;   // byte offset of the scale region
     int64_t meta_off;    // byte offset of the NVFP4 tensor-scale record (or -1)
     int64_t total;       // total bytes
@@ -32,17 +30,22 @@ struct Layout {
 
 // Scale bytes of one row for one slab: Q8_0 two fp16, MXFP4 four E8M0,
 // NVFP4 eight E4M3.
-__host__ __device__ static inline int scale_bytes_per_slab(int fmt)
+__host__ __device__ constexpr int scale_bytes_per_slab(int fmt)
 {
     return fmt == FMT_NV ? 8 : 4;
 }
 
-// Byte offset of the scales of row r (0..15) of row tile rt for slab s.
-__host__ __device__ static inline int64_t scale_offset(int64_t scale_off, int64_t SG, int fmt, int64_t rt,
-                                                       int r, int s)
+// Bytes of the scale record of one (row tile, slab): 16 rows.
+__host__ __device__ constexpr int scale_record_bytes(int fmt)
 {
-    const int g = fmt == FMT_NV ? 2 : 4;
-    return scale_off + ((rt * SG + s / g) << 8) + (r << 4) + (s % g) * scale_bytes_per_slab(fmt);
+    return 16 * scale_bytes_per_slab(fmt);
+}
+
+// Byte offset of the scales of row r (0..15) of row tile rt for slab s.
+__host__ __device__ static inline int64_t scale_offset(int64_t scale_off, int64_t S, int fmt, int64_t rt, int r,
+                                                       int64_t s)
+{
+    return scale_off + (rt * S + s) * scale_record_bytes(fmt) + r * scale_bytes_per_slab(fmt);
 }
 
 static inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
@@ -63,11 +66,9 @@ static inline bool make_layout(int fmt, int64_t N, int64_t K, Layout *L)
     L->Kp = round_up(K, L->KS);
     L->S = L->Kp / L->KS;
     L->RT = L->Np / 16;
-    L->G = fmt == FMT_NV ? 2 : 4;
-    L->SG = (L->S + L->G - 1) / L->G;
     int64_t codes = L->RT * L->S * 1024;
     L->scale_off = round_up(codes, QGEMM_ALIGN);
-    int64_t end = L->scale_off + L->RT * L->SG * 256;
+    int64_t end = L->scale_off + L->RT * L->S * scale_record_bytes(fmt);
     if (fmt == FMT_NV) {
         L->meta_off = round_up(end, QGEMM_ALIGN);
         L->total = L->meta_off + 256;

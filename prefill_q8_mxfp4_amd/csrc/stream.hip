@@ -47,7 +47,6 @@ __global__ __launch_bounds__(64 * st_max_waves(NPH)) void stream_kernel(KArgs a,
     constexpr int NTA = ACT == ACT_F32 ? NTERM : 1;
     constexpr int XPU = ACT == ACT_F32 ? 2 : 1;  // 16-byte activation loads per unit
     constexpr int XB = ACT == ACT_F32 ? 4 : 2;   // bytes per activation
-    constexpr int SG_SLABS = FMT == FMT_NV ? 2 : 4;  // slabs per 256-byte scale record
     constexpr int SBYTES = FMT == FMT_NV ? 8 : 4;    // scale bytes per row and slab
 
     extern __shared__ f32x4 red[];             // [W][ST_RG][64]: one phase's partial tiles
@@ -86,7 +85,7 @@ __global__ __launch_bounds__(64 * st_max_waves(NPH)) void stream_kernel(KArgs a,
     // goes into a scalar buffer resource (or scalar offset), so no load needs
     // vector address arithmetic.
     const int xvoff = (xb * a.K + 8 * gq) * XB;
-    const int wvoff = lane << 4, svoff = r << 4;
+    const int wvoff = lane << 4, svoff = r * SBYTES;
     const __amdgpu_buffer_rsrc_t xres = make_rsrc(a.x, (int64_t)a.B * a.K * XB);
     // row tile of the group's tile g (tiles past the last read a copy of it;
     // their outputs are never stored)
@@ -142,15 +141,14 @@ __global__ __launch_bounds__(64 * st_max_waves(NPH)) void stream_kernel(KArgs a,
             for (int g = 0; g < ST_RG; g++) {
                 const int64_t rt = tile_of(g);
                 wr[ph][g] = bload16(make_rsrc(a.w + ((rt * a.S + sc) << 10), live ? 1024 : 0), wvoff, 0);
-                const __amdgpu_buffer_rsrc_t srs =
-                    make_rsrc(a.w + a.scale_off + ((rt * a.SG + sc / SG_SLABS) << 8), live ? 256 : 0);
-                const int so = (sc % SG_SLABS) * SBYTES;
+                const __amdgpu_buffer_rsrc_t srs = make_rsrc(
+                    a.w + a.scale_off + (rt * a.S + sc) * (16 * SBYTES), live ? 16 * SBYTES : 0);
                 if constexpr (FMT == FMT_NV) {
-                    const u32x2 v = bload8(srs, svoff, so);
+                    const u32x2 v = bload8(srs, svoff, 0);
                     sr[ph][g][0] = v[0];
                     sr[ph][g][1] = v[1];
                 } else {
-                    sr[ph][g][0] = bload4(srs, svoff, so);
+                    sr[ph][g][0] = bload4(srs, svoff, 0);
                     sr[ph][g][1] = 0u;
                 }
             }

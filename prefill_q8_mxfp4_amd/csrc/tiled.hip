@@ -96,13 +96,14 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
     const int gate_rt0 = n0 / 16;                          // first (gate) row tile
     const int up_rt0 = DUAL ? (Nh + n0) / 16 : gate_rt0 + BN / 32;
     const int64_t code_bytes = (int64_t)a.RT * a.S * 1024;
-    const int64_t sc_bytes = (int64_t)a.RT * a.SG * 256;
+    constexpr int SREC = 16 * scale_bytes_per_slab(FMT);  // scale record of a (row tile, slab)
+    const int64_t sc_bytes = (int64_t)a.RT * a.S * SREC;
     const __amdgpu_buffer_rsrc_t xres =
         make_rsrc((const uint8_t *)a.x + (int64_t)b0 * a.K * ESZ, (int64_t)(a.B - b0) * a.K * ESZ);
     // weight chunk i of a thread covers staged row tile c >> 6 with c = tid + 512 i:
     // i = 0 the first BN/32 tiles, i = 1 the second (SwiGLU: gate, then up)
     const int64_t wb0 = (int64_t)gate_rt0 * a.S * 1024, wb1 = (int64_t)up_rt0 * a.S * 1024;
-    const int64_t sb0 = (int64_t)gate_rt0 * a.SG * 256, sb1 = (int64_t)up_rt0 * a.SG * 256;
+    const int64_t sb0 = (int64_t)gate_rt0 * a.S * SREC, sb1 = (int64_t)up_rt0 * a.S * SREC;
     const __amdgpu_buffer_rsrc_t wres[2] = {make_rsrc(a.w + wb0, code_bytes - wb0),
                                             make_rsrc(a.w + wb1, code_bytes - wb1)};
     const __amdgpu_buffer_rsrc_t sres[2] = {make_rsrc(a.w + a.scale_off + sb0, sc_bytes - sb0),
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
         xoff[i] = ((c / (KT / CE)) * a.K + (c % (KT / CE)) * CE) * ESZ;
     }
     const int woff = ((((tid >> 6) & (BN / 32 - 1)) * a.S) << 10) + (lane << 4);
-    const int soff = (((tid >> 6) & (BN / 32 - 1)) * a.SG << 8) + ((lane & 15) << 4);
+    const int soff = ((tid >> 6) & (BN / 32 - 1)) * a.S * SREC + (lane & 15) * scale_bytes_per_slab(FMT);
     const bool ktail = a.K % KT != 0;  // the last step has columns past K
 
     u32x4 xr[XCH];
@@ -124,8 +125,7 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
     auto load_wstage = [&](int step) {
         const int s = FP4 ? step >> 1 : step;   // slab
         const int half = FP4 ? step & 1 : 0;    // which 64 k of an FP4 slab
-        constexpr int G = FMT == FMT_NV ? 2 : 4;
-        const int ssc = ((s / G) << 8) + (s % G) * scale_bytes_per_slab(FMT);
+        const int ssc = s * SREC;
 #pragma unroll
         for (int i = 0; i < WCH; i++) {
             if constexpr (FP4) {

@@ -141,24 +141,22 @@ def _unpack(fmt, buf, n, k):
             else:
                 byte = int(buf[base + 4 * u + j // 2])
                 codes[row, kk] = (byte >> (4 * (j & 1))) & 15
-    g = 2 if fmt == "nvfp4" else 4                  # slabs per scale record
-    sg = -(-S // g)                                  # records per row tile
     soff = -(-(np_ // 16) * S * 1024 // 256) * 256
     blk = 16 if fmt == "nvfp4" else 32
     esz = 2 if fmt == "q8_0" else 1
     per_slab = ks // blk
+    rec = 8 if fmt == "nvfp4" else 4                 # scale bytes per row and slab
     nsc = k // blk
     sc = np.zeros((n, nsc * esz), dtype=np.uint8)
     for row in range(n):
         rt, r = divmod(row, 16)
         for j in range(nsc):
             s, i = divmod(j, per_slab)
-            q, p = divmod(s, g)
-            off = soff + (rt * sg + q) * 256 + r * 16 + p * per_slab * esz + i * esz
+            off = soff + ((rt * S + s) * 16 + r) * rec + i * esz
             sc[row, j * esz:(j + 1) * esz] = buf[off:off + esz]
     if fmt == "q8_0":
         sc = sc.view(np.uint16)
-    return codes, sc, soff + (np_ // 16) * sg * 256
+    return codes, sc, soff + (np_ // 16) * S * 16 * rec
 
 
 @pytest.mark.parametrize("fmt,n,k", [("q8_0", 37, 96), ("mxfp4", 21, 160), ("nvfp4", 18, 144)])
