@@ -173,6 +173,24 @@ def test_workspace_reused_across_batch_widths(cfg2):
         assert oracle.rel_fro(y, ref[:B]) <= TOL_FP32, B
 
 
+def test_workspace_shared_by_both_tiers(cfg2):
+    """One workspace for small- and large-batch calls of a bf16 plan: the
+    large-batch pieces (left as written) must not land where the small-batch
+    kernels look for published partial tiles.  Every call must match, bit for
+    bit, the same call on a fresh zeroed workspace."""
+    w, x, ref, wd = cfg2
+    plan = q.Plan("q8_0", 5120, 5120, act="bf16", out="f32")
+    xb = np.tile(torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy(), (8, 1))  # 2048 rows
+    need = max(plan.workspace_bytes(b) for b in (2048, 300, 16, 1))
+    ws = torch.zeros(need, dtype=torch.uint8, device=_dev())
+    for B in (2048, 16, 300, 1, 2048, 7, 16):
+        xs = xb[:B]
+        y = run(plan, xs, wd, workspace=ws)
+        fresh = torch.zeros(plan.workspace_bytes(B), dtype=torch.uint8, device=_dev())
+        y0 = run(plan, xs, wd, workspace=fresh if fresh.numel() else None)
+        assert np.array_equal(y.view(np.uint32), y0.view(np.uint32)), B
+
+
 # ------------------------------------------------- exact read-outs
 
 @pytest.mark.parametrize("fmt,act,tier", [("q8_0", "f32", "skinny"), ("mxfp4", "bf16", "skinny"),
