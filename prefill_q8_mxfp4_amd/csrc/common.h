@@ -55,18 +55,19 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e)
     return __uint_as_float(bits);
 }
 
-// FP8 E4M3 byte -> fp32 (exact).  Subnormals 2^-9 * M; 0x7F / 0xFF -> NaN.
+// FP8 E4M3 byte SEL of v -> fp32 (exact), one conversion: gfx950 decodes
+// the OCP E4M3 format (subnormals 2^-9 * M, signed zero, 0x7F / 0xFF -> NaN);
+// checked against a table of all 256 codes.
+template <int SEL>
+__device__ __forceinline__ float e4m3_byte_to_f32(uint32_t v)
+{
+    return __builtin_amdgcn_cvt_f32_fp8((int)v, SEL);
+}
+
+// FP8 E4M3 byte (the low byte of b) -> fp32 (exact).
 __device__ __forceinline__ float e4m3_to_f32(uint32_t b)
 {
-    uint32_t s = (b & 0x80u) << 24;
-    uint32_t em = b & 0x7Fu;
-    float v;
-    if ((em >> 3) == 0)
-        v = (float)em * 0.001953125f;  // M * 2^-9, exact
-    else
-        v = __uint_as_float(((em >> 3) + 120u) << 23 | (em & 7u) << 20);
-    v = __uint_as_float(__float_as_uint(v) | s);
-    return em == 0x7Fu ? __uint_as_float(0x7FC00000u) : v;
+    return e4m3_byte_to_f32<0>(b);
 }
 
 // E2M1 code -> fp32 (exact).

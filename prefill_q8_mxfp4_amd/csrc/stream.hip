@@ -86,6 +86,7 @@ __global__ __launch_bounds__(64 * st_max_waves(NPH)) void stream_kernel(KArgs a,
     // vector address arithmetic.
     const int xvoff = (xb * a.K + 8 * gq) * XB;
     const int wvoff = lane << 4, svoff = r * SBYTES;
+    const uint32_t nvsh = 8 * (gq >> 1);  // NVFP4: this lane's scale byte within a unit's pair
     const __amdgpu_buffer_rsrc_t xres = make_rsrc(a.x, (int64_t)a.B * a.K * XB);
     // row tile of the group's tile g (tiles past the last read a copy of it;
     // their outputs are never stored)
@@ -211,9 +212,11 @@ __global__ __launch_bounds__(64 * st_max_waves(NPH)) void stream_kernel(KArgs a,
                             for (int i = 0; i < 4; i++)
                                 part[i] = __builtin_fmaf(ps, tacc[i], part[i]);
                         } else {
-                            const int si = 2 * u + (gq >> 1);
-                            const uint32_t sb = (si < 4 ? s0 >> (8 * si) : s1 >> (8 * (si - 4))) & 0xFFu;
-                            const bf16x8 Bw = fp4_to_bf16_mul(wc[u], e4m3_to_f32(sb));
+                            // this lane's block of unit u: byte 2u + gq/2 of the row's
+                            // 8 scale bytes (shifted to a fixed byte position first)
+                            const uint32_t sv = (u < 2 ? s0 : s1) >> nvsh;
+                            const float bs = (u & 1) ? e4m3_byte_to_f32<2>(sv) : e4m3_byte_to_f32<0>(sv);
+                            const bf16x8 Bw = fp4_to_bf16_mul(wc[u], bs);
 #pragma unroll
                             for (int tt = 0; tt < NTA; tt++)
                                 part = mfma(A[u][tt], Bw, part);
