@@ -9,7 +9,8 @@ total) that every call streams them from HBM, not from the 256 MB Infinity
 Cache.  Steps are replayed from a HIP graph so host launch cost is not timed.
 
 Extra keys carry the rest of the B sweep of that shape and the prefill
-workloads (Q8_0 FFN B = 2048, MXFP4 down projection, NVFP4 fused gate+up),
+workloads (Q8_0 FFN B = 2048, MXFP4 down projection, NVFP4 fused gate+up at
+B = 1 and 16 as well as 2048),
 plus the roofline of the dominant kernel and the CPU oracle baseline.
 
     python bench.py [--steps K] [--warmup W] [--headline-only] [--no-cpu-baseline]
@@ -261,7 +262,7 @@ def main():
             w.free()
         line["sweep_q8_0_5120x5120_fp32"] = sweep
         pre = {}
-        for name, bs in (("cfg3", (2048,)), ("cfg4", (1, 16, 256, 2048)), ("cfg5", (2048,))):
+        for name, bs in (("cfg3", (2048,)), ("cfg4", (1, 16, 256, 2048)), ("cfg5", (1, 16, 2048))):
             for b in bs:
                 c = synth.CONFIGS[name]
                 nb = q.weight_bytes(c["fmt"], c["N"], c["K"])
