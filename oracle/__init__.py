@@ -12,7 +12,9 @@ What it computes (plain definitions, see qgemm_oracle.c for the decoders):
   NVFP4 ``E2M1(c) * E4M3(s)`` and ``g(n)`` the fp32 tensor scale of row n's
   tensor, applied after the sum (Atlas issue "[job] Qwen3.8-27B on Strix
   Halo: prefill 2.4x gap + DP4A verify tiers for K=5..9", section
-  "Kernel-level root cause of the gfx1151 NVFP4 prefill gap", Fix).
+  "Kernel-level root cause of the gfx1151 NVFP4 prefill gap", Fix); FP8
+  ``s * E4M3(c)`` with one fp32 scale per row and 128-wide K block (the same
+  issue's FP8-weight projection GEMM; the block rule is this build's reading).
 * fused gate+up: ``out[b][j] = SiLU(G) * U`` with G from row j and U from row
   Nh + j (Atlas issue, "What's the job?" asks for the fused gate+up
   dual-accumulator GEMM; the workload names SiLU(gate)*up).
@@ -34,7 +36,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qgemm_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-FMT = {"q8_0": 0, "mxfp4": 1, "nvfp4": 2}
+FMT = {"q8_0": 0, "mxfp4": 1, "nvfp4": 2, "fp8": 3}
 ACT = {"f32": 0, "bf16": 1}
 
 _lib = None

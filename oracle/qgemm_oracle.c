@@ -26,9 +26,15 @@
  *  - The workload definitions (Q8_0: 32 int8 + fp16 scale, w = d*q; MXFP4:
  *    32 E2M1 + E8M0; NVFP4: 16 E2M1 + E4M3 + fp32 tensor scale; fused
  *    gate+up output SiLU(gate)*up).
+ *  - Atlas issue, "Kernel ranking" and "Next lever" sections: the FP8-weight
+ *    GEMM (FP8 weights times 16-bit activations) of the GDN and attention
+ *    projections.  The pages give no block rule for it; this oracle reads it
+ *    as E4M3 codes times one fp32 scale per row and 128-wide K block (the
+ *    last block may be shorter): w = s * E4M3(c).
  *
  * Arithmetic: every decoded weight is exact in double (Q8_0 d*q has at most
- * 19 significant bits, FP4 values times their scales at most 6), and every
+ * 19 significant bits, FP4 values times their scales at most 6, an fp32
+ * scale times an E4M3 value at most 28), and every
  * product x*w is exact in double (fp32 x has 24 bits).  Sums run in fp64 in
  * increasing k.  Compile with -ffp-contract=off.
  */
@@ -40,6 +46,7 @@
 #define OR_Q8_0 0
 #define OR_MXFP4 1
 #define OR_NVFP4 2
+#define OR_FP8 3
 
 #define OR_ACT_F32 0
 #define OR_ACT_BF16 1
@@ -117,6 +124,12 @@ static double weight(int fmt, const void *codes, const void *scales,
         const uint8_t *c = (const uint8_t *)codes;
         const uint8_t *s = (const uint8_t *)scales;
         return oracle_e2m1(c[n * K + k]) * oracle_e4m3(s[n * (K / 16) + k / 16]);
+    }
+    case OR_FP8: {
+        const uint8_t *c = (const uint8_t *)codes;
+        const float *s = (const float *)scales;
+        const int64_t nb = (K + 127) / 128;  /* blocks per row */
+        return (double)s[n * nb + k / 128] * oracle_e4m3(c[n * K + k]);
     }
     }
     return NAN;

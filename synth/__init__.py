@@ -34,6 +34,10 @@ the plainest reading of the workloads:
 * NVFP4 (16-wide blocks): per-tensor fp32 ``g = amax_tensor / (448 * 6)``;
   block scale ``s = E4M3_rne(amax_block / (6 g))``; elements
   ``E2M1_rne_sat(w / (g s))``; a zero scale stores zero codes.
+* FP8 (E4M3 weights, 128-wide blocks along K, the last one possibly
+  shorter): block scale ``s = amax_block / 448`` in fp32; elements
+  ``E4M3_rne(clamp(w / s, -448, 448))``; an all-zero block stores s = 0 and
+  zero codes.
 
 E2M1 codes are 4-bit sign-magnitude: bit 3 is the sign, bits 0-2 index the
 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.  Rounding to nearest with ties to the
@@ -57,8 +61,9 @@ SID_W_UP = 4
 QK8_0 = 32
 QK_MX = 32
 QK_NV = 16
+QK_FP8 = 128  # weights per FP8 block scale along K
 
-FORMATS = ("q8_0", "mxfp4", "nvfp4")
+FORMATS = ("q8_0", "mxfp4", "nvfp4", "fp8")
 
 
 def _mix64(z: np.ndarray) -> np.ndarray:
@@ -210,6 +215,26 @@ def quantize_nvfp4(w: np.ndarray):
     return codes.reshape(n, k), sbyte, np.float32(g)
 
 
+def quantize_fp8(w: np.ndarray):
+    """w fp32 [N][K] -> (e4m3 uint8 [N][K], s float32 [N][ceil(K/128)])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    n, k = w.shape
+    if k % 32:
+        raise ValueError("K must be a multiple of 32")
+    nb = -(-k // QK_FP8)
+    wp = np.zeros((n, nb * QK_FP8), dtype=np.float32)
+    wp[:, :k] = w
+    blk = wp.reshape(n, nb, QK_FP8)
+    amax = np.max(np.abs(blk), axis=2)
+    s = (amax / np.float32(448.0)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    r = np.clip((blk / safe[:, :, None]).astype(np.float32), -448.0, 448.0).astype(np.float32)
+    codes, _ = _e4m3_rne(r)
+    codes = codes.reshape(n, nb, QK_FP8)
+    codes[s == 0] = 0
+    return np.ascontiguousarray(codes.reshape(n, nb * QK_FP8)[:, :k]), s
+
+
 def quantize(fmt: str, w: np.ndarray) -> dict:
     """Quantize fp32 weights into the logical arrays of ``fmt``."""
     if fmt == "q8_0":
@@ -221,6 +246,9 @@ def quantize(fmt: str, w: np.ndarray) -> dict:
     if fmt == "nvfp4":
         c, s, g = quantize_nvfp4(w)
         return {"fmt": fmt, "codes": c, "scales": s, "g": np.array([g], dtype=np.float32)}
+    if fmt == "fp8":
+        c, s = quantize_fp8(w)
+        return {"fmt": fmt, "codes": c, "scales": s, "g": None}
     raise ValueError(fmt)
 
 
@@ -293,6 +321,10 @@ CONFIGS = {
                  epi="none", math="bf16"),
     "cfg5": dict(fmt="nvfp4", act="bf16", N=2 * 17408, K=5120, Bs=(2048,), out="bf16",
                  epi="swiglu", math="bf16"),
+    # not one of the five: the FP8-weight (W8A16) attention-projection shape
+    # of the follow-on format
+    "fp8_attn": dict(fmt="fp8", act="bf16", N=5120, K=5120, Bs=(1, 16, 256, 2048), out="f32",
+                     epi="none", math="bf16"),
 }
 
 

@@ -143,6 +143,9 @@ def _lib_decode(w):
     if w["fmt"] == "mxfp4":
         sc = torch.from_numpy(s.copy()).view(torch.float8_e8m0fnu).double().numpy()
         return fp4[c] * np.repeat(sc, 32, axis=1)
+    if w["fmt"] == "fp8":
+        v = torch.from_numpy(c.copy()).view(torch.float8_e4m3fn).double().numpy()
+        return v * np.repeat(s.astype(np.float64), 128, axis=1)[:, :k]
     sc = torch.from_numpy(s.copy()).view(torch.float8_e4m3fn).double().numpy()
     v = fp4[c] * np.repeat(sc, 16, axis=1)
     g = w["g"].astype(np.float64)
@@ -156,6 +159,11 @@ def _lib_x(x):
 
 
 def _rand_weights(fmt, n, k, rng, ntensors=1):
+    if fmt == "fp8":
+        c = rng.integers(0, 0x7F, size=(n, k), dtype=np.uint8)   # no NaN codes
+        c |= (rng.integers(0, 2, size=c.shape, dtype=np.uint8) << 7)
+        s = (rng.random((n, -(-k // 128))) * 0.01 + 1e-4).astype(np.float32)
+        return {"fmt": fmt, "codes": c, "scales": s, "g": None}
     if fmt == "q8_0":
         q = rng.integers(-128, 128, size=(n, k), dtype=np.int16).astype(np.int8)
         d = np.float16(rng.standard_normal((n, k // 32)) * 0.01).view(np.uint16)
@@ -175,7 +183,7 @@ def _rand_x(act, b, k, rng):
     return x if act == "f32" else synth.f32_to_bf16_bits(x)
 
 
-CASES = [(f, a) for f in ("q8_0", "mxfp4", "nvfp4") for a in ("f32", "bf16")]
+CASES = [(f, a) for f in ("q8_0", "mxfp4", "nvfp4", "fp8") for a in ("f32", "bf16")]
 
 
 @pytest.mark.parametrize("fmt,act", CASES)
@@ -200,7 +208,7 @@ def test_gemm_bruteforce_exact_rational(fmt, act):
                     assert abs(Fraction(got[bi, ni]) - exact) <= Fraction(gam * mag * 1.0001)
 
 
-@pytest.mark.parametrize("fmt", ["q8_0", "mxfp4", "nvfp4"])
+@pytest.mark.parametrize("fmt", ["q8_0", "mxfp4", "nvfp4", "fp8"])
 def test_gemm_bruteforce_dyadic_equal(fmt):
     """Operands whose every partial sum is exact: the oracle must equal the
     exact rational result exactly."""
@@ -211,6 +219,8 @@ def test_gemm_bruteforce_dyadic_equal(fmt):
         w["scales"][:] = np.float16(0.25).view(np.uint16)
     elif fmt == "mxfp4":
         w["scales"][:] = 125
+    elif fmt == "fp8":
+        w["scales"][:] = 0.125
     else:
         w["scales"][:] = 0x38  # 1.0
         w["g"] = np.array([0.5], dtype=np.float32)
@@ -266,6 +276,28 @@ def test_closed_form_constant_fp4():
     y = oracle.gemm(w, x)
     assert np.all(y[:, : n // 2] == 0.25 * k * -1.5 * 2.0 * 2.0)
     assert np.all(y[:, n // 2:] == 4.0 * k * -1.5 * 2.0 * 2.0)
+
+
+def test_closed_form_constant_fp8():
+    """Constant E4M3 code and block scale: y = K * s * E4M3(c) * x exactly."""
+    n, k, b = 8, 1024, 2
+    x = synth.f32_to_bf16_bits(np.full((b, k), 0.5, dtype=np.float32))
+    w = {"fmt": "fp8", "codes": np.full((n, k), 0x40, dtype=np.uint8),      # 2.0
+         "scales": np.full((n, k // 128), 0.25, dtype=np.float32), "g": None}
+    assert np.all(oracle.gemm(w, x) == k * 0.25 * 2.0 * 0.5)
+
+
+def test_fp8_block_boundaries():
+    """One fp32 scale per 128 columns, the last block shorter: a code of 1.0
+    decodes to the scale of its own block (an off-by-one block index or a
+    32-wide block would show here)."""
+    n, k = 3, 320
+    s = np.array([[1.0, 2.0, 4.0], [8.0, 16.0, 32.0], [0.5, 0.25, 0.125]], dtype=np.float32)
+    w = {"fmt": "fp8", "codes": np.full((n, k), 0x38, dtype=np.uint8), "scales": s, "g": None}
+    d = oracle.dequant(w)
+    for r in range(n):
+        want = np.concatenate([np.full(128, s[r, 0]), np.full(128, s[r, 1]), np.full(64, s[r, 2])])
+        assert np.array_equal(d[r], want)
 
 
 def test_row_independence_and_boundary_chunks():

@@ -85,3 +85,20 @@ def test_outlier_mask_rate():
     assert not np.array_equal(w_plain["scales"], w_out["scales"])
     u = synth.uniform(0, synth.SID_W + 100, 0, 64 * 1024)
     assert 20 < int((u < 0.001).sum()) < 120
+
+
+def test_fp8_quantizer_error_bound():
+    """E4M3 keeps 3 mantissa bits: each weight is within half a step of its
+    E4M3 grid point (relative 2^-4 above 2^-6 * s, absolute 2^-10 * s below)."""
+    w = synth.normal_f32(0, 6, 32, 320, std=0.02)
+    c, s = synth.quantize_fp8(w)
+    assert c.shape == (32, 320) and s.shape == (32, 3)
+    v = torch.from_numpy(c.copy()).view(torch.float8_e4m3fn).double().numpy()
+    assert np.all(np.isfinite(v)) and np.abs(v).max() <= 448.0
+    sv = np.repeat(s.astype(np.float64), 128, axis=1)[:, :320]
+    rec = v * sv
+    err = np.abs(rec - w.astype(np.float64))
+    bound = np.maximum(np.abs(w) * 2.0 ** -4, sv * 2.0 ** -10) * (1 + 1e-6)
+    assert np.all(err <= bound)
+    amax = np.max(np.abs(np.pad(w, ((0, 0), (0, 64))).reshape(32, 3, 128)), axis=2)
+    assert np.array_equal(s, (amax / np.float32(448.0)).astype(np.float32))
