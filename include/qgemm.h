@@ -12,7 +12,8 @@
  * 2.4x gap + DP4A verify tiers for K=5..9", section "Kernel-level root cause
  * of the gfx1151 NVFP4 prefill gap", Fix), plus the fused gate+up
  * dual-accumulator GEMM with a SiLU*mul epilogue that the same Atlas issue
- * asks for in "What's the job?".
+ * asks for in "What's the job?", and the FP8-weight (W8A16) GEMM of the
+ * attention and GDN projections in the same issue's "Kernel ranking".
  *
  * There is no batch limit: every B >= 0 runs in one call, with no host loop
  * over batch chunks (B = 0 is a no-op).
@@ -34,6 +35,12 @@
  *  - QGEMM_NVFP4: E2M1 codes c[N][K] and FP8-E4M3 s[N][K/16], plus an fp32
  *                 tensor scale g per tensor;  w = g * E2M1(c) * E4M3(s), with
  *                 g applied to the finished sum.
+ *  - QGEMM_FP8:   FP8-E4M3 codes c[N][K] (OCP E4M3: bias 7, no infinities,
+ *                 0x7F/0xFF NaN) and one fp32 scale s[N][ceil(K/128)] per
+ *                 128-wide block along K (the last block may be shorter);
+ *                 w = s * E4M3(c).  (The pages fix no block rule for their
+ *                 FP8 weights; per-row 128-blocks also carry per-channel and
+ *                 128x128-block scales.)
  *  E2M1 code bits: sign (bit 3), exponent (bits 2-1, bias 1), mantissa (bit 0):
  *  magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
  */
@@ -59,7 +66,8 @@ typedef enum qgemm_status {
 typedef enum qgemm_format {
     QGEMM_Q8_0 = 0,
     QGEMM_MXFP4 = 1,
-    QGEMM_NVFP4 = 2
+    QGEMM_NVFP4 = 2,
+    QGEMM_FP8 = 3
 } qgemm_format;
 
 typedef enum qgemm_dtype {
@@ -83,8 +91,9 @@ typedef enum qgemm_math {
     QGEMM_MATH_FP32 = 0,
     /* bf16 operands: fp32 activations are rounded to bf16 (nearest even) in the
      * kernel; bf16 activations enter as they are.  Decoded MXFP4 and NVFP4
-     * weights are exact in bf16; a Q8_0 weight d*q is rounded once to bf16 in
-     * the large-batch tier.  Relative Frobenius error <= 1e-2. */
+     * weights are exact in bf16; a Q8_0 weight d*q or an FP8 weight s*E4M3(c)
+     * is rounded once to bf16 in the large-batch tier.  Relative Frobenius
+     * error <= 1e-2. */
     QGEMM_MATH_BF16 = 1
 } qgemm_math;
 
@@ -102,7 +111,7 @@ typedef enum qgemm_tier {
  * The packed device buffer that qgemm_pack writes and every kernel reads.
  *
  * Rows are grouped in row tiles of 16 (Np = N rounded up to 16) and K is cut
- * into slabs of KS = 64 (Q8_0) or 128 (MXFP4, NVFP4) weights (Kp = K rounded
+ * into slabs of KS = 64 (Q8_0, FP8) or 128 (MXFP4, NVFP4) weights (Kp = K rounded
  * up to KS; S = Kp / KS).  Padding rows and columns hold zero codes and zero
  * scale bytes.
  *
@@ -111,6 +120,7 @@ typedef enum qgemm_tier {
  *    g = L / 16, and holds, for each 32-wide unit u of the slab, the eight
  *    weights k = s*KS + 32u + 8g + 0..7 of that row:
  *      Q8_0 : byte 8u + j is q (int8) for j = 0..7, u = 0..1;
+ *      FP8  : byte 8u + j is the E4M3 code, as for Q8_0;
  *      FP4  : byte 4u + j holds the codes of k = ... + 2j (low nibble) and
  *             ... + 2j + 1 (high nibble), u = 0..3.
  * 2. Scales: at a QGEMM_ALIGN-rounded offset, one record per slab, in the
@@ -118,7 +128,9 @@ typedef enum qgemm_tier {
  *    E*r .. E*r+E-1 hold row r's scales of the slab, blocks in k order:
  *      Q8_0 : E = 4, 2 fp16 d;
  *      MXFP4: E = 4, 4 E8M0 bytes;
- *      NVFP4: E = 8, 8 E4M3 bytes (one per 16 weights).
+ *      NVFP4: E = 8, 8 E4M3 bytes (one per 16 weights);
+ *      FP8  : E = 4, the fp32 scale of the 128-wide block holding the slab
+ *             (each block's scale appears in both of its slabs' records).
  * 3. NVFP4 only, at the next QGEMM_ALIGN offset, 256 bytes:
  *      int32 ntensors, int32 rows_per_tensor, int32 0, int32 0,
  *      float g[QGEMM_MAX_TENSORS];  row n uses g[n / rows_per_tensor].
@@ -131,8 +143,9 @@ size_t qgemm_weight_bytes(qgemm_format fmt, int64_t N, int64_t K);
 
 /* Host-side packer: logical arrays (host pointers) -> packed buffer (host
  * pointer, out_bytes >= qgemm_weight_bytes).  codes: Q8_0 int8 [N][K]; FP4
- * uint8 [N][K], one code (0..15) per byte.  scales: Q8_0 uint16 fp16 bits
- * [N][K/32]; MXFP4 uint8 [N][K/32]; NVFP4 uint8 [N][K/16].  tensor_scales:
+ * uint8 [N][K], one code (0..15) per byte; FP8 uint8 [N][K] E4M3 codes.
+ * scales: Q8_0 uint16 fp16 bits [N][K/32]; MXFP4 uint8 [N][K/32]; NVFP4
+ * uint8 [N][K/16]; FP8 float [N][ceil(K/128)].  tensor_scales:
  * NVFP4 only, ntensors (1..QGEMM_MAX_TENSORS, dividing N) fp32 values; NULL
  * and 0 for the other formats.  Pure host code, callable without a GPU. */
 int qgemm_pack(qgemm_format fmt, int64_t N, int64_t K, const void *codes, const void *scales,
@@ -194,8 +207,8 @@ int qgemm_destroy(qgemm_plan *plan);
 
 /* Device decode of a packed buffer to fp32 w_out[N][K] (device pointer),
  * using the kernels' own decoders: Q8_0 d*q; MXFP4 E2M1 * 2^(e-127); NVFP4
- * g * (E2M1 * E4M3) rounded once to fp32.  Every value except the NVFP4
- * product with g is exact. */
+ * g * (E2M1 * E4M3) rounded once to fp32; FP8 s * E4M3(c) rounded once to
+ * fp32.  Every other value is exact. */
 int qgemm_dequantize(qgemm_format fmt, const void *w, float *w_out, int64_t N, int64_t K,
                      void *stream);
 

@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqgemm.so")
 
 OK, EINVAL, ENOTSUP, EHIP, ENOMEM = 0, 1, 2, 3, 4
-FORMATS = {"q8_0": 0, "mxfp4": 1, "nvfp4": 2}
+FORMATS = {"q8_0": 0, "mxfp4": 1, "nvfp4": 2, "fp8": 3}
 DTYPES = {"f32": 0, "bf16": 1}
 EPILOGUES = {"none": 0, "swiglu": 1}
 MATHS = {"fp32": 0, "bf16": 1}
@@ -97,13 +97,20 @@ def weight_bytes(fmt: str, N: int, K: int) -> int:
 def pack(fmt: str, N: int, K: int, codes: np.ndarray, scales: np.ndarray, g=None) -> np.ndarray:
     """Pack logical arrays (host numpy) into the device layout (host uint8).
 
-    codes: Q8_0 int8 [N][K]; FP4 uint8 [N][K] (one code per byte).
-    scales: Q8_0 uint16 fp16 bits [N][K/32]; MXFP4 uint8 [N][K/32]; NVFP4 uint8 [N][K/16].
+    codes: Q8_0 int8 [N][K]; FP4 uint8 [N][K] (one code per byte); FP8 uint8
+    [N][K] E4M3 codes.
+    scales: Q8_0 uint16 fp16 bits [N][K/32]; MXFP4 uint8 [N][K/32]; NVFP4 uint8 [N][K/16];
+    FP8 float32 [N][ceil(K/128)].
     g: NVFP4 tensor scales (1..60 fp32 values; rows split evenly among them).
     """
     codes = np.ascontiguousarray(codes)
     scales = np.ascontiguousarray(scales)
-    assert codes.shape == (N, K)
+    if codes.shape != (N, K) or codes.itemsize != 1:
+        raise QgemmError(EINVAL, f"codes must be one byte per weight, shape ({N}, {K})")
+    want = {"q8_0": (np.uint16, K // 32), "mxfp4": (np.uint8, K // 32),
+            "nvfp4": (np.uint8, K // 16), "fp8": (np.float32, -(-K // 128))}[fmt]
+    if scales.dtype != want[0] or scales.shape != (N, want[1]):
+        raise QgemmError(EINVAL, f"{fmt} scales must be {np.dtype(want[0]).name} [{N}][{want[1]}]")
     nbytes = weight_bytes(fmt, N, K)
     if nbytes == 0:
         raise QgemmError(EINVAL, f"bad shape for {fmt}: N={N} K={K}")

@@ -309,7 +309,7 @@ int qgemm_pack(qgemm_format fmt, int64_t N, int64_t K, const void *codes, const 
     } else if (tensor_scales || ntensors) {
         return fail(QGEMM_EINVAL, "qgemm_pack: tensor scales are for NVFP4 only");
     }
-    if (fmt != QGEMM_Q8_0) {
+    if (fmt == QGEMM_MXFP4 || fmt == QGEMM_NVFP4) {
         const uint8_t *c = (const uint8_t *)codes;
         for (int64_t i = 0; i < N * K; i++)
             if (c[i] > 15)
@@ -324,7 +324,7 @@ int qgemm_pack(qgemm_format fmt, int64_t N, int64_t K, const void *codes, const 
             const int64_t s = k / L.KS, kk = k % L.KS;
             const int64_t u = kk / 32, g = (kk % 32) / 8, j = kk % 8;
             uint8_t *chunk = o + ((rt * L.S + s) << 10) + ((g * 16 + r) << 4);
-            if (fmt == QGEMM_Q8_0) {
+            if (fmt == QGEMM_Q8_0 || fmt == QGEMM_FP8) {
                 chunk[8 * u + j] = ((const uint8_t *)codes)[n * K + k];
             } else {
                 const uint8_t c = ((const uint8_t *)codes)[n * K + k];
@@ -333,6 +333,15 @@ int qgemm_pack(qgemm_format fmt, int64_t N, int64_t K, const void *codes, const 
         }
     }
     // scales: per row and slab, the slab's blocks in k order (blocks past K stay 0)
+    if (fmt == QGEMM_FP8) {
+        // one fp32 scale per 128-wide block: each slab's record holds its block's
+        const int64_t nb = (K + FP8_BLOCK - 1) / FP8_BLOCK;
+        for (int64_t n = 0; n < N; n++)
+            for (int64_t s = 0; s * L.KS < K; s++)
+                memcpy(o + scale_offset(L.scale_off, L.S, (int)fmt, n / 16, (int)(n % 16), s),
+                       (const float *)scales + n * nb + s * L.KS / FP8_BLOCK, sizeof(float));
+        return QGEMM_OK;
+    }
     const int64_t nsc = K / L.blk;                       // scales per row
     const int64_t esz = fmt == QGEMM_Q8_0 ? 2 : 1;        // bytes per scale
     const int64_t per_slab = L.KS / L.blk;               // scales per row per slab
@@ -361,7 +370,7 @@ int qgemm_create(qgemm_plan **plan, qgemm_format fmt, qgemm_dtype act, qgemm_dty
     if (!plan)
         return fail(QGEMM_EINVAL, "qgemm_create: null plan pointer");
     *plan = nullptr;
-    if ((int)fmt < 0 || (int)fmt > 2)
+    if ((int)fmt < 0 || (int)fmt > 3)
         return fail(QGEMM_EINVAL, "qgemm_create: unknown format %d", (int)fmt);
     if ((act != QGEMM_F32 && act != QGEMM_BF16) || (out != QGEMM_F32 && out != QGEMM_BF16))
         return fail(QGEMM_EINVAL, "qgemm_create: unknown dtype");

@@ -24,6 +24,7 @@ namespace qg {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -106,6 +107,37 @@ __device__ __forceinline__ bf16x8 q8_to_bf16(uint32_t lo, uint32_t hi)
     r[2] = (__bf16)sbyte_to_f32<2>(lo); r[3] = (__bf16)sbyte_to_f32<3>(lo);
     r[4] = (__bf16)sbyte_to_f32<0>(hi); r[5] = (__bf16)sbyte_to_f32<1>(hi);
     r[6] = (__bf16)sbyte_to_f32<2>(hi); r[7] = (__bf16)sbyte_to_f32<3>(hi);
+    return r;
+}
+
+// Eight FP8 E4M3 codes (two dwords, byte j = element j) -> bf16x8, exact
+// (an E4M3 value has 4 significant bits): gfx950's packed FP8 conversion,
+// unscaled; checked against all 256 codes.
+__device__ __forceinline__ bf16x8 fp8_to_bf16(uint32_t lo, uint32_t hi)
+{
+    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+    bf16x8 r;
+    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+    return r;
+}
+
+// Eight FP8 E4M3 codes times an fp32 scale -> bf16x8 (codes to fp32 exactly,
+// one fp32 multiply, one rounding to bf16).
+__device__ __forceinline__ bf16x8 fp8_scaled_to_bf16(uint32_t lo, uint32_t hi, float d)
+{
+    const f32x2 f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
+    const f32x2 f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+    const f32x2 f2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+    const f32x2 f3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+    bf16x8 r;
+    r[0] = (__bf16)(f0[0] * d); r[1] = (__bf16)(f0[1] * d);
+    r[2] = (__bf16)(f1[0] * d); r[3] = (__bf16)(f1[1] * d);
+    r[4] = (__bf16)(f2[0] * d); r[5] = (__bf16)(f2[1] * d);
+    r[6] = (__bf16)(f3[0] * d); r[7] = (__bf16)(f3[1] * d);
     return r;
 }
 
@@ -299,7 +331,7 @@ struct SkinnyWs {
 // LDS bytes of one staged slab: NTA terms x MB x units x 64 lanes x 16 B.
 __host__ __device__ constexpr int skinny_lds_per_slab(int fmt, int nta, int mb)
 {
-    return nta * mb * (fmt == FMT_Q8 ? 2 : 4) * 64 * 16;
+    return nta * mb * (slab_k(fmt) / 32) * 64 * 16;
 }
 
 // Small-batch streaming kernel for B <= 16: workgroups of W waves (8..16)

@@ -9,7 +9,7 @@ namespace qg {
 template <int FMT>
 __global__ __launch_bounds__(256) void dequant_kernel(KArgs a, float *out)
 {
-    constexpr int KS = FMT == FMT_Q8 ? 64 : 128;
+    constexpr int KS = slab_k(FMT);
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t groups = (int64_t)a.K / 8;
     if (idx >= (int64_t)a.N * groups)
@@ -27,6 +27,11 @@ __global__ __launch_bounds__(256) void dequant_kernel(KArgs a, float *out)
 #pragma unroll
         for (int j = 0; j < 8; j++)
             v[j] = (float)(int8_t)chunk[8 * u + j] * d;
+    } else if constexpr (FMT == FMT_FP8) {
+        const float d = *(const float *)sp;  // the slab's block scale
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+            v[j] = e4m3_to_f32(chunk[8 * u + j]) * d;
     } else {
         const uint32_t codes = *(const uint32_t *)(chunk + 4 * u);
         float sc;
@@ -55,6 +60,7 @@ hipError_t launch_dequant(int fmt, const KArgs &a, float *out, hipStream_t st)
     switch (fmt) {
     case FMT_Q8: hipLaunchKernelGGL(dequant_kernel<FMT_Q8>, grid, dim3(256), 0, st, a, out); break;
     case FMT_MX: hipLaunchKernelGGL(dequant_kernel<FMT_MX>, grid, dim3(256), 0, st, a, out); break;
+    case FMT_FP8: hipLaunchKernelGGL(dequant_kernel<FMT_FP8>, grid, dim3(256), 0, st, a, out); break;
     default: hipLaunchKernelGGL(dequant_kernel<FMT_NV>, grid, dim3(256), 0, st, a, out); break;
     }
     return hipGetLastError();

@@ -14,7 +14,7 @@
 
 namespace qg {
 
-enum { FMT_Q8 = 0, FMT_MX = 1, FMT_NV = 2 };
+enum { FMT_Q8 = 0, FMT_MX = 1, FMT_NV = 2, FMT_FP8 = 3 };
 
 struct Layout {
     int64_t N, K;
@@ -25,11 +25,11 @@ struct Layout {
     int64_t scale_off;   // byte offset of the scale region
     int64_t meta_off;    // byte offset of the NVFP4 tensor-scale record (or -1)
     int64_t total;       // total bytes
-    int64_t blk;         // weights per scale
+    int64_t blk;         // K granularity: weights per scale (FP8: per 32, its scales cover 128)
 };
 
 // Scale bytes of one row for one slab: Q8_0 two fp16, MXFP4 four E8M0,
-// NVFP4 eight E4M3.
+// NVFP4 eight E4M3, FP8 the fp32 scale of the 128-wide block holding the slab.
 __host__ __device__ constexpr int scale_bytes_per_slab(int fmt)
 {
     return fmt == FMT_NV ? 8 : 4;
@@ -52,16 +52,21 @@ static inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * 
 
 static inline int64_t block_of(int fmt) { return fmt == FMT_NV ? 16 : 32; }
 
+// Weights per slab along K: 64 for the byte formats, 128 for the FP4 ones.
+__host__ __device__ constexpr int slab_k(int fmt) { return fmt == FMT_Q8 || fmt == FMT_FP8 ? 64 : 128; }
+
+constexpr int FP8_BLOCK = 128;  // weights per FP8 block scale along K
+
 static inline bool make_layout(int fmt, int64_t N, int64_t K, Layout *L)
 {
-    if (fmt < FMT_Q8 || fmt > FMT_NV || N <= 0 || K <= 0)
+    if (fmt < FMT_Q8 || fmt > FMT_FP8 || N <= 0 || K <= 0)
         return false;
     if (K % block_of(fmt))
         return false;
     L->N = N;
     L->K = K;
     L->blk = block_of(fmt);
-    L->KS = fmt == FMT_Q8 ? 64 : 128;
+    L->KS = slab_k(fmt);
     L->Np = round_up(N, 16);
     L->Kp = round_up(K, L->KS);
     L->S = L->Kp / L->KS;

@@ -39,7 +39,7 @@ namespace qg {
 template <int FMT, int ACT, int NTERM, int MB, int NT, int D, int OUTT>
 __global__ __launch_bounds__(256) void skinny_kernel(KArgs a, SkinnyWs ws)
 {
-    constexpr int KS = FMT == FMT_Q8 ? 64 : 128;
+    constexpr int KS = slab_k(FMT);
     constexpr int U = KS / 32;                 // 32-wide units per slab
     constexpr bool POST = FMT != FMT_NV;       // block scale applied after the MFMA
     constexpr int NTA = ACT == ACT_F32 ? NTERM : 1;
@@ -203,6 +203,9 @@ __global__ __launch_bounds__(256) void skinny_kernel(KArgs a, SkinnyWs ws)
                         if constexpr (FMT == FMT_Q8) {
                             Bw = q8_to_bf16(wc[nt][2 * u], wc[nt][2 * u + 1]);
                             ps = fp16_bits_to_f32((sc[nt][0] >> (16 * u)) & 0xFFFFu);
+                        } else if constexpr (FMT == FMT_FP8) {
+                            Bw = fp8_to_bf16(wc[nt][2 * u], wc[nt][2 * u + 1]);
+                            ps = __uint_as_float(sc[nt][0]);  // the slab's block scale
                         } else if constexpr (FMT == FMT_MX) {
                             Bw = fp4_to_bf16(wc[nt][u], 1.0f);
                             ps = e8m0_to_f32((sc[nt][0] >> (8 * u)) & 0xFFu);
@@ -352,6 +355,7 @@ hipError_t launch_skinny(const Problem &p, const KArgs &a, const SkCfg &c, const
     switch (p.fmt) {
     case FMT_Q8: launch_f<FMT_Q8>(p, a, c, ws, nterm, st); break;
     case FMT_MX: launch_f<FMT_MX>(p, a, c, ws, nterm, st); break;
+    case FMT_FP8: launch_f<FMT_FP8>(p, a, c, ws, nterm, st); break;
     default: launch_f<FMT_NV>(p, a, c, ws, nterm, st); break;
     }
     return hipGetLastError();

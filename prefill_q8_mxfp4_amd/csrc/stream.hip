@@ -42,7 +42,7 @@ namespace qg {
 template <int FMT, int ACT, int NTERM, int NPH, int OUTT, bool FULLK>
 __global__ __launch_bounds__(64 * st_max_waves(NPH)) void stream_kernel(KArgs a, SkinnyWs ws, int ngroups, int Nh)
 {
-    constexpr int KS = FMT == FMT_Q8 ? 64 : 128;
+    constexpr int KS = slab_k(FMT);
     constexpr int U = KS / 32;                 // 32-wide units per slab
     constexpr int NTA = ACT == ACT_F32 ? NTERM : 1;
     constexpr int XPU = ACT == ACT_F32 ? 2 : 1;  // 16-byte activation loads per unit
@@ -201,6 +201,16 @@ __global__ __launch_bounds__(64 * st_max_waves(NPH)) void stream_kernel(KArgs a,
 #pragma unroll
                             for (int i = 0; i < 4; i++)
                                 part[i] = __builtin_fmaf(ps, tacc[i], part[i]);
+                        } else if constexpr (FMT == FMT_FP8) {
+                            const bf16x8 Bw = fp8_to_bf16(wc[2 * u], wc[2 * u + 1]);
+                            f32x4 tacc = mfma(A[u][0], Bw, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                            for (int tt = 1; tt < NTA; tt++)
+                                tacc = mfma(A[u][tt], Bw, tacc);
+                            const float ps = __uint_as_float(s0);  // the slab's block scale
+#pragma unroll
+                            for (int i = 0; i < 4; i++)
+                                part[i] = __builtin_fmaf(ps, tacc[i], part[i]);
                         } else if constexpr (FMT == FMT_MX) {
                             const bf16x8 Bw = fp4_to_bf16(wc[u], 1.0f);
                             f32x4 tacc = mfma(A[u][0], Bw, f32x4{0.f, 0.f, 0.f, 0.f});
@@ -334,7 +344,7 @@ static void launch_kf(const KArgs &a, const StCfg &c, const SkinnyWs &ws, hipStr
 template <int FMT, int ACT, int NTERM, int OUTT>
 static void launch_kc(const KArgs &a, const StCfg &c, const SkinnyWs &ws, hipStream_t st)
 {
-    constexpr int KS = FMT == FMT_Q8 ? 64 : 128;
+    constexpr int KS = slab_k(FMT);
     if (a.K % KS == 0)
         launch_kf<FMT, ACT, NTERM, OUTT, true>(a, c, ws, st);
     else
@@ -367,6 +377,7 @@ hipError_t launch_stream(const Problem &p, const KArgs &a, const StCfg &c, const
     switch (p.fmt) {
     case FMT_Q8: launch_sf<FMT_Q8>(p, a, c, ws, nterm, st); break;
     case FMT_MX: launch_sf<FMT_MX>(p, a, c, ws, nterm, st); break;
+    case FMT_FP8: launch_sf<FMT_FP8>(p, a, c, ws, nterm, st); break;
     default: launch_sf<FMT_NV>(p, a, c, ws, nterm, st); break;
     }
     return hipGetLastError();

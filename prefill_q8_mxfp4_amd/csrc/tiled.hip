@@ -45,7 +45,7 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
     constexpr int CE = ACT == ACT_F32 ? 4 : 8; // activations per 16-byte load
     constexpr int XCH = BM * KT / CE / NTHR;   // activation loads per thread per step
     constexpr int WCH = (BN / 16) * 64 / NTHR; // weight chunks per thread per step (2)
-    constexpr bool FP4 = FMT != FMT_Q8;
+    constexpr bool FP4 = FMT == FMT_MX || FMT == FMT_NV;  // 128-wide slabs, two steps each
     static_assert(XCH * NTHR * CE == BM * KT, "activation staging");
 
     __shared__ u32x4 xs[2][KG * XP];
@@ -190,6 +190,8 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
         if constexpr (FMT == FMT_Q8) {
             const float d = fp16_bits_to_f32((sr[i][0] >> (16 * ul)) & 0xFFFFu);
             h = q8_scaled_to_bf16(wr[i][2 * ul], wr[i][2 * ul + 1], d);
+        } else if constexpr (FMT == FMT_FP8) {
+            h = fp8_scaled_to_bf16(wr[i][2 * ul], wr[i][2 * ul + 1], __uint_as_float(sr[i][0]));
         } else if constexpr (FMT == FMT_MX) {
             const int u = 2 * half + ul;
             h = fp4_to_bf16(wr[i][ul], e8m0_to_f32((sr[i][0] >> (8 * u)) & 0xFFu));
@@ -439,6 +441,7 @@ hipError_t launch_tiled(const Problem &p, const KArgs &a, const TiCfg &c, hipStr
     switch (p.fmt) {
     case FMT_Q8: launch_tiled_f<FMT_Q8>(p, a, c, st); break;
     case FMT_MX: launch_tiled_f<FMT_MX>(p, a, c, st); break;
+    case FMT_FP8: launch_tiled_f<FMT_FP8>(p, a, c, st); break;
     default: launch_tiled_f<FMT_NV>(p, a, c, st); break;
     }
     return hipGetLastError();

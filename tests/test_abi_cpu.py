@@ -46,7 +46,8 @@ def _create(*args):
     ((0, 0, 0, 0, 0, 256, 48, 0), q.EINVAL),         # K % 32
     ((2, 1, 0, 0, 1, 256, 48, 0), q.OK),             # NVFP4: 16-wide blocks
     ((1, 1, 0, 0, 1, 256, 48, 0), q.EINVAL),         # MXFP4: K % 32
-    ((3, 0, 0, 0, 0, 256, 512, 0), q.EINVAL),        # unknown format
+    ((4, 0, 0, 0, 0, 256, 512, 0), q.EINVAL),        # unknown format
+    ((3, 0, 0, 0, 0, 256, 512, 0), q.OK),            # FP8
     ((0, 2, 0, 0, 0, 256, 512, 0), q.EINVAL),        # unknown dtype
     ((0, 0, 0, 2, 0, 256, 512, 0), q.EINVAL),        # unknown epilogue
     ((0, 0, 0, 0, 2, 256, 512, 0), q.EINVAL),        # unknown math
@@ -124,7 +125,7 @@ def test_mxfp4_density_matches_page():
 def _unpack(fmt, buf, n, k):
     """Read logical arrays back out of a packed buffer, following the layout
     the header documents (row tiles of 16, slabs, lane chunks, scale rows)."""
-    ks = 64 if fmt == "q8_0" else 128
+    ks = 64 if fmt in ("q8_0", "fp8") else 128
     kp = -(-k // ks) * ks
     np_ = -(-n // 16) * 16
     S = kp // ks
@@ -138,10 +139,26 @@ def _unpack(fmt, buf, n, k):
             base = (rt * S + s) * 1024 + (g * 16 + r) * 16
             if fmt == "q8_0":
                 codes[row, kk] = np.int8(buf[base + 8 * u + j].view(np.int8))
+            elif fmt == "fp8":
+                codes[row, kk] = buf[base + 8 * u + j]
             else:
                 byte = int(buf[base + 4 * u + j // 2])
                 codes[row, kk] = (byte >> (4 * (j & 1))) & 15
     soff = -(-(np_ // 16) * S * 1024 // 256) * 256
+    if fmt == "fp8":
+        # one fp32 per row and slab: the scale of the 128-wide block holding it
+        nb = -(-k // 128)
+        sc = np.zeros((n, nb), dtype=np.float32)
+        for row in range(n):
+            rt, r = divmod(row, 16)
+            for s_ in range(S):
+                off = soff + ((rt * S + s_) * 16 + r) * 4
+                v = buf[off:off + 4].view(np.float32)[0]
+                if s_ * 64 < k:
+                    if s_ % 2:
+                        assert v == sc[row, s_ // 2]  # both slabs of a block agree
+                    sc[row, s_ // 2] = v
+        return codes, sc, soff + (np_ // 16) * S * 16 * 4
     blk = 16 if fmt == "nvfp4" else 32
     esz = 2 if fmt == "q8_0" else 1
     per_slab = ks // blk
@@ -159,10 +176,15 @@ def _unpack(fmt, buf, n, k):
     return codes, sc, soff + (np_ // 16) * S * 16 * rec
 
 
-@pytest.mark.parametrize("fmt,n,k", [("q8_0", 37, 96), ("mxfp4", 21, 160), ("nvfp4", 18, 144)])
+@pytest.mark.parametrize("fmt,n,k", [("q8_0", 37, 96), ("mxfp4", 21, 160), ("nvfp4", 18, 144),
+                                     ("fp8", 19, 352)])
 def test_pack_layout_roundtrip(fmt, n, k):
     rng = np.random.default_rng(0)
-    if fmt == "q8_0":
+    if fmt == "fp8":
+        codes = rng.integers(0, 256, (n, k)).astype(np.uint8)
+        scales = rng.standard_normal((n, -(-k // 128))).astype(np.float32)
+        g = None
+    elif fmt == "q8_0":
         codes = rng.integers(-128, 128, (n, k)).astype(np.int8)
         scales = rng.integers(0, 65536, (n, k // 32)).astype(np.uint16)
         g = None

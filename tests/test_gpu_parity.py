@@ -53,6 +53,13 @@ def run(plan, x, wd, B=None, workspace="auto"):
 # ----------------------------------------------------------- dequantize
 
 def _edge_weights(fmt, n, k, rng):
+    if fmt == "fp8":
+        # every E4M3 byte (NaN, subnormals, signed zero) and edge block scales
+        codes = (np.arange(n * k) % 256).astype(np.uint8).reshape(n, k)
+        rng.shuffle(codes.reshape(-1))
+        s = (rng.standard_normal((n, -(-k // 128))) * 0.01).astype(np.float32)
+        s.flat[:6] = [0.0, -0.0, 1e-40, 3e36, -2.0 ** -126, 1.0]  # subnormal, overflowing
+        return {"fmt": fmt, "codes": codes, "scales": s, "g": None}
     if fmt == "q8_0":
         codes = rng.integers(-128, 128, (n, k)).astype(np.int8)
         d = rng.standard_normal((n, k // 32)).astype(np.float16).view(np.uint16)
@@ -70,7 +77,8 @@ def _edge_weights(fmt, n, k, rng):
 
 
 @pytest.mark.parametrize("fmt,n,k", [("q8_0", 100, 96), ("mxfp4", 98, 160), ("nvfp4", 98, 144),
-                                     ("q8_0", 256, 512), ("mxfp4", 64, 17408 // 8)])
+                                     ("q8_0", 256, 512), ("mxfp4", 64, 17408 // 8),
+                                     ("fp8", 100, 320), ("fp8", 64, 96)])
 def test_dequantize_bit_exact(fmt, n, k):
     rng = np.random.default_rng(n + k)
     w = _edge_weights(fmt, n, k, rng)
@@ -195,7 +203,8 @@ def test_workspace_shared_by_both_tiers(cfg2):
 
 @pytest.mark.parametrize("fmt,act,tier", [("q8_0", "f32", "skinny"), ("mxfp4", "bf16", "skinny"),
                                           ("nvfp4", "bf16", "skinny"), ("mxfp4", "bf16", "tiled"),
-                                          ("nvfp4", "bf16", "tiled")])
+                                          ("nvfp4", "bf16", "tiled"), ("fp8", "f32", "skinny"),
+                                          ("fp8", "bf16", "skinny")])
 def test_one_hot_reads_out_decoded_weights(fmt, act, tier):
     """x = e_j makes y[b][n] = w[n][j]: the decoded weights, read through the
     whole GEMM path, must be exact."""
@@ -207,6 +216,9 @@ def test_one_hot_reads_out_decoded_weights(fmt, act, tier):
         w["scales"] = rng.standard_normal((n, k // 32)).astype(np.float16).view(np.uint16)
     elif fmt == "mxfp4":
         w["scales"] = rng.integers(110, 140, (n, k // 32)).astype(np.uint8)
+    elif fmt == "fp8":
+        w["scales"] = (rng.random((n, k // 128)) + 0.5).astype(np.float32)
+        w["codes"][(w["codes"] & 0x7F) == 0x7F] = 0x3C  # no NaN codes
     else:
         w["scales"] = rng.integers(1, 0x7E, (n, k // 16)).astype(np.uint8)
         w["g"] = np.array([1.0, 1.0], dtype=np.float32)
@@ -219,6 +231,28 @@ def test_one_hot_reads_out_decoded_weights(fmt, act, tier):
     y = run(plan, x, w_dev(w))
     dq = oracle.dequant(w, apply_g=True)
     assert np.array_equal(y, dq[:, cols].T.astype(np.float32).astype(np.float64))
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "fp8"])
+def test_one_hot_tiled_rounds_decoded_weights_once(fmt):
+    """The large-batch tier folds the block scale into a bf16 operand: the
+    one-hot read-out is the decoded weight rounded (fp32, then bf16) once."""
+    n, k = 80, 512
+    rng = np.random.default_rng(10)
+    w = _edge_weights(fmt, n, k, rng)
+    if fmt == "q8_0":
+        w["scales"] = rng.standard_normal((n, k // 32)).astype(np.float16).view(np.uint16)
+    else:
+        w["scales"] = (rng.random((n, k // 128)) + 0.5).astype(np.float32)
+        w["codes"][(w["codes"] & 0x7F) == 0x7F] = 0x3C
+    cols = [0, 1, 31, 32, 63, 64, 127, 128, 300, 511]
+    x = np.zeros((len(cols), k), dtype=np.float32)
+    for i, j in enumerate(cols):
+        x[i, j] = 1.0
+    plan = q.Plan(fmt, n, k, act="bf16", out="f32", tier="tiled")
+    y = run(plan, synth.f32_to_bf16_bits(x), w_dev(w))
+    ref = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(oracle.dequant(w)[:, cols].T.astype(np.float32)))
+    assert np.array_equal(y, ref.astype(np.float64))
 
 
 @pytest.mark.parametrize("tier,math", [("skinny", "fp32"), ("tiled", "bf16")])
@@ -241,13 +275,14 @@ def test_closed_form_constant_is_exact(tier, math):
 @pytest.mark.parametrize("fmt,act,math,out", [
     ("q8_0", "f32", "fp32", "f32"), ("q8_0", "f32", "bf16", "f32"), ("q8_0", "bf16", "bf16", "bf16"),
     ("mxfp4", "bf16", "bf16", "f32"), ("mxfp4", "f32", "fp32", "f32"),
-    ("nvfp4", "bf16", "bf16", "f32"), ("nvfp4", "f32", "fp32", "bf16")])
+    ("nvfp4", "bf16", "bf16", "f32"), ("nvfp4", "f32", "fp32", "bf16"),
+    ("fp8", "bf16", "bf16", "f32"), ("fp8", "f32", "fp32", "f32")])
 @pytest.mark.parametrize("tier", ["skinny", "tiled"])
 def test_ragged_shapes(fmt, act, math, out, tier):
     if tier == "tiled" and math == "fp32":
         pytest.skip("fp32 math runs in the skinny tier only")
     n = 100
-    k = {"q8_0": 96, "mxfp4": 160, "nvfp4": 144}[fmt]
+    k = {"q8_0": 96, "mxfp4": 160, "nvfp4": 144, "fp8": 160}[fmt]
     w = synth.gen_weights(fmt, n, k, seed=1)
     for B in (1, 3, 17, 33, 65, 130):
         xf = synth.gen_x_f32(B, k, seed=2)
@@ -311,6 +346,40 @@ def test_mxfp4_down_projection(cfg4, B):
     err = oracle.rel_fro(y[bi, ni], oracle.gemm_at(w, x[:B], bi, ni))
     print(f"cfg4 B={B} tier={plan.tier(B)} rel_fro(sampled)={err:.3e}")
     assert err <= TOL_BF16
+
+
+@pytest.fixture(scope="module")
+def fp8_attn():
+    w = synth.gen_config_weights("fp8_attn")
+    x = synth.gen_config_x("fp8_attn", 2048)
+    return w, x, w_dev(w)
+
+
+@pytest.mark.parametrize("B", synth.CONFIGS["fp8_attn"]["Bs"])
+def test_fp8_attention_projection(fp8_attn, B):
+    """FP8 E4M3 weights (128-wide block scales) x bf16 activations at the
+    K = N = 5120 projection shape, every tier by B."""
+    w, x, wd = fp8_attn
+    plan = q.Plan("fp8", 5120, 5120, act="bf16", out="f32")
+    y = run(plan, x[:B], wd)
+    assert np.all(np.isfinite(y))
+    bi, ni = _samples(B, 5120, 3000, B + 7)
+    err = oracle.rel_fro(y[bi, ni], oracle.gemm_at(w, x[:B], bi, ni))
+    print(f"fp8 B={B} tier={plan.tier(B)} rel_fro(sampled)={err:.3e}")
+    assert err <= TOL_BF16
+
+
+@pytest.mark.parametrize("B", [1, 16, 70])
+def test_fp8_fp32_math(fp8_attn, B):
+    """FP8 weights with fp32 activations in fp32-faithful math: 1e-5."""
+    w, _, wd = fp8_attn
+    x = synth.gen_x_f32(B, 5120, seed=3)
+    plan = q.Plan("fp8", 5120, 5120, act="f32", out="f32", math="fp32")
+    y = run(plan, x, wd)
+    bi, ni = _samples(B, 5120, 3000, B + 11)
+    err = oracle.rel_fro(y[bi, ni], oracle.gemm_at(w, x, bi, ni))
+    print(f"fp8 fp32-math B={B} rel_fro(sampled)={err:.3e}")
+    assert err <= TOL_FP32
 
 
 def test_nvfp4_fused_gate_up_swiglu_2048():
