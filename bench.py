@@ -10,7 +10,7 @@ Cache.  Steps are replayed from a HIP graph so host launch cost is not timed.
 
 Extra keys carry the rest of the B sweep of that shape and the prefill
 workloads (Q8_0 FFN B = 2048, MXFP4 down projection, NVFP4 fused gate+up at
-B = 1 and 16 as well as 2048),
+B = 1 and 16 as well as 2048, FP8-weight attention projection),
 plus the roofline of the dominant kernel and the CPU oracle baseline.
 
     python bench.py [--steps K] [--warmup W] [--headline-only] [--no-cpu-baseline]
@@ -262,7 +262,8 @@ def main():
             w.free()
         line["sweep_q8_0_5120x5120_fp32"] = sweep
         pre = {}
-        for name, bs in (("cfg3", (2048,)), ("cfg4", (1, 16, 256, 2048)), ("cfg5", (1, 16, 2048))):
+        for name, bs in (("cfg3", (2048,)), ("cfg4", (1, 16, 256, 2048)), ("cfg5", (1, 16, 2048)),
+                         ("fp8_attn", (1, 16, 256, 2048))):
             for b in bs:
                 c = synth.CONFIGS[name]
                 nb = q.weight_bytes(c["fmt"], c["N"], c["K"])
