@@ -66,10 +66,12 @@ static int act_terms(const Problem &p)
 }
 
 // Shape of the streaming kernel (B <= 16): W waves per workgroup, NPH slabs
-// per wave, so KC = W * NPH slabs per K split.  The search minimises the work
-// (row tiles x slabs) of the busiest CU, assuming one workgroup per CU and
-// rounds of 256; ties go to fewer splits (less partial-tile traffic), then to
-// fewer waves.  It depends on N and K only.
+// per wave, so KC = W * NPH slabs per K split.  The search minimises the
+// slabs of the busiest SIMD (a CU's four SIMDs share its W waves, and a
+// wave's decode and MFMA work is per slab), assuming one workgroup per CU and
+// rounds of 256; ties go to fewer rounds, then to fewer splits (fewer
+// partial tiles to publish and add), then to fewer waves.  It depends on N
+// and K only.
 struct StShape {
     int W, NPH;
 };
@@ -80,7 +82,7 @@ static StShape stream_shape(const Problem &p)
     const int64_t S = p.L.S;
     const int fw = env_int("QGEMM_ST_WAVES", 0), fp = env_int("QGEMM_ST_NPH", 0);
     StShape best = {8, 1};
-    int64_t best_cost = -1, best_splits = 0;
+    int64_t best_cost = -1, best_rounds = 0, best_splits = 0;
     for (int nph = 1; nph <= 2; nph++) {
         if (fp && nph != fp)
             continue;
@@ -90,10 +92,14 @@ static StShape stream_shape(const Problem &p)
             const int64_t kc = (int64_t)w * nph;
             const int64_t splits = (S + kc - 1) / kc;
             const int64_t rounds = (groups * splits + 255) / 256;
-            const int64_t cost = rounds * ST_RG * (kc < S ? kc : S);
-            if (best_cost < 0 || cost < best_cost || (cost == best_cost && splits < best_splits)) {
+            const int64_t per_wave = (kc < S ? kc : S) < w ? 1 : nph;  // slabs a wave walks
+            const int64_t cost = rounds * ((w + 3) / 4) * per_wave;
+            if (best_cost < 0 || cost < best_cost ||
+                (cost == best_cost &&
+                 (rounds < best_rounds || (rounds == best_rounds && splits < best_splits)))) {
                 best = {w, nph};
                 best_cost = cost;
+                best_rounds = rounds;
                 best_splits = splits;
             }
         }
