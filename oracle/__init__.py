@@ -199,6 +199,21 @@ def swiglu_at(w: dict, x: np.ndarray, bidx, jidx) -> np.ndarray:
     return out
 
 
+def gemm_grouped(ws: list, offsets, x: np.ndarray, swiglu_epi: bool = False) -> np.ndarray:
+    """Routed experts (Atlas issue, "Per-32-K-step hot loop" table: the routed
+    expert GEMMs reached through an expert pointer table): rows
+    offsets[e] .. offsets[e+1]-1 of x use expert e's weights ws[e].  Each
+    expert's rows are the plain GEMM (or fused gate+up) of that expert."""
+    off = np.asarray(offsets, dtype=np.int64)
+    n = ws[0]["codes"].shape[0]
+    out = np.zeros((x.shape[0], n // 2 if swiglu_epi else n), dtype=np.float64)
+    for e, w in enumerate(ws):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 > r0:
+            out[r0:r1] = swiglu(w, x[r0:r1]) if swiglu_epi else gemm(w, x[r0:r1])
+    return out
+
+
 def rel_fro(y, ref) -> float:
     """||y - ref||_F / ||ref||_F in fp64."""
     y = np.asarray(y, dtype=np.float64)

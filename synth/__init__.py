@@ -57,6 +57,8 @@ SID_W = 1
 SID_X = 2
 SID_OUTLIER = 3
 SID_W_UP = 4
+SID_ROUTE = 5
+SID_EXPERT0 = 1000  # expert e's weights use stream SID_EXPERT0 + 2e (gate) and + 2e + 1 (up)
 
 QK8_0 = 32
 QK_MX = 32
@@ -342,3 +344,33 @@ def gen_config_weights(name: str, seed: int = 0) -> dict:
 def gen_config_x(name: str, b: int, seed: int = 0) -> np.ndarray:
     c = CONFIGS[name]
     return gen_x_f32(b, c["K"], seed) if c["act"] == "f32" else gen_x_bf16(b, c["K"], seed)
+
+
+# ------------------------------------------------------------ routed experts
+
+def gen_routing(tokens: int, topk: int, experts: int, seed: int = 0):
+    """Top-k routing of `tokens` tokens over `experts` experts, each token to
+    `topk` distinct experts drawn uniformly (the experts with the k smallest
+    of its per-expert uniform keys).  Returns (token index of each routed
+    row, rows sorted by expert, stable in token order) and the expert offsets
+    [E + 1] (rows of expert e are offsets[e] .. offsets[e+1]-1)."""
+    keys = uniform(seed, SID_ROUTE, 0, tokens * experts).reshape(tokens, experts)
+    choice = np.argsort(keys, axis=1, kind="stable")[:, :topk]          # [T][topk]
+    tok = np.repeat(np.arange(tokens, dtype=np.int64), topk)
+    exp = choice.reshape(-1)
+    order = np.lexsort((tok, exp))                                       # by expert, then token
+    counts = np.bincount(exp, minlength=experts)
+    offsets = np.zeros(experts + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    return tok[order], offsets
+
+
+def gen_expert_weights(fmt: str, n: int, k: int, e: int, seed: int = 0, swiglu: bool = False) -> dict:
+    """Weights of expert e: N(0, 0.02) from the expert's own streams; with
+    swiglu, n = 2*nh rows (gate on top of up), each half its own tensor."""
+    if swiglu:
+        nh = n // 2
+        gate = gen_weights(fmt, nh, k, seed=seed, sid=SID_EXPERT0 + 2 * e)
+        up = gen_weights(fmt, nh, k, seed=seed, sid=SID_EXPERT0 + 2 * e + 1)
+        return concat_rows([gate, up])
+    return gen_weights(fmt, n, k, seed=seed, sid=SID_EXPERT0 + 2 * e)

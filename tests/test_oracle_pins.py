@@ -374,3 +374,27 @@ def test_swiglu_gate_zero_gives_zero():
     w["codes"][:nh] = 0
     x = _rand_x("bf16", 2, k, rng)
     assert np.all(oracle.swiglu(w, x) == 0.0)
+
+
+# ------------------------------------------------------------ routed experts
+
+@pytest.mark.parametrize("fmt,act,epi", [("nvfp4", "bf16", True), ("mxfp4", "bf16", False),
+                                         ("fp8", "f32", False)])
+def test_grouped_equals_per_expert_matmul(fmt, act, epi):
+    """Each expert's rows against numpy float64 matmul on that expert's
+    library-decoded weights (an off-by-one row offset or a wrong expert
+    index fails here); empty experts produce no rows."""
+    rng = np.random.default_rng(21)
+    E, n, k = 5, 32, 256
+    offsets = np.array([0, 3, 3, 20, 21, 29], dtype=np.int32)   # expert 1 empty
+    ws = [_rand_weights(fmt, n, k, rng, ntensors=2 if fmt == "nvfp4" else 1) for _ in range(E)]
+    x = _rand_x(act, int(offsets[-1]), k, rng)
+    got = oracle.gemm_grouped(ws, offsets, x, swiglu_epi=epi)
+    X = _lib_x(x)
+    for e in range(E):
+        r0, r1 = offsets[e], offsets[e + 1]
+        ref = X[r0:r1] @ _lib_decode(ws[e]).T
+        if epi:
+            G, U = ref[:, : n // 2], ref[:, n // 2:]
+            ref = G / (1.0 + np.exp(-G)) * U
+        assert np.allclose(got[r0:r1], ref, rtol=1e-12, atol=1e-300)

@@ -102,3 +102,15 @@ def test_fp8_quantizer_error_bound():
     assert np.all(err <= bound)
     amax = np.max(np.abs(np.pad(w, ((0, 0), (0, 64))).reshape(32, 3, 128)), axis=2)
     assert np.array_equal(s, (amax / np.float32(448.0)).astype(np.float32))
+
+
+def test_routing_is_topk_distinct_and_sorted():
+    tok, off = synth.gen_routing(50, 4, 12, seed=0)
+    assert off[0] == 0 and off[-1] == 50 * 4 and np.all(np.diff(off) >= 0)
+    assert np.array_equal(np.bincount(tok, minlength=50), np.full(50, 4))
+    exp = np.repeat(np.arange(12), np.diff(off))
+    for t in range(50):
+        assert len(set(exp[tok == t])) == 4          # distinct experts per token
+    for e in range(12):                              # token order inside an expert
+        r = tok[off[e]:off[e + 1]]
+        assert np.all(np.diff(r) > 0)
