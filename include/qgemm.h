@@ -178,6 +178,26 @@ int qgemm_create(qgemm_plan **plan, qgemm_format fmt, qgemm_dtype act, qgemm_dty
 int qgemm_run(const qgemm_plan *plan, int64_t B, const void *w, const void *x, void *y,
               void *stream);
 
+/* Routed experts (the Atlas issue's routed-expert GEMMs reached through an
+ * expert pointer table, "Per-32-K-step hot loop" and the 512-expert, top-10
+ * routed MoE of its validation plan): E experts share the plan's format,
+ * shape, dtypes and epilogue; rows offsets[e] .. offsets[e+1]-1 of x and y
+ * use expert e's packed weights w_table[e].
+ *   w_table: device array of E device pointers (each 16-byte aligned, laid out
+ *            as above for the plan's N and K; NVFP4 tensor scales per expert);
+ *   offsets: device int32 [E + 1], offsets[0] = 0, non-decreasing,
+ *            offsets[E] = T (the caller sorts the routed rows by expert);
+ *   x: [T][K] routed activation rows; y: [T][N] (or [T][N/2] with SwiGLU).
+ * Experts with no rows cost only a scan.  One launch of the large-batch
+ * kernel, unsplit, so each expert's rows are bitwise those of a qgemm_run of
+ * that expert in the large-batch tier without a workspace.  Needs
+ * QGEMM_MATH_BF16 and a plan not forced to the small-batch tier
+ * (QGEMM_ENOTSUP otherwise).  T = 0 returns QGEMM_OK and enqueues nothing.
+ * The offsets are read on the device and not validated there: offsets that
+ * break the rules above make the kernel read and write outside x and y. */
+int qgemm_run_grouped(const qgemm_plan *plan, int64_t E, int64_t T, const void *const *w_table,
+                      const int32_t *offsets, const void *x, void *y, void *stream);
+
 /* Bytes of device workspace with which qgemm_run_ws may split K across
  * workgroups for this plan and B (0 when the chosen tier does not use one). */
 size_t qgemm_workspace_bytes(const qgemm_plan *plan, int64_t B);

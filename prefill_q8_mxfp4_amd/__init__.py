@@ -33,6 +33,7 @@ ALIGN = 256
 MAX_TENSORS = 60
 
 EXPORTS = ("qgemm_weight_bytes", "qgemm_pack", "qgemm_create", "qgemm_run", "qgemm_run_ws",
+           "qgemm_run_grouped",
            "qgemm_workspace_bytes", "qgemm_plan_tier",
            "qgemm_destroy", "qgemm_dequantize", "qgemm_strerror", "qgemm_last_error",
            "qgemm_version")
@@ -67,6 +68,8 @@ def lib():
     L.qgemm_run.argtypes = [vp, i64, vp, vp, vp, vp]
     L.qgemm_run_ws.restype = i32
     L.qgemm_run_ws.argtypes = [vp, i64, vp, vp, vp, vp, sz, vp]
+    L.qgemm_run_grouped.restype = i32
+    L.qgemm_run_grouped.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
     L.qgemm_workspace_bytes.restype = sz
     L.qgemm_workspace_bytes.argtypes = [vp, i64]
     L.qgemm_plan_tier.restype = i32
@@ -217,6 +220,28 @@ class Plan:
             wsp, wsn = _dev_ptr(workspace, "workspace"), workspace.numel()
         _check(lib().qgemm_run_ws(self._h, B, _dev_ptr(w, "w"), _dev_ptr(x, "x"),
                                   _dev_ptr(y, "y"), wsp, wsn, _stream_ptr(stream)))
+        return y
+
+    def run_grouped(self, x, w_table, offsets, y, stream=None):
+        """Routed experts: rows offsets[e] .. offsets[e+1]-1 of x and y use the
+        packed weights at device address w_table[e].  w_table: int64 tensor of
+        E device addresses (e.g. [t.data_ptr() for t in expert_buffers]) on the
+        GPU; offsets: int32 [E + 1] on the GPU; x [T][K], y [T][out_cols]."""
+        import torch
+
+        T = x.shape[0]
+        E = w_table.numel()
+        want_x = torch.float32 if self.act == "f32" else torch.bfloat16
+        want_y = torch.float32 if self.out == "f32" else torch.bfloat16
+        if x.dtype != want_x or y.dtype != want_y:
+            raise TypeError("dtype mismatch: x %s, y %s" % (x.dtype, y.dtype))
+        if w_table.dtype != torch.int64 or offsets.dtype != torch.int32 or offsets.numel() != E + 1:
+            raise TypeError("w_table must be int64 [E], offsets int32 [E + 1]")
+        if x.numel() < T * self.K or y.numel() < T * self.out_cols:
+            raise ValueError("x or y too small")
+        _check(lib().qgemm_run_grouped(self._h, E, T, _dev_ptr(w_table, "w_table"),
+                                       _dev_ptr(offsets, "offsets"), _dev_ptr(x, "x"),
+                                       _dev_ptr(y, "y"), _stream_ptr(stream)))
         return y
 
     def close(self):

@@ -536,6 +536,46 @@ int qgemm_run_ws(const qgemm_plan *plan, int64_t B, const void *w, const void *x
     return QGEMM_OK;
 }
 
+int qgemm_run_grouped(const qgemm_plan *plan, int64_t E, int64_t T, const void *const *w_table,
+                      const int32_t *offsets, const void *x, void *y, void *stream)
+{
+    if (!plan || plan->magic != PLAN_MAGIC)
+        return fail(QGEMM_EINVAL, "qgemm_run_grouped: not a live plan");
+    const Problem &p = plan->p;
+    if (E < 1 || E > (1 << 20))
+        return fail(QGEMM_EINVAL, "qgemm_run_grouped: E=%lld outside 1..2^20", (long long)E);
+    if (T < 0 || T > (1ll << 30))
+        return fail(QGEMM_EINVAL, "qgemm_run_grouped: T=%lld outside 0..2^30", (long long)T);
+    if (p.math == QGEMM_MATH_FP32 || plan->forced_tier == QGEMM_TIER_SKINNY)
+        return fail(QGEMM_ENOTSUP, "qgemm_run_grouped: routed experts run in the large-batch tier "
+                                   "(bf16 math, tier not forced to skinny)");
+    if (T == 0)
+        return QGEMM_OK;
+    if (!w_table || !offsets || !x || !y)
+        return fail(QGEMM_EINVAL, "qgemm_run_grouped: null pointer");
+    if (!aligned16(x) || !aligned16(y) || ((uintptr_t)w_table & 7u) || ((uintptr_t)offsets & 3u))
+        return fail(QGEMM_EINVAL, "qgemm_run_grouped: misaligned pointer");
+    const int64_t ncols = p.epi == QGEMM_EPI_SWIGLU ? p.N / 2 : p.N;
+    if (T * p.K > (1ll << 31) - 1 || T * ncols > (1ll << 31) - 1)
+        return fail(QGEMM_EINVAL, "qgemm_run_grouped: T*K or T*N above 2^31 elements");
+    KArgs a = make_args(p, T, nullptr, x, y);
+    // BM by the mean rows per expert; an upper bound on the experts' row tiles
+    // (each expert adds at most one partial tile, and at most T experts have rows)
+    const int BM = T / E >= 192 ? 256 : 128;
+    const int64_t tiles = T / BM + (E < T ? E : T);
+    Groups g;
+    g.wtab = (const uint8_t *const *)w_table;
+    g.off = offsets;
+    g.E = (int)E;
+    g.ntiles = (int)((ncols + (p.epi == QGEMM_EPI_SWIGLU ? 127 : 255)) / (p.epi == QGEMM_EPI_SWIGLU ? 128 : 256));
+    if (tiles * g.ntiles > 0x7FFFFFFFll)
+        return fail(QGEMM_EINVAL, "qgemm_run_grouped: grid too large");
+    const hipError_t e = launch_grouped(p, a, g, BM, tiles, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "qgemm_run_grouped: kernel launch");
+    return QGEMM_OK;
+}
+
 int qgemm_run(const qgemm_plan *plan, int64_t B, const void *w, const void *x, void *y, void *stream)
 {
     return qgemm_run_ws(plan, B, w, x, y, nullptr, 0, stream);

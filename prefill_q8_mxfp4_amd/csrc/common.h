@@ -398,6 +398,18 @@ struct TiCfg {
 };
 
 hipError_t launch_tiled(const Problem &p, const KArgs &a, const TiCfg &c, hipStream_t st);
+
+// Routed experts in the large-batch kernel: E packed weight buffers (device
+// array of device pointers) and E + 1 row offsets (device int32, rows of
+// expert e are off[e] .. off[e+1]-1); ntiles weight tiles per expert.
+struct Groups {
+    const uint8_t *const *wtab;
+    const int *off;
+    int E;
+    int ntiles;
+};
+hipError_t launch_grouped(const Problem &p, const KArgs &a, const Groups &g, int BM, int64_t tiles,
+                          hipStream_t st);
 hipError_t launch_dequant(int fmt, const KArgs &a, float *out, hipStream_t st);
 
 }  // namespace qg

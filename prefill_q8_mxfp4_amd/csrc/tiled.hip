@@ -32,8 +32,8 @@
 
 namespace qg {
 
-template <int FMT, int ACT, int OUTT, bool DUAL, int BM>
-__global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles, TiSplit sp)
+template <int FMT, int ACT, int OUTT, bool DUAL, int BM, bool GROUPED>
+__global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles, TiSplit sp, Groups grp)
 {
     constexpr int BN = 256;                    // staged weight rows
     constexpr int KT = 64;                     // K per step
@@ -55,32 +55,89 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
     const int lane = tid & 63, wid = tid >> 6;
     const int wm = wid & 1, wn = wid >> 1;
 
-    // XCD-aware order: hardware hands consecutive workgroup ids to different
-    // XCDs (id mod 8); give each XCD a contiguous range of tiles, batch tiles
-    // fastest, so the workgroups sharing an XCD's L2 share weight tiles and
-    // the same activation rows.  Whole tiles and split pieces are remapped as
-    // two separate groups (ids below and from sp.full), so both spread evenly
-    // over the XCDs.
-    const bool piece = (int)blockIdx.x >= sp.full;
-    const int g0 = piece ? sp.full : 0;
-    const int ng = piece ? (int)gridDim.x - sp.full : sp.full;
-    int t = (int)blockIdx.x - g0;
-    {
-        const int per = (ng + 7) / 8;
-        const int xcd = t % 8, loc = t / 8;
-        const int full = ng % 8 == 0 ? 8 : ng % 8;  // XCDs that own 'per' tiles
-        t = xcd < full ? xcd * per + loc : full * per + (xcd - full) * (per - 1) + loc;
+    int tile = 0, ks = 0, mt = 0, ntl = 0;
+    bool split = false;
+    if constexpr (GROUPED) {
+        // Routed experts: workgroup ids run over the experts' row tiles in
+        // expert order (weight tiles fastest).  A block scan of the per-expert
+        // row-tile counts finds this workgroup's expert and row tile; the rest
+        // of the kernel then runs on that expert's weights and rows, unsplit.
+        __shared__ int s_wsum[NTHR / 64];
+        __shared__ int s_e, s_mt;
+        const int j = (int)blockIdx.x / grp.ntiles;
+        ntl = (int)blockIdx.x % grp.ntiles;
+        if (tid == 0)
+            s_e = -1;
+        int base = 0;  // row tiles of the experts before this chunk
+        for (int e0 = 0; e0 < grp.E; e0 += NTHR) {
+            const int e = e0 + tid;
+            const int c = e < grp.E ? (grp.off[e + 1] - grp.off[e] + BM - 1) / BM : 0;
+            int v = c;  // inclusive scan within the wave
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int up = __shfl_up(v, d, 64);
+                if (lane >= d)
+                    v += up;
+            }
+            if (lane == 63)
+                s_wsum[wid] = v;
+            __syncthreads();
+            int pre = 0, tot = 0;
+#pragma unroll
+            for (int w2 = 0; w2 < NTHR / 64; w2++) {
+                const int ws2 = s_wsum[w2];
+                pre += w2 < wid ? ws2 : 0;
+                tot += ws2;
+            }
+            const int inc = base + pre + v;  // row tiles of experts <= e
+            if (c > 0 && j >= inc - c && j < inc) {
+                s_e = e;
+                s_mt = j - (inc - c);
+            }
+            base += tot;
+            __syncthreads();  // s_wsum is rewritten by the next chunk
+            if (base > j)
+                break;  // uniform
+        }
+        if (s_e < 0)
+            return;  // past the experts' last row tile (uniform)
+        const int e = s_e;
+        mt = s_mt;
+        const int r0 = grp.off[e];
+        constexpr int XSZ = ACT == ACT_F32 ? 4 : 2, YSZ = OUTT == OUT_F32 ? 4 : 2;
+        a.B = grp.off[e + 1] - r0;
+        a.w = grp.wtab[e];
+        a.x = (const uint8_t *)a.x + (int64_t)r0 * a.K * XSZ;
+        a.y = (uint8_t *)a.y + (int64_t)r0 * (DUAL ? Nh : a.N) * YSZ;
+    } else {
+        // XCD-aware order: hardware hands consecutive workgroup ids to different
+        // XCDs (id mod 8); give each XCD a contiguous range of tiles, batch tiles
+        // fastest, so the workgroups sharing an XCD's L2 share weight tiles and
+        // the same activation rows.  Whole tiles and split pieces are remapped as
+        // two separate groups (ids below and from sp.full), so both spread evenly
+        // over the XCDs.
+        const bool piece = (int)blockIdx.x >= sp.full;
+        const int g0 = piece ? sp.full : 0;
+        const int ng = piece ? (int)gridDim.x - sp.full : sp.full;
+        int t = (int)blockIdx.x - g0;
+        {
+            const int per = (ng + 7) / 8;
+            const int xcd = t % 8, loc = t / 8;
+            const int full = ng % 8 == 0 ? 8 : ng % 8;  // XCDs that own 'per' tiles
+            t = xcd < full ? xcd * per + loc : full * per + (xcd - full) * (per - 1) + loc;
+        }
+        t += g0;
+        // Tiles below sp.full run whole; each later tile is split along K into
+        // sp.S pieces (workgroups).
+        tile = t;
+        if (piece) {
+            tile = sp.full + (t - sp.full) / sp.S;
+            ks = (t - sp.full) % sp.S;
+        }
+        split = piece && sp.S > 1;
+        mt = tile % mtiles;
+        ntl = tile / mtiles;
     }
-    t += g0;
-    // Tiles below sp.full run whole; each later tile is split along K into
-    // sp.S pieces (workgroups).
-    int tile = t, ks = 0;
-    if (piece) {
-        tile = sp.full + (t - sp.full) / sp.S;
-        ks = (t - sp.full) % sp.S;
-    }
-    const bool split = piece && sp.S > 1;
-    const int mt = tile % mtiles, ntl = tile / mtiles;
     const int b0 = mt * BM;
     const int n0 = ntl * (DUAL ? BN / 2 : BN);  // first output column
     const int nsteps = (a.K + KT - 1) / KT;
@@ -400,17 +457,18 @@ static void launch_tiled_t(const KArgs &a, const TiCfg &c, hipStream_t st, int N
 {
     const dim3 grid((unsigned)c.wgs);
     const int nsplit = c.tiles - c.sp.full;
+    const Groups none = {nullptr, nullptr, 0, 0};
     if (c.BM == 128) {
-        hipLaunchKernelGGL((tiled_kernel<FMT, ACT, OUTT, DUAL, 128>), grid, dim3(512), 0, st, a, Nh, c.mtiles,
-                           c.sp);
+        hipLaunchKernelGGL((tiled_kernel<FMT, ACT, OUTT, DUAL, 128, false>), grid, dim3(512), 0, st, a, Nh,
+                           c.mtiles, c.sp, none);
         if (c.sp.S > 1) {
             const int64_t n = (int64_t)nsplit * (128 / 32) * (DUAL ? 2 : 4) * 512;
             hipLaunchKernelGGL((tiled_reduce<FMT, OUTT, DUAL, 128>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                                st, a, Nh, c.mtiles, c.sp, nsplit);
         }
     } else {
-        hipLaunchKernelGGL((tiled_kernel<FMT, ACT, OUTT, DUAL, 256>), grid, dim3(512), 0, st, a, Nh, c.mtiles,
-                           c.sp);
+        hipLaunchKernelGGL((tiled_kernel<FMT, ACT, OUTT, DUAL, 256, false>), grid, dim3(512), 0, st, a, Nh,
+                           c.mtiles, c.sp, none);
         if (c.sp.S > 1) {
             const int64_t n = (int64_t)nsplit * (256 / 32) * (DUAL ? 2 : 4) * 512;
             hipLaunchKernelGGL((tiled_reduce<FMT, OUTT, DUAL, 256>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
@@ -419,13 +477,30 @@ static void launch_tiled_t(const KArgs &a, const TiCfg &c, hipStream_t st, int N
     }
 }
 
+// Routed experts: one launch over every expert's row tiles (grid: an upper
+// bound, extra workgroups leave after the scan), BM rows per tile.
+template <int FMT, int ACT, int OUTT, bool DUAL>
+static void launch_grouped_t(const KArgs &a, const Groups &g, int BM, int64_t tiles, hipStream_t st, int Nh)
+{
+    const dim3 grid((unsigned)(tiles * g.ntiles));
+    const TiSplit none = {0, 1, nullptr, nullptr};
+    if (BM == 128)
+        hipLaunchKernelGGL((tiled_kernel<FMT, ACT, OUTT, DUAL, 128, true>), grid, dim3(512), 0, st, a, Nh, 1,
+                           none, g);
+    else
+        hipLaunchKernelGGL((tiled_kernel<FMT, ACT, OUTT, DUAL, 256, true>), grid, dim3(512), 0, st, a, Nh, 1,
+                           none, g);
+}
+
 template <int FMT>
-static void launch_tiled_f(const Problem &p, const KArgs &a, const TiCfg &c, hipStream_t st)
+static void launch_tiled_f(const Problem &p, const KArgs &a, const TiCfg &c, hipStream_t st, const Groups *g,
+                           int gBM, int64_t gtiles)
 {
     const bool f32 = p.act == QGEMM_F32, o32 = p.out == QGEMM_F32;
     const bool dual = p.epi == QGEMM_EPI_SWIGLU;
     const int Nh = (int)(p.N / 2);
-#define QG_T(A, O, D) launch_tiled_t<FMT, A, O, D>(a, c, st, Nh)
+#define QG_T(A, O, D) \
+    (g ? launch_grouped_t<FMT, A, O, D>(a, *g, gBM, gtiles, st, Nh) : launch_tiled_t<FMT, A, O, D>(a, c, st, Nh))
     if (f32) {
         if (o32) { if (dual) QG_T(ACT_F32, OUT_F32, true); else QG_T(ACT_F32, OUT_F32, false); }
         else { if (dual) QG_T(ACT_F32, OUT_BF16, true); else QG_T(ACT_F32, OUT_BF16, false); }
@@ -439,10 +514,23 @@ static void launch_tiled_f(const Problem &p, const KArgs &a, const TiCfg &c, hip
 hipError_t launch_tiled(const Problem &p, const KArgs &a, const TiCfg &c, hipStream_t st)
 {
     switch (p.fmt) {
-    case FMT_Q8: launch_tiled_f<FMT_Q8>(p, a, c, st); break;
-    case FMT_MX: launch_tiled_f<FMT_MX>(p, a, c, st); break;
-    case FMT_FP8: launch_tiled_f<FMT_FP8>(p, a, c, st); break;
-    default: launch_tiled_f<FMT_NV>(p, a, c, st); break;
+    case FMT_Q8: launch_tiled_f<FMT_Q8>(p, a, c, st, nullptr, 0, 0); break;
+    case FMT_MX: launch_tiled_f<FMT_MX>(p, a, c, st, nullptr, 0, 0); break;
+    case FMT_FP8: launch_tiled_f<FMT_FP8>(p, a, c, st, nullptr, 0, 0); break;
+    default: launch_tiled_f<FMT_NV>(p, a, c, st, nullptr, 0, 0); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_grouped(const Problem &p, const KArgs &a, const Groups &g, int BM, int64_t tiles,
+                          hipStream_t st)
+{
+    const TiCfg none{};
+    switch (p.fmt) {
+    case FMT_Q8: launch_tiled_f<FMT_Q8>(p, a, none, st, &g, BM, tiles); break;
+    case FMT_MX: launch_tiled_f<FMT_MX>(p, a, none, st, &g, BM, tiles); break;
+    case FMT_FP8: launch_tiled_f<FMT_FP8>(p, a, none, st, &g, BM, tiles); break;
+    default: launch_tiled_f<FMT_NV>(p, a, none, st, &g, BM, tiles); break;
     }
     return hipGetLastError();
 }

@@ -229,3 +229,23 @@ def test_synth_configs_pack():
     w = synth.gen_config_weights("cfg1")
     buf = q.pack_logical(w)
     assert buf.size == q.weight_bytes("q8_0", 256, 512)
+
+
+def test_grouped_argument_checks():
+    """qgemm_run_grouped validates on the host before touching the device."""
+    L = q.lib()
+    h = ctypes.c_void_p()
+    assert L.qgemm_create(ctypes.byref(h), 2, 1, 0, 0, 1, 256, 512, 0) == q.OK
+    fake = ctypes.c_void_p(0x1000)
+    assert L.qgemm_run_grouped(h, 0, 10, fake, fake, fake, fake, None) == q.EINVAL    # E = 0
+    assert L.qgemm_run_grouped(h, 4, -1, fake, fake, fake, fake, None) == q.EINVAL    # T < 0
+    assert L.qgemm_run_grouped(h, 4, 0, None, None, None, None, None) == q.OK        # T = 0: no-op
+    assert L.qgemm_run_grouped(h, 4, 10, None, fake, fake, fake, None) == q.EINVAL   # null table
+    assert L.qgemm_run_grouped(h, 4, 10, fake, fake, ctypes.c_void_p(0x1008), fake, None) == q.EINVAL
+    L.qgemm_destroy(h)
+    assert L.qgemm_create(ctypes.byref(h), 0, 0, 0, 0, 0, 256, 512, 0) == q.OK        # fp32 math
+    assert L.qgemm_run_grouped(h, 4, 10, fake, fake, fake, fake, None) == q.ENOTSUP
+    L.qgemm_destroy(h)
+    assert L.qgemm_create(ctypes.byref(h), 2, 1, 0, 0, 1, 256, 512, 1) == q.OK        # forced skinny
+    assert L.qgemm_run_grouped(h, 4, 10, fake, fake, fake, fake, None) == q.ENOTSUP
+    L.qgemm_destroy(h)
