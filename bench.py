@@ -10,7 +10,8 @@ Cache.  Steps are replayed from a HIP graph so host launch cost is not timed.
 
 Extra keys carry the rest of the B sweep of that shape and the prefill
 workloads (Q8_0 FFN B = 2048, MXFP4 down projection, NVFP4 fused gate+up at
-B = 1 and 16 as well as 2048, FP8-weight attention projection),
+B = 1 and 16 as well as 2048, FP8-weight attention projection, routed-expert
+fused gate+up),
 plus the roofline of the dominant kernel and the CPU oracle baseline.
 
     python bench.py [--steps K] [--warmup W] [--headline-only] [--no-cpu-baseline]
@@ -186,6 +187,60 @@ def copy_calibration(mib=512, reps=5):
     log(f"[bench] copy calibration: {reps} copies of {mib} MiB")
 
 
+def bench_moe(steps):
+    """Routed-expert NVFP4 fused gate+up at the scale of the Atlas issue's
+    validation plan (512 experts, top-10, 2048 tokens).  The pages give no
+    expert dimensions; K = 2048 and 2 x 512 gate/up rows stand in.  Eight
+    generated experts are copied into 512 separate buffers (real memory
+    traffic, repeating values) to bound the input generation time."""
+    import numpy as np
+    import torch
+
+    import prefill_q8_mxfp4_amd as q
+    import synth
+
+    E, topk, tokens, nh, K = 512, 10, 2048, 512, 2048
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    distinct = [torch.from_numpy(q.pack_logical(synth.gen_expert_weights("nvfp4", 2 * nh, K, e, swiglu=True)))
+                for e in range(8)]
+    bufs = [distinct[e % 8].to(dev) for e in range(E)]
+    table = torch.tensor([b.data_ptr() for b in bufs], dtype=torch.int64, device=dev)
+    tok, offsets = synth.gen_routing(tokens, topk, E)
+    T = int(offsets[-1])
+    x = torch.from_numpy(synth.gen_x_bf16(tokens, K)[tok].view(np.int16)).view(torch.bfloat16).to(dev)
+    off = torch.from_numpy(offsets).to(dev)
+    plan = q.Plan("nvfp4", 2 * nh, K, act="bf16", out="bf16", epilogue="swiglu")
+    y = torch.empty((T, nh), dtype=torch.bfloat16, device=dev)
+    log(f"[bench] moe ready in {time.time() - t0:.1f}s")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            plan.run_grouped(x, table, off, y)
+    stream.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        plan.run_grouped(x, table, off, y)
+    reps = max(10, steps // 10)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        g.replay()
+        start.record(stream)
+        for _ in range(reps):
+            g.replay()
+        end.record(stream)
+    end.synchronize()
+    ms = start.elapsed_time(end) / reps
+    flops = 2.0 * T * 2 * nh * K
+    wbytes = sum(b.numel() for b in bufs)
+    rec = {"us": round(ms * 1e3, 2), "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
+           "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+           "weight_GBs": round(wbytes / (ms * 1e-3) / 1e9, 1), "rows": T, "experts": E, "top_k": topk}
+    log(f"[bench] moe {rec}")
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -282,6 +337,7 @@ def main():
                 w.free()
                 torch.cuda.empty_cache()
         line["prefill"] = pre
+        line["routed_moe:nvfp4:512x(2x512)x2048:top10:tokens2048"] = bench_moe(args.steps)
 
     print(json.dumps(line), flush=True)
 
