@@ -85,9 +85,10 @@ typedef enum qgemm_epilogue {
 } qgemm_epilogue;
 
 typedef enum qgemm_math {
-    /* fp32-faithful: used with fp32 activations.  Weights enter exactly and
-     * activations are split into bf16 terms that together hold their full fp32
-     * value; relative Frobenius error against an exact product <= 1e-5. */
+    /* fp32-faithful: used with fp32 activations, in both tiers.  Weights enter
+     * exactly and activations are split into bf16 terms that together hold
+     * their full fp32 value; relative Frobenius error against an exact
+     * product <= 1e-5. */
     QGEMM_MATH_FP32 = 0,
     /* bf16 operands: fp32 activations are rounded to bf16 (nearest even) in the
      * kernel; bf16 activations enter as they are.  Decoded MXFP4 and NVFP4
@@ -101,7 +102,8 @@ typedef enum qgemm_math {
 typedef enum qgemm_tier {
     QGEMM_TIER_SKINNY = 1, /* weights streamed once per 16..64 batch rows straight
                               into matrix-core operands; for small B */
-    QGEMM_TIER_TILED = 2   /* batch x weight tiles staged through LDS; for large B */
+    QGEMM_TIER_TILED = 2   /* batch x weight tiles staged through LDS; for large B
+                              (B > 64 with bf16 math, B > 16 with fp32 math) */
 } qgemm_tier;
 
 #define QGEMM_FLAG_FORCE_SKINNY 0x1u
@@ -190,9 +192,8 @@ int qgemm_run(const qgemm_plan *plan, int64_t B, const void *w, const void *x, v
  *   x: [T][K] routed activation rows; y: [T][N] (or [T][N/2] with SwiGLU).
  * Experts with no rows cost only a scan.  One launch of the large-batch
  * kernel, unsplit, so each expert's rows are bitwise those of a qgemm_run of
- * that expert in the large-batch tier without a workspace.  Needs
- * QGEMM_MATH_BF16 and a plan not forced to the small-batch tier
- * (QGEMM_ENOTSUP otherwise).  T = 0 returns QGEMM_OK and enqueues nothing.
+ * that expert in the large-batch tier without a workspace.  Either math
+ * mode; a plan forced to the small-batch tier returns QGEMM_ENOTSUP.  T = 0 returns QGEMM_OK and enqueues nothing.
  * The offsets are read on the device and not validated there: offsets that
  * break the rules above make the kernel read and write outside x and y. */
 int qgemm_run_grouped(const qgemm_plan *plan, int64_t E, int64_t T, const void *const *w_table,

@@ -18,8 +18,8 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqgemm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-UNITS = ("api.hip", "skinny.hip", "stream.hip", "tiled.hip", "dequant.hip")
-HEADERS = ("common.h", "layout.h")
+UNITS = ("api.hip", "skinny.hip", "stream.hip", "tiled.hip", "tiled_fp32.hip", "dequant.hip")
+HEADERS = ("common.h", "layout.h", "tiled.h")
 
 FLAGS = [
     "--offload-arch=gfx950",

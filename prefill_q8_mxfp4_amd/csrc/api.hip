@@ -192,7 +192,7 @@ static SkCfg skinny_cfg(const Problem &p, int64_t B, bool split)
 static TiCfg tiled_cfg(const Problem &p, int64_t B, bool split)
 {
     TiCfg c;
-    c.BM = B <= 128 ? 128 : 256;
+    c.BM = p.math == QGEMM_MATH_FP32 ? 64 : B <= 128 ? 128 : 256;
     const bool dual = p.epi == QGEMM_EPI_SWIGLU;
     const int64_t cols = dual ? p.N / 2 : p.N;
     c.mtiles = (int)((B + c.BM - 1) / c.BM);
@@ -243,8 +243,8 @@ static int choose_tier(const qgemm_plan *plan, int64_t B)
     const Problem &p = plan->p;
     if (plan->forced_tier)
         return plan->forced_tier;
-    if (p.math == QGEMM_MATH_FP32)
-        return QGEMM_TIER_SKINNY;  // the only tier with the fp32-faithful split
+    if (p.math == QGEMM_MATH_FP32)  // the streaming kernel, else the faithful tiled variant
+        return B <= ST_MAX_B ? QGEMM_TIER_SKINNY : QGEMM_TIER_TILED;
     if (p.epi == QGEMM_EPI_SWIGLU)  // fused gate+up: the streaming kernel or the tiled tier
         return B <= ST_MAX_B ? QGEMM_TIER_SKINNY : QGEMM_TIER_TILED;
     return B <= 64 ? QGEMM_TIER_SKINNY : QGEMM_TIER_TILED;
@@ -414,9 +414,6 @@ int qgemm_create(qgemm_plan **plan, qgemm_format fmt, qgemm_dtype act, qgemm_dty
         else if (e && !strcmp(e, "tiled"))
             forced = QGEMM_TIER_TILED;
     }
-    if (forced == QGEMM_TIER_TILED && math == QGEMM_MATH_FP32)
-        return fail(QGEMM_ENOTSUP, "qgemm_create: the tiled tier computes in bf16; fp32 math runs "
-                                   "in the skinny tier");
     qgemm_plan *p = new (std::nothrow) qgemm_plan;
     if (!p)
         return fail(QGEMM_ENOMEM, "qgemm_create: out of host memory");
@@ -546,9 +543,9 @@ int qgemm_run_grouped(const qgemm_plan *plan, int64_t E, int64_t T, const void *
         return fail(QGEMM_EINVAL, "qgemm_run_grouped: E=%lld outside 1..2^20", (long long)E);
     if (T < 0 || T > (1ll << 30))
         return fail(QGEMM_EINVAL, "qgemm_run_grouped: T=%lld outside 0..2^30", (long long)T);
-    if (p.math == QGEMM_MATH_FP32 || plan->forced_tier == QGEMM_TIER_SKINNY)
+    if (plan->forced_tier == QGEMM_TIER_SKINNY)
         return fail(QGEMM_ENOTSUP, "qgemm_run_grouped: routed experts run in the large-batch tier "
-                                   "(bf16 math, tier not forced to skinny)");
+                                   "(tier not forced to skinny)");
     if (T == 0)
         return QGEMM_OK;
     if (!w_table || !offsets || !x || !y)
@@ -561,7 +558,7 @@ int qgemm_run_grouped(const qgemm_plan *plan, int64_t E, int64_t T, const void *
     KArgs a = make_args(p, T, nullptr, x, y);
     // BM by the mean rows per expert; an upper bound on the experts' row tiles
     // (each expert adds at most one partial tile, and at most T experts have rows)
-    const int BM = T / E >= 192 ? 256 : 128;
+    const int BM = p.math == QGEMM_MATH_FP32 ? 64 : T / E >= 192 ? 256 : 128;
     const int64_t tiles = T / BM + (E < T ? E : T);
     Groups g;
     g.wtab = (const uint8_t *const *)w_table;

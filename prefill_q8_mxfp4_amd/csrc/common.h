@@ -398,6 +398,7 @@ struct TiCfg {
 };
 
 hipError_t launch_tiled(const Problem &p, const KArgs &a, const TiCfg &c, hipStream_t st);
+hipError_t launch_tiled_fp32(const Problem &p, const KArgs &a, const TiCfg &c, hipStream_t st);
 
 // Routed experts in the large-batch kernel: E packed weight buffers (device
 // array of device pointers) and E + 1 row offsets (device int32, rows of
@@ -410,6 +411,8 @@ struct Groups {
 };
 hipError_t launch_grouped(const Problem &p, const KArgs &a, const Groups &g, int BM, int64_t tiles,
                           hipStream_t st);
+hipError_t launch_grouped_fp32(const Problem &p, const KArgs &a, const Groups &g, int BM, int64_t tiles,
+                               hipStream_t st);
 hipError_t launch_dequant(int fmt, const KArgs &a, float *out, hipStream_t st);
 
 }  // namespace qg

@@ -1,538 +1,23 @@
-// Large-batch tier: one BM x BN output tile per workgroup, bf16 MFMA from
-// LDS-staged fragments.
-//
-// 8 waves (two per SIMD) arranged 2 (batch) x 4 (weight rows); each wave owns
-// BM/2 x 64 outputs as (BM/32) x 4 tiles of v_mfma_f32_16x16x32_bf16.  K
-// advances 64 per step:
-//
-//  * activations: BM x 64 (fp32 input rounded to bf16 on the way);
-//  * weights: BN rows x 64, i.e. one Q8_0 slab or half an FP4 slab of each of
-//    the BN/16 row tiles; a thread's 16-byte (Q8_0) or 8-byte (FP4) piece of a
-//    slab chunk is decoded with its block scale folded in (exact for the FP4
-//    formats, one rounding for Q8_0) into the two bf16 fragments it feeds.
-//
-// LDS holds both operands as 16-byte fragment entries [k-group][row], rows
-// padded by one entry so neither the stage writes nor the fragment reads
-// collide in banks; it is double-buffered.  Global loads go through buffer
-// resources (fixed per-lane offsets, the step in the scalar offset, zero
-// past the data) two steps ahead, and the conversion and LDS stores of the
-// next step are interleaved by hand with the MFMA groups of the current one,
-// so each step ends in one barrier.
-//
-// Tile counts: whole rounds of 256 tiles (one per CU) run unsplit; the tiles
-// of a last, partial round may be split along K into pieces, one workgroup
-// each, whose partial tiles tiled_reduce adds in piece order.
-//
-// SwiGLU: the staged rows are BN/2 gate rows j and the BN/2 up rows Nh + j,
-// and every wave owns matching gate and up columns, so G and U of an output
-// sit in the same lane for the epilogue.
-#include <type_traits>
-
-#include "common.h"
+// Large-batch tier, bf16 math: the kernel instantiations for 128- and
+// 256-row tiles.  fp32-faithful math has its own translation unit
+// (tiled_fp32.hip) so the two compile in parallel.
+#include "tiled.h"
 
 namespace qg {
 
-template <int FMT, int ACT, int OUTT, bool DUAL, int BM, bool GROUPED>
-__global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles, TiSplit sp, Groups grp)
-{
-    constexpr int BN = 256;                    // staged weight rows
-    constexpr int KT = 64;                     // K per step
-    constexpr int KG = KT / 8;                 // 16-byte k-groups per step
-    constexpr int NTHR = 512;
-    constexpr int XP = BM + 1, WP = BN + 1;    // padded LDS row counts
-    constexpr int TM = BM / 2 / 16;            // 16-row MFMA tiles per wave (batch)
-    constexpr int TN = 4;                      // 16-col MFMA tiles per wave (weights)
-    constexpr int CE = ACT == ACT_F32 ? 4 : 8; // activations per 16-byte load
-    constexpr int XCH = BM * KT / CE / NTHR;   // activation loads per thread per step
-    constexpr int WCH = (BN / 16) * 64 / NTHR; // weight chunks per thread per step (2)
-    constexpr bool FP4 = FMT == FMT_MX || FMT == FMT_NV;  // 128-wide slabs, two steps each
-    static_assert(XCH * NTHR * CE == BM * KT, "activation staging");
-
-    __shared__ u32x4 xs[2][KG * XP];
-    __shared__ u32x4 ws[2][KG * WP];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wid = tid >> 6;
-    const int wm = wid & 1, wn = wid >> 1;
-
-    int tile = 0, ks = 0, mt = 0, ntl = 0;
-    bool split = false;
-    if constexpr (GROUPED) {
-        // Routed experts: workgroup ids run over the experts' row tiles in
-        // expert order (weight tiles fastest).  A block scan of the per-expert
-        // row-tile counts finds this workgroup's expert and row tile; the rest
-        // of the kernel then runs on that expert's weights and rows, unsplit.
-        __shared__ int s_wsum[NTHR / 64];
-        __shared__ int s_e, s_mt;
-        const int j = (int)blockIdx.x / grp.ntiles;
-        ntl = (int)blockIdx.x % grp.ntiles;
-        if (tid == 0)
-            s_e = -1;
-        int base = 0;  // row tiles of the experts before this chunk
-        for (int e0 = 0; e0 < grp.E; e0 += NTHR) {
-            const int e = e0 + tid;
-            const int c = e < grp.E ? (grp.off[e + 1] - grp.off[e] + BM - 1) / BM : 0;
-            int v = c;  // inclusive scan within the wave
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const int up = __shfl_up(v, d, 64);
-                if (lane >= d)
-                    v += up;
-            }
-            if (lane == 63)
-                s_wsum[wid] = v;
-            __syncthreads();
-            int pre = 0, tot = 0;
-#pragma unroll
-            for (int w2 = 0; w2 < NTHR / 64; w2++) {
-                const int ws2 = s_wsum[w2];
-                pre += w2 < wid ? ws2 : 0;
-                tot += ws2;
-            }
-            const int inc = base + pre + v;  // row tiles of experts <= e
-            if (c > 0 && j >= inc - c && j < inc) {
-                s_e = e;
-                s_mt = j - (inc - c);
-            }
-            base += tot;
-            __syncthreads();  // s_wsum is rewritten by the next chunk
-            if (base > j)
-                break;  // uniform
-        }
-        if (s_e < 0)
-            return;  // past the experts' last row tile (uniform)
-        const int e = s_e;
-        mt = s_mt;
-        const int r0 = grp.off[e];
-        constexpr int XSZ = ACT == ACT_F32 ? 4 : 2, YSZ = OUTT == OUT_F32 ? 4 : 2;
-        a.B = grp.off[e + 1] - r0;
-        a.w = grp.wtab[e];
-        a.x = (const uint8_t *)a.x + (int64_t)r0 * a.K * XSZ;
-        a.y = (uint8_t *)a.y + (int64_t)r0 * (DUAL ? Nh : a.N) * YSZ;
-    } else {
-        // XCD-aware order: hardware hands consecutive workgroup ids to different
-        // XCDs (id mod 8); give each XCD a contiguous range of tiles, batch tiles
-        // fastest, so the workgroups sharing an XCD's L2 share weight tiles and
-        // the same activation rows.  Whole tiles and split pieces are remapped as
-        // two separate groups (ids below and from sp.full), so both spread evenly
-        // over the XCDs.
-        const bool piece = (int)blockIdx.x >= sp.full;
-        const int g0 = piece ? sp.full : 0;
-        const int ng = piece ? (int)gridDim.x - sp.full : sp.full;
-        int t = (int)blockIdx.x - g0;
-        {
-            const int per = (ng + 7) / 8;
-            const int xcd = t % 8, loc = t / 8;
-            const int full = ng % 8 == 0 ? 8 : ng % 8;  // XCDs that own 'per' tiles
-            t = xcd < full ? xcd * per + loc : full * per + (xcd - full) * (per - 1) + loc;
-        }
-        t += g0;
-        // Tiles below sp.full run whole; each later tile is split along K into
-        // sp.S pieces (workgroups).
-        tile = t;
-        if (piece) {
-            tile = sp.full + (t - sp.full) / sp.S;
-            ks = (t - sp.full) % sp.S;
-        }
-        split = piece && sp.S > 1;
-        mt = tile % mtiles;
-        ntl = tile / mtiles;
-    }
-    const int b0 = mt * BM;
-    const int n0 = ntl * (DUAL ? BN / 2 : BN);  // first output column
-    const int nsteps = (a.K + KT - 1) / KT;
-    // this workgroup's K steps [sb, se)
-    const int spp = split ? (nsteps + sp.S - 1) / sp.S : nsteps;
-    const int sb = split ? min(nsteps, ks * spp) : 0;
-    const int se = split ? min(nsteps, sb + spp) : nsteps;
-
-    // ---- register stage of one K step.  Loads go through buffer resources:
-    // per-lane offsets are fixed, the step only moves the scalar offset, and
-    // rows or tiles past the end of the data read as zero.
-    constexpr int ESZ = ACT == ACT_F32 ? 4 : 2;
-    const int gate_rt0 = n0 / 16;                          // first (gate) row tile
-    const int up_rt0 = DUAL ? (Nh + n0) / 16 : gate_rt0 + BN / 32;
-    const int64_t code_bytes = (int64_t)a.RT * a.S * 1024;
-    constexpr int SREC = 16 * scale_bytes_per_slab(FMT);  // scale record of a (row tile, slab)
-    const int64_t sc_bytes = (int64_t)a.RT * a.S * SREC;
-    const __amdgpu_buffer_rsrc_t xres =
-        make_rsrc((const uint8_t *)a.x + (int64_t)b0 * a.K * ESZ, (int64_t)(a.B - b0) * a.K * ESZ);
-    // weight chunk i of a thread covers staged row tile c >> 6 with c = tid + 512 i:
-    // i = 0 the first BN/32 tiles, i = 1 the second (SwiGLU: gate, then up)
-    const int64_t wb0 = (int64_t)gate_rt0 * a.S * 1024, wb1 = (int64_t)up_rt0 * a.S * 1024;
-    const int64_t sb0 = (int64_t)gate_rt0 * a.S * SREC, sb1 = (int64_t)up_rt0 * a.S * SREC;
-    const __amdgpu_buffer_rsrc_t wres[2] = {make_rsrc(a.w + wb0, code_bytes - wb0),
-                                            make_rsrc(a.w + wb1, code_bytes - wb1)};
-    const __amdgpu_buffer_rsrc_t sres[2] = {make_rsrc(a.w + a.scale_off + sb0, sc_bytes - sb0),
-                                            make_rsrc(a.w + a.scale_off + sb1, sc_bytes - sb1)};
-    int xoff[XCH];
-#pragma unroll
-    for (int i = 0; i < XCH; i++) {
-        const int c = tid + i * NTHR;
-        xoff[i] = ((c / (KT / CE)) * a.K + (c % (KT / CE)) * CE) * ESZ;
-    }
-    const int woff = ((((tid >> 6) & (BN / 32 - 1)) * a.S) << 10) + (lane << 4);
-    const int soff = ((tid >> 6) & (BN / 32 - 1)) * a.S * SREC + (lane & 15) * scale_bytes_per_slab(FMT);
-    const bool ktail = a.K % KT != 0;  // the last step has columns past K
-
-    u32x4 xr[XCH];
-    uint32_t wr[WCH][FP4 ? 2 : 4];
-    uint32_t sr[WCH][2];
-
-    auto load_wstage = [&](int step) {
-        const int s = FP4 ? step >> 1 : step;   // slab
-        const int half = FP4 ? step & 1 : 0;    // which 64 k of an FP4 slab
-        const int ssc = s * SREC;
-#pragma unroll
-        for (int i = 0; i < WCH; i++) {
-            if constexpr (FP4) {
-                const u32x2 v = bload8(wres[i], woff, (s << 10) + 8 * half);
-                wr[i][0] = v[0];
-                wr[i][1] = v[1];
-            } else {
-                const u32x4 v = bload16(wres[i], woff, s << 10);
-                wr[i][0] = v[0]; wr[i][1] = v[1]; wr[i][2] = v[2]; wr[i][3] = v[3];
-            }
-            if constexpr (FMT == FMT_NV) {
-                const u32x2 v = bload8(sres[i], soff, ssc);
-                sr[i][0] = v[0];
-                sr[i][1] = v[1];
-            } else {
-                sr[i][0] = bload4(sres[i], soff, ssc);
-                sr[i][1] = 0;
-            }
-        }
-    };
-
-    // The last step of a K that is not a multiple of the step reads the next
-    // row's first columns: zero them (rare; a branch of its own so the common
-    // steps carry no masking work).
-    auto tail_mask = [&](int step) {
-        if (ktail && step == nsteps - 1) {
-#pragma unroll
-            for (int i = 0; i < XCH; i++) {
-                const int c = tid + i * NTHR;
-                if (step * KT + (c % (KT / CE)) * CE >= a.K)
-                    xr[i] = u32x4{0u, 0u, 0u, 0u};
-            }
-        }
-    };
-    // One activation chunk (i < XCH) of the next stage into LDS buffer buf.
-    auto xpiece = [&](int buf, int i) {
-        const int c = tid + i * NTHR;
-        const int row = c / (KT / CE), kk = (c % (KT / CE)) * CE;
-        const u32x4 v = xr[i];
-        if constexpr (ACT == ACT_F32) {
-            bf16x2 p0, p1;
-            p0[0] = (__bf16)__uint_as_float(v[0]);
-            p0[1] = (__bf16)__uint_as_float(v[1]);
-            p1[0] = (__bf16)__uint_as_float(v[2]);
-            p1[1] = (__bf16)__uint_as_float(v[3]);
-            u32x2 *dst = (u32x2 *)&xs[buf][(kk >> 3) * XP + row] + ((kk & 7) >> 2);
-            *dst = u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
-        } else {
-            xs[buf][(kk >> 3) * XP + row] = v;
-        }
-    };
-    // One decoded weight unit (p < 2 * WCH: chunk p / 2, unit p % 2) of the
-    // next stage (step `step`) into LDS buffer buf, block scale folded in.
-    auto wpiece = [&](int buf, int step, int p) {
-        const int i = p >> 1, ul = p & 1;
-        const int half = FP4 ? step & 1 : 0;
-        const int c = tid + i * NTHR;
-        const int tr = c >> 6, L = c & 63;
-        const int col = tr * 16 + (L & 15);
-        const int g = L >> 4;
-        bf16x8 h;
-        if constexpr (FMT == FMT_Q8) {
-            const float d = fp16_bits_to_f32((sr[i][0] >> (16 * ul)) & 0xFFFFu);
-            h = q8_scaled_to_bf16(wr[i][2 * ul], wr[i][2 * ul + 1], d);
-        } else if constexpr (FMT == FMT_FP8) {
-            h = fp8_scaled_to_bf16(wr[i][2 * ul], wr[i][2 * ul + 1], __uint_as_float(sr[i][0]));
-        } else if constexpr (FMT == FMT_MX) {
-            const int u = 2 * half + ul;
-            h = fp4_to_bf16(wr[i][ul], e8m0_to_f32((sr[i][0] >> (8 * u)) & 0xFFu));
-        } else {
-            const int u = 2 * half + ul;
-            const int si = 2 * u + (g >> 1);
-            const uint32_t sb = (si < 4 ? sr[i][0] >> (8 * si) : sr[i][1] >> (8 * (si - 4))) & 0xFFu;
-            h = fp4_to_bf16_mul(wr[i][ul], e4m3_to_f32(sb));
-        }
-        ws[buf][(4 * ul + g) * WP + col] = __builtin_bit_cast(u32x4, h);
-    };
-    auto store_stage = [&](int buf, int step) {
-#pragma unroll
-        for (int i = 0; i < XCH; i++)
-            xpiece(buf, i);
-#pragma unroll
-        for (int p = 0; p < 2 * WCH; p++)
-            wpiece(buf, step, p);
-    };
-
-    // staged column of the wave's n-tile j (SwiGLU: tiles 0,1 gate, 2,3 the
-    // matching up columns)
-    auto wcol = [&](int j) {
-        if constexpr (DUAL)
-            return j < 2 ? wn * 32 + 16 * j : BN / 2 + wn * 32 + 16 * (j - 2);
-        else
-            return wn * 64 + 16 * j;
-    };
-
-    f32x4 acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; i++)
-#pragma unroll
-        for (int j = 0; j < TN; j++)
-            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    auto load_stage = [&](int step) {
-#pragma unroll
-        for (int i = 0; i < XCH; i++)
-            xr[i] = bload16(xres, xoff[i], step * KT * ESZ);
-        load_wstage(step);
-    };
-
-    load_stage(sb);
-    tail_mask(sb);
-    store_stage(sb & 1, sb);
-    load_stage(min(sb + 1, se - 1));
-    __syncthreads();
-
-    // One step: the MFMAs of step s from LDS buffer s & 1, interleaved by
-    // hand (fences keep the order) with the next stage: after each group of
-    // TN MFMAs one piece of work on step s + 1 (a weight unit during the
-    // first k-step, an activation chunk during the second), whose registers
-    // are then refilled by the global loads of step s + 2.  Past the last step
-    // the pieces repeat the last step's data into a buffer no one reads.
-    static_assert(XCH <= TM && 2 * WCH <= TM, "one piece per MFMA group");
-    // The loop exists twice: with the K-tail masking (K not a multiple of the
-    // step) and without it, so the common case carries no masking work.
-    auto main_loop = [&](auto masking) {
-    for (int step = sb; step < se; step++) {
-        const int buf = step & 1;
-        const int nst = min(step + 1, se - 1);
-        if constexpr (decltype(masking)::value)
-            tail_mask(nst);
-#pragma unroll
-        for (int kk = 0; kk < 2; kk++) {        // two 32-wide MFMA k-steps
-            const int kg = 4 * kk + (lane >> 4);
-            const u32x4 *xrow = &xs[buf][kg * XP + wm * (BM / 2) + (lane & 15)];
-            bf16x8 bw[TN];
-#pragma unroll
-            for (int j = 0; j < TN; j++)
-                bw[j] = __builtin_bit_cast(bf16x8, ws[buf][kg * WP + wcol(j) + (lane & 15)]);
-            bf16x8 af = __builtin_bit_cast(bf16x8, xrow[0]);
-#pragma unroll
-            for (int i = 0; i < TM; i++) {
-                bf16x8 afn = af;
-                if (i + 1 < TM)
-                    afn = __builtin_bit_cast(bf16x8, xrow[16 * (i + 1)]);
-#pragma unroll
-                for (int j = 0; j < TN; j++)
-                    acc[i][j] = mfma(af, bw[j], acc[i][j]);
-                if (kk == 0 && i < 2 * WCH)
-                    wpiece(buf ^ 1, nst, i);
-                if (kk == 1 && i < XCH)
-                    xpiece(buf ^ 1, i);
-                __builtin_amdgcn_sched_barrier(0);
-                af = afn;
-            }
-            // refill what this half consumed: a full step ahead of its use
-            if (kk == 0) {
-                load_wstage(min(step + 2, se - 1));
-            } else {
-#pragma unroll
-                for (int i = 0; i < XCH; i++)
-                    xr[i] = bload16(xres, xoff[i], min(step + 2, se - 1) * KT * ESZ);
-            }
-        }
-        __syncthreads();
-    }
-    };
-    if (ktail)
-        main_loop(std::true_type{});
-    else
-        main_loop(std::false_type{});
-
-    // ---- K split: this piece's tile goes to the workspace; tiled_reduce (the
-    // next kernel on the stream) adds the pieces in order and stores y
-    if (split) {
-        const int r = tile - sp.full;               // split tile index
-        f32x4 *dst = (f32x4 *)sp.part + ((int64_t)r * sp.S + ks) * (NTHR * TM * TN) + tid;
-#pragma unroll
-        for (int i = 0; i < TM; i++)
-#pragma unroll
-            for (int j = 0; j < TN; j++)
-                dst[(i * TN + j) * NTHR] = acc[i][j];
-        return;
-    }
-
-    // ---- epilogue (lane holds rows 4*(lane/16)+e of each 16x16 tile, column lane%16)
-#pragma unroll
-    for (int j = 0; j < (DUAL ? TN / 2 : TN); j++) {
-        const int col = n0 + (DUAL ? wn * 32 + 16 * j : wn * 64 + 16 * j) + (lane & 15);
-        if (col >= (DUAL ? Nh : a.N))
-            continue;
-        float g0 = 1.f, g1 = 1.f;
-        if constexpr (FMT == FMT_NV) {
-            g0 = tensor_scale(a, col);
-            if constexpr (DUAL)
-                g1 = tensor_scale(a, Nh + col);
-        }
-#pragma unroll
-        for (int i = 0; i < TM; i++)
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int b = b0 + wm * (BM / 2) + 16 * i + 4 * (lane >> 4) + e;
-                if (b >= a.B)
-                    continue;
-                if constexpr (DUAL) {
-                    const float G = g0 * acc[i][j][e];
-                    const float U = g1 * acc[i][j + 2][e];
-                    store_out<OUTT>(a.y, (int64_t)b * Nh + col, silu(G) * U);
-                } else {
-                    store_out<OUTT>(a.y, (int64_t)b * a.N + col, g0 * acc[i][j][e]);
-                }
-            }
-    }
-}
-
-// Sum of the K-split pieces of the split tiles, in piece order, then the
-// tiled_kernel epilogue.  The partial layout is the one tiled_kernel writes:
-// [split tile][piece][MFMA tile i * TN + j][thread][4], one thread of this
-// kernel per (split tile, i, j-pair, thread of the tiled workgroup).
-template <int FMT, int OUTT, bool DUAL, int BM>
-__global__ __launch_bounds__(256) void tiled_reduce(KArgs a, int Nh, int mtiles, TiSplit sp, int nsplit)
-{
-    constexpr int NTHR = 512, TM = BM / 2 / 16, TN = 4;
-    constexpr int JN = DUAL ? TN / 2 : TN;      // output column tiles per wave
-    const int64_t per_piece = (int64_t)NTHR * TM * TN;
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= (int64_t)nsplit * TM * JN * NTHR)
-        return;
-    const int th = (int)(idx % NTHR);
-    const int64_t q = idx / NTHR;
-    const int jj = (int)(q % JN);
-    const int i = (int)(q / JN % TM);
-    const int r = (int)(q / JN / TM);
-    const int tile = sp.full + r;
-    const int mt = tile % mtiles, ntl = tile / mtiles;
-    const int lane = th & 63, wid = th >> 6, wm = wid & 1, wn = wid >> 1;
-    const int b0 = mt * BM, n0 = ntl * (DUAL ? 128 : 256);
-    const f32x4 *src = (const f32x4 *)sp.part + (int64_t)r * sp.S * per_piece + th;
-    f32x4 v0 = f32x4{0.f, 0.f, 0.f, 0.f}, v1 = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < sp.S; k++) {
-        const f32x4 t0 = src[k * per_piece + (i * TN + jj) * NTHR];
-        v0[0] += t0[0]; v0[1] += t0[1]; v0[2] += t0[2]; v0[3] += t0[3];
-        if constexpr (DUAL) {
-            const f32x4 t1 = src[k * per_piece + (i * TN + jj + 2) * NTHR];
-            v1[0] += t1[0]; v1[1] += t1[1]; v1[2] += t1[2]; v1[3] += t1[3];
-        }
-    }
-    const int col = n0 + (DUAL ? wn * 32 + 16 * jj : wn * 64 + 16 * jj) + (lane & 15);
-    if (col >= (DUAL ? Nh : a.N))
-        return;
-    float g0 = 1.f, g1 = 1.f;
-    if constexpr (FMT == FMT_NV) {
-        g0 = tensor_scale(a, col);
-        if constexpr (DUAL)
-            g1 = tensor_scale(a, Nh + col);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-        const int b = b0 + wm * (BM / 2) + 16 * i + 4 * (lane >> 4) + e;
-        if (b >= a.B)
-            continue;
-        if constexpr (DUAL)
-            store_out<OUTT>(a.y, (int64_t)b * Nh + col, silu(g0 * v0[e]) * (g1 * v1[e]));
-        else
-            store_out<OUTT>(a.y, (int64_t)b * a.N + col, g0 * v0[e]);
-    }
-}
-
-// ------------------------------------------------------------------ host
-
-template <int FMT, int ACT, int OUTT, bool DUAL>
-static void launch_tiled_t(const KArgs &a, const TiCfg &c, hipStream_t st, int Nh)
-{
-    const dim3 grid((unsigned)c.wgs);
-    const int nsplit = c.tiles - c.sp.full;
-    const Groups none = {nullptr, nullptr, 0, 0};
-    if (c.BM == 128) {
-        hipLaunchKernelGGL((tiled_kernel<FMT, ACT, OUTT, DUAL, 128, false>), grid, dim3(512), 0, st, a, Nh,
-                           c.mtiles, c.sp, none);
-        if (c.sp.S > 1) {
-            const int64_t n = (int64_t)nsplit * (128 / 32) * (DUAL ? 2 : 4) * 512;
-            hipLaunchKernelGGL((tiled_reduce<FMT, OUTT, DUAL, 128>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                               st, a, Nh, c.mtiles, c.sp, nsplit);
-        }
-    } else {
-        hipLaunchKernelGGL((tiled_kernel<FMT, ACT, OUTT, DUAL, 256, false>), grid, dim3(512), 0, st, a, Nh,
-                           c.mtiles, c.sp, none);
-        if (c.sp.S > 1) {
-            const int64_t n = (int64_t)nsplit * (256 / 32) * (DUAL ? 2 : 4) * 512;
-            hipLaunchKernelGGL((tiled_reduce<FMT, OUTT, DUAL, 256>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                               st, a, Nh, c.mtiles, c.sp, nsplit);
-        }
-    }
-}
-
-// Routed experts: one launch over every expert's row tiles (grid: an upper
-// bound, extra workgroups leave after the scan), BM rows per tile.
-template <int FMT, int ACT, int OUTT, bool DUAL>
-static void launch_grouped_t(const KArgs &a, const Groups &g, int BM, int64_t tiles, hipStream_t st, int Nh)
-{
-    const dim3 grid((unsigned)(tiles * g.ntiles));
-    const TiSplit none = {0, 1, nullptr, nullptr};
-    if (BM == 128)
-        hipLaunchKernelGGL((tiled_kernel<FMT, ACT, OUTT, DUAL, 128, true>), grid, dim3(512), 0, st, a, Nh, 1,
-                           none, g);
-    else
-        hipLaunchKernelGGL((tiled_kernel<FMT, ACT, OUTT, DUAL, 256, true>), grid, dim3(512), 0, st, a, Nh, 1,
-                           none, g);
-}
-
-template <int FMT>
-static void launch_tiled_f(const Problem &p, const KArgs &a, const TiCfg &c, hipStream_t st, const Groups *g,
-                           int gBM, int64_t gtiles)
-{
-    const bool f32 = p.act == QGEMM_F32, o32 = p.out == QGEMM_F32;
-    const bool dual = p.epi == QGEMM_EPI_SWIGLU;
-    const int Nh = (int)(p.N / 2);
-#define QG_T(A, O, D) \
-    (g ? launch_grouped_t<FMT, A, O, D>(a, *g, gBM, gtiles, st, Nh) : launch_tiled_t<FMT, A, O, D>(a, c, st, Nh))
-    if (f32) {
-        if (o32) { if (dual) QG_T(ACT_F32, OUT_F32, true); else QG_T(ACT_F32, OUT_F32, false); }
-        else { if (dual) QG_T(ACT_F32, OUT_BF16, true); else QG_T(ACT_F32, OUT_BF16, false); }
-    } else {
-        if (o32) { if (dual) QG_T(ACT_BF16, OUT_F32, true); else QG_T(ACT_BF16, OUT_F32, false); }
-        else { if (dual) QG_T(ACT_BF16, OUT_BF16, true); else QG_T(ACT_BF16, OUT_BF16, false); }
-    }
-#undef QG_T
-}
-
 hipError_t launch_tiled(const Problem &p, const KArgs &a, const TiCfg &c, hipStream_t st)
 {
-    switch (p.fmt) {
-    case FMT_Q8: launch_tiled_f<FMT_Q8>(p, a, c, st, nullptr, 0, 0); break;
-    case FMT_MX: launch_tiled_f<FMT_MX>(p, a, c, st, nullptr, 0, 0); break;
-    case FMT_FP8: launch_tiled_f<FMT_FP8>(p, a, c, st, nullptr, 0, 0); break;
-    default: launch_tiled_f<FMT_NV>(p, a, c, st, nullptr, 0, 0); break;
-    }
-    return hipGetLastError();
+    if (p.math == QGEMM_MATH_FP32)
+        return launch_tiled_fp32(p, a, c, st);
+    return launch_tiled_math<false>(p, a, &c, nullptr, c.BM, 0, st);
 }
 
 hipError_t launch_grouped(const Problem &p, const KArgs &a, const Groups &g, int BM, int64_t tiles,
                           hipStream_t st)
 {
-    const TiCfg none{};
-    switch (p.fmt) {
-    case FMT_Q8: launch_tiled_f<FMT_Q8>(p, a, none, st, &g, BM, tiles); break;
-    case FMT_MX: launch_tiled_f<FMT_MX>(p, a, none, st, &g, BM, tiles); break;
-    case FMT_FP8: launch_tiled_f<FMT_FP8>(p, a, none, st, &g, BM, tiles); break;
-    default: launch_tiled_f<FMT_NV>(p, a, none, st, &g, BM, tiles); break;
-    }
-    return hipGetLastError();
+    if (p.math == QGEMM_MATH_FP32)
+        return launch_grouped_fp32(p, a, g, BM, tiles, st);
+    return launch_tiled_math<false>(p, a, nullptr, &g, BM, tiles, st);
 }
 
 }  // namespace qg

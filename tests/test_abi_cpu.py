@@ -56,7 +56,7 @@ def _create(*args):
     ((2, 1, 1, 1, 1, 40, 512, 0), q.ENOTSUP),        # SwiGLU with N/2 % 16
     ((0, 0, 0, 0, 0, 256, 512, 3), q.EINVAL),        # both tiers forced
     ((0, 0, 0, 0, 0, 256, 512, 0x10), q.EINVAL),     # unknown flag
-    ((0, 0, 0, 0, 0, 256, 512, 2), q.ENOTSUP),       # fp32 math in the tiled tier
+    ((0, 0, 0, 0, 0, 256, 512, 2), q.OK),            # fp32 math in the tiled tier
     ((2, 1, 1, 1, 1, 64, 512, 1), q.OK),             # SwiGLU in the skinny tier (B <= 16)
     ((2, 0, 0, 1, 0, 64, 512, 0), q.ENOTSUP),        # SwiGLU with fp32 math
 ])
@@ -91,7 +91,9 @@ def test_run_validation_before_any_hip_call():
     assert L.qgemm_run(None, 4, p16, p16, p16, None) == q.EINVAL
     assert L.qgemm_run(h, 1 << 31, p16, p16, p16, None) == q.EINVAL
     assert L.qgemm_plan_tier(h, 16) == 1
-    assert L.qgemm_plan_tier(h, 2048) == 1    # fp32 math stays in the skinny tier
+    assert L.qgemm_plan_tier(h, 17) == 2      # fp32 math above the streaming kernel's 16 rows:
+    assert L.qgemm_plan_tier(h, 256) == 2     # the faithful variant of the large-batch tier
+    assert L.qgemm_plan_tier(h, 2048) == 2
     assert L.qgemm_plan_tier(h, -1) == 0
     assert L.qgemm_destroy(h) == q.OK
 
@@ -220,9 +222,6 @@ def test_plan_errors_raise():
     with pytest.raises(q.QgemmError) as e:
         q.Plan("q8_0", 256, 48, act="f32")
     assert e.value.status == q.EINVAL
-    with pytest.raises(q.QgemmError) as e:
-        q.Plan("q8_0", 256, 512, act="f32", math="fp32", tier="tiled")
-    assert e.value.status == q.ENOTSUP
 
 
 def test_synth_configs_pack():
@@ -244,7 +243,8 @@ def test_grouped_argument_checks():
     assert L.qgemm_run_grouped(h, 4, 10, fake, fake, ctypes.c_void_p(0x1008), fake, None) == q.EINVAL
     L.qgemm_destroy(h)
     assert L.qgemm_create(ctypes.byref(h), 0, 0, 0, 0, 0, 256, 512, 0) == q.OK        # fp32 math
-    assert L.qgemm_run_grouped(h, 4, 10, fake, fake, fake, fake, None) == q.ENOTSUP
+    assert L.qgemm_run_grouped(h, 4, 0, None, None, None, None, None) == q.OK
+    assert L.qgemm_run_grouped(h, 4, 10, fake, None, fake, fake, None) == q.EINVAL   # null offsets
     L.qgemm_destroy(h)
     assert L.qgemm_create(ctypes.byref(h), 2, 1, 0, 0, 1, 256, 512, 1) == q.OK        # forced skinny
     assert L.qgemm_run_grouped(h, 4, 10, fake, fake, fake, fake, None) == q.ENOTSUP

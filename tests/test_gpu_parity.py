@@ -140,11 +140,11 @@ def test_boundary_matrix_chunked_is_bitwise(cfg2, tier):
 
 
 def test_deterministic_and_row_independent(cfg2):
-    """Repeated calls agree bit for bit, and a row's result does not depend on
-    how many other rows share the call (the summation order is fixed by N
-    and K alone)."""
+    """Repeated calls agree bit for bit, and within the small-batch tiers a
+    row's result does not depend on how many other rows share the call (the
+    summation order is fixed by N and K alone)."""
     w, x, ref, wd = cfg2
-    plan = q.Plan("q8_0", 5120, 5120, act="f32", out="f32", math="fp32")
+    plan = q.Plan("q8_0", 5120, 5120, act="f32", out="f32", math="fp32", tier="skinny")
     y16 = run(plan, x[:16], wd)
     assert np.array_equal(y16, run(plan, x[:16], wd))
     for B in (1, 5, 33, 256):
@@ -204,10 +204,13 @@ def test_workspace_shared_by_both_tiers(cfg2):
 @pytest.mark.parametrize("fmt,act,tier", [("q8_0", "f32", "skinny"), ("mxfp4", "bf16", "skinny"),
                                           ("nvfp4", "bf16", "skinny"), ("mxfp4", "bf16", "tiled"),
                                           ("nvfp4", "bf16", "tiled"), ("fp8", "f32", "skinny"),
-                                          ("fp8", "bf16", "skinny")])
+                                          ("fp8", "bf16", "skinny"), ("q8_0", "f32", "tiled"),
+                                          ("mxfp4", "f32", "tiled"), ("nvfp4", "f32", "tiled"),
+                                          ("fp8", "f32", "tiled")])
 def test_one_hot_reads_out_decoded_weights(fmt, act, tier):
     """x = e_j makes y[b][n] = w[n][j]: the decoded weights, read through the
-    whole GEMM path, must be exact."""
+    whole GEMM path, must be exact (fp32 activations run fp32-faithful math,
+    in the large-batch tier too)."""
     n, k = 80, 512
     rng = np.random.default_rng(9)
     w = _edge_weights(fmt, n, k, rng)
@@ -255,7 +258,7 @@ def test_one_hot_tiled_rounds_decoded_weights_once(fmt):
     assert np.array_equal(y, ref.astype(np.float64))
 
 
-@pytest.mark.parametrize("tier,math", [("skinny", "fp32"), ("tiled", "bf16")])
+@pytest.mark.parametrize("tier,math", [("skinny", "fp32"), ("tiled", "bf16"), ("tiled", "fp32")])
 def test_closed_form_constant_is_exact(tier, math):
     """Constant q = 3, d = 2^-7, x = 0.5 over K = 5120: every output is
     K*d*q*x = 60 exactly and each row sums to N*K*d*q*x."""
@@ -279,8 +282,6 @@ def test_closed_form_constant_is_exact(tier, math):
     ("fp8", "bf16", "bf16", "f32"), ("fp8", "f32", "fp32", "f32")])
 @pytest.mark.parametrize("tier", ["skinny", "tiled"])
 def test_ragged_shapes(fmt, act, math, out, tier):
-    if tier == "tiled" and math == "fp32":
-        pytest.skip("fp32 math runs in the skinny tier only")
     n = 100
     k = {"q8_0": 96, "mxfp4": 160, "nvfp4": 144, "fp8": 160}[fmt]
     w = synth.gen_weights(fmt, n, k, seed=1)
@@ -409,8 +410,8 @@ def test_swiglu_small_exhaustive():
         assert oracle.rel_fro(y, oracle.swiglu(w, x)) <= 1e-3
 
 
-@pytest.mark.parametrize("tier", ["skinny", "tiled"])
-def test_mxfp4_extreme_scales_one_hot(tier):
+@pytest.mark.parametrize("tier,math", [("skinny", "bf16"), ("tiled", "bf16"), ("tiled", "fp32")])
+def test_mxfp4_extreme_scales_one_hot(tier, math):
     """E8M0 scale bytes at both ends of the range (subnormal and near-overflow
     products) read out exactly through the GEMM path."""
     n, k = 32, 256
@@ -422,8 +423,12 @@ def test_mxfp4_extreme_scales_one_hot(tier):
     xf = np.zeros((len(cols), k), dtype=np.float32)
     for i, j in enumerate(cols):
         xf[i, j] = 1.0
-    plan = q.Plan("mxfp4", n, k, act="bf16", out="f32", tier=tier)
-    y = run(plan, synth.f32_to_bf16_bits(xf), w_dev(w))
+    if math == "fp32":
+        plan = q.Plan("mxfp4", n, k, act="f32", out="f32", math="fp32", tier=tier)
+        y = run(plan, xf, w_dev(w))
+    else:
+        plan = q.Plan("mxfp4", n, k, act="bf16", out="f32", tier=tier)
+        y = run(plan, synth.f32_to_bf16_bits(xf), w_dev(w))
     ref = oracle.dequant(w)[:, cols].T.astype(np.float32).astype(np.float64)
     bad = np.argwhere(y != ref)
     assert bad.size == 0, [(int(i), int(j), y[i, j], ref[i, j]) for i, j in bad[:8]]
@@ -484,7 +489,7 @@ def test_swiglu_forced_skinny_above_16_is_not_supported():
 
 # ------------------------------------------------------------ routed experts
 
-def _grouped_case(fmt, act, out, epi, E, n, k, offsets, seed):
+def _grouped_case(fmt, act, out, epi, E, n, k, offsets, seed, math="bf16"):
     ws = [synth.gen_expert_weights(fmt, n, k, e, seed=seed, swiglu=epi == "swiglu") for e in range(E)]
     T = int(offsets[-1])
     xf = synth.gen_x_f32(T, k, seed=seed + 1)
@@ -492,7 +497,7 @@ def _grouped_case(fmt, act, out, epi, E, n, k, offsets, seed):
     bufs = [w_dev(w) for w in ws]
     table = torch.tensor([b.data_ptr() for b in bufs], dtype=torch.int64, device=_dev())
     off = torch.from_numpy(np.asarray(offsets, dtype=np.int32)).to(_dev())
-    plan = q.Plan(fmt, n, k, act=act, out=out, epilogue=epi, math="bf16")
+    plan = q.Plan(fmt, n, k, act=act, out=out, epilogue=epi, math=math)
     y = y_new(plan, T)
     plan.run_grouped(x_dev(x), table, off, y)
     torch.cuda.synchronize()
@@ -517,6 +522,27 @@ def test_grouped_matches_oracle_and_per_expert_calls(fmt, act, out, epi):
     print(f"grouped {fmt} {epi} rel_fro={err:.3e}")
     assert err <= TOL_BF16
     solo = q.Plan(fmt, n, k, act=act, out=out, epilogue=epi, math="bf16", tier="tiled")
+    for e in range(E):
+        r0, r1 = offsets[e], offsets[e + 1]
+        if r1 > r0:
+            ye = run(solo, x[r0:r1], bufs[e], workspace=None)
+            assert np.array_equal(ye.view(np.uint64), y[r0:r1].view(np.uint64)), e
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "mxfp4", "nvfp4", "fp8"])
+def test_grouped_fp32_math(fmt):
+    """Routed experts with fp32-faithful math: within the fp32 bound of the
+    oracle and, bit for bit, an unsplit large-batch call of each expert."""
+    n, k = 256, 512
+    rows = [5, 0, 1, 150, 17, 64, 65, 2]
+    offsets = np.concatenate([[0], np.cumsum(rows)])
+    E = len(rows)
+    ws, bufs, x, y, plan = _grouped_case(fmt, "f32", "f32", "none", E, n, k, offsets, seed=4,
+                                         math="fp32")
+    err = oracle.rel_fro(y, oracle.gemm_grouped(ws, offsets, x))
+    print(f"grouped fp32 {fmt} rel_fro={err:.3e}")
+    assert err <= TOL_FP32
+    solo = q.Plan(fmt, n, k, act="f32", out="f32", math="fp32", tier="tiled")
     for e in range(E):
         r0, r1 = offsets[e], offsets[e + 1]
         if r1 > r0:
