@@ -193,6 +193,8 @@ static TiCfg tiled_cfg(const Problem &p, int64_t B, bool split)
 {
     TiCfg c;
     c.BM = p.math == QGEMM_MATH_FP32 ? 64 : B <= 128 ? 128 : 256;
+    if (p.math != QGEMM_MATH_FP32 && (env_int("QGEMM_TI_BM", 0) == 128 || env_int("QGEMM_TI_BM", 0) == 256))
+        c.BM = env_int("QGEMM_TI_BM", 0);
     const bool dual = p.epi == QGEMM_EPI_SWIGLU;
     const int64_t cols = dual ? p.N / 2 : p.N;
     c.mtiles = (int)((B + c.BM - 1) / c.BM);

@@ -178,12 +178,11 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
                                             make_rsrc(a.w + wb1, code_bytes - wb1)};
     const __amdgpu_buffer_rsrc_t sres[2] = {make_rsrc(a.w + a.scale_off + sb0, sc_bytes - sb0),
                                             make_rsrc(a.w + a.scale_off + sb1, sc_bytes - sb1)};
-    int xoff[XCH];
-#pragma unroll
-    for (int i = 0; i < XCH; i++) {
-        const int c = tid + i * NTHR;
-        xoff[i] = ((c / (KT / CE)) * a.K + (c % (KT / CE)) * CE) * ESZ;
-    }
+    // activation chunk i of a thread is row tid / (KT / CE) + i * XRI of the
+    // tile: one per-lane offset, the chunk's rows in the scalar offset
+    constexpr int XRI = NTHR / (KT / CE);
+    const int xoff = ((tid / (KT / CE)) * a.K + (tid % (KT / CE)) * CE) * ESZ;
+    const int xrow_bytes = XRI * a.K * ESZ;
     const int woff = ((((tid >> 6) & (BN / 32 - 1)) * a.S) << 10) + (lane << 4);
     const int soff = ((tid >> 6) & (BN / 32 - 1)) * a.S * SREC + (lane & 15) * scale_bytes_per_slab(FMT);
     const bool ktail = a.K % KT != 0;  // the last step has columns past K
@@ -328,7 +327,7 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
     auto load_stage = [&](int step) {
 #pragma unroll
         for (int i = 0; i < XCH; i++)
-            xr[i] = bload16(xres, xoff[i], step * KT * ESZ);
+            xr[i] = bload16(xres, xoff, i * xrow_bytes + step * KT * ESZ);
         load_wstage(step);
     };
 
@@ -412,7 +411,7 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
             } else {
 #pragma unroll
                 for (int i = 0; i < XCH; i++)
-                    xr[i] = bload16(xres, xoff[i], min(step + 2, se - 1) * KT * ESZ);
+                    xr[i] = bload16(xres, xoff, i * xrow_bytes + min(step + 2, se - 1) * KT * ESZ);
             }
         }
         __syncthreads();
