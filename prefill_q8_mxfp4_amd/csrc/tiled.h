@@ -187,11 +187,17 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
     const int soff = ((tid >> 6) & (BN / 32 - 1)) * a.S * SREC + (lane & 15) * scale_bytes_per_slab(FMT);
     const bool ktail = a.K % KT != 0;  // the last step has columns past K
 
-    u32x4 xr[XCH];
-    uint32_t wr[WCH][FP4 ? 2 : 4];
-    uint32_t sr[WCH][2];
+    // Register stages: PF slots, each one step's global loads; slot r is
+    // refilled PF steps after it was loaded.  Routed experts in 64- and
+    // 128-row tiles, whose workgroups have little MFMA work per step, keep
+    // two or three steps in flight (as many as the registers hold; deeper
+    // stages measured no faster for the dense GEMM).
+    constexpr int PF = GROUPED && BM <= 128 ? (ACT == ACT_BF16 ? 3 : 2) : 1;
+    u32x4 xr[PF][XCH];
+    uint32_t wr[PF][WCH][FP4 ? 2 : 4];
+    uint32_t sr[PF][WCH][2];
 
-    auto load_wstage = [&](int step) {
+    auto load_wstage = [&](int r, int step) {
         const int s = FP4 ? step >> 1 : step;   // slab
         const int half = FP4 ? step & 1 : 0;    // which 64 k of an FP4 slab
         const int ssc = s * SREC;
@@ -199,19 +205,19 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
         for (int i = 0; i < WCH; i++) {
             if constexpr (FP4) {
                 const u32x2 v = bload8(wres[i], woff, (s << 10) + 8 * half);
-                wr[i][0] = v[0];
-                wr[i][1] = v[1];
+                wr[r][i][0] = v[0];
+                wr[r][i][1] = v[1];
             } else {
                 const u32x4 v = bload16(wres[i], woff, s << 10);
-                wr[i][0] = v[0]; wr[i][1] = v[1]; wr[i][2] = v[2]; wr[i][3] = v[3];
+                wr[r][i][0] = v[0]; wr[r][i][1] = v[1]; wr[r][i][2] = v[2]; wr[r][i][3] = v[3];
             }
             if constexpr (FMT == FMT_NV) {
                 const u32x2 v = bload8(sres[i], soff, ssc);
-                sr[i][0] = v[0];
-                sr[i][1] = v[1];
+                sr[r][i][0] = v[0];
+                sr[r][i][1] = v[1];
             } else {
-                sr[i][0] = bload4(sres[i], soff, ssc);
-                sr[i][1] = 0;
+                sr[r][i][0] = bload4(sres[i], soff, ssc);
+                sr[r][i][1] = 0;
             }
         }
     };
@@ -219,21 +225,21 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
     // The last step of a K that is not a multiple of the step reads the next
     // row's first columns: zero them (rare; a branch of its own so the common
     // steps carry no masking work).
-    auto tail_mask = [&](int step) {
+    auto tail_mask = [&](int r, int step) {
         if (ktail && step == nsteps - 1) {
 #pragma unroll
             for (int i = 0; i < XCH; i++) {
                 const int c = tid + i * NTHR;
                 if (step * KT + (c % (KT / CE)) * CE >= a.K)
-                    xr[i] = u32x4{0u, 0u, 0u, 0u};
+                    xr[r][i] = u32x4{0u, 0u, 0u, 0u};
             }
         }
     };
     // One activation chunk (i < XCH) of the next stage into LDS buffer buf.
-    auto xpiece = [&](int buf, int i) {
+    auto xpiece = [&](int r, int buf, int i) {
         const int c = tid + i * NTHR;
         const int row = c / (KT / CE), kk = (c % (KT / CE)) * CE;
-        const u32x4 v = xr[i];
+        const u32x4 v = xr[r][i];
         if constexpr (NTA > 1) {
             float f[4];
 #pragma unroll
@@ -260,7 +266,7 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
     };
     // One decoded weight unit (p < 2 * WCH: chunk p / 2, unit p % 2) of the
     // next stage (step `step`) into LDS buffer buf, block scale folded in.
-    auto wpiece = [&](int buf, int step, int p) {
+    auto wpiece = [&](int r, int buf, int step, int p) {
         const int i = p >> 1, ul = p & 1;
         const int half = FP4 ? step & 1 : 0;
         const int c = tid + i * NTHR;
@@ -272,40 +278,40 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
             // exact codes; the block scale goes to LDS once per staged row
             float d;
             if constexpr (FMT == FMT_Q8) {
-                h = q8_to_bf16(wr[i][2 * ul], wr[i][2 * ul + 1]);
-                d = fp16_bits_to_f32((sr[i][0] >> (16 * ul)) & 0xFFFFu);
+                h = q8_to_bf16(wr[r][i][2 * ul], wr[r][i][2 * ul + 1]);
+                d = fp16_bits_to_f32((sr[r][i][0] >> (16 * ul)) & 0xFFFFu);
             } else if constexpr (FMT == FMT_FP8) {
-                h = fp8_to_bf16(wr[i][2 * ul], wr[i][2 * ul + 1]);
-                d = __uint_as_float(sr[i][0]);
+                h = fp8_to_bf16(wr[r][i][2 * ul], wr[r][i][2 * ul + 1]);
+                d = __uint_as_float(sr[r][i][0]);
             } else {
-                h = fp4_to_bf16(wr[i][ul], 1.0f);
-                d = e8m0_to_f32((sr[i][0] >> (8 * (2 * half + ul))) & 0xFFu);
+                h = fp4_to_bf16(wr[r][i][ul], 1.0f);
+                d = e8m0_to_f32((sr[r][i][0] >> (8 * (2 * half + ul))) & 0xFFu);
             }
             if (g == 0)
                 ss[(buf * 2 + ul) * BN + col] = d;
         } else if constexpr (FMT == FMT_Q8) {
-            const float d = fp16_bits_to_f32((sr[i][0] >> (16 * ul)) & 0xFFFFu);
-            h = q8_scaled_to_bf16(wr[i][2 * ul], wr[i][2 * ul + 1], d);
+            const float d = fp16_bits_to_f32((sr[r][i][0] >> (16 * ul)) & 0xFFFFu);
+            h = q8_scaled_to_bf16(wr[r][i][2 * ul], wr[r][i][2 * ul + 1], d);
         } else if constexpr (FMT == FMT_FP8) {
-            h = fp8_scaled_to_bf16(wr[i][2 * ul], wr[i][2 * ul + 1], __uint_as_float(sr[i][0]));
+            h = fp8_scaled_to_bf16(wr[r][i][2 * ul], wr[r][i][2 * ul + 1], __uint_as_float(sr[r][i][0]));
         } else if constexpr (FMT == FMT_MX) {
             const int u = 2 * half + ul;
-            h = fp4_to_bf16(wr[i][ul], e8m0_to_f32((sr[i][0] >> (8 * u)) & 0xFFu));
+            h = fp4_to_bf16(wr[r][i][ul], e8m0_to_f32((sr[r][i][0] >> (8 * u)) & 0xFFu));
         } else {
             const int u = 2 * half + ul;
             const int si = 2 * u + (g >> 1);
-            const uint32_t sb = (si < 4 ? sr[i][0] >> (8 * si) : sr[i][1] >> (8 * (si - 4))) & 0xFFu;
-            h = fp4_to_bf16_mul(wr[i][ul], e4m3_to_f32(sb));
+            const uint32_t sb = (si < 4 ? sr[r][i][0] >> (8 * si) : sr[r][i][1] >> (8 * (si - 4))) & 0xFFu;
+            h = fp4_to_bf16_mul(wr[r][i][ul], e4m3_to_f32(sb));
         }
         ws[buf][(4 * ul + g) * WP + col] = __builtin_bit_cast(u32x4, h);
     };
-    auto store_stage = [&](int buf, int step) {
+    auto store_stage = [&](int r, int buf, int step) {
 #pragma unroll
         for (int i = 0; i < XCH; i++)
-            xpiece(buf, i);
+            xpiece(r, buf, i);
 #pragma unroll
         for (int p = 0; p < 2 * WCH; p++)
-            wpiece(buf, step, p);
+            wpiece(r, buf, step, p);
     };
 
     // staged column of the wave's n-tile j (SwiGLU: tiles 0,1 gate, 2,3 the
@@ -324,17 +330,21 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
         for (int j = 0; j < TN; j++)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto load_stage = [&](int step) {
+    auto load_xstage = [&](int r, int step) {
 #pragma unroll
         for (int i = 0; i < XCH; i++)
-            xr[i] = bload16(xres, xoff, i * xrow_bytes + step * KT * ESZ);
-        load_wstage(step);
+            xr[r][i] = bload16(xres, xoff, i * xrow_bytes + step * KT * ESZ);
     };
 
-    load_stage(sb);
-    tail_mask(sb);
-    store_stage(sb & 1, sb);
-    load_stage(min(sb + 1, se - 1));
+    load_xstage(0, sb);
+    load_wstage(0, sb);
+    tail_mask(0, sb);
+    store_stage(0, sb & 1, sb);
+#pragma unroll
+    for (int r = 0; r < PF; r++) {
+        load_xstage(r, min(sb + 1 + r, se - 1));
+        load_wstage(r, min(sb + 1 + r, se - 1));
+    }
     __syncthreads();
 
     // One step: the MFMAs of step s from LDS buffer s & 1, interleaved by
@@ -342,18 +352,23 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
     // TN MFMAs (one A fragment: a batch tile, or one term of it) pieces of
     // work on step s + 1 (weight units during the first k-step, activation
     // chunks during the second, dealt round-robin over the groups), whose
-    // registers are then refilled by the global loads of step s + 2.  Past
-    // the last step the pieces repeat the last step's data into a buffer no
-    // one reads.
+    // register slot is then refilled by the global loads of step s + 1 + PF.
+    // Past the last step the pieces repeat the last step's data into a
+    // buffer no one reads.
     constexpr int NG = TM * NTA;  // MFMA groups per k-step
     // The loop exists twice: with the K-tail masking (K not a multiple of the
     // step) and without it, so the common case carries no masking work.
     auto main_loop = [&](auto masking) {
-    for (int step = sb; step < se; step++) {
+    for (int step0 = sb; step0 < se; step0 += PF) {
+#pragma unroll
+    for (int r = 0; r < PF; r++) {  // slot r holds step + 1
+        const int step = step0 + r;
+        if (step >= se)
+            break;  // uniform
         const int buf = step & 1;
         const int nst = min(step + 1, se - 1);
         if constexpr (decltype(masking)::value)
-            tail_mask(nst);
+            tail_mask(r, nst);
 #pragma unroll
         for (int kk = 0; kk < 2; kk++) {        // two 32-wide MFMA k-steps
             const int kg = 4 * kk + (lane >> 4);
@@ -388,11 +403,11 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
 #pragma unroll
                 for (int p = q; p < 2 * WCH; p += NG)
                     if (kk == 0)
-                        wpiece(buf ^ 1, nst, p);
+                        wpiece(r, buf ^ 1, nst, p);
 #pragma unroll
                 for (int p = q; p < XCH; p += NG)
                     if (kk == 1)
-                        xpiece(buf ^ 1, p);
+                        xpiece(r, buf ^ 1, p);
                 __builtin_amdgcn_sched_barrier(0);
                 af = afn;
             }
@@ -405,16 +420,14 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
                         for (int e = 0; e < 4; e++)
                             acc[i][j][e] = __builtin_fmaf(bsc[j], part[i][j][e], acc[i][j][e]);
             }
-            // refill what this half consumed: a full step ahead of its use
-            if (kk == 0) {
-                load_wstage(min(step + 2, se - 1));
-            } else {
-#pragma unroll
-                for (int i = 0; i < XCH; i++)
-                    xr[i] = bload16(xres, xoff, i * xrow_bytes + min(step + 2, se - 1) * KT * ESZ);
-            }
+            // refill the slot this half consumed, PF steps ahead of its use
+            if (kk == 0)
+                load_wstage(r, min(step + 1 + PF, se - 1));
+            else
+                load_xstage(r, min(step + 1 + PF, se - 1));
         }
         __syncthreads();
+    }
     }
     };
     if (ktail)
@@ -540,8 +553,9 @@ template <int FMT, int ACT, int OUTT, bool DUAL, int BM, bool FAITH>
 static void launch_grouped_bm(const KArgs &a, const Groups &g, int64_t tiles, hipStream_t st, int Nh)
 {
     const TiSplit none = {0, 1, nullptr, nullptr};
-    hipLaunchKernelGGL((tiled_kernel<FMT, ACT, OUTT, DUAL, BM, true, FAITH>), dim3((unsigned)(tiles * g.ntiles)),
-                       dim3(512), 0, st, a, Nh, 1, none, g);
+    const dim3 grid((unsigned)(tiles * g.ntiles));
+    hipLaunchKernelGGL((tiled_kernel<FMT, ACT, OUTT, DUAL, BM, true, FAITH>), grid, dim3(512), 0, st, a, Nh, 1,
+                       none, g);
 }
 
 // One (format, math) pair: the activation, output and epilogue variants.

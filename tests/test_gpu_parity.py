@@ -127,13 +127,16 @@ def test_q8_0_5120_sweep_fp32(cfg2, B):
 def test_boundary_matrix_chunked_is_bitwise(cfg2, tier):
     """hipfire PR 'fix(mtp): chunk scalar Q8 batched GEMM above 64 rows',
     Scalar-Q8 boundary matrix: one call at B = 64/65/70/76/256 equals the
-    same rows computed in contiguous chunks of 64, bit for bit."""
+    same rows computed in contiguous chunks of 64, bit for bit.  The
+    large-batch tier is compared on its unsplit route: its K split depends on
+    the tile count, hence on B."""
     w, x, ref, wd = cfg2
     math = "fp32" if tier == "skinny" else "bf16"
     plan = q.Plan("q8_0", 5120, 5120, act="f32", out="f32", math=math, tier=tier)
+    wsp = "auto" if tier == "skinny" else None
     for B in (64, 65, 70, 76, 256):
-        whole = run(plan, x[:B], wd)
-        parts = [run(plan, x[r0:min(B, r0 + 64)], wd) for r0 in range(0, B, 64)]
+        whole = run(plan, x[:B], wd, workspace=wsp)
+        parts = [run(plan, x[r0:min(B, r0 + 64)], wd, workspace=wsp) for r0 in range(0, B, 64)]
         assert np.array_equal(whole, np.concatenate(parts, axis=0)), B
         tol = TOL_FP32 if math == "fp32" else TOL_BF16
         assert oracle.rel_fro(whole, ref[:B]) <= tol
