@@ -156,7 +156,8 @@ int qgemm_pack(qgemm_format fmt, int64_t N, int64_t K, const void *codes, const 
 /* ------------------------------------------------------------------ plan */
 typedef struct qgemm_plan qgemm_plan;
 
-/* Validate and record a problem shape.  act: activation dtype; out: output
+/* Validate and record a problem shape: 1 <= N <= 2^30, 1 <= K <= 2^20, K a
+ * multiple of the format's block.  act: activation dtype; out: output
  * dtype; math: see qgemm_math (QGEMM_MATH_FP32 needs act = QGEMM_F32; the
  * SwiGLU epilogue needs QGEMM_MATH_BF16, else QGEMM_ENOTSUP); flags:
  * 0 or one QGEMM_FLAG_FORCE_* bit (also settable with the environment

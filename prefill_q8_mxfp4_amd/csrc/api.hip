@@ -391,8 +391,10 @@ int qgemm_create(qgemm_plan **plan, qgemm_format fmt, qgemm_dtype act, qgemm_dty
     if (N <= 0 || K <= 0)
         return fail(QGEMM_EINVAL, "qgemm_create: N and K must be positive (N=%lld K=%lld)",
                     (long long)N, (long long)K);
-    if (N > (1ll << 30) || K > (1ll << 30))
-        return fail(QGEMM_EINVAL, "qgemm_create: N or K above 2^30");
+    // K: a workgroup's activation rows (up to 256 of K fp32 values) and
+    // weight rows stay below 2^31 bytes, so the kernels' 32-bit offsets hold
+    if (N > (1ll << 30) || K > (1ll << 20))
+        return fail(QGEMM_EINVAL, "qgemm_create: N above 2^30 or K above 2^20");
     const int64_t blk = fmt == QGEMM_NVFP4 ? 16 : 32;
     if (K % blk)
         return fail(QGEMM_EINVAL, "qgemm_create: K=%lld is not a multiple of the %lld-wide block",

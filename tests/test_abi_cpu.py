@@ -44,6 +44,9 @@ def _create(*args):
     ((0, 0, 0, 0, 0, 0, 512, 0), q.EINVAL),          # N = 0
     ((0, 0, 0, 0, 0, 256, -32, 0), q.EINVAL),        # K < 0
     ((0, 0, 0, 0, 0, 256, 48, 0), q.EINVAL),         # K % 32
+    ((0, 0, 0, 0, 0, 256, 1 << 20, 0), q.OK),        # largest K
+    ((0, 0, 0, 0, 0, 256, (1 << 20) + 32, 0), q.EINVAL),  # K above 2^20
+    ((0, 0, 0, 0, 0, (1 << 30) + 16, 512, 0), q.EINVAL),  # N above 2^30
     ((2, 1, 0, 0, 1, 256, 48, 0), q.OK),             # NVFP4: 16-wide blocks
     ((1, 1, 0, 0, 1, 256, 48, 0), q.EINVAL),         # MXFP4: K % 32
     ((4, 0, 0, 0, 0, 256, 512, 0), q.EINVAL),        # unknown format
