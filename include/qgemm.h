@@ -209,7 +209,10 @@ size_t qgemm_workspace_bytes(const qgemm_plan *plan, int64_t B);
  * splits K over several workgroups per output tile (the last workgroup of a
  * tile to finish adds the partial tiles in a fixed order), and the
  * large-batch tier splits the tiles of a last, partial round of tiles along K
- * (a second kernel on the stream adds the pieces in order).  Results stay
+ * (a second kernel on the stream adds the pieces in order) and, for fp32
+ * activations with bf16 math, first rounds x to bf16 once into the workspace
+ * (the rounding its kernel applies anyway: results are unchanged by it).
+ * Results stay
  * deterministic; they can differ in rounding from the unsplit route, and in
  * the large-batch tier from one B to another.
  * Contract: the workspace must be all zero before its first use with a plan;

@@ -455,13 +455,22 @@ int qgemm_plan_tier(const qgemm_plan *plan, int64_t B)
     return choose_tier(plan, B);
 }
 
+// Large-batch tier, fp32 activations with bf16 math: bytes of the bf16 copy
+// of x that a workspace can hold (converted once per call instead of once
+// per weight tile by every workgroup that stages it).
+static int64_t xconv_bytes(const Problem &p, int64_t B)
+{
+    return p.act == QGEMM_F32 && p.math == QGEMM_MATH_BF16 ? round_up(B * p.K * 2, 256) : 0;
+}
+
 size_t qgemm_workspace_bytes(const qgemm_plan *plan, int64_t B)
 {
     if (!plan || plan->magic != PLAN_MAGIC || B <= 0 || B > (1ll << 30))
         return 0;
     if (choose_tier(plan, B) != QGEMM_TIER_SKINNY) {
         const TiCfg c = tiled_cfg(plan->p, B, true);
-        return c.part_bytes ? (size_t)(ws_data_off(plan->p) + c.part_bytes) : 0;
+        const int64_t extra = round_up(c.part_bytes, 256) + xconv_bytes(plan->p, B);
+        return extra ? (size_t)(ws_data_off(plan->p) + extra) : 0;
     }
     return (size_t)skinny_ws_bytes(plan->p, B);
 }
@@ -532,7 +541,23 @@ int qgemm_run_ws(const qgemm_plan *plan, int64_t B, const void *w, const void *x
             c.sp.cnt = (uint32_t *)((uint8_t *)workspace + split_cnt_bytes(p));
             c.sp.part = (float *)((uint8_t *)workspace + ws_data_off(p));
         }
-        e = launch_tiled(p, a, c, st);
+        // fp32 activations, bf16 math: with room after the partial tiles, x is
+        // rounded to bf16 once into the workspace (the same rounding the
+        // kernel applies when it stages fp32 rows) and the bf16 kernel runs
+        const int64_t xoff = ws_data_off(p) + round_up(c.part_bytes, 256), xcb = xconv_bytes(p, B);
+        if (workspace && xcb && (size_t)(xoff + xcb) <= ws_bytes) {
+            void *xb = (uint8_t *)workspace + xoff;
+            e = launch_x_to_bf16((const float *)x, xb, B * p.K, st);
+            if (e != hipSuccess)
+                return hip_fail(e, "qgemm_run: kernel launch");
+            Problem pb = p;
+            pb.act = QGEMM_BF16;
+            KArgs ab = a;
+            ab.x = xb;
+            e = launch_tiled(pb, ab, c, st);
+        } else {
+            e = launch_tiled(p, a, c, st);
+        }
     }
     if (e != hipSuccess)
         return hip_fail(e, "qgemm_run: kernel launch");

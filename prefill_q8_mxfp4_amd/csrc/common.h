@@ -399,6 +399,9 @@ struct TiCfg {
 
 hipError_t launch_tiled(const Problem &p, const KArgs &a, const TiCfg &c, hipStream_t st);
 hipError_t launch_tiled_fp32(const Problem &p, const KArgs &a, const TiCfg &c, hipStream_t st);
+// x[n] fp32 -> xb[n] bf16, round to nearest even (n a multiple of 8, both
+// 16-byte aligned).
+hipError_t launch_x_to_bf16(const float *x, void *xb, int64_t n, hipStream_t st);
 
 // Routed experts in the large-batch kernel: E packed weight buffers (device
 // array of device pointers) and E + 1 row offsets (device int32, rows of

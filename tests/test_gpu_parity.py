@@ -298,6 +298,31 @@ def test_ragged_shapes(fmt, act, math, out, tier):
         assert err <= tol, (B, err)
 
 
+@pytest.mark.parametrize("fmt", ["q8_0", "mxfp4", "fp8"])
+def test_fp32_activations_rounded_once_in_the_workspace(fmt):
+    """fp32 activations with bf16 math in the large-batch tier: with a
+    workspace, x is rounded to bf16 once (nearest even) and the bf16 kernel
+    runs, so the result equals, bit for bit, a bf16-activation call on the
+    host-rounded rows with the same workspace; without one, the kernel rounds
+    while staging and meets the same bound."""
+    n, k, B = 1024, 512, 300
+    w = synth.gen_weights(fmt, n, k, seed=21)
+    xf = synth.gen_x_f32(B, k, seed=22)
+    wd = w_dev(w)
+    p32 = q.Plan(fmt, n, k, act="f32", out="f32", math="bf16")
+    p16 = q.Plan(fmt, n, k, act="bf16", out="f32")
+    assert p32.tier(B) == "tiled"
+    need = p32.workspace_bytes(B)
+    assert need >= p16.workspace_bytes(B) + B * k * 2
+    ws = torch.zeros(need, dtype=torch.uint8, device=_dev())
+    y32 = run(p32, xf, wd, workspace=ws)
+    y16 = run(p16, synth.f32_to_bf16_bits(xf), wd, workspace=ws)
+    assert np.array_equal(y32.view(np.uint64), y16.view(np.uint64))
+    ref = oracle.gemm(w, xf)
+    assert oracle.rel_fro(y32, ref) <= TOL_BF16
+    assert oracle.rel_fro(run(p32, xf, wd, workspace=None), ref) <= TOL_BF16
+
+
 def test_b_zero_is_a_noop():
     w = synth.gen_weights("q8_0", 32, 64, seed=1)
     plan = q.Plan("q8_0", 32, 64, act="f32")
