@@ -322,7 +322,9 @@ def main():
             for b in bs:
                 c = synth.CONFIGS[name]
                 nb = q.weight_bytes(c["fmt"], c["N"], c["K"])
-                w = Workload(name, b, copies=copies_for(nb) if b <= 16 else 1)
+                # several calls per graph replay (distinct weight copies) so the
+                # replay overhead is spread as in the B sweep
+                w = Workload(name, b, copies=copies_for(nb) if b <= 16 else 4)
                 t, _ = w.time_ms(max(20, args.steps // 10) if b > 16 else max(40, args.steps // 4),
                                  3)
                 c = w.c
