@@ -33,8 +33,8 @@
 // exact; the three terms' MFMAs of a 32-wide block run into a block partial
 // from zero, and the Q8_0 / MXFP4 / FP8 block scale (staged in LDS beside the
 // weights, one fp32 per staged row and block) multiplies that partial into
-// the accumulator.  Tiles are BM = 64 rows so the three activation planes fit
-// in LDS.
+// the accumulator.  Tiles are BM = 64 or 96 rows so the three activation
+// planes fit in LDS.
 #include <type_traits>
 
 #include "common.h"
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
     constexpr int NTA = FAITH && ACT == ACT_F32 ? 3 : 1;  // activation terms
     constexpr bool POST = FAITH && FMT != FMT_NV;         // block scale after the MFMA
     static_assert(XCH * NTHR * CE == BM * KT, "activation staging");
-    static_assert(!FAITH || BM == 64, "the faithful variant runs 64-row tiles");
+    static_assert(!FAITH || BM == 64 || BM == 96, "the faithful variant runs 64- or 96-row tiles");
 
     __shared__ u32x4 xs[2][NTA][KG * XP];
     __shared__ u32x4 ws[2][KG * WP];
@@ -577,9 +577,13 @@ static void launch_tiled_f(const Problem &p, const KArgs &a, const TiCfg *c, hip
             else
                 launch_tiled_bm<FMT, A, O, D, M, FAITH>(a, *c, st, Nh);
         };
-        if constexpr (FAITH)
-            bm(std::integral_constant<int, 64>{});
-        else if (BM == 128)
+        if constexpr (FAITH) {
+            // 64-row tiles, or 96 for B in (64, 96] (plain GEMM only)
+            if (!g && BM == 96)
+                launch_tiled_bm<FMT, A, O, D, 96, FAITH>(a, *c, st, Nh);
+            else
+                bm(std::integral_constant<int, 64>{});
+        } else if (BM == 128)
             bm(std::integral_constant<int, 128>{});
         else
             bm(std::integral_constant<int, 256>{});
