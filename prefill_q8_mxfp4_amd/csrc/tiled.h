@@ -15,9 +15,10 @@
 // padded by one entry so neither the stage writes nor the fragment reads
 // collide in banks; it is double-buffered.  Global loads go through buffer
 // resources (fixed per-lane offsets, the step in the scalar offset, zero
-// past the data) two steps ahead, and the conversion and LDS stores of the
-// next step are interleaved by hand with the MFMA groups of the current one,
-// so each step ends in one barrier.
+// past the data) into register stages two steps ahead of their use (three or
+// four for routed experts), and the conversion and LDS stores of the next
+// step are interleaved by hand with the MFMA groups of the current one, so
+// each step ends in one barrier.
 //
 // Tile counts: whole rounds of 256 tiles (one per CU) run unsplit; the tiles
 // of a last, partial round may be split along K into pieces, one workgroup
