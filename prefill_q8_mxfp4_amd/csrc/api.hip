@@ -591,7 +591,7 @@ int qgemm_run_grouped(const qgemm_plan *plan, int64_t E, int64_t T, const void *
     KArgs a = make_args(p, T, nullptr, x, y);
     // BM by the mean rows per expert; an upper bound on the experts' row tiles
     // (each expert adds at most one partial tile, and at most T experts have rows)
-    const int BM = p.math == QGEMM_MATH_FP32 ? 64 : T / E >= 192 ? 256 : 128;
+    const int BM = p.math == QGEMM_MATH_FP32 ? 64 : T / E >= 192 ? 256 : T / E >= 64 ? 128 : 64;
     const int64_t tiles = T / BM + (E < T ? E : T);
     Groups g;
     g.wtab = (const uint8_t *const *)w_table;

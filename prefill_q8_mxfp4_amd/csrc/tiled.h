@@ -584,10 +584,14 @@ static void launch_tiled_f(const Problem &p, const KArgs &a, const TiCfg *c, hip
                 launch_tiled_bm<FMT, A, O, D, 96, FAITH>(a, *c, st, Nh);
             else
                 bm(std::integral_constant<int, 64>{});
-        } else if (BM == 128)
+        } else if (g && BM == 64) {
+            // routed experts with few rows each
+            launch_grouped_bm<FMT, A, O, D, 64, FAITH>(a, *g, gtiles, st, Nh);
+        } else if (BM == 128) {
             bm(std::integral_constant<int, 128>{});
-        else
+        } else {
             bm(std::integral_constant<int, 256>{});
+        }
     };
     using F32 = std::integral_constant<int, ACT_F32>;
     using B16 = std::integral_constant<int, ACT_BF16>;
