@@ -252,6 +252,9 @@ def main():
                     help="launch calls one by one instead of replaying a HIP graph (profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 512 MiB copy (scales profiler byte counters)")
+    ap.add_argument("--calls-of", nargs=2, metavar=("CONFIG", "B"),
+                    help="only launch CONFIG at batch B eagerly --steps times, print nothing "
+                         "else (a short program for counter passes)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path; "
@@ -268,6 +271,13 @@ def main():
     sha = kernel_src_sha()
     if args.copy_calibration:
         copy_calibration()
+    if args.calls_of:
+        w = Workload(args.calls_of[0], int(args.calls_of[1]))
+        for _ in range(args.steps):
+            w.plan.run(w.x, w.ws[0], w.y)
+        torch.cuda.synchronize()
+        log(f"[bench] {args.steps} calls of {args.calls_of[0]} B={args.calls_of[1]} done")
+        return
 
     # ---- headline: q8_0 5120x5120, B = 16, fp32 activations
     B = 16
