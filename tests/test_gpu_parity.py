@@ -358,6 +358,49 @@ def test_q8_0_ffn_prefill_2048_bf16():
     assert err <= TOL_BF16
 
 
+# -------------------------------------- full outputs against a library GEMM
+
+def _library_ref(w, x, swiglu=False):
+    """Every output at full size: the oracle's decoded weights (fp64 -> fp32,
+    tensor scales applied) times the activations as given, through torch's
+    fp32 GEMM on the GPU (rocBLAS / hipBLASLt, no reduced-precision inputs),
+    then SiLU(G) * U in fp32 for the fused epilogue."""
+    torch.backends.cuda.matmul.allow_tf32 = False
+    xf = x if x.dtype == np.float32 else synth.bf16_bits_to_f32(x)
+    W = torch.from_numpy(oracle.dequant(w, apply_g=True).astype(np.float32)).to(_dev())
+    y = torch.mm(torch.from_numpy(np.ascontiguousarray(xf)).to(_dev()), W.t().contiguous())
+    del W
+    if swiglu:
+        nh = y.shape[1] // 2
+        G, U = y[:, :nh], y[:, nh:]
+        y = G * torch.sigmoid(G) * U
+    out = y.double().cpu().numpy()
+    del y
+    torch.cuda.empty_cache()
+    return out
+
+
+@pytest.mark.parametrize("name,B", [("cfg3", 2048), ("cfg4", 256), ("cfg4", 2048), ("cfg5", 2048),
+                                    ("fp8_attn", 2048), ("cfg2", 256)])
+def test_full_output_against_library_gemm(name, B):
+    """Every output of the prefill-size workloads (not only the oracle's
+    samples): against the dequantize-then-GEMM textbook reduction, within
+    the path's bound (1e-5 fp32-faithful, 1e-2 bf16)."""
+    c = synth.CONFIGS[name]
+    w = synth.gen_config_weights(name)
+    x = synth.gen_config_x(name, B)
+    swiglu = c["epi"] == "swiglu"
+    plan = q.Plan(c["fmt"], c["N"], c["K"], act=c["act"], out=c["out"],
+                  epilogue="swiglu" if swiglu else "none", math=c["math"])
+    y = run(plan, x, w_dev(w))
+    ref = _library_ref(w, x, swiglu)
+    err = oracle.rel_fro(y, ref)
+    tol = TOL_FP32 if (c["math"] == "fp32" and c["out"] == "f32") else TOL_BF16
+    print(f"{name} B={B} full output vs library GEMM rel_fro={err:.3e}")
+    assert np.all(np.isfinite(y))
+    assert err <= tol
+
+
 @pytest.fixture(scope="module")
 def cfg4():
     w = synth.gen_config_weights("cfg4")
