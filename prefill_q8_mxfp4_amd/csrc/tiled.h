@@ -9,7 +9,9 @@
 //  * weights: BN rows x 64, i.e. one Q8_0 slab or half an FP4 slab of each of
 //    the BN/16 row tiles; a thread's 16-byte (Q8_0) or 8-byte (FP4) piece of a
 //    slab chunk is decoded with its block scale folded in (exact for the FP4
-//    formats, one rounding for Q8_0) into the two bf16 fragments it feeds.
+//    formats, one rounding for Q8_0) into the two bf16 fragments it feeds;
+//    MXFP4 instead stages the codes with their scale and decodes each
+//    fragment as it is read (half the LDS bytes, the same values).
 //
 // LDS holds both operands as 16-byte fragment entries [k-group][row], rows
 // padded by one entry so neither the stage writes nor the fragment reads
@@ -62,7 +64,12 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
     static_assert(!FAITH || BM == 64 || BM == 96, "the faithful variant runs 64- or 96-row tiles");
 
     __shared__ u32x4 xs[2][NTA][KG * XP];
-    __shared__ u32x4 ws[2][KG * WP];
+    // MXFP4 (bf16 math) stages the packed codes instead of decoded bf16: each
+    // entry is one lane's 8 codes of a fragment and its E8M0 scale as fp32
+    // (8 bytes, not 16), decoded when the fragment is read
+    constexpr bool CMX = FMT == FMT_MX && !FAITH;
+    __shared__ u32x4 ws[2][CMX ? 1 : KG * WP];
+    __shared__ u32x2 wsc[2][CMX ? KG * WP : 1];
     __shared__ float ss[POST ? 2 * 2 * BN : 1];  // [buf][32-wide block of the step][staged row]
 
     const int tid = threadIdx.x;
@@ -297,7 +304,9 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
             h = fp8_scaled_to_bf16(wr[r][i][2 * ul], wr[r][i][2 * ul + 1], __uint_as_float(sr[r][i][0]));
         } else if constexpr (FMT == FMT_MX) {
             const int u = 2 * half + ul;
-            h = fp4_to_bf16(wr[r][i][ul], e8m0_to_f32((sr[r][i][0] >> (8 * u)) & 0xFFu));
+            const float d = e8m0_to_f32((sr[r][i][0] >> (8 * u)) & 0xFFu);
+            wsc[buf][(4 * ul + g) * WP + col] = u32x2{wr[r][i][ul], __float_as_uint(d)};
+            return;
         } else {
             const int u = 2 * half + ul;
             const int si = 2 * u + (g >> 1);
@@ -382,7 +391,12 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
             float bsc[TN];  // block scale of each n-tile's column (POST)
 #pragma unroll
             for (int j = 0; j < TN; j++) {
-                bw[j] = __builtin_bit_cast(bf16x8, ws[buf][kg * WP + wcol(j) + (lane & 15)]);
+                if constexpr (CMX) {
+                    const u32x2 e = wsc[buf][kg * WP + wcol(j) + (lane & 15)];
+                    bw[j] = fp4_to_bf16(e[0], __uint_as_float(e[1]));
+                } else {
+                    bw[j] = __builtin_bit_cast(bf16x8, ws[buf][kg * WP + wcol(j) + (lane & 15)]);
+                }
                 if constexpr (POST)
                     bsc[j] = ss[(buf * 2 + kk) * BN + wcol(j) + (lane & 15)];
             }
