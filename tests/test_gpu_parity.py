@@ -323,6 +323,47 @@ def test_fp32_activations_rounded_once_in_the_workspace(fmt):
     assert oracle.rel_fro(run(p32, xf, wd, workspace=None), ref) <= TOL_BF16
 
 
+@pytest.mark.parametrize("fmt,act,math,B", [("q8_0", "f32", "fp32", 16),     # streaming, K split
+                                           ("mxfp4", "bf16", "bf16", 40),   # skinny
+                                           ("q8_0", "f32", "fp32", 100),    # fp32-faithful tiled
+                                           ("nvfp4", "bf16", "bf16", 300),  # tiled, K split + reduce
+                                           ("q8_0", "f32", "bf16", 300)])   # x rounded in the workspace
+def test_graph_capture_replays(fmt, act, math, B):
+    """qgemm_run captured in a HIP graph: every replay, with other work on
+    the GPU between replays, reproduces the eager result bit for bit (the
+    split counters are re-armed by the kernels; nothing is memset)."""
+    n, k = 2048, 1024
+    w = synth.gen_weights(fmt, n, k, seed=31)
+    xf = synth.gen_x_f32(B, k, seed=32)
+    x = xf if act == "f32" else synth.f32_to_bf16_bits(xf)
+    wd, xd = w_dev(w), x_dev(x)
+    plan = q.Plan(fmt, n, k, act=act, out="f32", math=math)
+    ws = torch.zeros(max(plan.workspace_bytes(B), 256), dtype=torch.uint8, device=_dev())
+    y0 = y_new(plan, B)
+    plan.run(xd, wd, y0, workspace=ws)
+    torch.cuda.synchronize()
+    ref = host(y0)
+    assert oracle.rel_fro(ref, oracle.gemm(w, x)) <= (TOL_FP32 if math == "fp32" else TOL_BF16)
+    other = q.Plan(fmt, n, k, act=act, out="f32", math=math)
+    yo = y_new(other, 7)
+    st = torch.cuda.Stream()
+    yg = y_new(plan, B)
+    with torch.cuda.stream(st):
+        plan.run(xd, wd, yg, workspace=ws)  # warm-up on the capture stream
+    st.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        plan.run(xd, wd, yg, workspace=ws)
+    for rep in range(3):
+        yg.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(yg).view(np.uint64), ref.view(np.uint64)), rep
+        other.run(xd[:7], wd, yo, workspace=None)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+
+
 def test_b_zero_is_a_noop():
     w = synth.gen_weights("q8_0", 32, 64, seed=1)
     plan = q.Plan("q8_0", 32, 64, act="f32")
