@@ -309,6 +309,10 @@ def main():
                      "kernel_src_sha": sha},
     }
     log(f"[bench] headline {ms * 1e3:.2f} us/call  {value:.1f} GB/s weights")
+    # spread: 7 more trials of the same loop (the value above stays the timed K steps)
+    trials = sorted(wl.time_ms(max(50, args.steps // 8), 0, eager=args.eager)[0] * 1e3 for _ in range(7))
+    line["headline_trials_us"] = {"n": 7, "min": round(trials[0], 3), "median": round(trials[3], 3),
+                                  "max": round(trials[-1], 3)}
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl)
