@@ -364,6 +364,31 @@ def test_graph_capture_replays(fmt, act, math, B):
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("fmt,act,math,B,tier", [("q8_0", "f32", "fp32", 5, "skinny"),    # streaming
+                                                ("mxfp4", "f32", "fp32", 100, "tiled"),   # fp32-faithful tiled
+                                                ("fp8", "f32", "fp32", 40, "tiled"),
+                                                ("nvfp4", "bf16", "bf16", 40, "skinny"),
+                                                ("q8_0", "f32", "bf16", 300, "tiled")])
+def test_activation_dynamic_range(fmt, act, math, B, tier):
+    """Rows of one call scaled from 1e-20 to 1e20 (the pages' adversarial
+    large-activation case, and its mirror): every row meets the bound on its
+    own, so no row's accuracy depends on the others' magnitude."""
+    n, k = 512, 1024
+    w = synth.gen_weights(fmt, n, k, seed=41)
+    xf = synth.gen_x_f32(B, k, seed=42)
+    scale = (10.0 ** np.linspace(-20, 20, B)).astype(np.float32)
+    xf = (xf * scale[:, None]).astype(np.float32)
+    x = xf if act == "f32" else synth.f32_to_bf16_bits(xf)
+    plan = q.Plan(fmt, n, k, act=act, out="f32", math=math, tier=tier)
+    y = run(plan, x, w_dev(w))
+    ref = oracle.gemm(w, x)
+    tol = TOL_FP32 if math == "fp32" else TOL_BF16
+    worst = max(oracle.rel_fro(y[b], ref[b]) for b in range(B))
+    print(f"{fmt} {tier} {math} dynamic range: worst row rel_fro={worst:.3e}")
+    assert np.all(np.isfinite(y))
+    assert worst <= tol
+
+
 def test_b_zero_is_a_noop():
     w = synth.gen_weights("q8_0", 32, 64, seed=1)
     plan = q.Plan("q8_0", 32, 64, act="f32")
