@@ -282,7 +282,7 @@ def main():
     # ---- headline: q8_0 5120x5120, B = 16, fp32 activations
     B = 16
     probe = q.weight_bytes("q8_0", 5120, 5120)
-    wl = Workload("cfg2", B, copies=copies_for(probe))
+    wl = Workload("q8_0_5120x5120", B, copies=copies_for(probe))
     ms, steps_done = wl.time_ms(args.steps, args.warmup, eager=args.eager)
     value = wl.wbytes / (ms * 1e-3) / 1e9
     achieved = wl.io_bytes() / (ms * 1e-3) / 1e9
@@ -321,7 +321,7 @@ def main():
     if not args.headline_only:
         sweep = {}
         for b in (1, 4, 8, 16, 64, 65, 70, 76, 256):
-            w = Workload("cfg2", b, copies=copies_for(probe) if b <= 16 else 4)
+            w = Workload("q8_0_5120x5120", b, copies=copies_for(probe) if b <= 16 else 4)
             t, _ = w.time_ms(max(40, args.steps // 4), 5)
             sweep[str(b)] = {"us": round(t * 1e3, 2),
                              "weight_GBs": round(w.wbytes / (t * 1e-3) / 1e9, 1),
@@ -331,8 +331,8 @@ def main():
             w.free()
         line["sweep_q8_0_5120x5120_fp32"] = sweep
         pre = {}
-        for name, bs in (("cfg3", (2048,)), ("cfg4", (1, 16, 256, 2048)), ("cfg5", (1, 16, 2048)),
-                         ("fp8_attn", (1, 16, 256, 2048))):
+        for name, bs in (("q8_0_ffn_17408x5120", (2048,)), ("mxfp4_down_5120x17408", (1, 16, 256, 2048)), ("nvfp4_gate_up_34816x5120", (1, 16, 2048)),
+                         ("fp8_5120x5120", (1, 16, 256, 2048))):
             for b in bs:
                 c = synth.CONFIGS[name]
                 nb = q.weight_bytes(c["fmt"], c["N"], c["K"])
@@ -342,7 +342,7 @@ def main():
                 t, _ = w.time_ms(max(20, args.steps // 10) if b > 16 else max(40, args.steps // 4),
                                  3)
                 c = w.c
-                key = f"{name}:{c['fmt']}:{c['N']}x{c['K']}:B={b}"
+                key = f"{name}:B={b}"
                 rec = {"us": round(t * 1e3, 2), "TFLOPs": round(w.flops() / (t * 1e-3) / 1e12, 2),
                        "mfma_frac": round(w.flops() / (t * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                        "weight_GBs": round(w.wbytes / (t * 1e-3) / 1e9, 1),

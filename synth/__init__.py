@@ -311,22 +311,27 @@ def gen_x_bf16(b, k, seed=0, sid=SID_X):
     return f32_to_bf16_bits(normal_f32(seed, sid, b, k, 1.0))
 
 
-# The five workloads (all seed 0).
+# The workloads (all seed 0), named by format, role and N x K; Bs are the
+# batch widths each is checked and measured at.
 CONFIGS = {
-    "cfg1": dict(fmt="q8_0", act="f32", N=256, K=512, Bs=(70,), out="f32", epi="none",
-                 math="fp32"),
-    "cfg2": dict(fmt="q8_0", act="f32", N=5120, K=5120,
-                 Bs=(1, 4, 8, 16, 64, 65, 70, 76, 256), out="f32", epi="none", math="fp32"),
-    "cfg3": dict(fmt="q8_0", act="f32", N=17408, K=5120, Bs=(2048,), out="f32", epi="none",
-                 math="bf16", outlier_p=0.001),
-    "cfg4": dict(fmt="mxfp4", act="bf16", N=5120, K=17408, Bs=(1, 16, 256, 2048), out="f32",
-                 epi="none", math="bf16"),
-    "cfg5": dict(fmt="nvfp4", act="bf16", N=2 * 17408, K=5120, Bs=(2048,), out="bf16",
-                 epi="swiglu", math="bf16"),
-    # not one of the five: the FP8-weight (W8A16) attention-projection shape
-    # of the follow-on format
-    "fp8_attn": dict(fmt="fp8", act="bf16", N=5120, K=5120, Bs=(1, 16, 256, 2048), out="f32",
-                     epi="none", math="bf16"),
+    # the small Q8_0 parity case (crosses the old 64-row limit)
+    "q8_0_256x512": dict(fmt="q8_0", act="f32", N=256, K=512, Bs=(70,), out="f32", epi="none",
+                         math="fp32"),
+    # Q8_0 attention projection over the verify widths
+    "q8_0_5120x5120": dict(fmt="q8_0", act="f32", N=5120, K=5120,
+                           Bs=(1, 4, 8, 16, 64, 65, 70, 76, 256), out="f32", epi="none", math="fp32"),
+    # Q8_0 FFN gate/up prefill chunk, weights with 0.1 % outliers x20
+    "q8_0_ffn_17408x5120": dict(fmt="q8_0", act="f32", N=17408, K=5120, Bs=(2048,), out="f32",
+                                epi="none", math="bf16", outlier_p=0.001),
+    # MXFP4 FFN down projection
+    "mxfp4_down_5120x17408": dict(fmt="mxfp4", act="bf16", N=5120, K=17408, Bs=(1, 16, 256, 2048),
+                                  out="f32", epi="none", math="bf16"),
+    # NVFP4 fused gate+up (SwiGLU), two 17408 x 5120 halves
+    "nvfp4_gate_up_34816x5120": dict(fmt="nvfp4", act="bf16", N=2 * 17408, K=5120, Bs=(2048,),
+                                     out="bf16", epi="swiglu", math="bf16"),
+    # the FP8-weight (W8A16) attention-projection shape of the follow-on format
+    "fp8_5120x5120": dict(fmt="fp8", act="bf16", N=5120, K=5120, Bs=(1, 16, 256, 2048), out="f32",
+                          epi="none", math="bf16"),
 }
 
 

@@ -228,7 +228,7 @@ def test_plan_errors_raise():
 
 
 def test_synth_configs_pack():
-    w = synth.gen_config_weights("cfg1")
+    w = synth.gen_config_weights("q8_0_256x512")
     buf = q.pack_logical(w)
     assert buf.size == q.weight_bytes("q8_0", 256, 512)
 

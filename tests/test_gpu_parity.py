@@ -90,47 +90,47 @@ def test_dequantize_bit_exact(fmt, n, k):
     assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
 
 
-# ------------------------------------------------ small workload (cfg1)
+# ------------------------------------------------ small workload (Q8_0 256 x 512)
 
 def test_q8_0_256x512_b70_fp32():
-    c = synth.CONFIGS["cfg1"]
-    w = synth.gen_config_weights("cfg1")
-    x = synth.gen_config_x("cfg1", 70)
+    c = synth.CONFIGS["q8_0_256x512"]
+    w = synth.gen_config_weights("q8_0_256x512")
+    x = synth.gen_config_x("q8_0_256x512", 70)
     plan = q.Plan("q8_0", c["N"], c["K"], act="f32", out="f32", math="fp32")
     y = run(plan, x, w_dev(w))
     err = oracle.rel_fro(y, oracle.gemm(w, x))
-    print(f"cfg1 B=70 rel_fro={err:.3e}")
+    print(f"q8_0 256x512 B=70 rel_fro={err:.3e}")
     assert err <= TOL_FP32
 
 
 # ------------------------------------------- attention projection sweep
 
 @pytest.fixture(scope="module")
-def cfg2():
-    w = synth.gen_config_weights("cfg2")
-    x = synth.gen_config_x("cfg2", 256)
+def q8_attn():
+    w = synth.gen_config_weights("q8_0_5120x5120")
+    x = synth.gen_config_x("q8_0_5120x5120", 256)
     ref = oracle.gemm(w, x)  # rows are independent: prefixes serve every B
     return w, x, ref, w_dev(w)
 
 
-@pytest.mark.parametrize("B", synth.CONFIGS["cfg2"]["Bs"])
-def test_q8_0_5120_sweep_fp32(cfg2, B):
-    w, x, ref, wd = cfg2
+@pytest.mark.parametrize("B", synth.CONFIGS["q8_0_5120x5120"]["Bs"])
+def test_q8_0_5120_sweep_fp32(q8_attn, B):
+    w, x, ref, wd = q8_attn
     plan = q.Plan("q8_0", 5120, 5120, act="f32", out="f32", math="fp32")
     y = run(plan, x[:B], wd)
     err = oracle.rel_fro(y, ref[:B])
-    print(f"cfg2 B={B} tier={plan.tier(B)} rel_fro={err:.3e}")
+    print(f"q8_0 5120x5120 B={B} tier={plan.tier(B)} rel_fro={err:.3e}")
     assert err <= TOL_FP32
 
 
 @pytest.mark.parametrize("tier", ["skinny", "tiled"])
-def test_boundary_matrix_chunked_is_bitwise(cfg2, tier):
+def test_boundary_matrix_chunked_is_bitwise(q8_attn, tier):
     """hipfire PR 'fix(mtp): chunk scalar Q8 batched GEMM above 64 rows',
     Scalar-Q8 boundary matrix: one call at B = 64/65/70/76/256 equals the
     same rows computed in contiguous chunks of 64, bit for bit.  The
     large-batch tier is compared on its unsplit route: its K split depends on
     the tile count, hence on B."""
-    w, x, ref, wd = cfg2
+    w, x, ref, wd = q8_attn
     math = "fp32" if tier == "skinny" else "bf16"
     plan = q.Plan("q8_0", 5120, 5120, act="f32", out="f32", math=math, tier=tier)
     wsp = "auto" if tier == "skinny" else None
@@ -142,11 +142,11 @@ def test_boundary_matrix_chunked_is_bitwise(cfg2, tier):
         assert oracle.rel_fro(whole, ref[:B]) <= tol
 
 
-def test_deterministic_and_row_independent(cfg2):
+def test_deterministic_and_row_independent(q8_attn):
     """Repeated calls agree bit for bit, and within the small-batch tiers a
     row's result does not depend on how many other rows share the call (the
     summation order is fixed by N and K alone)."""
-    w, x, ref, wd = cfg2
+    w, x, ref, wd = q8_attn
     plan = q.Plan("q8_0", 5120, 5120, act="f32", out="f32", math="fp32", tier="skinny")
     y16 = run(plan, x[:16], wd)
     assert np.array_equal(y16, run(plan, x[:16], wd))
@@ -157,10 +157,10 @@ def test_deterministic_and_row_independent(cfg2):
 
 
 @pytest.mark.parametrize("B", (1, 16, 65, 256))
-def test_split_k_and_unsplit_agree(cfg2, B):
+def test_split_k_and_unsplit_agree(q8_attn, B):
     """The K-split route (with a workspace) and the unsplit route both meet
     the fp32 bound, and the tile counters are re-armed after every call."""
-    w, x, ref, wd = cfg2
+    w, x, ref, wd = q8_attn
     plan = q.Plan("q8_0", 5120, 5120, act="f32", out="f32", math="fp32")
     assert plan.workspace_bytes(B) > 0
     ws = torch.zeros(plan.workspace_bytes(256) + (1 << 20), dtype=torch.uint8, device=_dev())
@@ -171,11 +171,11 @@ def test_split_k_and_unsplit_agree(cfg2, B):
     assert torch.count_nonzero(ws[:128]) == 0  # tile counters re-armed
 
 
-def test_workspace_reused_across_batch_widths(cfg2):
+def test_workspace_reused_across_batch_widths(q8_attn):
     """One workspace, calls of alternating widths: every output is written and
     correct (the counters of one width are never hit by another width's
     partial tiles).  Outputs start as NaN so a skipped tile shows up."""
-    w, x, ref, wd = cfg2
+    w, x, ref, wd = q8_attn
     plan = q.Plan("q8_0", 5120, 5120, act="f32", out="f32", math="fp32")
     ws = torch.zeros(plan.workspace_bytes(256), dtype=torch.uint8, device=_dev())
     for B in (70, 6, 70, 64, 1, 256, 16, 70, 6):
@@ -184,12 +184,12 @@ def test_workspace_reused_across_batch_widths(cfg2):
         assert oracle.rel_fro(y, ref[:B]) <= TOL_FP32, B
 
 
-def test_workspace_shared_by_both_tiers(cfg2):
+def test_workspace_shared_by_both_tiers(q8_attn):
     """One workspace for small- and large-batch calls of a bf16 plan: the
     large-batch pieces (left as written) must not land where the small-batch
     kernels look for published partial tiles.  Every call must match, bit for
     bit, the same call on a fresh zeroed workspace."""
-    w, x, ref, wd = cfg2
+    w, x, ref, wd = q8_attn
     plan = q.Plan("q8_0", 5120, 5120, act="bf16", out="f32")
     xb = np.tile(torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy(), (8, 1))  # 2048 rows
     need = max(plan.workspace_bytes(b) for b in (2048, 300, 16, 1))
@@ -411,16 +411,16 @@ def _samples(B, ncols, count, seed):
 
 
 def test_q8_0_ffn_prefill_2048_bf16():
-    c = synth.CONFIGS["cfg3"]
-    w = synth.gen_config_weights("cfg3")
-    x = synth.gen_config_x("cfg3", 2048)
+    c = synth.CONFIGS["q8_0_ffn_17408x5120"]
+    w = synth.gen_config_weights("q8_0_ffn_17408x5120")
+    x = synth.gen_config_x("q8_0_ffn_17408x5120", 2048)
     plan = q.Plan("q8_0", c["N"], c["K"], act="f32", out="f32", math="bf16")
     assert plan.tier(2048) == "tiled"
     y = run(plan, x, w_dev(w))
     assert np.all(np.isfinite(y))
     bi, ni = _samples(2048, c["N"], 6000, 3)
     err = oracle.rel_fro(y[bi, ni], oracle.gemm_at(w, x, bi, ni))
-    print(f"cfg3 rel_fro(sampled)={err:.3e}")
+    print(f"q8_0 ffn rel_fro(sampled)={err:.3e}")
     assert err <= TOL_BF16
 
 
@@ -446,8 +446,8 @@ def _library_ref(w, x, swiglu=False):
     return out
 
 
-@pytest.mark.parametrize("name,B", [("cfg3", 2048), ("cfg4", 256), ("cfg4", 2048), ("cfg5", 2048),
-                                    ("fp8_attn", 2048), ("cfg2", 256)])
+@pytest.mark.parametrize("name,B", [("q8_0_ffn_17408x5120", 2048), ("mxfp4_down_5120x17408", 256), ("mxfp4_down_5120x17408", 2048), ("nvfp4_gate_up_34816x5120", 2048),
+                                    ("fp8_5120x5120", 2048), ("q8_0_5120x5120", 256)])
 def test_full_output_against_library_gemm(name, B):
     """Every output of the prefill-size workloads (not only the oracle's
     samples): against the dequantize-then-GEMM textbook reduction, within
@@ -468,32 +468,32 @@ def test_full_output_against_library_gemm(name, B):
 
 
 @pytest.fixture(scope="module")
-def cfg4():
-    w = synth.gen_config_weights("cfg4")
-    x = synth.gen_config_x("cfg4", 2048)
+def mx_down():
+    w = synth.gen_config_weights("mxfp4_down_5120x17408")
+    x = synth.gen_config_x("mxfp4_down_5120x17408", 2048)
     return w, x, w_dev(w)
 
 
-@pytest.mark.parametrize("B", synth.CONFIGS["cfg4"]["Bs"])
-def test_mxfp4_down_projection(cfg4, B):
-    w, x, wd = cfg4
+@pytest.mark.parametrize("B", synth.CONFIGS["mxfp4_down_5120x17408"]["Bs"])
+def test_mxfp4_down_projection(mx_down, B):
+    w, x, wd = mx_down
     plan = q.Plan("mxfp4", 5120, 17408, act="bf16", out="f32")
     y = run(plan, x[:B], wd)
     assert np.all(np.isfinite(y))
     bi, ni = _samples(B, 5120, 3000, B)
     err = oracle.rel_fro(y[bi, ni], oracle.gemm_at(w, x[:B], bi, ni))
-    print(f"cfg4 B={B} tier={plan.tier(B)} rel_fro(sampled)={err:.3e}")
+    print(f"mxfp4 down B={B} tier={plan.tier(B)} rel_fro(sampled)={err:.3e}")
     assert err <= TOL_BF16
 
 
 @pytest.fixture(scope="module")
 def fp8_attn():
-    w = synth.gen_config_weights("fp8_attn")
-    x = synth.gen_config_x("fp8_attn", 2048)
+    w = synth.gen_config_weights("fp8_5120x5120")
+    x = synth.gen_config_x("fp8_5120x5120", 2048)
     return w, x, w_dev(w)
 
 
-@pytest.mark.parametrize("B", synth.CONFIGS["fp8_attn"]["Bs"])
+@pytest.mark.parametrize("B", synth.CONFIGS["fp8_5120x5120"]["Bs"])
 def test_fp8_attention_projection(fp8_attn, B):
     """FP8 E4M3 weights (128-wide block scales) x bf16 activations at the
     K = N = 5120 projection shape, every tier by B."""
@@ -521,16 +521,16 @@ def test_fp8_fp32_math(fp8_attn, B):
 
 
 def test_nvfp4_fused_gate_up_swiglu_2048():
-    c = synth.CONFIGS["cfg5"]
-    w = synth.gen_config_weights("cfg5")
-    x = synth.gen_config_x("cfg5", 2048)
+    c = synth.CONFIGS["nvfp4_gate_up_34816x5120"]
+    w = synth.gen_config_weights("nvfp4_gate_up_34816x5120")
+    x = synth.gen_config_x("nvfp4_gate_up_34816x5120", 2048)
     plan = q.Plan("nvfp4", c["N"], c["K"], act="bf16", out="bf16", epilogue="swiglu")
     y = run(plan, x, w_dev(w))
     assert y.shape == (2048, c["N"] // 2)
     assert np.all(np.isfinite(y))
     bi, ji = _samples(2048, c["N"] // 2, 4000, 5)
     err = oracle.rel_fro(y[bi, ji], oracle.swiglu_at(w, x, bi, ji))
-    print(f"cfg5 rel_fro(sampled)={err:.3e}")
+    print(f"nvfp4 gate+up rel_fro(sampled)={err:.3e}")
     assert err <= TOL_BF16
 
 
@@ -601,12 +601,12 @@ def test_swiglu_streaming_small_batch(fmt):
             assert err <= 1e-4, (B, ws, err)
 
 
-def test_swiglu_streaming_cfg5_shape_b16():
+def test_swiglu_streaming_gate_up_shape_b16():
     """The NVFP4 fused gate+up shape (K = 5120, N = 2 x 17408) at B = 16,
     bf16 output, checked on sampled outputs."""
-    c = synth.CONFIGS["cfg5"]
-    w = synth.gen_config_weights("cfg5")
-    x = synth.gen_config_x("cfg5", 16)
+    c = synth.CONFIGS["nvfp4_gate_up_34816x5120"]
+    w = synth.gen_config_weights("nvfp4_gate_up_34816x5120")
+    x = synth.gen_config_x("nvfp4_gate_up_34816x5120", 16)
     plan = q.Plan("nvfp4", c["N"], c["K"], act="bf16", out="bf16", epilogue="swiglu")
     assert plan.tier(16) == "skinny"
     y = run(plan, x, w_dev(w))
