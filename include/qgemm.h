@@ -103,7 +103,7 @@ typedef enum qgemm_tier {
     QGEMM_TIER_SKINNY = 1, /* weights streamed once per 16..64 batch rows straight
                               into matrix-core operands; for small B */
     QGEMM_TIER_TILED = 2   /* batch x weight tiles staged through LDS; for large B
-                              (B > 64 with bf16 math, B > 16 with fp32 math) */
+                              (B > 32 with bf16 math, B > 16 with fp32 math) */
 } qgemm_tier;
 
 #define QGEMM_FLAG_FORCE_SKINNY 0x1u

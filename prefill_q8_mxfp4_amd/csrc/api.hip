@@ -253,7 +253,11 @@ static int choose_tier(const qgemm_plan *plan, int64_t B)
         return B <= ST_MAX_B ? QGEMM_TIER_SKINNY : QGEMM_TIER_TILED;
     if (p.epi == QGEMM_EPI_SWIGLU)  // fused gate+up: the streaming kernel or the tiled tier
         return B <= ST_MAX_B ? QGEMM_TIER_SKINNY : QGEMM_TIER_TILED;
-    return B <= 64 ? QGEMM_TIER_SKINNY : QGEMM_TIER_TILED;
+    // bf16 math: the skinny kernel's cost grows per 16-row group, the tiled
+    // kernel's 128-row tile costs about the same from B = 17 to 128; measured
+    // on the box the tiled tier wins from B = 48 in every format (and at 32 for
+    // MXFP4 and Q8_0)
+    return B <= 32 ? QGEMM_TIER_SKINNY : QGEMM_TIER_TILED;
 }
 
 static KArgs make_args(const Problem &p, int64_t B, const void *w, const void *x, void *y)

@@ -104,6 +104,7 @@ def test_run_validation_before_any_hip_call():
 def test_tier_choice():
     p = q.Plan("mxfp4", 5120, 17408, act="bf16")
     assert p.tier(1) == "skinny" and p.tier(16) == "skinny" and p.tier(2048) == "tiled"
+    assert p.tier(32) == "skinny" and p.tier(33) == "tiled"  # bf16 math: tiled from B = 33
     p = q.Plan("nvfp4", 2 * 17408, 5120, act="bf16", out="bf16", epilogue="swiglu")
     assert p.tier(2048) == "tiled" and p.tier(17) == "tiled"
     assert p.tier(1) == "skinny" and p.tier(16) == "skinny"
