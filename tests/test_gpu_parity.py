@@ -446,6 +446,26 @@ def _library_ref(w, x, swiglu=False):
     return out
 
 
+@pytest.mark.parametrize("act,math,B", [("f32", "fp32", 4),     # streaming
+                                         ("f32", "fp32", 100),   # fp32-faithful tiled, 96-row tiles
+                                         ("bf16", "bf16", 300)])  # tiled, 128-row tiles
+def test_largest_k(act, math, B):
+    """K = 2^20, the largest K a plan accepts: every per-workgroup offset
+    stays in range (against the dequantize-then-fp32-GEMM reduction)."""
+    n, k = 256, 1 << 20
+    w = synth.gen_weights("q8_0", n, k, seed=51)
+    xf = synth.gen_x_f32(B, k, seed=52)
+    x = xf if act == "f32" else synth.f32_to_bf16_bits(xf)
+    plan = q.Plan("q8_0", n, k, act=act, out="f32", math=math)
+    y = run(plan, x, w_dev(w))
+    bi, ni = _samples(B, n, 200, 53)
+    err = oracle.rel_fro(y[bi, ni], oracle.gemm_at(w, x, bi, ni))
+    lib = oracle.rel_fro(y, _library_ref(w, x))
+    print(f"K=2^20 B={B} {math} rel_fro(oracle samples)={err:.3e} (vs fp32 library GEMM {lib:.3e})")
+    assert np.all(np.isfinite(y))
+    assert err <= (TOL_FP32 if math == "fp32" else TOL_BF16)
+
+
 @pytest.mark.parametrize("name,B", [("q8_0_ffn_17408x5120", 2048), ("mxfp4_down_5120x17408", 256), ("mxfp4_down_5120x17408", 2048), ("nvfp4_gate_up_34816x5120", 2048),
                                     ("fp8_5120x5120", 2048), ("q8_0_5120x5120", 256)])
 def test_full_output_against_library_gemm(name, B):
