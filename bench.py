@@ -302,7 +302,7 @@ def main():
         "config": {"workload": "Q8_0 batched GEMM K=5120 N=5120 B=16, fp32 activations "
                                "~N(0,1), weights ~N(0,0.02), fp32 out, fp32-faithful math",
                    "B": B, "N": 5120, "K": 5120, "weight_copies": len(wl.ws),
-                   "tier": wl.plan.tier(B)},
+                   "tier": wl.plan.tier(B), "xcd_local_exchange": q.xcd_local()},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_record(sha), "algorithmic_bytes": wl.io_bytes(),

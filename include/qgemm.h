@@ -161,8 +161,13 @@ typedef struct qgemm_plan qgemm_plan;
  * dtype; math: see qgemm_math (QGEMM_MATH_FP32 needs act = QGEMM_F32; the
  * SwiGLU epilogue needs QGEMM_MATH_BF16, else QGEMM_ENOTSUP); flags:
  * 0 or one QGEMM_FLAG_FORCE_* bit (also settable with the environment
- * variable QGEMM_FORCE_TIER=skinny|tiled).  Host only: allocates the small
- * plan object, no device memory and no HIP call.  *plan receives the handle. */
+ * variable QGEMM_FORCE_TIER=skinny|tiled).  Allocates the small plan
+ * object and no device memory.  The first call on a device (the current one)
+ * also runs a one-time dispatch probe there: a small kernel on a stream of
+ * its own and a synchronous 8 KB copy from a static device array, which
+ * decides whether the small-batch kernel's K splits can meet in one XCD's L2
+ * (results are bitwise the same either way); without a device the probe is
+ * skipped.  *plan receives the handle. */
 int qgemm_create(qgemm_plan **plan, qgemm_format fmt, qgemm_dtype act, qgemm_dtype out,
                  qgemm_epilogue epi, qgemm_math math, int64_t N, int64_t K, uint32_t flags);
 
@@ -226,6 +231,14 @@ int qgemm_run_ws(const qgemm_plan *plan, int64_t B, const void *w, const void *x
 
 /* The tier qgemm_run would use for B (QGEMM_TIER_*), or 0 for a bad plan. */
 int qgemm_plan_tier(const qgemm_plan *plan, int64_t B);
+
+/* Outcome of qgemm_create's dispatch probe on the current device: 1 when
+ * workgroup ids congruent mod 8 ran on one XCD (the small-batch kernel's K
+ * splits then meet in that XCD's L2), 0 when they did not or the probe
+ * failed, -1 when no plan was created on this device yet or there is no
+ * device.  The environment variable QGEMM_ST_XLOCAL=0|1 overrides the
+ * outcome for runs (not for this report). */
+int qgemm_xcd_local(void);
 
 /* Release a plan (NULL is accepted). */
 int qgemm_destroy(qgemm_plan *plan);

@@ -34,7 +34,7 @@ MAX_TENSORS = 60
 
 EXPORTS = ("qgemm_weight_bytes", "qgemm_pack", "qgemm_create", "qgemm_run", "qgemm_run_ws",
            "qgemm_run_grouped",
-           "qgemm_workspace_bytes", "qgemm_plan_tier",
+           "qgemm_workspace_bytes", "qgemm_plan_tier", "qgemm_xcd_local",
            "qgemm_destroy", "qgemm_dequantize", "qgemm_strerror", "qgemm_last_error",
            "qgemm_version")
 
@@ -84,6 +84,8 @@ def lib():
     L.qgemm_last_error.argtypes = []
     L.qgemm_version.restype = i32
     L.qgemm_version.argtypes = []
+    L.qgemm_xcd_local.restype = i32
+    L.qgemm_xcd_local.argtypes = []
     _lib = L
     return L
 
@@ -264,6 +266,12 @@ def dequantize(fmt: str, w, N: int, K: int, stream=None):
     _check(lib().qgemm_dequantize(FORMATS[fmt], _dev_ptr(w, "w"), _dev_ptr(out, "out"), N, K,
                                   _stream_ptr(stream)))
     return out
+
+
+def xcd_local() -> int:
+    """Dispatch probe outcome on the current device (see qgemm_xcd_local):
+    1 XCD-local K-split exchange, 0 device-coherent, -1 not probed."""
+    return int(lib().qgemm_xcd_local())
 
 
 def version() -> tuple:

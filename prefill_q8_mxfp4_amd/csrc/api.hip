@@ -6,6 +6,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
 #include <new>
 
 #include "common.h"
@@ -134,6 +136,82 @@ static bool use_stream(const Problem &p, int64_t B)
     return B <= ST_MAX_B && env_int("QGEMM_SK_STREAM", 1) != 0;
 }
 
+// XCD dispatch probe.  The streaming kernel's XCD-local split exchange
+// needs every workgroup id congruent mod 8 to run on one XCD, so that one L2
+// holds all partial tiles of a row group (the hardware dispatcher deals
+// consecutive workgroup ids to the XCDs round-robin).  qgemm_create checks
+// this once per device: a probe kernel records the XCC id (hardware register
+// XCC_ID) of 2048 workgroups, three times, and the exchange is enabled on a
+// device only if ids b and b mod 8 always ran on the same XCC.  Devices never
+// probed, or that fail, use the device-coherent exchange; both give bitwise
+// the same result (same partials, same split order).
+static const int XCC_PROBE_WGS = 2048;
+static const int MAX_DEVICES = 64;
+static std::atomic<int> g_xlocal[MAX_DEVICES];  // 0 not probed, 1 round-robin, 2 not
+static std::mutex g_probe_mu;
+static __device__ uint32_t g_xcc_probe[XCC_PROBE_WGS];  // the probe's output, one word per workgroup
+
+__global__ void xcc_probe_kernel(uint32_t *o)
+{
+    // s_getreg of HW_REG_XCC_ID (id 20), bits [3:0]
+    if (threadIdx.x == 0)
+        o[blockIdx.x] = __builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) & 15u;
+}
+
+static int current_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) {
+        (void)hipGetLastError();
+        return -1;
+    }
+    return dev;
+}
+
+static void probe_xcd_dispatch()
+{
+    const int dev = current_device();
+    if (dev < 0 || g_xlocal[dev].load() != 0)
+        return;
+    std::lock_guard<std::mutex> lock(g_probe_mu);
+    if (g_xlocal[dev].load() != 0)
+        return;
+    // relaxed capture mode for this thread and a stream of its own, so a
+    // graph being captured on another stream is not disturbed
+    hipStreamCaptureMode mode = hipStreamCaptureModeRelaxed;
+    (void)hipThreadExchangeStreamCaptureMode(&mode);
+    bool good = false;
+    uint32_t *d = nullptr;  // device address of g_xcc_probe on this device
+    hipStream_t st = nullptr;
+    static uint32_t h[XCC_PROBE_WGS];
+    if (hipGetSymbolAddress((void **)&d, HIP_SYMBOL(g_xcc_probe)) == hipSuccess && d &&
+        hipStreamCreateWithFlags(&st, hipStreamNonBlocking) == hipSuccess) {
+        good = true;
+        for (int rep = 0; rep < 3 && good; rep++) {
+            hipLaunchKernelGGL(xcc_probe_kernel, dim3(XCC_PROBE_WGS), dim3(64), 0, st, d);
+            good = hipMemcpyAsync(h, d, sizeof h, hipMemcpyDeviceToHost, st) == hipSuccess &&
+                   hipStreamSynchronize(st) == hipSuccess;
+            for (int b = 8; good && b < XCC_PROBE_WGS; b++)
+                good = h[b] == h[b % 8];
+        }
+    }
+    if (st)
+        (void)hipStreamDestroy(st);
+    (void)hipGetLastError();
+    (void)hipThreadExchangeStreamCaptureMode(&mode);
+    g_xlocal[dev].store(good ? 1 : 2);
+}
+
+// Whether the current device passed the probe; QGEMM_ST_XLOCAL=0/1 overrides.
+static bool xcd_local_exchange()
+{
+    const int f = env_int("QGEMM_ST_XLOCAL", -1);
+    if (f >= 0)
+        return f != 0;
+    const int dev = current_device();
+    return dev >= 0 && g_xlocal[dev].load(std::memory_order_relaxed) == 1;
+}
+
 // The streaming kernel's shape: 8 row tiles per workgroup and KC-slab splits
 // (split_kc).  Depends on the problem only, not on B.
 static StCfg stream_cfg(const Problem &p, bool split)
@@ -148,6 +226,9 @@ static StCfg stream_cfg(const Problem &p, bool split)
     c.kc = split ? c.KC : (S + c.KC - 1) / c.KC * c.KC;
     c.ksplit = (S + c.kc - 1) / c.kc;
     c.ngroups = (int)((p.L.RT + 7) / 8);
+    c.xlocal = c.ksplit > 1 && xcd_local_exchange();
+    // XCD-local exchange: 8 XCDs x ceil(groups / 8) groups x ksplit
+    c.grid = c.xlocal ? (c.ngroups + 7) / 8 * 8 * c.ksplit : c.ngroups * c.ksplit;
     if (c.ksplit > 1) {
         c.cnt_bytes = ws_data_off(p);
         c.part_bytes = (int64_t)c.ksplit * c.ngroups * 8 * 1024;
@@ -440,6 +521,7 @@ int qgemm_create(qgemm_plan **plan, qgemm_format fmt, qgemm_dtype act, qgemm_dty
     p->p.N = N;
     p->p.K = K;
     make_layout((int)fmt, N, K, &p->p.L);
+    probe_xcd_dispatch();
     *plan = p;
     return QGEMM_OK;
 }
@@ -453,6 +535,15 @@ int qgemm_destroy(qgemm_plan *plan)
     plan->magic = 0;
     delete plan;
     return QGEMM_OK;
+}
+
+int qgemm_xcd_local(void)
+{
+    const int dev = current_device();
+    if (dev < 0)
+        return -1;
+    const int v = g_xlocal[dev].load();
+    return v == 0 ? -1 : v == 1 ? 1 : 0;
 }
 
 int qgemm_plan_tier(const qgemm_plan *plan, int64_t B)
@@ -522,6 +613,7 @@ int qgemm_run_ws(const qgemm_plan *plan, int64_t B, const void *w, const void *x
             ws.ksplit = c.ksplit;
             ws.kc = c.kc;
             ws.kch = c.KC;
+            ws.xlocal = c.xlocal;
             e = launch_stream(p, a, c, ws, nterm, st);
             if (e != hipSuccess)
                 return hip_fail(e, "qgemm_run: kernel launch");
@@ -539,6 +631,7 @@ int qgemm_run_ws(const qgemm_plan *plan, int64_t B, const void *w, const void *x
         ws.ksplit = c.ksplit;
         ws.kc = c.kc;
         ws.kch = c.kch;
+        ws.xlocal = 0;
         e = launch_skinny(p, a, c, ws, nterm, st);
     } else {
         TiCfg c = tiled_cfg(p, B, workspace != nullptr);

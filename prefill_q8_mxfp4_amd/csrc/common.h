@@ -326,6 +326,11 @@ struct SkinnyWs {
     int ksplit;
     int kc;           // a multiple of kch
     int kch;          // a multiple of SK_RING
+    // streaming kernel only: every K split of a row group runs on one XCD
+    // (workgroup ids congruent mod 8; the dispatcher deals ids to the XCDs
+    // round-robin), so partial tiles are exchanged through that XCD's L2
+    // (workgroup-scope stores and loads) instead of device-coherent memory
+    int xlocal;
 };
 
 // LDS bytes of one staged slab: NTA terms x MB x units x 64 lanes x 16 B.
@@ -345,14 +350,17 @@ struct StCfg {
     int W, NPH, KC;
     int Nh;  // SwiGLU: gate rows (N / 2), else 0
     int ngroups, ksplit, kc;
+    int xlocal, grid;  // XCD-local split exchange (SkinnyWs::xlocal); workgroups launched
     int64_t cnt_bytes, part_bytes;
 };
 
 // Last workgroup of a K split: sum the ksplit partial tiles of `tile` in
 // split order (its own partial `own` in place ks), loading up to 8 partials
-// at a time so their latencies overlap.
-__device__ __forceinline__ f32x4 reduce_partials(const uint64_t *part, int ksplit, int ks, int64_t tiles,
-                                                 int64_t tile, int lane, f32x4 own)
+// at a time so their latencies overlap.  SCOPE is the scope the partials
+// were stored with (see SkinnyWs::xlocal).
+template <int SCOPE>
+__device__ __forceinline__ f32x4 reduce_partials_s(const uint64_t *part, int ksplit, int ks, int64_t tiles,
+                                                   int64_t tile, int lane, f32x4 own)
 {
     f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int k0 = 0; k0 < ksplit; k0 += 8) {
@@ -361,8 +369,8 @@ __device__ __forceinline__ f32x4 reduce_partials(const uint64_t *part, int kspli
         for (int j = 0; j < 8; j++) {
             const int kk = min(k0 + j, ksplit - 1);
             const uint64_t *src = part + (((int64_t)kk * tiles + tile) * 64 + lane) * 2;
-            lo[j] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            hi[j] = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            lo[j] = __hip_atomic_load(src, __ATOMIC_RELAXED, SCOPE);
+            hi[j] = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, SCOPE);
         }
 #pragma unroll
         for (int j = 0; j < 8; j++) {
@@ -376,6 +384,12 @@ __device__ __forceinline__ f32x4 reduce_partials(const uint64_t *part, int kspli
         }
     }
     return sum;
+}
+
+__device__ __forceinline__ f32x4 reduce_partials(const uint64_t *part, int ksplit, int ks, int64_t tiles,
+                                                 int64_t tile, int lane, f32x4 own)
+{
+    return reduce_partials_s<__HIP_MEMORY_SCOPE_AGENT>(part, ksplit, ks, tiles, tile, lane, own);
 }
 
 hipError_t launch_skinny(const Problem &p, const KArgs &a, const SkCfg &c, const SkinnyWs &ws,

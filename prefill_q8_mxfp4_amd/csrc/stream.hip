@@ -33,8 +33,12 @@
 // Summation order (also used by the B > 16 kernel, so a batch row's result
 // does not depend on B): per slab, its units in order into a partial from
 // zero; partials added to the running tile in slab order; K splits added in
-// split order by the last workgroup of a row group to arrive (device-scope
-// stores, a device-scope counter, no device-wide fence).
+// split order by the last workgroup of a row group to arrive (partial-tile
+// stores, a device-scope counter, no device-wide fence).  The partial tiles
+// go through device-coherent memory, or, when the dispatcher is known to put
+// workgroup ids congruent mod 8 on one XCD and all splits of a row group are
+// given such ids, through that XCD's L2 (workgroup-scope stores and loads:
+// no write-through to memory, and the last workgroup's reads hit in L2).
 #include "common.h"
 
 namespace qg {
@@ -61,17 +65,27 @@ __global__ __launch_bounds__(64 * st_max_waves(NPH)) void stream_kernel(KArgs a,
     const int r = lane & 15, gq = lane >> 4;
 
     // XCD-aware order: consecutive workgroup ids go to different XCDs (id mod
-    // 8).  Give each XCD a contiguous run of (split, group) pairs, split
-    // major, so an XCD's workgroups share few activation slices in its L2.
-    int t = blockIdx.x;
-    {
+    // 8).  With the XCD-local exchange, XCD x runs the row groups x, x + 8,
+    // ..., each with all its K splits in a row (workgroups past the last
+    // group leave at once); otherwise each XCD gets a contiguous run of
+    // (split, group) pairs, split major, so an XCD's workgroups share few
+    // activation slices in its L2.
+    int ks, grp;
+    if (ws.xlocal) {
+        const int xcd = blockIdx.x % 8, loc = blockIdx.x / 8;
+        grp = (loc / ws.ksplit) * 8 + xcd;
+        ks = loc % ws.ksplit;
+        if (grp >= ngroups)
+            return;  // uniform over the workgroup
+    } else {
         const int nwg = gridDim.x;
         const int per = (nwg + 7) / 8;
-        const int xcd = t % 8, loc = t / 8;
+        const int xcd = blockIdx.x % 8, loc = blockIdx.x / 8;
         const int full = nwg % 8 == 0 ? 8 : nwg % 8;
-        t = xcd < full ? xcd * per + loc : full * per + (xcd - full) * (per - 1) + loc;
+        const int t = xcd < full ? xcd * per + loc : full * per + (xcd - full) * (per - 1) + loc;
+        ks = t / ngroups;
+        grp = t % ngroups;
     }
-    const int ks = t / ngroups, grp = t % ngroups;
     // the group's row tiles g = 0..7: 8 consecutive ones, or with SwiGLU
     // (Nh > 0) 4 gate tiles and the 4 matching up tiles Nh/16 further on
     const int rt0 = Nh ? grp * (ST_RG / 2) : grp * ST_RG;
@@ -265,10 +279,15 @@ __global__ __launch_bounds__(64 * st_max_waves(NPH)) void stream_kernel(KArgs a,
         if (wid < ST_RG) {
             uint64_t *dst = part + (((int64_t)ks * tiles + tile) * 64 + lane) * 2;
             const u32x4 v = __builtin_bit_cast(u32x4, acc);
-            __hip_atomic_store(dst, (uint64_t)v[0] | ((uint64_t)v[1] << 32), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(dst + 1, (uint64_t)v[2] | ((uint64_t)v[3] << 32), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+            const uint64_t v0 = (uint64_t)v[0] | ((uint64_t)v[1] << 32);
+            const uint64_t v1 = (uint64_t)v[2] | ((uint64_t)v[3] << 32);
+            if (ws.xlocal) {  // every reader of these lines runs on this XCD
+                __hip_atomic_store(dst, v0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                __hip_atomic_store(dst + 1, v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            } else {
+                __hip_atomic_store(dst, v0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(dst + 1, v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
         __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are acknowledged
         __syncthreads();
@@ -280,8 +299,12 @@ __global__ __launch_bounds__(64 * st_max_waves(NPH)) void stream_kernel(KArgs a,
         __syncthreads();
         if (!s_is_last)
             return;  // uniform over the workgroup
-        if (wid < ST_RG)
-            acc = reduce_partials(part, ws.ksplit, ks, tiles, tile, lane, acc);
+        if (wid < ST_RG) {
+            if (ws.xlocal)
+                acc = reduce_partials_s<__HIP_MEMORY_SCOPE_WORKGROUP>(part, ws.ksplit, ks, tiles, tile, lane, acc);
+            else
+                acc = reduce_partials(part, ws.ksplit, ks, tiles, tile, lane, acc);
+        }
         if (tid == 0)
             __hip_atomic_store(&ws.cnt[grp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -329,7 +352,7 @@ __global__ __launch_bounds__(64 * st_max_waves(NPH)) void stream_kernel(KArgs a,
 template <int FMT, int ACT, int NTERM, int OUTT, bool FULLK>
 static void launch_kf(const KArgs &a, const StCfg &c, const SkinnyWs &ws, hipStream_t st)
 {
-    const dim3 grid((unsigned)(c.ngroups * c.ksplit));
+    const dim3 grid((unsigned)c.grid);
     const dim3 block((unsigned)(64 * c.W));
     const size_t lds = (size_t)c.W * ST_RG * 1024;
     if (c.NPH == 2)

@@ -33,6 +33,11 @@ def test_library_exports_every_declared_symbol():
     assert q.version() == (1, 0)
 
 
+def _has_device():
+    import torch
+    return torch.cuda.device_count() > 0
+
+
 def _create(*args):
     h = ctypes.c_void_p()
     st = q.lib().qgemm_create(ctypes.byref(h), *args)
@@ -98,6 +103,8 @@ def test_run_validation_before_any_hip_call():
     assert L.qgemm_plan_tier(h, 256) == 2     # the faithful variant of the large-batch tier
     assert L.qgemm_plan_tier(h, 2048) == 2
     assert L.qgemm_plan_tier(h, -1) == 0
+    if not _has_device():
+        assert L.qgemm_xcd_local() == -1      # no device: the dispatch probe is skipped
     assert L.qgemm_destroy(h) == q.OK
 
 

@@ -171,6 +171,50 @@ def test_split_k_and_unsplit_agree(q8_attn, B):
     assert torch.count_nonzero(ws[:128]) == 0  # tile counters re-armed
 
 
+def test_dispatch_probe_finds_xcd_round_robin():
+    """On the MI355X the dispatcher deals workgroup ids to the XCDs
+    round-robin, so qgemm_create's probe enables the XCD-local exchange."""
+    q.Plan("q8_0", 256, 512, act="f32", out="f32")
+    assert q.xcd_local() == 1
+
+
+@pytest.mark.parametrize("fmt,n,k,act,epi", [
+    ("q8_0", 5120, 5120, "f32", "none"),      # 40 row groups, 6 K splits: one round
+    ("q8_0", 1664, 5120, "bf16", "none"),     # 13 groups: XCDs with one group more than others
+    ("mxfp4", 6272, 8192, "f32", "none"),     # 49 groups, several rounds of workgroups
+    ("nvfp4", 2 * 1040, 4096, "bf16", "swiglu"),  # 17 groups of 4 gate + 4 up tiles
+])
+def test_stream_split_exchange_modes_agree(fmt, n, k, act, epi, monkeypatch):
+    """The streaming kernel's K splits meet through device-coherent memory or,
+    with every split of a row group on one XCD, through that XCD's L2.  Both
+    exchanges give bitwise the same output (same partials, same split order),
+    it meets the oracle's bound, and the tile counters are re-armed."""
+    if epi == "swiglu":
+        w = _gate_up(fmt, n // 2, k, 41)
+    else:
+        w = synth.quantize(fmt, synth.normal_f32(41, synth.SID_W, n, k, 0.02))
+    wd = w_dev(w)
+    math = "fp32" if act == "f32" else "bf16"
+    plan = q.Plan(fmt, n, k, act=act, out="f32", math=math, epilogue=epi)
+    for B in (1, 16):
+        assert plan.tier(B) == "skinny"
+        x = synth.gen_x_f32(B, k, seed=B) if act == "f32" else synth.gen_x_bf16(B, k, seed=B)
+        ws = torch.zeros(plan.workspace_bytes(B), dtype=torch.uint8, device=_dev())
+        outs = []
+        for mode in ("0", "1", "0", "1"):
+            monkeypatch.setenv("QGEMM_ST_XLOCAL", mode)
+            outs.append(run(plan, x, wd, workspace=ws))
+        monkeypatch.delenv("QGEMM_ST_XLOCAL")
+        outs.append(run(plan, x, wd, workspace=ws))  # the probed default
+        for o in outs[1:]:
+            assert np.array_equal(o, outs[0]), (B, fmt)
+        assert torch.count_nonzero(ws[:4 * -(-n // 128)]) == 0  # row-group counters re-armed
+        ref = oracle.swiglu(w, x) if epi == "swiglu" else oracle.gemm(w, x)
+        err = oracle.rel_fro(outs[0], ref)
+        tol = TOL_FP32 if math == "fp32" else (1e-4 if epi == "swiglu" else TOL_BF16)
+        assert err <= tol, (B, fmt, err)
+
+
 def test_workspace_reused_across_batch_widths(q8_attn):
     """One workspace, calls of alternating widths: every output is written and
     correct (the counters of one width are never hit by another width's
