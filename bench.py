@@ -54,6 +54,10 @@ def log(msg):
     sys.stderr.flush()
 
 
+# GPU work run untimed before each timed loop (the clock's ramp after host-side set-up)
+WARM_MS = 20.0
+
+
 class Workload:
     """Packed weights (rotating copies), activations and output on the GPU."""
 
@@ -95,15 +99,20 @@ class Workload:
         yb = self.y.numel() * self.y.element_size()
         return self.wbytes + xb + yb
 
-    def time_ms(self, steps, warmup, eager=False):
+    def time_ms(self, steps, warmup, eager=False, warm_ms=WARM_MS):
         """Average ms per call over `steps` calls replayed from a HIP graph
         holding one call per weight copy (or launched one by one when
-        `eager`), bracketed by events on the stream the calls run on."""
+        `eager`), bracketed by events on the stream the calls run on.  Before
+        the timed calls: `warmup` (at least one per weight copy) eager calls,
+        then untimed replays until about `warm_ms` of GPU work has run, so the
+        timed calls see the steady clock rather than the ramp after the host
+        set the workload up (`self.untimed_calls` counts them all)."""
         import torch
 
         n = len(self.ws)
         reps = max(1, math.ceil(steps / n))
         stream = torch.cuda.Stream()
+        self.untimed_calls = max(warmup, n)
         with torch.cuda.stream(stream):
             for i in range(max(warmup, n)):
                 self.plan.run(self.x, self.ws[i % n], self.y)
@@ -122,9 +131,19 @@ class Workload:
         with torch.cuda.graph(g, stream=stream):
             for i in range(n):
                 self.plan.run(self.x, self.ws[i], self.y)
+        w0 = torch.cuda.Event(enable_timing=True)
+        w1 = torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(stream):
+            w0.record(stream)
             g.replay()
+            w1.record(stream)
+        w1.synchronize()
+        more = math.ceil(warm_ms / max(w0.elapsed_time(w1), 1e-3)) - 1
+        with torch.cuda.stream(stream):
+            for _ in range(max(0, min(more, 100000))):
+                g.replay()
         stream.synchronize()
+        self.untimed_calls += n * (1 + max(0, min(more, 100000)))
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -221,6 +240,10 @@ def bench_moe(steps):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
         plan.run_grouped(x, table, off, y)
+    with torch.cuda.stream(stream):  # untimed: about WARM_MS of work (one call is ~0.35 ms)
+        for _ in range(max(1, math.ceil(WARM_MS / 0.35))):
+            g.replay()
+    stream.synchronize()
     reps = max(10, steps // 10)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -293,6 +316,7 @@ def main():
         "n_gpus": 1,
         "steps": steps_done,
         "warmup": args.warmup,
+        "untimed_calls": wl.untimed_calls,
         "ms_per_step": round(ms, 6),
         "higher_is_better": True,
         "scaling": "weak",
