@@ -266,46 +266,86 @@ static SkCfg skinny_cfg(const Problem &p, int64_t B, bool split)
 }
 
 // Large-batch tier shape.  Whole rounds of 256 tiles (one per CU) run
-// unsplit; the tiles of a last, partial round are split along K into S
-// pieces, S chosen by a small cost model: rounds of work plus a charge for
-// the partial tiles' traffic.  Without a large enough workspace nothing is
-// split.
+// unsplit; the tiles of a last, partial round may be split along K into S
+// pieces whose partial tiles a reduce kernel adds.  A cost model in
+// microseconds picks the row-tile height (bf16 math: 128 or 256 rows; the
+// fp32-faithful variant: 64, or 96 for 64 < B <= 96) and S: rounds of tile
+// work plus the partial tiles' traffic.  Its constants are fits to times
+// measured on MI355X: a 256 x 256 tile takes about 0.03 us per K column on
+// one CU (MXFP4, which stages packed codes, 0.026), a 128-row tile 0.6 of that (its weight decode is
+// shared by half the rows), the fp32-faithful variant three times the MFMA
+// work, and partial tiles cost about 0.25 us per MB (written, then read by
+// the reduce kernel).  On the measured shapes it picks the fastest of the
+// forced choices: e.g. FP8 5120^2 at B = 2048 takes 128-row tiles (320
+// tiles, 123 us, against 137 us for 160 256-row tiles split in three), the
+// other formats keep 256 rows at B = 1024 and 2048, and 128-row tiles win
+// at B = 384.  Without a large enough workspace nothing is split.
+struct TiPick {
+    int S;
+    double us;
+};
+
+static TiPick pick_split(int tiles, int nsteps, int BM, double tile_us, bool split)
+{
+    const int full = tiles / 256 * 256, rem = tiles - full;
+    const int forced = env_int("QGEMM_TI_SPLIT", 0);
+    TiPick best = {1, (double)(full / 256 + (rem ? 1 : 0)) * tile_us};
+    if (!split || rem == 0)
+        return best;
+    if (forced)
+        best.us = 1e30;  // a valid forced S replaces the unsplit choice
+    for (int s = 1; s <= 16; s++) {
+        const int spp = (nsteps + s - 1) / s;
+        if (s > 1 && (s - 1) * spp >= nsteps)
+            continue;  // a piece would be empty
+        if (forced && s != forced)
+            continue;
+        const int64_t rounds = ((int64_t)rem * s + 255) / 256;
+        const double part_mb = s > 1 ? (double)rem * s * BM * 256 * 4 / 1e6 : 0.0;
+        const double t = (double)(full / 256) * tile_us + (double)rounds * tile_us / s + 0.25 * part_mb;
+        if (t < best.us - 1e-9)
+            best = {s, t};
+    }
+    return best;
+}
+
 static TiCfg tiled_cfg(const Problem &p, int64_t B, bool split)
 {
     TiCfg c;
-    // 128-row tiles up to B = 512 (twice the tiles, half the partial-tile
-    // traffic of a K split: FP8 5120^2 at B = 256 39 -> 33 us, at B = 384 in
-    // every format 8-16 % faster than 256-row tiles), 256 above
-    c.BM = p.math == QGEMM_MATH_FP32 ? (B > 64 && B <= 96 ? 96 : 64) : B <= 512 ? 128 : 256;
-    if (p.math == QGEMM_MATH_FP32 && (env_int("QGEMM_TI_BM", 0) == 64 || env_int("QGEMM_TI_BM", 0) == 96))
-        c.BM = env_int("QGEMM_TI_BM", 0);
-    if (p.math != QGEMM_MATH_FP32 && (env_int("QGEMM_TI_BM", 0) == 128 || env_int("QGEMM_TI_BM", 0) == 256))
-        c.BM = env_int("QGEMM_TI_BM", 0);
+    const bool faith = p.math == QGEMM_MATH_FP32;
     const bool dual = p.epi == QGEMM_EPI_SWIGLU;
     const int64_t cols = dual ? p.N / 2 : p.N;
-    c.mtiles = (int)((B + c.BM - 1) / c.BM);
-    c.ntiles = (int)((cols + (dual ? 127 : 255)) / (dual ? 128 : 256));
-    c.tiles = c.mtiles * c.ntiles;
+    const int ntiles = (int)((cols + (dual ? 127 : 255)) / (dual ? 128 : 256));
     const int nsteps = (int)((p.K + 63) / 64);
-    const int full = c.tiles / 256 * 256, rem = c.tiles - full;
-    int S = 1;
-    if (split && rem > 0) {
-        double best = 1e30;
-        const int forced = env_int("QGEMM_TI_SPLIT", 0);
-        for (int s = 1; s <= 16; s++) {
-            const int spp = (nsteps + s - 1) / s;
-            if (s > 1 && (s - 1) * spp >= nsteps)
-                continue;  // a piece would be empty
-            if (forced && s != forced)
-                continue;
-            const int64_t rounds = ((int64_t)rem * s + 255) / 256;
-            const double t = (double)rounds / s + 0.04 * (s - 1) * rem / 256.0;
-            if (t < best - 1e-9) {
-                best = t;
-                S = s;
-            }
+    const int fbm = env_int("QGEMM_TI_BM", 0);
+    int cand[2], nc = 1;
+    if (faith) {
+        cand[0] = (fbm == 64 || fbm == 96) ? fbm : (B > 64 && B <= 96 ? 96 : 64);
+    } else if (fbm == 128 || fbm == 256) {
+        cand[0] = fbm;
+    } else {
+        cand[0] = 128;
+        if (B > 128)
+            cand[nc++] = 256;
+    }
+    TiPick best = {1, 1e300};
+    c.BM = cand[0];
+    for (int i = 0; i < nc; i++) {
+        const int bm = cand[i];
+        const int tiles = (int)((B + bm - 1) / bm) * ntiles;
+        const double per_k = p.fmt == FMT_MX ? 0.026 : 0.03;  // MXFP4 stages packed codes
+        const double tile_us = per_k * (double)p.K * (bm / 256.0) * (faith ? 3.0 : 1.0) * (bm == 128 ? 1.2 : 1.0);
+        const TiPick t = pick_split(tiles, nsteps, bm, tile_us, split);
+        if (t.us < best.us) {
+            best = t;
+            c.BM = bm;
         }
     }
+    c.mtiles = (int)((B + c.BM - 1) / c.BM);
+    c.ntiles = ntiles;
+    c.tiles = c.mtiles * c.ntiles;
+    const int full = c.tiles / 256 * 256, rem = c.tiles - full;
+    const int S = best.S;
     c.sp.S = S;
     c.sp.full = S > 1 ? full : c.tiles;
     c.wgs = S > 1 ? full + rem * S : c.tiles;
