@@ -456,10 +456,13 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
         const int r = tile - sp.full;               // split tile index
         f32x4 *dst = (f32x4 *)sp.part + ((int64_t)r * sp.S + ks) * (NTHR * TM * TN) + tid;
 #pragma unroll
-        for (int i = 0; i < TM; i++)
+        for (int i = 0; i < TM; i++) {
+            if (b0 + wm * (BM / 2) + 16 * i >= a.B)
+                continue;  // a 16-row block wholly past B: tiled_reduce skips it too
 #pragma unroll
             for (int j = 0; j < TN; j++)
                 dst[(i * TN + j) * NTHR] = acc[i][j];
+        }
         return;
     }
 
@@ -515,14 +518,29 @@ __global__ __launch_bounds__(256) void tiled_reduce(KArgs a, int Nh, int mtiles,
     const int mt = tile % mtiles, ntl = tile / mtiles;
     const int lane = th & 63, wid = th >> 6, wm = wid & 1, wn = wid >> 1;
     const int b0 = mt * BM, n0 = ntl * (DUAL ? 128 : 256);
+    if (b0 + wm * (BM / 2) + 16 * i >= a.B)
+        return;  // a 16-row block wholly past B: its partials were never stored
     const f32x4 *src = (const f32x4 *)sp.part + (int64_t)r * sp.S * per_piece + th;
+    // pieces in order; up to 8 loads in flight before the first add (a piece
+    // index past S re-reads the last piece and is not added)
     f32x4 v0 = f32x4{0.f, 0.f, 0.f, 0.f}, v1 = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < sp.S; k++) {
-        const f32x4 t0 = src[k * per_piece + (i * TN + jj) * NTHR];
-        v0[0] += t0[0]; v0[1] += t0[1]; v0[2] += t0[2]; v0[3] += t0[3];
-        if constexpr (DUAL) {
-            const f32x4 t1 = src[k * per_piece + (i * TN + jj + 2) * NTHR];
-            v1[0] += t1[0]; v1[1] += t1[1]; v1[2] += t1[2]; v1[3] += t1[3];
+    for (int k0 = 0; k0 < sp.S; k0 += 8) {
+        f32x4 t0[8], t1[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            const int k = min(k0 + u, sp.S - 1);
+            t0[u] = src[k * per_piece + (i * TN + jj) * NTHR];
+            if constexpr (DUAL)
+                t1[u] = src[k * per_piece + (i * TN + jj + 2) * NTHR];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            if (k0 + u >= sp.S)
+                break;
+            v0[0] += t0[u][0]; v0[1] += t0[u][1]; v0[2] += t0[u][2]; v0[3] += t0[u][3];
+            if constexpr (DUAL) {
+                v1[0] += t1[u][0]; v1[1] += t1[u][1]; v1[2] += t1[u][2]; v1[3] += t1[u][3];
+            }
         }
     }
     const int col = n0 + (DUAL ? wn * 32 + 16 * jj : wn * 64 + 16 * jj) + (lane & 15);
