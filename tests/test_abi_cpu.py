@@ -119,6 +119,36 @@ def test_tier_choice():
     assert p.tier(256) == "skinny"
 
 
+def _split_part_bytes(plan, B, N):
+    """Partial-tile bytes of the large-batch split: the workspace minus the
+    counters (small-batch counters for ceil(N/16) row tiles, then 1 KB)."""
+    rt = -(-N // 16)
+    cnt = -(-(8 * ((rt + 3) // 4) * 4) // 256) * 256 + 1024
+    return plan.workspace_bytes(B) - cnt
+
+
+@pytest.mark.parametrize("fmt,N,K,act,B,bm,s,rem", [
+    # FP8 5120^2 at B = 2048: 320 128-row tiles (256 whole, the last 64 in 4 pieces)
+    # beat 160 256-row tiles split in three (126 MB of partials)
+    ("fp8", 5120, 5120, "bf16", 2048, 128, 4, 64),
+    ("fp8", 5120, 5120, "bf16", 1024, 256, 3, 80),    # 80 256-row tiles in 3 pieces
+    ("fp8", 5120, 5120, "bf16", 256, 128, 6, 40),
+    ("mxfp4", 5120, 17408, "bf16", 2048, 256, 3, 160),
+    ("mxfp4", 5120, 17408, "bf16", 384, 128, 4, 60),
+    ("q8_0", 17408, 5120, "bf16", 2048, 256, 8, 32),  # 544 tiles: 512 whole, 32 in 8 pieces
+    ("q8_0", 5120, 5120, "f32", 70, 96, 12, 20),      # fp32-faithful, 96-row tiles
+    ("q8_0", 5120, 5120, "f32", 256, 64, 3, 80),
+])
+def test_large_batch_shape_choices(fmt, N, K, act, B, bm, s, rem):
+    """The large-batch cost model's row-tile height and split count on the
+    measured shapes (each the fastest of the forced choices on the box),
+    read back through the workspace size: rem tiles x s pieces x bm x 256
+    fp32 partials."""
+    plan = q.Plan(fmt, N, K, act=act, out="f32")
+    assert plan.tier(B) == "tiled"
+    assert _split_part_bytes(plan, B, N) == rem * s * bm * 256 * 4
+
+
 def test_weight_bytes_match_format_density():
     # N, K multiples of the tile: exactly the algorithmic bytes per weight
     assert q.weight_bytes("q8_0", 5120, 5120) == 5120 * 5120 * 17 // 16
