@@ -272,10 +272,10 @@ static SkCfg skinny_cfg(const Problem &p, int64_t B, bool split)
 // fp32-faithful variant: 64, or 96 for 64 < B <= 96) and S: rounds of tile
 // work plus the partial tiles' traffic.  Its constants are fits to times
 // measured on MI355X: a 256 x 256 tile takes about 0.03 us per K column on
-// one CU (MXFP4, which stages packed codes, 0.026), a 128-row tile 0.6 of that (its weight decode is
-// shared by half the rows), the fp32-faithful variant three times the MFMA
-// work, and partial tiles cost about 0.25 us per MB (written, then read by
-// the reduce kernel).  On the measured shapes it picks the fastest of the
+// one CU (MXFP4, which stages packed codes, 0.026), a 128-row tile 0.6 of
+// that (its weight decode is shared by half the rows), the fp32-faithful
+// variant three times the MFMA work, and partial tiles cost about 0.25 us
+// per MB (written, then read by the reduce kernel).  On the measured shapes it picks the fastest of the
 // forced choices: e.g. FP8 5120^2 at B = 2048 takes 128-row tiles (320
 // tiles, 123 us, against 137 us for 160 256-row tiles split in three), the
 // other formats keep 256 rows at B = 1024 and 2048, and 128-row tiles win

@@ -37,8 +37,9 @@
 // stores, a device-scope counter, no device-wide fence).  The partial tiles
 // go through device-coherent memory, or, when the dispatcher is known to put
 // workgroup ids congruent mod 8 on one XCD and all splits of a row group are
-// given such ids, through that XCD's L2 (workgroup-scope stores and loads:
-// no write-through to memory, and the last workgroup's reads hit in L2).
+// given such ids, through that XCD's L2 (workgroup-scope stores, which that
+// L2 acknowledges without writing them through to memory, and
+// workgroup-scope loads).
 #include "common.h"
 
 namespace qg {
