@@ -178,6 +178,40 @@ def test_dispatch_probe_finds_xcd_round_robin():
     assert q.xcd_local() == 1
 
 
+def test_dispatch_probe_during_graph_capture():
+    """A fresh process whose first plan is created while a graph is being
+    captured on another stream: the probe runs on a stream of its own in
+    relaxed capture mode, the capture stays valid, and its replays match an
+    eager call."""
+    import subprocess
+    import sys
+    code = r"""
+import numpy as np, torch, synth, prefill_q8_mxfp4_amd as q
+w = synth.quantize("q8_0", synth.normal_f32(5, synth.SID_W, 1024, 2048, 0.02))
+wd = torch.from_numpy(q.pack_logical(w)).cuda()
+x = torch.from_numpy(synth.gen_x_f32(8, 2048, seed=3)).cuda()
+y = torch.zeros((8, 1024), dtype=torch.float32, device="cuda")
+st = torch.cuda.Stream()
+g = torch.cuda.CUDAGraph()
+with torch.cuda.graph(g, stream=st):
+    plan = q.Plan("q8_0", 1024, 2048, act="f32", out="f32")  # first plan: the probe runs here
+    plan.run(x, wd, y, workspace=None)
+assert q.xcd_local() == 1, q.xcd_local()
+for _ in range(3):
+    y.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    ye = torch.zeros_like(y)
+    plan.run(x, wd, ye, workspace=None)
+    torch.cuda.synchronize()
+    assert torch.equal(y, ye)
+print("ok")
+"""
+    root = __file__.rsplit("/tests/", 1)[0]
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=180)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout[-2000:] + r.stderr[-2000:]
+
+
 @pytest.mark.parametrize("fmt,n,k,act,epi", [
     ("q8_0", 5120, 5120, "f32", "none"),      # 40 row groups, 6 K splits: one round
     ("q8_0", 1664, 5120, "bf16", "none"),     # 13 groups: XCDs with one group more than others
