@@ -27,6 +27,7 @@ closed forms, exact rational brute force and invariants.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 
@@ -72,7 +73,7 @@ def _load():
         lib.oracle_gemm.argtypes = [i32, vp, vp, vp, i64, i32, vp, i64, i64, i64, vp]
         lib.oracle_swiglu.restype = None
         lib.oracle_swiglu.argtypes = [i32, vp, vp, vp, i64, i32, vp, i64, i64, i64, vp]
-        for name in ("oracle_gemm_at", "oracle_swiglu_at"):
+        for name in ("oracle_gemm_at", "oracle_swiglu_at", "oracle_gemm_abs_at"):
             f = getattr(lib, name)
             f.restype = None
             f.argtypes = [i32, vp, vp, vp, i64, i32, vp, i64, i64, vp, vp, i64, vp]
@@ -173,6 +174,35 @@ def gemm_at(w: dict, x: np.ndarray, bidx, nidx) -> np.ndarray:
     return y
 
 
+def gemm_abs_at(w: dict, x: np.ndarray, bidx, nidx) -> np.ndarray:
+    """M[bidx[i]][nidx[i]] = |g(n)| * sum_k |x[b][k]| * |w[n][k]| in fp64: the
+    magnitude sum that bounds the rounding error of any fp summation order of
+    y[b][n] (|computed - exact| <= gamma(n_adds, u) * M, see :func:`gamma`)."""
+    fmt, codes, scales, g, nt = _prep(w)
+    a, x = _act(x)
+    n, k = codes.shape
+    bi = np.ascontiguousarray(bidx, dtype=np.int64)
+    ni = np.ascontiguousarray(nidx, dtype=np.int64)
+    assert bi.shape == ni.shape
+    assert bi.size == 0 or (bi.max() < x.shape[0] and ni.max() < n and bi.min() >= 0
+                            and ni.min() >= 0)
+    m = np.empty(bi.size, dtype=np.float64)
+    _load().oracle_gemm_abs_at(fmt, _ptr(codes), _ptr(scales), _ptr(g), nt, a, _ptr(x), n, k,
+                               _ptr(bi), _ptr(ni), bi.size, _ptr(m))
+    return m
+
+
+def gamma(n: int, u: float) -> float:
+    """gamma_n = n u / (1 - n u): a sum of n + 1 terms computed with n
+    roundings of relative size at most u, in any order, differs from the
+    exact sum by at most gamma_n times the sum of the terms' magnitudes
+    (the standard forward error bound of recursive summation)."""
+    nu = n * u
+    if nu >= 1.0:
+        return math.inf
+    return nu / (1.0 - nu)
+
+
 def swiglu(w: dict, x: np.ndarray) -> np.ndarray:
     """out[B][N/2] = SiLU(gate) * up, fp64."""
     fmt, codes, scales, g, nt = _prep(w)
@@ -215,9 +245,46 @@ def gemm_grouped(ws: list, offsets, x: np.ndarray, swiglu_epi: bool = False) -> 
 
 
 def rel_fro(y, ref) -> float:
-    """||y - ref||_F / ||ref||_F in fp64."""
+    """||y - ref||_F / ||ref||_F in fp64.  A zero reference gives 0 when y is
+    zero too and inf otherwise (a relative error is undefined there, so it
+    must not pass any bound); NaN anywhere gives NaN (which fails every
+    ``err <= tol``)."""
     y = np.asarray(y, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
-    den = np.linalg.norm(ref.ravel())
-    num = np.linalg.norm((y - ref).ravel())
-    return float(num / den) if den > 0 else float(num)
+    if y.shape != ref.shape:
+        raise ValueError(f"shape mismatch {y.shape} vs {ref.shape}")
+    d = (y - ref).ravel()
+    r = ref.ravel()
+    if np.isnan(d).any() or np.isnan(r).any():
+        return math.nan
+    # both norms in units of the largest magnitude, so that squares of very
+    # small or very large outputs neither underflow nor overflow
+    s = max(float(np.max(np.abs(d), initial=0.0)), float(np.max(np.abs(r), initial=0.0)))
+    if s == 0.0:
+        return 0.0
+    if math.isinf(s):
+        return math.nan if np.isinf(r).any() else math.inf
+    num = np.linalg.norm(d / s)
+    den = np.linalg.norm(r / s)
+    if den > 0:
+        return float(num / den)
+    return 0.0 if num == 0 else math.inf
+
+
+def rel_fro_groups(y, ref, groups, ngroups: int) -> np.ndarray:
+    """Per-group relative Frobenius error: element i belongs to group
+    groups[i] (0 <= groups[i] < ngroups); result[g] is rel_fro over the
+    elements of group g (an output tile, say), with rel_fro's conventions,
+    and NaN for a group with no element."""
+    y = np.asarray(y, dtype=np.float64).ravel()
+    ref = np.asarray(ref, dtype=np.float64).ravel()
+    gi = np.asarray(groups, dtype=np.int64).ravel()
+    if not (y.shape == ref.shape == gi.shape):
+        raise ValueError("y, ref and groups must have the same size")
+    if gi.size and (gi.min() < 0 or gi.max() >= ngroups):
+        raise ValueError("group index out of range")
+    out = np.empty(ngroups, dtype=np.float64)
+    for g in range(ngroups):
+        sel = gi == g
+        out[g] = rel_fro(y[sel], ref[sel]) if sel.any() else math.nan
+    return out

@@ -198,6 +198,25 @@ void oracle_gemm_at(int fmt, const void *codes, const void *scales, const float 
         y[i] = dot_row(fmt, codes, scales, g, ntensors, act_dtype, x, N, K, bidx[i], nidx[i]);
 }
 
+/* Magnitude sum behind the floating-point error bound of a dot product,
+ * M[b][n] = |g(n)| * sum_k |x[b][k]| * |w[n][k]|: a summation of the K
+ * products in any order, rounding each addition to precision u, lies within
+ * gamma_n * M of the exact sum, gamma_n = n u / (1 - n u) (the standard
+ * recursive-summation bound).  Selected outputs, as oracle_gemm_at. */
+void oracle_gemm_abs_at(int fmt, const void *codes, const void *scales, const float *g,
+                        int64_t ntensors, int act_dtype, const void *x, int64_t N, int64_t K,
+                        const int64_t *bidx, const int64_t *nidx, int64_t count, double *m)
+{
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < count; i++) {
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; k++)
+            acc += fabs(act(act_dtype, x, K, bidx[i], k)) *
+                   fabs(weight(fmt, codes, scales, K, nidx[i], k));
+        m[i] = fabs(tensor_scale(fmt, g, ntensors, N, nidx[i])) * acc;
+    }
+}
+
 /* SiLU(t) = t * sigmoid(t) = t / (1 + e^-t). */
 /* Threads an OpenMP region of this library runs on (for reporting only). */
 int oracle_threads(void)

@@ -398,3 +398,96 @@ def test_grouped_equals_per_expert_matmul(fmt, act, epi):
             G, U = ref[:, : n // 2], ref[:, n // 2:]
             ref = G / (1.0 + np.exp(-G)) * U
         assert np.allclose(got[r0:r1], ref, rtol=1e-12, atol=1e-300)
+
+
+# ------------------------------------------------ the parity metric itself
+
+def test_rel_fro_hand_computed():
+    """rel_fro against values worked out by hand: a 3-4-5 triangle, one wrong
+    element in a block of ones, zero error, a zero reference, NaN."""
+    assert oracle.rel_fro([3.0, 4.0], [3.0, 4.0]) == 0.0
+    # error (0.3, 0.4) has norm 0.5, the reference (3, 4) norm 5
+    assert oracle.rel_fro([3.3, 4.4], [3.0, 4.0]) == pytest.approx(0.1, rel=1e-14)
+    ref = np.ones((4, 4))
+    y = ref.copy()
+    y[1, 2] = 3.0                       # one element off by 2; ||ref|| = 4
+    assert oracle.rel_fro(y, ref) == 0.5
+    assert oracle.rel_fro(-ref, ref) == 2.0      # sign flip: ||2 ref|| / ||ref||
+    assert oracle.rel_fro(np.zeros(5), np.zeros(5)) == 0.0
+    assert oracle.rel_fro([0.0, 1e-300], [0.0, 0.0]) == math.inf
+    # magnitudes whose squares under- or overflow fp64 still give the ratio
+    assert oracle.rel_fro([3e-200, 4.4e-200], [3e-200, 4e-200]) == pytest.approx(0.4 / 5, rel=1e-12)
+    assert oracle.rel_fro([3e200, 4.4e200], [3e200, 4e200]) == pytest.approx(0.4 / 5, rel=1e-12)
+    assert oracle.rel_fro([math.inf, 1.0], [1.0, 1.0]) == math.inf
+    e = oracle.rel_fro([1.0, math.nan], [1.0, 2.0])
+    assert math.isnan(e) and not (e <= 1.0)
+    with pytest.raises(ValueError):
+        oracle.rel_fro(np.ones(3), np.ones(4))
+
+
+def test_rel_fro_groups_finds_one_wrong_tile():
+    """A 64 x 64 output cut into 16 x 16 tiles: one tile scaled by 1.02 is
+    2 % off while the global figure over all 16 tiles is only 0.5 %; the
+    per-tile errors are zero elsewhere, and a group with no element is NaN."""
+    rng = np.random.default_rng(8)
+    ref = rng.standard_normal((64, 64))
+    y = ref.copy()
+    y[16:32, 48:64] *= 1.02
+    tiles = (np.arange(64)[:, None] // 16) * 4 + np.arange(64)[None, :] // 16
+    per = oracle.rel_fro_groups(y, ref, tiles, 17)
+    assert per[1 * 4 + 3] == pytest.approx(0.02, rel=1e-12)
+    assert np.all(np.delete(per[:16], 7) == 0.0)
+    assert math.isnan(per[16])
+    glob = oracle.rel_fro(y, ref)
+    assert glob < 0.006 and per.max(initial=0, where=~np.isnan(per)) > 0.019
+
+
+def test_gamma_closed_form():
+    u = 2.0 ** -24
+    assert oracle.gamma(0, u) == 0.0
+    assert oracle.gamma(1, u) == u / (1 - u)
+    assert oracle.gamma(5120, u) == pytest.approx(5120 * u, rel=1e-3)
+    assert oracle.gamma(2 ** 24, u) == math.inf
+
+
+@pytest.mark.parametrize("fmt,act", CASES)
+def test_gemm_abs_at_vs_library_and_bruteforce(fmt, act):
+    """The magnitude sum sum_k |x||w| (times |g|) against numpy's float64
+    matmul of |library-decoded operands|, and against an exact rational sum
+    on a few outputs; NVFP4 with two tensors and a negative tensor scale."""
+    rng = np.random.default_rng(31)
+    n, k, b = 24, 256, 7
+    w = _rand_weights(fmt, n, k, rng, ntensors=2 if fmt == "nvfp4" else 1)
+    if fmt == "nvfp4":
+        w["g"] = np.array([0.003, -0.02], dtype=np.float32)
+    x = _rand_x(act, b, k, rng)
+    X, W = _lib_x(x), _lib_decode(w)
+    ref = np.abs(X) @ np.abs(W).T
+    bi = np.repeat(np.arange(b), n)
+    ni = np.tile(np.arange(n), b)
+    got = oracle.gemm_abs_at(w, x, bi, ni).reshape(b, n)
+    assert np.all(got >= 0)
+    assert oracle.rel_fro(got, ref) < 1e-14
+    for i in range(4):
+        bb, nn = int(bi[i * 37 % bi.size]), int(ni[i * 37 % ni.size])
+        exact = sum(abs(Fraction(X[bb, kk]) * Fraction(W[nn, kk])) for kk in range(k))
+        assert abs(Fraction(got[bb, nn]) - exact) <= exact * Fraction(k * 2.0 ** -52)
+
+
+def test_dequant_apply_g_vs_library_two_tensors():
+    """dequant(apply_g=True) for NVFP4 with two tensor scales (the fused
+    gate+up matrix): every row's decoded weights times its own tensor's g,
+    against the library decode (torch float8, transformers' FP4 table), and
+    apply_g=False leaves g out."""
+    rng = np.random.default_rng(41)
+    w = _rand_weights("nvfp4", 32, 96, rng, ntensors=2)
+    w["g"] = np.array([0.75, 3e-5], dtype=np.float32)
+    got = oracle.dequant(w, apply_g=True)
+    assert np.array_equal(got, _lib_decode(w))
+    plain = oracle.dequant(w, apply_g=False)
+    assert np.array_equal(got[:16], plain[:16] * np.float64(np.float32(0.75)))
+    assert np.array_equal(got[16:], plain[16:] * np.float64(np.float32(3e-5)))
+    # the other formats have no tensor scale: apply_g changes nothing
+    for fmt in ("q8_0", "mxfp4", "fp8"):
+        wf = _rand_weights(fmt, 8, 128, rng)
+        assert np.array_equal(oracle.dequant(wf, apply_g=True), oracle.dequant(wf))
