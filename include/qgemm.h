@@ -161,13 +161,10 @@ typedef struct qgemm_plan qgemm_plan;
  * dtype; math: see qgemm_math (QGEMM_MATH_FP32 needs act = QGEMM_F32; the
  * SwiGLU epilogue needs QGEMM_MATH_BF16, else QGEMM_ENOTSUP); flags:
  * 0 or one QGEMM_FLAG_FORCE_* bit (also settable with the environment
- * variable QGEMM_FORCE_TIER=skinny|tiled).  Allocates the small plan
- * object and no device memory.  The first call on a device (the current one)
- * also runs a one-time dispatch probe there: a small kernel on a stream of
- * its own and a synchronous 8 KB copy from a static device array, which
- * decides whether the small-batch kernel's K splits can meet in one XCD's L2
- * (results are bitwise the same either way); without a device the probe is
- * skipped.  *plan receives the handle. */
+ * variable QGEMM_FORCE_TIER=skinny|tiled).  Host-only: allocates the small
+ * plan object, makes no HIP call and works without a device.  Tuning
+ * overrides in the environment (QGEMM_ST_*, QGEMM_SK_*, QGEMM_TI_*) are read
+ * here, once.  *plan receives the handle. */
 int qgemm_create(qgemm_plan **plan, qgemm_format fmt, qgemm_dtype act, qgemm_dtype out,
                  qgemm_epilogue epi, qgemm_math math, int64_t N, int64_t K, uint32_t flags);
 
@@ -195,13 +192,16 @@ int qgemm_run(const qgemm_plan *plan, int64_t B, const void *w, const void *x, v
  *            as above for the plan's N and K; NVFP4 tensor scales per expert);
  *   offsets: device int32 [E + 1], offsets[0] = 0, non-decreasing,
  *            offsets[E] = T (the caller sorts the routed rows by expert);
+ *            1 <= E <= 2^16;
  *   x: [T][K] routed activation rows; y: [T][N] (or [T][N/2] with SwiGLU).
  * Experts with no rows cost only a scan.  One launch of the large-batch
  * kernel, unsplit, so each expert's rows are bitwise those of a qgemm_run of
  * that expert in the large-batch tier without a workspace.  Either math
  * mode; a plan forced to the small-batch tier returns QGEMM_ENOTSUP.  T = 0 returns QGEMM_OK and enqueues nothing.
- * The offsets are read on the device and not validated there: offsets that
- * break the rules above make the kernel read and write outside x and y. */
+ * The offsets are read and checked on the device: when they break a rule
+ * above, the kernel reads and writes nothing outside the offsets array and
+ * the table and sets QGEMM_DEV_BAD_OFFSETS in the device status word (y is
+ * left unwritten; qgemm_device_status reports it). */
 int qgemm_run_grouped(const qgemm_plan *plan, int64_t E, int64_t T, const void *const *w_table,
                       const int32_t *offsets, const void *x, void *y, void *stream);
 
@@ -232,13 +232,39 @@ int qgemm_run_ws(const qgemm_plan *plan, int64_t B, const void *w, const void *x
 /* The tier qgemm_run would use for B (QGEMM_TIER_*), or 0 for a bad plan. */
 int qgemm_plan_tier(const qgemm_plan *plan, int64_t B);
 
-/* Outcome of qgemm_create's dispatch probe on the current device: 1 when
- * workgroup ids congruent mod 8 ran on one XCD (the small-batch kernel's K
- * splits then meet in that XCD's L2), 0 when they did not or the probe
- * failed, -1 when no plan was created on this device yet or there is no
- * device.  The environment variable QGEMM_ST_XLOCAL=0|1 overrides the
- * outcome for runs (not for this report). */
+/* Optional one-time set-up of the current device; calling it again is cheap.
+ * It runs a dispatch probe there (a small kernel on a stream of its own, in
+ * relaxed capture mode so a graph being captured elsewhere stays valid, and
+ * a synchronous 8 KB copy) that decides whether the small-batch kernel's K
+ * splits may meet in one XCD's L2: the hardware deals workgroup ids to the
+ * XCDs round-robin, and the probe checks that ids congruent mod 8 share an
+ * XCC.  Until it has run on a device, or where the probe fails, the K splits
+ * meet in device-coherent memory; results are bitwise the same either way.
+ * (The XCD that id 0 lands on can change from launch to launch; only the
+ * congruence matters.)  Every launch that uses the XCD-local exchange checks
+ * it again: the K splits of each row group count themselves per XCC, and
+ * when the last one finds them spread over more than one XCD it sets
+ * QGEMM_DEV_XCD_MISMATCH in the device status word; that launch's output is
+ * then not to be trusted (rerun with the exchange off).  QGEMM_ST_XLOCAL=0
+ * in the environment (read at plan creation) turns the exchange off.
+ * Returns QGEMM_EHIP when there is no device or the probe cannot run. */
+int qgemm_init_device(void);
+
+/* Outcome of qgemm_init_device's dispatch probe on the current device: 1 when
+ * workgroup ids congruent mod 8 ran on one XCD, 0 when they did not, -1 when
+ * the device was not initialised or there is no device. */
 int qgemm_xcd_local(void);
+
+/* Device status word bits: conditions a kernel detected while it ran. */
+#define QGEMM_DEV_XCD_MISMATCH 0x1u /* the K splits of a row group ran on different XCDs */
+#define QGEMM_DEV_BAD_OFFSETS 0x2u  /* qgemm_run_grouped offsets broke their rules; no work done */
+
+/* Read the current device's status word into *bits (the OR of every bit set
+ * since it was last cleared), after synchronising `stream` (the word is set
+ * by kernels, so the caller names the stream whose work it asks about);
+ * clear != 0 then zeroes it.  Synchronous; not for use during graph
+ * capture. */
+int qgemm_device_status(uint32_t *bits, int clear, void *stream);
 
 /* Release a plan (NULL is accepted). */
 int qgemm_destroy(qgemm_plan *plan);

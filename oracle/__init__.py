@@ -283,8 +283,22 @@ def rel_fro_groups(y, ref, groups, ngroups: int) -> np.ndarray:
         raise ValueError("y, ref and groups must have the same size")
     if gi.size and (gi.min() < 0 or gi.max() >= ngroups):
         raise ValueError("group index out of range")
-    out = np.empty(ngroups, dtype=np.float64)
-    for g in range(ngroups):
-        sel = gi == g
-        out[g] = rel_fro(y[sel], ref[sel]) if sel.any() else math.nan
+    d = y - ref
+    cnt = np.bincount(gi, minlength=ngroups)
+    bad = np.bincount(gi, weights=(np.isnan(d) | np.isnan(ref)).astype(np.float64),
+                      minlength=ngroups) > 0
+    # per-group scale: the largest |d| or |ref| of the group (no under/overflow)
+    s = np.zeros(ngroups)
+    np.maximum.at(s, gi, np.where(np.isnan(d), 0.0, np.maximum(np.abs(d), np.abs(ref))))
+    si = s[gi]
+    safe = np.where((si > 0) & np.isfinite(si), si, 1.0)
+    num = np.sqrt(np.bincount(gi, weights=np.where(np.isnan(d), 0.0, d / safe) ** 2,
+                              minlength=ngroups))
+    den = np.sqrt(np.bincount(gi, weights=np.where(np.isnan(ref), 0.0, ref / safe) ** 2,
+                              minlength=ngroups))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        out = np.where(den > 0, num / np.where(den > 0, den, 1.0), np.where(num > 0, math.inf, 0.0))
+    out[np.isinf(s) & ~bad] = math.inf
+    out[bad] = math.nan
+    out[cnt == 0] = math.nan
     return out

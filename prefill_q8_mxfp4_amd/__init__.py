@@ -19,7 +19,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libqgemm.so")
+# QGEMM_LIB_PATH selects another build of the same library (the debug build
+# with its extra environment overrides, for tests)
+LIB_PATH = os.environ.get("QGEMM_LIB_PATH") or os.path.join(_HERE, "libqgemm.so")
 
 OK, EINVAL, ENOTSUP, EHIP, ENOMEM = 0, 1, 2, 3, 4
 FORMATS = {"q8_0": 0, "mxfp4": 1, "nvfp4": 2, "fp8": 3}
@@ -34,9 +36,12 @@ MAX_TENSORS = 60
 
 EXPORTS = ("qgemm_weight_bytes", "qgemm_pack", "qgemm_create", "qgemm_run", "qgemm_run_ws",
            "qgemm_run_grouped",
-           "qgemm_workspace_bytes", "qgemm_plan_tier", "qgemm_xcd_local",
+           "qgemm_workspace_bytes", "qgemm_plan_tier", "qgemm_init_device", "qgemm_xcd_local",
+           "qgemm_device_status",
            "qgemm_destroy", "qgemm_dequantize", "qgemm_strerror", "qgemm_last_error",
            "qgemm_version")
+DEV_XCD_MISMATCH = 0x1
+DEV_BAD_OFFSETS = 0x2
 
 _lib = None
 
@@ -86,8 +91,40 @@ def lib():
     L.qgemm_version.argtypes = []
     L.qgemm_xcd_local.restype = i32
     L.qgemm_xcd_local.argtypes = []
+    L.qgemm_init_device.restype = i32
+    L.qgemm_init_device.argtypes = []
+    L.qgemm_device_status.restype = i32
+    L.qgemm_device_status.argtypes = [ctypes.POINTER(u32), i32, vp]
     _lib = L
     return L
+
+
+_inited = set()
+
+
+def init_device(device=None):
+    """qgemm_init_device on a CUDA (HIP) device (default: the current one),
+    once per device and process: the dispatch probe that enables the
+    XCD-local K-split exchange.  Plans run without it (device-coherent
+    exchange); the binding calls it before a device's first launch."""
+    import torch
+
+    idx = torch.cuda.current_device() if device is None else torch.device(device).index
+    if idx is None:
+        idx = torch.cuda.current_device()
+    if idx in _inited:
+        return
+    with torch.cuda.device(idx):
+        _check(lib().qgemm_init_device())
+    _inited.add(idx)
+
+
+def device_status(clear: bool = False, stream=None) -> int:
+    """The current device's status word (DEV_* bits set by kernels since the
+    last clear), after synchronising `stream` (default: the current one)."""
+    bits = ctypes.c_uint32(0)
+    _check(lib().qgemm_device_status(ctypes.byref(bits), int(bool(clear)), _stream_ptr(stream)))
+    return int(bits.value)
 
 
 def _check(status: int):
@@ -185,8 +222,11 @@ class Plan:
     def workspace_bytes(self, B: int) -> int:
         return int(lib().qgemm_workspace_bytes(self._h, B))
 
-    def _workspace(self, B, device):
-        """Plan-owned zeroed workspace, grown on demand (one stream at a time)."""
+    def _workspace(self, B, device, stream):
+        """Plan-owned zeroed workspace, grown on demand.  It is zeroed on the
+        stream the call is launched on (so the kernels see it zeroed), and a
+        replaced buffer is kept alive until that stream's work on it is done
+        (record_stream).  Calls on one plan object must not overlap."""
         import torch
 
         need = self.workspace_bytes(B)
@@ -194,8 +234,14 @@ class Plan:
             return None
         ws = getattr(self, "_ws", None)
         if ws is None or ws.numel() < need or ws.device != device:
-            ws = torch.zeros(max(need, 1 << 20), dtype=torch.uint8, device=device)
+            with torch.cuda.stream(stream):
+                ws = torch.zeros(max(need, 1 << 20), dtype=torch.uint8, device=device)
+            old = getattr(self, "_ws", None)
+            if old is not None and old.device == device and not torch.cuda.is_current_stream_capturing():
+                old.record_stream(stream)
             self._ws = ws
+        if not torch.cuda.is_current_stream_capturing():
+            ws.record_stream(stream)
         return ws
 
     def run(self, x, w, y, stream=None, B: int | None = None, workspace="auto"):
@@ -215,8 +261,11 @@ class Plan:
             raise ValueError("x or y too small for B")
         if w.numel() < weight_bytes(self.fmt, self.N, self.K):
             raise ValueError("packed weight buffer too small")
+        if stream is None:
+            stream = torch.cuda.current_stream(x.device)
+        init_device(x.device)
         if isinstance(workspace, str):
-            workspace = self._workspace(B, x.device) if B > 0 else None
+            workspace = self._workspace(B, x.device, stream) if B > 0 else None
         wsp, wsn = None, 0
         if workspace is not None:
             wsp, wsn = _dev_ptr(workspace, "workspace"), workspace.numel()
@@ -241,6 +290,7 @@ class Plan:
             raise TypeError("w_table must be int64 [E], offsets int32 [E + 1]")
         if x.numel() < T * self.K or y.numel() < T * self.out_cols:
             raise ValueError("x or y too small")
+        init_device(x.device)
         _check(lib().qgemm_run_grouped(self._h, E, T, _dev_ptr(w_table, "w_table"),
                                        _dev_ptr(offsets, "offsets"), _dev_ptr(x, "x"),
                                        _dev_ptr(y, "y"), _stream_ptr(stream)))
@@ -270,7 +320,7 @@ def dequantize(fmt: str, w, N: int, K: int, stream=None):
 
 def xcd_local() -> int:
     """Dispatch probe outcome on the current device (see qgemm_xcd_local):
-    1 XCD-local K-split exchange, 0 device-coherent, -1 not probed."""
+    1 XCD-local K-split exchange, 0 device-coherent, -1 not initialised."""
     return int(lib().qgemm_xcd_local())
 
 

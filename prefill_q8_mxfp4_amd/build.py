@@ -17,6 +17,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqgemm.so")
+# the same kernels with the host side built to honour the debug-only
+# environment overrides (QGEMM_DEBUG_KNOBS in api.hip); for tests
+LIB_DEBUG = os.path.join(HERE, "libqgemm_debug.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 UNITS = ("api.hip", "skinny.hip", "stream.hip", "tiled.hip", "tiled_fp32.hip", "dequant.hip")
 HEADERS = ("common.h", "layout.h", "tiled.h")
@@ -58,18 +61,22 @@ def build(verbose: bool = False, extra=()) -> str:
     objs = [os.path.join(OBJ, u.replace(".hip", ".o")) for u in UNITS]
     cmds = [[HIPCC] + FLAGS + list(extra) + ["-c", os.path.join(CSRC, u), "-o", o]
             for u, o in zip(UNITS, objs)]
+    dbg_obj = os.path.join(OBJ, "api_debug.o")
+    cmds.append([HIPCC] + FLAGS + list(extra) + ["-DQGEMM_DEBUG_KNOBS", "-c",
+                                                 os.path.join(CSRC, "api.hip"), "-o", dbg_obj])
     with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
-    os.replace(tmp, LIB)
+    for lib, parts in ((LIB, objs), (LIB_DEBUG, [dbg_obj] + objs[1:])):
+        tmp = lib + ".tmp%d" % os.getpid()
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + parts + ["-o", tmp], verbose)
+        os.replace(tmp, lib)
     return LIB
 
 
 def is_stale() -> bool:
-    if not os.path.exists(LIB):
+    if not (os.path.exists(LIB) and os.path.exists(LIB_DEBUG)):
         return True
-    t = os.path.getmtime(LIB)
+    t = min(os.path.getmtime(LIB), os.path.getmtime(LIB_DEBUG))
     return any(os.path.getmtime(s) > t for s in sources())
 
 

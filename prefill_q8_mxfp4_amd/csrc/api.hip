@@ -32,6 +32,33 @@ static int hip_fail(hipError_t e, const char *what)
 
 static const uint32_t PLAN_MAGIC = 0x51474D31u;  // "QGM1"
 
+static int env_int(const char *name, int dflt)
+{
+    const char *v = getenv(name);
+    return (v && *v) ? atoi(v) : dflt;
+}
+
+// The environment overrides of a plan, read once at creation (see Knobs).
+static void read_knobs(Knobs *k)
+{
+    k->st_waves = env_int("QGEMM_ST_WAVES", 0);
+    k->st_nph = env_int("QGEMM_ST_NPH", 0);
+    k->sk_stream = env_int("QGEMM_SK_STREAM", 1);
+    k->sk_nt = env_int("QGEMM_SK_NT", 2);
+    k->ti_bm = env_int("QGEMM_TI_BM", 0);
+    k->ti_split = env_int("QGEMM_TI_SPLIT", 0);
+    k->xlocal = env_int("QGEMM_ST_XLOCAL", -1) == 0 ? 0 : -1;
+    k->fp32_terms = 3;
+    k->xcc_fake = 0;
+#ifdef QGEMM_DEBUG_KNOBS
+    if (env_int("QGEMM_ST_XLOCAL", -1) == 1)
+        k->xlocal = 1;
+    const int t = env_int("QGEMM_FP32_TERMS", 3);
+    k->fp32_terms = t >= 1 && t <= 3 ? t : 3;
+    k->xcc_fake = env_int("QGEMM_XCC_FAKE", 0) != 0;
+#endif
+}
+
 }  // namespace qg
 
 struct qgemm_plan {
@@ -43,12 +70,6 @@ struct qgemm_plan {
 namespace qg {
 
 static bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
-
-static int env_int(const char *name, int dflt)
-{
-    const char *v = getenv(name);
-    return (v && *v) ? atoi(v) : dflt;
-}
 
 // ---- small-batch tier shape
 //
@@ -82,7 +103,7 @@ static StShape stream_shape(const Problem &p)
 {
     const int64_t groups = (p.L.RT + ST_RG - 1) / ST_RG;
     const int64_t S = p.L.S;
-    const int fw = env_int("QGEMM_ST_WAVES", 0), fp = env_int("QGEMM_ST_NPH", 0);
+    const int fw = p.kn.st_waves, fp = p.kn.st_nph;
     StShape best = {8, 1};
     int64_t best_cost = -1, best_rounds = 0, best_splits = 0;
     for (int nph = 1; nph <= 2; nph++) {
@@ -133,23 +154,29 @@ static int64_t ws_data_off(const Problem &p)
 
 static bool use_stream(const Problem &p, int64_t B)
 {
-    return B <= ST_MAX_B && env_int("QGEMM_SK_STREAM", 1) != 0;
+    return B <= ST_MAX_B && p.kn.sk_stream != 0;
 }
 
 // XCD dispatch probe.  The streaming kernel's XCD-local split exchange
 // needs every workgroup id congruent mod 8 to run on one XCD, so that one L2
 // holds all partial tiles of a row group (the hardware dispatcher deals
-// consecutive workgroup ids to the XCDs round-robin).  qgemm_create checks
-// this once per device: a probe kernel records the XCC id (hardware register
-// XCC_ID) of 2048 workgroups, three times, and the exchange is enabled on a
-// device only if ids b and b mod 8 always ran on the same XCC.  Devices never
-// probed, or that fail, use the device-coherent exchange; both give bitwise
-// the same result (same partials, same split order).
+// consecutive workgroup ids to the XCDs round-robin).  qgemm_init_device
+// checks this once per device: a probe kernel records the XCC id (hardware
+// register XCC_ID) of 2048 workgroups, three times, and the exchange is
+// enabled on a device only if ids b and b mod 8 always ran on the same XCC.
+// Devices never probed, or that fail, use the device-coherent exchange; both
+// give bitwise the same result (same partials, same split order).  Every
+// launch with the exchange still checks that the K splits of each row group
+// ran on one XCD (the kernel's own check, see the streaming kernel).
 static const int XCC_PROBE_WGS = 2048;
 static const int MAX_DEVICES = 64;
 static std::atomic<int> g_xlocal[MAX_DEVICES];  // 0 not probed, 1 round-robin, 2 not
+static std::atomic<uint32_t *> g_status_ptr[MAX_DEVICES];  // device address of g_status there
 static std::mutex g_probe_mu;
 static __device__ uint32_t g_xcc_probe[XCC_PROBE_WGS];  // the probe's output, one word per workgroup
+// Device status word, one per device (DEV_* bits): kernels that detect a
+// broken assumption at run time set a bit here; qgemm_device_status reads it.
+static __device__ uint32_t g_status;
 
 __global__ void xcc_probe_kernel(uint32_t *o)
 {
@@ -168,19 +195,39 @@ static int current_device()
     return dev;
 }
 
-static void probe_xcd_dispatch()
+// Address of this device's status word (null when it cannot be had).  The
+// lookup runs once per device, with the calling thread in relaxed capture
+// mode so that a graph being captured stays valid.
+static uint32_t *status_word(int dev)
 {
-    const int dev = current_device();
-    if (dev < 0 || g_xlocal[dev].load() != 0)
-        return;
+    if (dev < 0)
+        return nullptr;
+    uint32_t *p = g_status_ptr[dev].load(std::memory_order_acquire);
+    if (p)
+        return p;
+    hipStreamCaptureMode mode = hipStreamCaptureModeRelaxed;
+    (void)hipThreadExchangeStreamCaptureMode(&mode);
+    if (hipGetSymbolAddress((void **)&p, HIP_SYMBOL(g_status)) != hipSuccess)
+        p = nullptr;
+    (void)hipGetLastError();
+    (void)hipThreadExchangeStreamCaptureMode(&mode);
+    if (p)
+        g_status_ptr[dev].store(p, std::memory_order_release);
+    return p;
+}
+
+static int probe_xcd_dispatch(int dev)
+{
+    if (g_xlocal[dev].load() != 0)
+        return QGEMM_OK;
     std::lock_guard<std::mutex> lock(g_probe_mu);
     if (g_xlocal[dev].load() != 0)
-        return;
+        return QGEMM_OK;
     // relaxed capture mode for this thread and a stream of its own, so a
     // graph being captured on another stream is not disturbed
     hipStreamCaptureMode mode = hipStreamCaptureModeRelaxed;
     (void)hipThreadExchangeStreamCaptureMode(&mode);
-    bool good = false;
+    bool good = false, ran = false;
     uint32_t *d = nullptr;  // device address of g_xcc_probe on this device
     hipStream_t st = nullptr;
     static uint32_t h[XCC_PROBE_WGS];
@@ -191,23 +238,31 @@ static void probe_xcd_dispatch()
             hipLaunchKernelGGL(xcc_probe_kernel, dim3(XCC_PROBE_WGS), dim3(64), 0, st, d);
             good = hipMemcpyAsync(h, d, sizeof h, hipMemcpyDeviceToHost, st) == hipSuccess &&
                    hipStreamSynchronize(st) == hipSuccess;
+            ran = ran || good;
             for (int b = 8; good && b < XCC_PROBE_WGS; b++)
                 good = h[b] == h[b % 8];
         }
     }
     if (st)
         (void)hipStreamDestroy(st);
-    (void)hipGetLastError();
+    const hipError_t e = hipGetLastError();
     (void)hipThreadExchangeStreamCaptureMode(&mode);
+    if (!ran)
+        return hip_fail(e != hipSuccess ? e : hipErrorUnknown, "qgemm_init_device: dispatch probe");
     g_xlocal[dev].store(good ? 1 : 2);
+    return QGEMM_OK;
 }
 
-// Whether the current device passed the probe; QGEMM_ST_XLOCAL=0/1 overrides.
-static bool xcd_local_exchange()
+// Whether the current device passed the probe.  QGEMM_ST_XLOCAL=0 turns the
+// exchange off; forcing it on is for debug builds only.
+static bool xcd_local_exchange(const Problem &p)
 {
-    const int f = env_int("QGEMM_ST_XLOCAL", -1);
-    if (f >= 0)
-        return f != 0;
+    if (p.kn.xlocal == 0)
+        return false;
+#ifdef QGEMM_DEBUG_KNOBS
+    if (p.kn.xlocal == 1)
+        return true;
+#endif
     const int dev = current_device();
     return dev >= 0 && g_xlocal[dev].load(std::memory_order_relaxed) == 1;
 }
@@ -226,7 +281,8 @@ static StCfg stream_cfg(const Problem &p, bool split)
     c.kc = split ? c.KC : (S + c.KC - 1) / c.KC * c.KC;
     c.ksplit = (S + c.kc - 1) / c.kc;
     c.ngroups = (int)((p.L.RT + 7) / 8);
-    c.xlocal = c.ksplit > 1 && xcd_local_exchange();
+    // the per-launch placement check counts splits in 4-bit fields
+    c.xlocal = c.ksplit > 1 && c.ksplit <= 15 && xcd_local_exchange(p);
     // XCD-local exchange: 8 XCDs x ceil(groups / 8) groups x ksplit
     c.grid = c.xlocal ? (c.ngroups + 7) / 8 * 8 * c.ksplit : c.ngroups * c.ksplit;
     if (c.ksplit > 1) {
@@ -247,7 +303,7 @@ static SkCfg skinny_cfg(const Problem &p, int64_t B, bool split)
         c.MB /= 2;
     const int per_slab = skinny_lds_per_slab(p.fmt, nta, c.MB);
     const int kch_max = SK_LDS_MAX / per_slab / SK_RING * SK_RING;  // >= SK_RING by the MB choice
-    c.NT = env_int("QGEMM_SK_NT", 2) == 1 ? 1 : 2;
+    c.NT = p.kn.sk_nt == 1 ? 1 : 2;
     c.ngroups = (int)((p.L.RT + 4 * c.NT - 1) / (4 * c.NT));
     c.nby = (int)((B + 16 * c.MB - 1) / (16 * c.MB));
     const int S = (int)p.L.S;
@@ -285,10 +341,9 @@ struct TiPick {
     double us;
 };
 
-static TiPick pick_split(int tiles, int nsteps, int BM, double tile_us, bool split)
+static TiPick pick_split(int tiles, int nsteps, int BM, double tile_us, bool split, int forced)
 {
     const int full = tiles / 256 * 256, rem = tiles - full;
-    const int forced = env_int("QGEMM_TI_SPLIT", 0);
     TiPick best = {1, (double)(full / 256 + (rem ? 1 : 0)) * tile_us};
     if (!split || rem == 0)
         return best;
@@ -317,7 +372,7 @@ static TiCfg tiled_cfg(const Problem &p, int64_t B, bool split)
     const int64_t cols = dual ? p.N / 2 : p.N;
     const int ntiles = (int)((cols + (dual ? 127 : 255)) / (dual ? 128 : 256));
     const int nsteps = (int)((p.K + 63) / 64);
-    const int fbm = env_int("QGEMM_TI_BM", 0);
+    const int fbm = p.kn.ti_bm;
     int cand[2], nc = 1;
     if (faith) {
         cand[0] = (fbm == 64 || fbm == 96) ? fbm : (B > 64 && B <= 96 ? 96 : 64);
@@ -335,7 +390,7 @@ static TiCfg tiled_cfg(const Problem &p, int64_t B, bool split)
         const int tiles = (int)((B + bm - 1) / bm) * ntiles;
         const double per_k = p.fmt == FMT_MX ? 0.026 : 0.03;  // MXFP4 stages packed codes
         const double tile_us = per_k * (double)p.K * (bm / 256.0) * (faith ? 3.0 : 1.0) * (bm == 128 ? 1.2 : 1.0);
-        const TiPick t = pick_split(tiles, nsteps, bm, tile_us, split);
+        const TiPick t = pick_split(tiles, nsteps, bm, tile_us, split, p.kn.ti_split);
         if (t.us < best.us) {
             best = t;
             c.BM = bm;
@@ -561,8 +616,38 @@ int qgemm_create(qgemm_plan **plan, qgemm_format fmt, qgemm_dtype act, qgemm_dty
     p->p.N = N;
     p->p.K = K;
     make_layout((int)fmt, N, K, &p->p.L);
-    probe_xcd_dispatch();
+    read_knobs(&p->p.kn);
     *plan = p;
+    return QGEMM_OK;
+}
+
+int qgemm_init_device(void)
+{
+    const int dev = current_device();
+    if (dev < 0)
+        return fail(QGEMM_EHIP, "qgemm_init_device: no current HIP device");
+    if (!status_word(dev))
+        return fail(QGEMM_EHIP, "qgemm_init_device: device status word unavailable");
+    return probe_xcd_dispatch(dev);
+}
+
+int qgemm_device_status(uint32_t *bits, int clear, void *stream)
+{
+    if (!bits)
+        return fail(QGEMM_EINVAL, "qgemm_device_status: null pointer");
+    *bits = 0;
+    uint32_t *d = status_word(current_device());
+    if (!d)
+        return fail(QGEMM_EHIP, "qgemm_device_status: no device status word");
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e == hipSuccess)
+        e = hipMemcpy(bits, d, sizeof *bits, hipMemcpyDeviceToHost);
+    if (e == hipSuccess && clear) {
+        const uint32_t zero = 0;
+        e = hipMemcpy(d, &zero, sizeof zero, hipMemcpyHostToDevice);
+    }
+    if (e != hipSuccess)
+        return hip_fail(e, "qgemm_device_status");
     return QGEMM_OK;
 }
 
@@ -641,9 +726,7 @@ int qgemm_run_ws(const qgemm_plan *plan, int64_t B, const void *w, const void *x
         if (p.epi == QGEMM_EPI_SWIGLU && !use_stream(p, B))
             return fail(QGEMM_ENOTSUP, "qgemm_run: the small-batch tier runs the fused gate+up epilogue "
                                        "for B <= %d only (B=%lld)", ST_MAX_B, (long long)B);
-        const int nterm = p.math == QGEMM_MATH_BF16 ? 1 : env_int("QGEMM_FP32_TERMS", 3);
-        if (nterm < 1 || nterm > 3)
-            return fail(QGEMM_EINVAL, "qgemm_run: QGEMM_FP32_TERMS must be 1..3");
+        const int nterm = p.math == QGEMM_MATH_BF16 ? 1 : p.kn.fp32_terms;
         const bool split = workspace != nullptr && (size_t)skinny_ws_bytes(p, B) <= ws_bytes;
         if (use_stream(p, B)) {
             const StCfg c = stream_cfg(p, split);
@@ -654,6 +737,8 @@ int qgemm_run_ws(const qgemm_plan *plan, int64_t B, const void *w, const void *x
             ws.kc = c.kc;
             ws.kch = c.KC;
             ws.xlocal = c.xlocal;
+            ws.xcc_fake = p.kn.xcc_fake;
+            ws.status = c.xlocal ? status_word(current_device()) : nullptr;
             e = launch_stream(p, a, c, ws, nterm, st);
             if (e != hipSuccess)
                 return hip_fail(e, "qgemm_run: kernel launch");
@@ -672,6 +757,8 @@ int qgemm_run_ws(const qgemm_plan *plan, int64_t B, const void *w, const void *x
         ws.kc = c.kc;
         ws.kch = c.kch;
         ws.xlocal = 0;
+        ws.xcc_fake = 0;
+        ws.status = nullptr;
         e = launch_skinny(p, a, c, ws, nterm, st);
     } else {
         TiCfg c = tiled_cfg(p, B, workspace != nullptr);
@@ -710,8 +797,8 @@ int qgemm_run_grouped(const qgemm_plan *plan, int64_t E, int64_t T, const void *
     if (!plan || plan->magic != PLAN_MAGIC)
         return fail(QGEMM_EINVAL, "qgemm_run_grouped: not a live plan");
     const Problem &p = plan->p;
-    if (E < 1 || E > (1 << 20))
-        return fail(QGEMM_EINVAL, "qgemm_run_grouped: E=%lld outside 1..2^20", (long long)E);
+    if (E < 1 || E > (1 << 16))
+        return fail(QGEMM_EINVAL, "qgemm_run_grouped: E=%lld outside 1..2^16", (long long)E);
     if (T < 0 || T > (1ll << 30))
         return fail(QGEMM_EINVAL, "qgemm_run_grouped: T=%lld outside 0..2^30", (long long)T);
     if (plan->forced_tier == QGEMM_TIER_SKINNY)
@@ -735,6 +822,10 @@ int qgemm_run_grouped(const qgemm_plan *plan, int64_t E, int64_t T, const void *
     g.wtab = (const uint8_t *const *)w_table;
     g.off = offsets;
     g.E = (int)E;
+    g.T = (int)T;
+    g.status = status_word(current_device());
+    if (!g.status)
+        return fail(QGEMM_EHIP, "qgemm_run_grouped: no device status word");
     g.ntiles = (int)((ncols + (p.epi == QGEMM_EPI_SWIGLU ? 127 : 255)) / (p.epi == QGEMM_EPI_SWIGLU ? 128 : 256));
     if (tiles * g.ntiles > 0x7FFFFFFFll)
         return fail(QGEMM_EINVAL, "qgemm_run_grouped: grid too large");

@@ -301,11 +301,34 @@ __device__ __forceinline__ void store_out(void *y, int64_t idx, float v)
 // ------------------------------------------------------------ launch API
 // (host side; one translation unit per tier)
 
+// Overrides of the tuned choices, read once from the environment when a plan
+// is created (for measurements and tests; 0 or -1 keeps the tuned choice).
+// Release builds honour only overrides that keep the documented results:
+// the shape knobs (results stay within the same bounds) and QGEMM_ST_XLOCAL=0
+// (the device-coherent exchange, bitwise the same result).  Builds with
+// QGEMM_DEBUG_KNOBS also honour QGEMM_ST_XLOCAL=1, QGEMM_FP32_TERMS=1|2 (fewer
+// activation terms: gives up the fp32-faithful bound) and QGEMM_XCC_FAKE=1
+// (odd K splits report the next XCC, to exercise the per-launch check).
+struct Knobs {
+    int st_waves, st_nph;  // streaming-kernel shape (QGEMM_ST_WAVES, QGEMM_ST_NPH)
+    int sk_stream;         // 0: B <= 16 through the skinny kernel (QGEMM_SK_STREAM)
+    int sk_nt;             // 1: one row tile per skinny wave (QGEMM_SK_NT)
+    int ti_bm, ti_split;   // large-batch row-tile height, K splits (QGEMM_TI_BM, QGEMM_TI_SPLIT)
+    int xlocal;            // -1 the probe decides, 0 device-coherent, 1 forced (debug)
+    int fp32_terms;        // activation terms of fp32-faithful math (3; debug 1..3)
+    int xcc_fake;          // debug: odd K splits report the next XCC to the placement check
+};
+
 struct Problem {
     int fmt, act, out, epi, math;
     int64_t N, K;
     Layout L;
+    Knobs kn;
 };
+
+// Bits of the device status word (qgemm_device_status).
+constexpr uint32_t DEV_XCD_MISMATCH = 1u;  // a workgroup ran off its probed XCD
+constexpr uint32_t DEV_BAD_OFFSETS = 2u;   // routed-expert offsets broke their rules
 
 // Small-batch tier shape: MB 16-row batch groups and 4*NT row tiles per
 // workgroup, kc slabs of K per workgroup staged kch at a time, ksplit
@@ -331,6 +354,8 @@ struct SkinnyWs {
     // round-robin), so partial tiles are exchanged through that XCD's L2
     // (workgroup-scope stores and loads) instead of device-coherent memory
     int xlocal;
+    int xcc_fake;      // debug builds: odd splits report the next XCC (exercises the check)
+    uint32_t *status;  // device status word (DEV_* bits), or null
 };
 
 // LDS bytes of one staged slab: NTA terms x MB x units x 64 lanes x 16 B.
@@ -425,6 +450,8 @@ struct Groups {
     const int *off;
     int E;
     int ntiles;
+    int T;             // rows: off[0] = 0, off non-decreasing, off[E] = T
+    uint32_t *status;  // device status word: DEV_BAD_OFFSETS when they are not
 };
 hipError_t launch_grouped(const Problem &p, const KArgs &a, const Groups &g, int BM, int64_t tiles,
                           hipStream_t st);

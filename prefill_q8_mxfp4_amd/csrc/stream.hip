@@ -293,9 +293,30 @@ __global__ __launch_bounds__(64 * st_max_waves(NPH)) void stream_kernel(KArgs a,
         __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are acknowledged
         __syncthreads();
         if (tid == 0) {
-            const uint32_t old =
-                __hip_atomic_fetch_add(&ws.cnt[grp], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            s_is_last = old == (uint32_t)(ws.ksplit - 1);
+            if (ws.xlocal) {
+                // Per-launch check of the placement the exchange rests on:
+                // each split adds one to the nibble of its XCC (at most 15
+                // splits), so the last to arrive sees where all of them ran.
+                // Splits spread over more than one XCD (a dispatcher that broke
+                // the round-robin the probe saw) set DEV_XCD_MISMATCH: that
+                // launch's result is not to be trusted.
+                uint32_t xcc = __builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) & 7u;
+                if (ws.xcc_fake && (ks & 1))
+                    xcc = (xcc + 1) & 7u;  // debug builds: pretend odd splits ran next door
+                const uint32_t mine = 1u << (4 * xcc);
+                const uint32_t now = __hip_atomic_fetch_add(&ws.cnt[grp], mine, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT) + mine;
+                uint32_t cnt = (now & 0x0F0F0F0Fu) + ((now >> 4) & 0x0F0F0F0Fu);
+                cnt = (cnt + (cnt >> 8) + (cnt >> 16) + (cnt >> 24)) & 0xFFu;
+                s_is_last = cnt == (uint32_t)ws.ksplit;
+                if (s_is_last && now != (uint32_t)ws.ksplit << (4 * xcc) && ws.status)
+                    __hip_atomic_fetch_or(ws.status, DEV_XCD_MISMATCH, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                const uint32_t old =
+                    __hip_atomic_fetch_add(&ws.cnt[grp], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                s_is_last = old == (uint32_t)(ws.ksplit - 1);
+            }
         }
         __syncthreads();
         if (!s_is_last)

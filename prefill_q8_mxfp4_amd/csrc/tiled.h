@@ -89,10 +89,21 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
         ntl = (int)blockIdx.x % grp.ntiles;
         if (tid == 0)
             s_e = -1;
+        // Every workgroup also checks the offsets it scans (all of them):
+        // off[0] = 0, non-decreasing, off[E] = T.  If they break a rule no
+        // workgroup does any work, and workgroup 0 sets DEV_BAD_OFFSETS in the
+        // device status word, so bad offsets never move a load or a store
+        // outside x and y.
         int base = 0;  // row tiles of the experts before this chunk
+        int bad = 0;
         for (int e0 = 0; e0 < grp.E; e0 += NTHR) {
             const int e = e0 + tid;
-            const int c = e < grp.E ? (grp.off[e + 1] - grp.off[e] + BM - 1) / BM : 0;
+            int c = 0;
+            if (e < grp.E) {
+                const int lo = grp.off[e], hi = grp.off[e + 1];
+                bad |= (hi < lo) | (e == 0 && lo != 0) | (e == grp.E - 1 && hi != grp.T);
+                c = hi > lo ? (int)(((int64_t)hi - lo + BM - 1) / BM) : 0;
+            }
             int v = c;  // inclusive scan within the wave
 #pragma unroll
             for (int d = 1; d < 64; d <<= 1) {
@@ -117,8 +128,11 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
             }
             base += tot;
             __syncthreads();  // s_wsum is rewritten by the next chunk
-            if (base > j)
-                break;  // uniform
+        }
+        if (__syncthreads_or(bad)) {
+            if (blockIdx.x == 0 && tid == 0)
+                __hip_atomic_fetch_or(grp.status, DEV_BAD_OFFSETS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;  // uniform over the workgroup
         }
         if (s_e < 0)
             return;  // past the experts' last row tile (uniform)

@@ -79,6 +79,34 @@ def test_create_validation(args, status):
         assert q.lib().qgemm_last_error()
 
 
+def test_create_is_host_only():
+    """qgemm_create makes no HIP call: in a process that sees no GPU (every
+    device hidden) plans are created and destroyed, nothing is probed, and
+    the calls that do need a device fail cleanly with QGEMM_EHIP."""
+    import subprocess
+    import sys
+    code = r"""
+import ctypes, prefill_q8_mxfp4_amd as q
+L = q.lib()
+for args in ((0, 0, 0, 0, 0, 5120, 5120, 0), (2, 1, 1, 1, 1, 2 * 17408, 5120, 0), (3, 1, 0, 0, 1, 256, 512, 2)):
+    h = ctypes.c_void_p()
+    assert L.qgemm_create(ctypes.byref(h), *args) == q.OK, L.qgemm_last_error()
+    assert h.value and L.qgemm_plan_tier(h, 16) in (1, 2)
+    assert L.qgemm_workspace_bytes(h, 16) > 0
+    assert L.qgemm_destroy(h) == q.OK
+assert L.qgemm_xcd_local() == -1
+assert L.qgemm_init_device() == q.EHIP and L.qgemm_last_error()
+bits = ctypes.c_uint32(7)
+assert L.qgemm_device_status(ctypes.byref(bits), 0, None) == q.EHIP and bits.value == 0
+assert L.qgemm_device_status(None, 0, None) == q.EINVAL
+print("ok")
+"""
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1", CUDA_VISIBLE_DEVICES="-1")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=120,
+                       env=env)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout[-2000:] + r.stderr[-2000:]
+
+
 def test_destroy_null_and_strerror():
     assert q.lib().qgemm_destroy(None) == q.OK
     for s in (q.OK, q.EINVAL, q.ENOTSUP, q.EHIP, q.ENOMEM):
@@ -104,7 +132,7 @@ def test_run_validation_before_any_hip_call():
     assert L.qgemm_plan_tier(h, 2048) == 2
     assert L.qgemm_plan_tier(h, -1) == 0
     if not _has_device():
-        assert L.qgemm_xcd_local() == -1      # no device: the dispatch probe is skipped
+        assert L.qgemm_xcd_local() == -1      # no device: nothing probed
     assert L.qgemm_destroy(h) == q.OK
 
 

@@ -4,6 +4,8 @@ unrounded fp64 oracle): 1e-5 for fp32 math, 1e-2 for bf16 math.  Decoded
 weights, exact closed forms, one-hot read-outs and batch chunking are
 compared bit for bit."""
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -98,9 +100,14 @@ def test_q8_0_256x512_b70_fp32():
     x = synth.gen_config_x("q8_0_256x512", 70)
     plan = q.Plan("q8_0", c["N"], c["K"], act="f32", out="f32", math="fp32")
     y = run(plan, x, w_dev(w))
-    err = oracle.rel_fro(y, oracle.gemm(w, x))
+    ref = oracle.gemm(w, x)
+    err = oracle.rel_fro(y, ref)
     print(f"q8_0 256x512 B=70 rel_fro={err:.3e}")
     assert err <= TOL_FP32
+    bi = np.repeat(np.arange(70), 256)
+    ni = np.tile(np.arange(256), 70)
+    mag = oracle.gemm_abs_at(w, x, bi, ni).reshape(70, 256)
+    _assert_componentwise(y, ref, 1.01 * mag, _nadds(512, 3), "q8_0 256x512 B=70 every output")
 
 
 # ------------------------------------------- attention projection sweep
@@ -121,6 +128,12 @@ def test_q8_0_5120_sweep_fp32(q8_attn, B):
     err = oracle.rel_fro(y, ref[:B])
     print(f"q8_0 5120x5120 B={B} tier={plan.tier(B)} rel_fro={err:.3e}")
     assert err <= TOL_FP32
+    tid, nt = _full_tiles(B, 5120, tb=64)
+    _assert_tiles(y.ravel(), ref[:B].ravel(), tid, nt, TOL_FP32, f"q8_0 5120 B={B} per tile")
+    # three exact bf16 terms per activation, exact int8 codes: exact products
+    bi, ni, _, _ = _tile_samples(B, 5120, 60 + B, tb=64)
+    _assert_componentwise(y[bi, ni], ref[:B][bi, ni], 1.01 * oracle.gemm_abs_at(w, x[:B], bi, ni),
+                          _nadds(5120, 3), f"q8_0 5120 B={B}")
 
 
 @pytest.mark.parametrize("tier", ["skinny", "tiled"])
@@ -173,14 +186,14 @@ def test_split_k_and_unsplit_agree(q8_attn, B):
 
 def test_dispatch_probe_finds_xcd_round_robin():
     """On the MI355X the dispatcher deals workgroup ids to the XCDs
-    round-robin, so qgemm_create's probe enables the XCD-local exchange."""
-    q.Plan("q8_0", 256, 512, act="f32", out="f32")
+    round-robin, so qgemm_init_device's probe enables the XCD-local exchange."""
+    q.init_device()
     assert q.xcd_local() == 1
 
 
 def test_dispatch_probe_during_graph_capture():
-    """A fresh process whose first plan is created while a graph is being
-    captured on another stream: the probe runs on a stream of its own in
+    """A fresh process whose first launch (the binding initialises the device
+    then) is captured into a graph: the probe runs on a stream of its own in
     relaxed capture mode, the capture stays valid, and its replays match an
     eager call."""
     import subprocess
@@ -194,8 +207,8 @@ y = torch.zeros((8, 1024), dtype=torch.float32, device="cuda")
 st = torch.cuda.Stream()
 g = torch.cuda.CUDAGraph()
 with torch.cuda.graph(g, stream=st):
-    plan = q.Plan("q8_0", 1024, 2048, act="f32", out="f32")  # first plan: the probe runs here
-    plan.run(x, wd, y, workspace=None)
+    plan = q.Plan("q8_0", 1024, 2048, act="f32", out="f32")
+    plan.run(x, wd, y, workspace=None)  # first launch: the binding's init_device probes here
 assert q.xcd_local() == 1, q.xcd_local()
 for _ in range(3):
     y.zero_()
@@ -229,17 +242,20 @@ def test_stream_split_exchange_modes_agree(fmt, n, k, act, epi, monkeypatch):
         w = synth.quantize(fmt, synth.normal_f32(41, synth.SID_W, n, k, 0.02))
     wd = w_dev(w)
     math = "fp32" if act == "f32" else "bf16"
-    plan = q.Plan(fmt, n, k, act=act, out="f32", math=math, epilogue=epi)
+    q.init_device()
+    assert q.xcd_local() == 1
+    plan = q.Plan(fmt, n, k, act=act, out="f32", math=math, epilogue=epi)  # XCD-local
+    monkeypatch.setenv("QGEMM_ST_XLOCAL", "0")   # read at plan creation
+    coh = q.Plan(fmt, n, k, act=act, out="f32", math=math, epilogue=epi)   # device-coherent
+    monkeypatch.delenv("QGEMM_ST_XLOCAL")
+    q.device_status(clear=True)
     for B in (1, 16):
         assert plan.tier(B) == "skinny"
         x = synth.gen_x_f32(B, k, seed=B) if act == "f32" else synth.gen_x_bf16(B, k, seed=B)
         ws = torch.zeros(plan.workspace_bytes(B), dtype=torch.uint8, device=_dev())
         outs = []
-        for mode in ("0", "1", "0", "1"):
-            monkeypatch.setenv("QGEMM_ST_XLOCAL", mode)
-            outs.append(run(plan, x, wd, workspace=ws))
-        monkeypatch.delenv("QGEMM_ST_XLOCAL")
-        outs.append(run(plan, x, wd, workspace=ws))  # the probed default
+        for p in (coh, plan, coh, plan):
+            outs.append(run(p, x, wd, workspace=ws))
         for o in outs[1:]:
             assert np.array_equal(o, outs[0]), (B, fmt)
         assert torch.count_nonzero(ws[:4 * -(-n // 128)]) == 0  # row-group counters re-armed
@@ -247,6 +263,48 @@ def test_stream_split_exchange_modes_agree(fmt, n, k, act, epi, monkeypatch):
         err = oracle.rel_fro(outs[0], ref)
         tol = TOL_FP32 if math == "fp32" else (1e-4 if epi == "swiglu" else TOL_BF16)
         assert err <= tol, (B, fmt, err)
+    assert q.device_status() == 0  # no workgroup ran off its probed XCD
+
+
+def test_xcd_mismatch_is_detected():
+    """The per-launch placement check of the XCD-local exchange, exercised in
+    a fresh process on the debug build of the library: with QGEMM_XCC_FAKE=1
+    the odd K splits of every row group report the next XCC, so the splits
+    look spread over two XCDs and the launch sets QGEMM_DEV_XCD_MISMATCH
+    (they really ran on one XCD, so the output is still bitwise that of the
+    unperturbed plan); the unperturbed plan sets nothing."""
+    import subprocess
+    import sys
+    code = r"""
+import os, numpy as np, torch, synth, prefill_q8_mxfp4_amd as q
+assert q.LIB_PATH.endswith("libqgemm_debug.so"), q.LIB_PATH
+w = synth.gen_config_weights("q8_0_5120x5120")
+wd = torch.from_numpy(q.pack_logical(w)).cuda()
+q.init_device()
+assert q.xcd_local() == 1
+good = q.Plan("q8_0", 5120, 5120, act="f32", out="f32")
+os.environ["QGEMM_XCC_FAKE"] = "1"
+bad = q.Plan("q8_0", 5120, 5120, act="f32", out="f32")
+q.device_status(clear=True)
+for B in (1, 16):
+    x = torch.from_numpy(synth.gen_config_x("q8_0_5120x5120", B)).cuda()
+    y0 = torch.full((B, 5120), float("nan"), device="cuda")
+    y1 = torch.full((B, 5120), float("nan"), device="cuda")
+    good.run(x, wd, y0)
+    assert q.device_status() == 0
+    bad.run(x, wd, y1)
+    assert q.device_status(clear=True) == q.DEV_XCD_MISMATCH
+    assert torch.equal(y0.view(torch.int32), y1.view(torch.int32)), B
+    good.run(x, wd, y1)
+    assert torch.equal(y0.view(torch.int32), y1.view(torch.int32)), B
+assert q.device_status() == 0
+print("ok")
+"""
+    root = __file__.rsplit("/tests/", 1)[0]
+    env = dict(os.environ, QGEMM_LIB_PATH=os.path.join(root, "prefill_q8_mxfp4_amd", "libqgemm_debug.so"))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=180,
+                       env=env)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout[-2000:] + r.stderr[-2000:]
 
 
 def test_workspace_reused_across_batch_widths(q8_attn):
@@ -488,6 +546,71 @@ def _samples(B, ncols, count, seed):
     return bi, ni
 
 
+# Output tiles for the per-tile checks: 128 x 128 is no larger than any
+# kernel's output tile in both directions (the large-batch tiles are 64-256
+# batch rows x 256 weight rows, or 128 with the fused epilogue; a streaming
+# workgroup owns 128 weight rows), so one wrong kernel tile makes at least
+# one check tile wrong.
+TB, TN = 128, 128
+PER_TILE = 64
+# Unit roundoff for the component-wise bounds: twice fp32's 2^-24, so that a
+# matrix-core adder that truncates instead of rounding to nearest is covered.
+U_ACC = 2.0 ** -23
+
+
+def _tile_samples(B, ncols, seed, tb=TB, tn=TN, per_tile=PER_TILE):
+    """per_tile random outputs inside every tb x tn tile of a [B][ncols]
+    output (ragged edge tiles included) plus the four corners; returns row
+    and column indices, each sample's tile id and the tile count."""
+    rng = np.random.default_rng(seed)
+    mt, nt = -(-B // tb), -(-ncols // tn)
+    t = np.repeat(np.arange(mt * nt), per_tile)
+    r0, c0 = (t // nt) * tb, (t % nt) * tn
+    bi = r0 + (rng.random(t.size) * np.minimum(tb, B - r0)).astype(np.int64)
+    ni = c0 + (rng.random(t.size) * np.minimum(tn, ncols - c0)).astype(np.int64)
+    bi[:4] = [0, B - 1, 0, B - 1]
+    ni[:4] = [0, 0, ncols - 1, ncols - 1]
+    return bi, ni, (bi // tb) * nt + ni // tn, mt * nt
+
+
+def _full_tiles(B, ncols, tb=TB, tn=TN):
+    nt = -(-ncols // tn)
+    return ((np.arange(B)[:, None] // tb) * nt + np.arange(ncols)[None, :] // tn).ravel(), \
+        -(-B // tb) * nt
+
+
+def _assert_tiles(y, ref, tid, ntiles, tol, label):
+    """Every tile's relative Frobenius error within tol (NaN fails)."""
+    per = oracle.rel_fro_groups(y, ref, tid, ntiles)
+    assert not np.isnan(per).any(), f"{label}: NaN or empty tile"
+    worst = int(np.argmax(per))
+    print(f"{label}: {ntiles} tiles, median {np.median(per):.3e}, worst {per[worst]:.3e} "
+          f"(tile {worst})")
+    assert per[worst] <= tol, (label, worst, per[worst])
+
+
+def _assert_componentwise(y, ref, mag, nadds, label):
+    """|y - ref| <= gamma(nadds, U_ACC) * mag element by element: the
+    forward error bound of a sum of exact products rounded nadds times (mag
+    is sum |x||w|, slightly enlarged for split activations)."""
+    y = np.asarray(y, dtype=np.float64).ravel()
+    ref = np.asarray(ref, dtype=np.float64).ravel()
+    bound = oracle.gamma(nadds, U_ACC) * np.asarray(mag, dtype=np.float64).ravel()
+    excess = np.abs(y - ref) - bound
+    assert not np.isnan(excess).any(), f"{label}: NaN"
+    i = int(np.argmax(excess))
+    print(f"{label}: component-wise max |err|/bound = "
+          f"{np.max(np.abs(y - ref) / np.maximum(bound, 1e-300)):.3e} (n={nadds})")
+    assert excess[i] <= 0, (label, i, float(y[i]), float(ref[i]), float(bound[i]))
+
+
+def _nadds(K, terms):
+    """Roundings per output of the exact-product paths: the K*terms products
+    of a split activation summed in fp32, one block-scale FMA per 16 or 32
+    columns, and the partial tiles of slabs and K splits (a generous 64)."""
+    return terms * K + K // 16 + 64
+
+
 def test_q8_0_ffn_prefill_2048_bf16():
     c = synth.CONFIGS["q8_0_ffn_17408x5120"]
     w = synth.gen_config_weights("q8_0_ffn_17408x5120")
@@ -496,32 +619,36 @@ def test_q8_0_ffn_prefill_2048_bf16():
     assert plan.tier(2048) == "tiled"
     y = run(plan, x, w_dev(w))
     assert np.all(np.isfinite(y))
-    bi, ni = _samples(2048, c["N"], 6000, 3)
-    err = oracle.rel_fro(y[bi, ni], oracle.gemm_at(w, x, bi, ni))
+    bi, ni, tid, nt = _tile_samples(2048, c["N"], 3)
+    ref = oracle.gemm_at(w, x, bi, ni)
+    err = oracle.rel_fro(y[bi, ni], ref)
     print(f"q8_0 ffn rel_fro(sampled)={err:.3e}")
     assert err <= TOL_BF16
+    _assert_tiles(y[bi, ni], ref, tid, nt, TOL_BF16, "q8_0 ffn B=2048 per tile (oracle samples)")
 
 
 # -------------------------------------- full outputs against a library GEMM
 
-def _library_ref(w, x, swiglu=False):
-    """Every output at full size: the oracle's decoded weights (fp64 -> fp32,
-    tensor scales applied) times the activations as given, through torch's
-    fp32 GEMM on the GPU (rocBLAS / hipBLASLt, no reduced-precision inputs),
-    then SiLU(G) * U in fp32 for the fused epilogue."""
-    torch.backends.cuda.matmul.allow_tf32 = False
-    xf = x if x.dtype == np.float32 else synth.bf16_bits_to_f32(x)
-    W = torch.from_numpy(oracle.dequant(w, apply_g=True).astype(np.float32)).to(_dev())
-    y = torch.mm(torch.from_numpy(np.ascontiguousarray(xf)).to(_dev()), W.t().contiguous())
-    del W
+def _library_ref(w, x, swiglu=False, magnitude=False):
+    """Every output at full size: the oracle's decoded weights (fp64, tensor
+    scales applied) times the activations as given, through torch's float64
+    GEMM on the GPU (rocBLAS dgemm: every operand exact, error ~1e-16 of
+    sum |x||w|), then SiLU(G) * U in fp64 for the fused epilogue.  With
+    magnitude=True also |x| @ |w|^T, the magnitude sum of every output."""
+    xf = (x if x.dtype == np.float32 else synth.bf16_bits_to_f32(x)).astype(np.float64)
+    W = torch.from_numpy(oracle.dequant(w, apply_g=True)).to(_dev())
+    X = torch.from_numpy(np.ascontiguousarray(xf)).to(_dev())
+    y = torch.mm(X, W.t().contiguous())
+    mag = torch.mm(X.abs(), W.abs().t().contiguous()).cpu().numpy() if magnitude else None
+    del W, X
     if swiglu:
         nh = y.shape[1] // 2
         G, U = y[:, :nh], y[:, nh:]
         y = G * torch.sigmoid(G) * U
-    out = y.double().cpu().numpy()
+    out = y.cpu().numpy()
     del y
     torch.cuda.empty_cache()
-    return out
+    return (out, mag) if magnitude else out
 
 
 @pytest.mark.parametrize("act,math,B", [("f32", "fp32", 4),     # streaming
@@ -538,10 +665,17 @@ def test_largest_k(act, math, B):
     y = run(plan, x, w_dev(w))
     bi, ni = _samples(B, n, 200, 53)
     err = oracle.rel_fro(y[bi, ni], oracle.gemm_at(w, x, bi, ni))
-    lib = oracle.rel_fro(y, _library_ref(w, x))
-    print(f"K=2^20 B={B} {math} rel_fro(oracle samples)={err:.3e} (vs fp32 library GEMM {lib:.3e})")
+    ref, mag = _library_ref(w, x, magnitude=True)
+    lib = oracle.rel_fro(y, ref)
+    print(f"K=2^20 B={B} {math} rel_fro(oracle samples)={err:.3e} (vs fp64 library GEMM {lib:.3e})")
     assert np.all(np.isfinite(y))
-    assert err <= (TOL_FP32 if math == "fp32" else TOL_BF16)
+    tol = TOL_FP32 if math == "fp32" else TOL_BF16
+    assert err <= tol
+    assert lib <= tol
+    tid, nt = _full_tiles(B, n, tn=64)
+    _assert_tiles(y.ravel(), ref.ravel(), tid, nt, tol, f"K=2^20 B={B} per tile")
+    if math == "fp32":
+        _assert_componentwise(y, ref, mag * 1.01, _nadds(k, 3), f"K=2^20 B={B}")
 
 
 @pytest.mark.parametrize("name,B", [("q8_0_ffn_17408x5120", 2048), ("mxfp4_down_5120x17408", 256), ("mxfp4_down_5120x17408", 2048), ("nvfp4_gate_up_34816x5120", 2048),
@@ -557,12 +691,24 @@ def test_full_output_against_library_gemm(name, B):
     plan = q.Plan(c["fmt"], c["N"], c["K"], act=c["act"], out=c["out"],
                   epilogue="swiglu" if swiglu else "none", math=c["math"])
     y = run(plan, x, w_dev(w))
-    ref = _library_ref(w, x, swiglu)
+    # products are exact where the weights are exact in bf16 and the
+    # activations are bf16 (MXFP4, NVFP4) or split into exact bf16 terms
+    # (fp32-faithful math); Q8_0 and FP8 weights are rounded to bf16 with bf16 math
+    exact = c["math"] == "fp32" or c["fmt"] in ("mxfp4", "nvfp4")
+    want_mag = exact and not swiglu
+    ref = _library_ref(w, x, swiglu, magnitude=want_mag)
+    ref, mag = ref if want_mag else (ref, None)
     err = oracle.rel_fro(y, ref)
     tol = TOL_FP32 if (c["math"] == "fp32" and c["out"] == "f32") else TOL_BF16
     print(f"{name} B={B} full output vs library GEMM rel_fro={err:.3e}")
     assert np.all(np.isfinite(y))
     assert err <= tol
+    tid, nt = _full_tiles(B, y.shape[1])
+    _assert_tiles(y.ravel(), ref.ravel(), tid, nt, tol, f"{name} B={B} per tile (every output)")
+    if want_mag:
+        terms = 3 if c["math"] == "fp32" else 1
+        _assert_componentwise(y, ref, mag * (1.01 if terms == 3 else 1.0), _nadds(c["K"], terms),
+                              f"{name} B={B}")
 
 
 @pytest.fixture(scope="module")
@@ -578,10 +724,15 @@ def test_mxfp4_down_projection(mx_down, B):
     plan = q.Plan("mxfp4", 5120, 17408, act="bf16", out="f32")
     y = run(plan, x[:B], wd)
     assert np.all(np.isfinite(y))
-    bi, ni = _samples(B, 5120, 3000, B)
-    err = oracle.rel_fro(y[bi, ni], oracle.gemm_at(w, x[:B], bi, ni))
+    bi, ni, tid, nt = _tile_samples(B, 5120, B)
+    ref = oracle.gemm_at(w, x[:B], bi, ni)
+    err = oracle.rel_fro(y[bi, ni], ref)
     print(f"mxfp4 down B={B} tier={plan.tier(B)} rel_fro(sampled)={err:.3e}")
     assert err <= TOL_BF16
+    _assert_tiles(y[bi, ni], ref, tid, nt, TOL_BF16, f"mxfp4 down B={B} per tile")
+    # E2M1 x E8M0 weights and bf16 activations: exact products
+    _assert_componentwise(y[bi, ni], ref, oracle.gemm_abs_at(w, x[:B], bi, ni), _nadds(17408, 1),
+                          f"mxfp4 down B={B}")
 
 
 @pytest.fixture(scope="module")
@@ -599,10 +750,12 @@ def test_fp8_attention_projection(fp8_attn, B):
     plan = q.Plan("fp8", 5120, 5120, act="bf16", out="f32")
     y = run(plan, x[:B], wd)
     assert np.all(np.isfinite(y))
-    bi, ni = _samples(B, 5120, 3000, B + 7)
-    err = oracle.rel_fro(y[bi, ni], oracle.gemm_at(w, x[:B], bi, ni))
+    bi, ni, tid, nt = _tile_samples(B, 5120, B + 7)
+    ref = oracle.gemm_at(w, x[:B], bi, ni)
+    err = oracle.rel_fro(y[bi, ni], ref)
     print(f"fp8 B={B} tier={plan.tier(B)} rel_fro(sampled)={err:.3e}")
     assert err <= TOL_BF16
+    _assert_tiles(y[bi, ni], ref, tid, nt, TOL_BF16, f"fp8 B={B} per tile")
 
 
 @pytest.mark.parametrize("B", [1, 16, 70])
@@ -612,10 +765,14 @@ def test_fp8_fp32_math(fp8_attn, B):
     x = synth.gen_x_f32(B, 5120, seed=3)
     plan = q.Plan("fp8", 5120, 5120, act="f32", out="f32", math="fp32")
     y = run(plan, x, wd)
-    bi, ni = _samples(B, 5120, 3000, B + 11)
-    err = oracle.rel_fro(y[bi, ni], oracle.gemm_at(w, x, bi, ni))
+    bi, ni, tid, nt = _tile_samples(B, 5120, B + 11)
+    ref = oracle.gemm_at(w, x, bi, ni)
+    err = oracle.rel_fro(y[bi, ni], ref)
     print(f"fp8 fp32-math B={B} rel_fro(sampled)={err:.3e}")
     assert err <= TOL_FP32
+    _assert_tiles(y[bi, ni], ref, tid, nt, TOL_FP32, f"fp8 fp32-math B={B} per tile")
+    _assert_componentwise(y[bi, ni], ref, 1.01 * oracle.gemm_abs_at(w, x, bi, ni), _nadds(5120, 3),
+                          f"fp8 fp32-math B={B}")
 
 
 def test_nvfp4_fused_gate_up_swiglu_2048():
@@ -626,10 +783,12 @@ def test_nvfp4_fused_gate_up_swiglu_2048():
     y = run(plan, x, w_dev(w))
     assert y.shape == (2048, c["N"] // 2)
     assert np.all(np.isfinite(y))
-    bi, ji = _samples(2048, c["N"] // 2, 4000, 5)
-    err = oracle.rel_fro(y[bi, ji], oracle.swiglu_at(w, x, bi, ji))
+    bi, ji, tid, nt = _tile_samples(2048, c["N"] // 2, 5)
+    ref = oracle.swiglu_at(w, x, bi, ji)
+    err = oracle.rel_fro(y[bi, ji], ref)
     print(f"nvfp4 gate+up rel_fro(sampled)={err:.3e}")
     assert err <= TOL_BF16
+    _assert_tiles(y[bi, ji], ref, tid, nt, TOL_BF16, "nvfp4 gate+up B=2048 per tile")
 
 
 def test_swiglu_small_exhaustive():
@@ -833,3 +992,87 @@ def test_grouped_single_expert_and_empty():
     xe = torch.empty((0, k), dtype=torch.bfloat16, device=_dev())
     ye = torch.empty((0, n), dtype=torch.float32, device=_dev())
     plan.run_grouped(xe, table, off, ye)
+
+
+def test_grouped_benched_moe_shape():
+    """The routed-expert workload the benchmark times: 512 NVFP4 experts of
+    2 x 512 gate+up rows, K = 2048, top-10 routing of 2048 tokens (20,480
+    rows; eight generated experts copied into 512 buffers, as the benchmark
+    does).  Every (expert, 128-column) output tile within the bf16 bound on
+    at least 64 oracle samples, and every expert's rows bitwise those of an
+    unsplit large-batch call of that expert alone."""
+    E, topk, tokens, nh, K = 512, 10, 2048, 512, 2048
+    distinct = [synth.gen_expert_weights("nvfp4", 2 * nh, K, e, swiglu=True) for e in range(8)]
+    packed = [w_dev(w) for w in distinct]
+    bufs = [packed[e % 8].clone() for e in range(E)]
+    table = torch.tensor([b.data_ptr() for b in bufs], dtype=torch.int64, device=_dev())
+    tok, offsets = synth.gen_routing(tokens, topk, E)
+    T = int(offsets[-1])
+    assert T == tokens * topk
+    x = synth.gen_x_bf16(tokens, K)[tok]
+    plan = q.Plan("nvfp4", 2 * nh, K, act="bf16", out="bf16", epilogue="swiglu")
+    y = y_new(plan, T)
+    plan.run_grouped(x_dev(x), table, torch.from_numpy(offsets.astype(np.int32)).to(_dev()), y)
+    torch.cuda.synchronize()
+    y = host(y)
+    assert np.all(np.isfinite(y))
+    # PER_TILE samples in every (expert with rows, 128-column) tile
+    rng = np.random.default_rng(77)
+    rows = np.diff(offsets)
+    live = np.nonzero(rows)[0]
+    ct = nh // 128
+    e_s = np.repeat(live, ct * PER_TILE)
+    c_s = np.tile(np.repeat(np.arange(ct), PER_TILE), live.size)
+    bi = offsets[e_s] + (rng.random(e_s.size) * rows[e_s]).astype(np.int64)
+    ji = c_s * 128 + rng.integers(0, 128, e_s.size)
+    tid = np.repeat(np.arange(live.size * ct), PER_TILE)
+    ref = np.empty(bi.size)
+    for d in range(8):
+        sel = e_s % 8 == d
+        ref[sel] = oracle.swiglu_at(distinct[d], x, bi[sel], ji[sel])
+    err = oracle.rel_fro(y[bi, ji], ref)
+    print(f"routed moe 512 experts rel_fro(sampled)={err:.3e}")
+    assert err <= TOL_BF16
+    _assert_tiles(y[bi, ji], ref, tid, live.size * ct, TOL_BF16, "routed moe per (expert, tile)")
+    solo = q.Plan("nvfp4", 2 * nh, K, act="bf16", out="bf16", epilogue="swiglu", tier="tiled")
+    yb = y.astype(np.float32).view(np.uint32)
+    for e in live:
+        r0, r1 = offsets[e], offsets[e + 1]
+        ye = run(solo, x[r0:r1], bufs[e], workspace=None)
+        assert np.array_equal(ye.astype(np.float32).view(np.uint32), yb[r0:r1]), e
+
+
+@pytest.mark.parametrize("case", ["decreasing", "first_not_zero", "last_not_T", "negative"])
+def test_grouped_bad_offsets_do_nothing_and_report(case):
+    """Offsets that break their rules (non-decreasing, offsets[0] = 0,
+    offsets[E] = T): the launch writes nothing (y keeps its NaN fill) and
+    sets QGEMM_DEV_BAD_OFFSETS; good offsets afterwards run normally and set
+    nothing."""
+    n, k = 256, 512
+    rows = [5, 0, 40, 17]
+    good = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    T = int(good[-1])
+    bad = good.copy()
+    if case == "decreasing":
+        bad[2], bad[3] = bad[3], bad[2]
+    elif case == "first_not_zero":
+        bad[0] = 3
+    elif case == "last_not_T":
+        bad[-1] = T + 1000000
+    else:
+        bad[1] = -1000000
+    ws = [synth.gen_expert_weights("mxfp4", n, k, e, seed=9) for e in range(len(rows))]
+    bufs = [w_dev(w) for w in ws]
+    table = torch.tensor([b.data_ptr() for b in bufs], dtype=torch.int64, device=_dev())
+    x = synth.gen_x_bf16(T, k, seed=10)
+    xd = x_dev(x)
+    plan = q.Plan("mxfp4", n, k, act="bf16", out="f32")
+    q.device_status(clear=True)
+    y = y_new(plan, T)
+    plan.run_grouped(xd, table, torch.from_numpy(bad).to(_dev()), y)
+    assert q.device_status(clear=True) == q.DEV_BAD_OFFSETS
+    assert torch.isnan(y).all()
+    plan.run_grouped(xd, table, torch.from_numpy(good).to(_dev()), y)
+    assert q.device_status() == 0
+    ref = oracle.gemm_grouped(ws, good, x)
+    assert oracle.rel_fro(host(y), ref) <= TOL_BF16

@@ -491,3 +491,24 @@ def test_dequant_apply_g_vs_library_two_tensors():
     for fmt in ("q8_0", "mxfp4", "fp8"):
         wf = _rand_weights(fmt, 8, 128, rng)
         assert np.array_equal(oracle.dequant(wf, apply_g=True), oracle.dequant(wf))
+
+
+def test_rel_fro_groups_equals_rel_fro_per_group():
+    """The vectorised per-group figure equals rel_fro over each group's
+    elements, NaN, inf, zero and tiny groups included."""
+    rng = np.random.default_rng(9)
+    n, G = 5000, 40
+    gi = rng.integers(0, G, n)
+    ref = rng.standard_normal(n) * 10.0 ** rng.integers(-150, 150, n)
+    y = ref * (1 + 1e-3 * rng.standard_normal(n))
+    ref[gi == 3] = 0.0
+    y[gi == 3] = 0.0
+    ref[gi == 4] = 0.0
+    y[(gi == 5)] = np.nan
+    y[(gi == 6)] = np.inf
+    gi[gi == 7] = 8                                  # group 7 empty
+    per = oracle.rel_fro_groups(y, ref, gi, G)
+    for g in range(G):
+        sel = gi == g
+        want = oracle.rel_fro(y[sel], ref[sel]) if sel.any() else math.nan
+        assert _same(per[g], want) or per[g] == pytest.approx(want, rel=1e-12), g
