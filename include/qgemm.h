@@ -229,6 +229,26 @@ size_t qgemm_workspace_bytes(const qgemm_plan *plan, int64_t B);
 int qgemm_run_ws(const qgemm_plan *plan, int64_t B, const void *w, const void *x, void *y,
                  void *workspace, size_t workspace_bytes, void *stream);
 
+/* qgemm_run_ws with the library's own scratch instead of a workspace, for
+ * callers that cannot allocate (code under graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): it calls no hipMalloc, hipFree or
+ * other allocating routine.  The scratch is one static device array of
+ * QGEMM_SCRATCH_BYTES per device (the first QGEMM_SCRATCH_COUNTER_BYTES hold
+ * counter words), held from the library's load until the process ends; it
+ * is set up by qgemm_init_device or by the first call on a device (which
+ * then also enqueues a small zeroing kernel on `stream` before its work).
+ * The call takes the same route, and gives bitwise the same result, as
+ * qgemm_run_ws with a workspace of qgemm_workspace_bytes(plan, B) bytes.  A
+ * call that needs more scratch than the array holds returns QGEMM_EINVAL
+ * (with the sizes in qgemm_last_error) and enqueues nothing.  Every call on
+ * a device shares that device's array and leaves its counters at zero:
+ * calls that may overlap in time on one device race (use one stream, or
+ * qgemm_run_ws with distinct workspaces). */
+#define QGEMM_SCRATCH_BYTES (64u << 20)
+#define QGEMM_SCRATCH_COUNTER_BYTES (1u << 20)
+int qgemm_run_noalloc(const qgemm_plan *plan, int64_t B, const void *w, const void *x, void *y,
+                      void *stream);
+
 /* The tier qgemm_run would use for B (QGEMM_TIER_*), or 0 for a bad plan. */
 int qgemm_plan_tier(const qgemm_plan *plan, int64_t B);
 

@@ -35,13 +35,15 @@ ALIGN = 256
 MAX_TENSORS = 60
 
 EXPORTS = ("qgemm_weight_bytes", "qgemm_pack", "qgemm_create", "qgemm_run", "qgemm_run_ws",
-           "qgemm_run_grouped",
+           "qgemm_run_noalloc", "qgemm_run_grouped",
            "qgemm_workspace_bytes", "qgemm_plan_tier", "qgemm_init_device", "qgemm_xcd_local",
            "qgemm_device_status",
            "qgemm_destroy", "qgemm_dequantize", "qgemm_strerror", "qgemm_last_error",
            "qgemm_version")
 DEV_XCD_MISMATCH = 0x1
 DEV_BAD_OFFSETS = 0x2
+SCRATCH_BYTES = 64 << 20          # QGEMM_SCRATCH_BYTES
+SCRATCH_COUNTER_BYTES = 1 << 20   # QGEMM_SCRATCH_COUNTER_BYTES
 
 _lib = None
 
@@ -73,6 +75,8 @@ def lib():
     L.qgemm_run.argtypes = [vp, i64, vp, vp, vp, vp]
     L.qgemm_run_ws.restype = i32
     L.qgemm_run_ws.argtypes = [vp, i64, vp, vp, vp, vp, sz, vp]
+    L.qgemm_run_noalloc.restype = i32
+    L.qgemm_run_noalloc.argtypes = [vp, i64, vp, vp, vp, vp]
     L.qgemm_run_grouped.restype = i32
     L.qgemm_run_grouped.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
     L.qgemm_workspace_bytes.restype = sz
@@ -271,6 +275,27 @@ class Plan:
             wsp, wsn = _dev_ptr(workspace, "workspace"), workspace.numel()
         _check(lib().qgemm_run_ws(self._h, B, _dev_ptr(w, "w"), _dev_ptr(x, "x"),
                                   _dev_ptr(y, "y"), wsp, wsn, _stream_ptr(stream)))
+        return y
+
+    def run_noalloc(self, x, w, y, stream=None, B: int | None = None):
+        """qgemm_run_noalloc: as run() with the library's static per-device
+        scratch instead of a workspace (no allocation anywhere in the call;
+        calls that overlap in time on one device race)."""
+        import torch
+
+        if B is None:
+            B = x.shape[0]
+        want_x = torch.float32 if self.act == "f32" else torch.bfloat16
+        want_y = torch.float32 if self.out == "f32" else torch.bfloat16
+        if x.dtype != want_x or y.dtype != want_y or w.dtype != torch.uint8:
+            raise TypeError("dtype mismatch: x %s, w %s, y %s" % (x.dtype, w.dtype, y.dtype))
+        if x.numel() < B * self.K or y.numel() < B * self.out_cols:
+            raise ValueError("x or y too small for B")
+        if w.numel() < weight_bytes(self.fmt, self.N, self.K):
+            raise ValueError("packed weight buffer too small")
+        init_device(x.device)
+        _check(lib().qgemm_run_noalloc(self._h, B, _dev_ptr(w, "w"), _dev_ptr(x, "x"),
+                                       _dev_ptr(y, "y"), _stream_ptr(stream)))
         return y
 
     def run_grouped(self, x, w_table, offsets, y, stream=None):

@@ -178,6 +178,24 @@ static __device__ uint32_t g_xcc_probe[XCC_PROBE_WGS];  // the probe's output, o
 // broken assumption at run time set a bit here; qgemm_device_status reads it.
 static __device__ uint32_t g_status;
 
+// Scratch of the allocation-free entry point (qgemm_run_noalloc), one array
+// per device for the life of the process: QGEMM_SCRATCH_COUNTER_BYTES of
+// counter words (zero between calls: each call re-arms those it used), then
+// the partial tiles and the rounded copy of x.  Counters of every plan sit in
+// the first region and data only in the second, so a call of one plan never
+// finds another plan's partial tiles in its counter words.  In host code
+// `scratch` is a stand-in, not a device address: kernels get the address
+// hipGetSymbolAddress returned for the current device (g_scratch_ptr).
+static __device__ __align__(256) uint8_t scratch[QGEMM_SCRATCH_BYTES];
+static std::atomic<uint8_t *> g_scratch_ptr[MAX_DEVICES];
+static std::mutex g_scratch_mu;
+
+__global__ void zero_words_kernel(uint32_t *p, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
 __global__ void xcc_probe_kernel(uint32_t *o)
 {
     // s_getreg of HW_REG_XCC_ID (id 20), bits [3:0]
@@ -213,6 +231,40 @@ static uint32_t *status_word(int dev)
     (void)hipThreadExchangeStreamCaptureMode(&mode);
     if (p)
         g_status_ptr[dev].store(p, std::memory_order_release);
+    return p;
+}
+
+// Device address of `scratch` on device dev, set up once: the address from
+// hipGetSymbolAddress (checked), and the counter region zeroed by a kernel
+// on `st` (stream-ordered before any use on st; graph-capturable, no memset).
+// sync: wait for the zeroing (the init call), else leave it queued.
+static uint8_t *scratch_setup(int dev, hipStream_t st, bool sync)
+{
+    if (dev < 0)
+        return nullptr;
+    uint8_t *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p)
+        return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p)
+        return p;
+    hipStreamCaptureMode mode = hipStreamCaptureModeRelaxed;
+    (void)hipThreadExchangeStreamCaptureMode(&mode);
+    hipError_t e = hipGetSymbolAddress((void **)&p, HIP_SYMBOL(scratch));
+    (void)hipThreadExchangeStreamCaptureMode(&mode);
+    if (e != hipSuccess || !p) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    hipLaunchKernelGGL(zero_words_kernel, dim3(256), dim3(256), 0, st, (uint32_t *)p,
+                       (int64_t)(QGEMM_SCRATCH_COUNTER_BYTES / 4));
+    e = hipGetLastError();
+    if (e == hipSuccess && sync)
+        e = hipStreamSynchronize(st);
+    if (e != hipSuccess)
+        return nullptr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
     return p;
 }
 
@@ -628,6 +680,18 @@ int qgemm_init_device(void)
         return fail(QGEMM_EHIP, "qgemm_init_device: no current HIP device");
     if (!status_word(dev))
         return fail(QGEMM_EHIP, "qgemm_init_device: device status word unavailable");
+    if (!g_scratch_ptr[dev].load()) {
+        hipStream_t st = nullptr;
+        hipStreamCaptureMode mode = hipStreamCaptureModeRelaxed;
+        (void)hipThreadExchangeStreamCaptureMode(&mode);
+        hipError_t e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+        uint8_t *sp = e == hipSuccess ? scratch_setup(dev, st, true) : nullptr;
+        if (st)
+            (void)hipStreamDestroy(st);
+        (void)hipThreadExchangeStreamCaptureMode(&mode);
+        if (!sp)
+            return fail(QGEMM_EHIP, "qgemm_init_device: static scratch unavailable");
+    }
     return probe_xcd_dispatch(dev);
 }
 
@@ -698,8 +762,12 @@ size_t qgemm_workspace_bytes(const qgemm_plan *plan, int64_t B)
     return (size_t)skinny_ws_bytes(plan->p, B);
 }
 
-int qgemm_run_ws(const qgemm_plan *plan, int64_t B, const void *w, const void *x, void *y,
-                 void *workspace, size_t ws_bytes, void *stream)
+}  // extern "C"
+
+namespace qg {
+
+// Checks shared by the run entry points.
+static int check_run(const qgemm_plan *plan, int64_t B, const void *w, const void *x, const void *y)
 {
     if (!plan || plan->magic != PLAN_MAGIC)
         return fail(QGEMM_EINVAL, "qgemm_run: not a live plan");
@@ -714,25 +782,37 @@ int qgemm_run_ws(const qgemm_plan *plan, int64_t B, const void *w, const void *x
         return fail(QGEMM_EINVAL, "qgemm_run: null pointer");
     if (!aligned16(w) || !aligned16(x) || !aligned16(y))
         return fail(QGEMM_EINVAL, "qgemm_run: w, x and y must be 16-byte aligned");
-    if (workspace && ((uintptr_t)workspace & 255u))
-        return fail(QGEMM_EINVAL, "qgemm_run: workspace must be 256-byte aligned");
     const int64_t ncols = p.epi == QGEMM_EPI_SWIGLU ? p.N / 2 : p.N;
     if (B * p.K > (1ll << 31) - 1 || B * ncols > (1ll << 31) - 1)
         return fail(QGEMM_EINVAL, "qgemm_run: B*K or B*N above 2^31 elements");
+    return QGEMM_OK;
+}
+
+// One call on arguments check_run accepted, with B > 0.  Scratch is two
+// regions: counter words at `cnt` (ws_data_off(p) bytes, zero between calls:
+// every call re-arms the ones it used) and partial tiles and the rounded
+// copy of x at `data` (data_bytes).  cnt == nullptr: no scratch at all, the
+// unsplit route.
+static int run_with(const qgemm_plan *plan, int64_t B, const void *w, const void *x, void *y,
+                    uint8_t *cnt, uint8_t *data, int64_t data_bytes, hipStream_t st)
+{
+    const Problem &p = plan->p;
+    if (!cnt)
+        data_bytes = -1;
     const KArgs a = make_args(p, B, w, x, y);
-    hipStream_t st = (hipStream_t)stream;
     hipError_t e;
     if (choose_tier(plan, B) == QGEMM_TIER_SKINNY) {
         if (p.epi == QGEMM_EPI_SWIGLU && !use_stream(p, B))
             return fail(QGEMM_ENOTSUP, "qgemm_run: the small-batch tier runs the fused gate+up epilogue "
                                        "for B <= %d only (B=%lld)", ST_MAX_B, (long long)B);
         const int nterm = p.math == QGEMM_MATH_BF16 ? 1 : p.kn.fp32_terms;
-        const bool split = workspace != nullptr && (size_t)skinny_ws_bytes(p, B) <= ws_bytes;
+        const int64_t need = skinny_ws_bytes(p, B);
+        const bool split = cnt != nullptr && (need == 0 || need - ws_data_off(p) <= data_bytes);
         if (use_stream(p, B)) {
             const StCfg c = stream_cfg(p, split);
             SkinnyWs ws;
-            ws.cnt = c.ksplit > 1 ? (uint32_t *)workspace : nullptr;
-            ws.part = c.ksplit > 1 ? (float *)((uint8_t *)workspace + c.cnt_bytes) : nullptr;
+            ws.cnt = c.ksplit > 1 ? (uint32_t *)cnt : nullptr;
+            ws.part = c.ksplit > 1 ? (float *)data : nullptr;
             ws.ksplit = c.ksplit;
             ws.kc = c.kc;
             ws.kch = c.KC;
@@ -745,14 +825,14 @@ int qgemm_run_ws(const qgemm_plan *plan, int64_t B, const void *w, const void *x
             return QGEMM_OK;
         }
         SkCfg c = skinny_cfg(p, B, split);
-        if (c.ksplit > 1 && (size_t)(c.cnt_bytes + c.part_bytes) > ws_bytes)
+        if (c.ksplit > 1 && c.part_bytes > data_bytes)
             c = skinny_cfg(p, B, false);  // workspace too small: no K split
         if (c.nby > 65535)
             return fail(QGEMM_EINVAL, "qgemm_run: B=%lld exceeds the small-batch tier's grid",
                         (long long)B);
         SkinnyWs ws;
-        ws.cnt = c.ksplit > 1 ? (uint32_t *)workspace : nullptr;
-        ws.part = c.ksplit > 1 ? (float *)((uint8_t *)workspace + c.cnt_bytes) : nullptr;
+        ws.cnt = c.ksplit > 1 ? (uint32_t *)cnt : nullptr;
+        ws.part = c.ksplit > 1 ? (float *)data : nullptr;
         ws.ksplit = c.ksplit;
         ws.kc = c.kc;
         ws.kch = c.kch;
@@ -761,19 +841,19 @@ int qgemm_run_ws(const qgemm_plan *plan, int64_t B, const void *w, const void *x
         ws.status = nullptr;
         e = launch_skinny(p, a, c, ws, nterm, st);
     } else {
-        TiCfg c = tiled_cfg(p, B, workspace != nullptr);
-        if (c.part_bytes && (size_t)(ws_data_off(p) + c.part_bytes) > ws_bytes)
+        TiCfg c = tiled_cfg(p, B, cnt != nullptr);
+        if (c.part_bytes && c.part_bytes > data_bytes)
             c = tiled_cfg(p, B, false);  // workspace too small: no K split
         if (c.part_bytes) {
-            c.sp.cnt = (uint32_t *)((uint8_t *)workspace + split_cnt_bytes(p));
-            c.sp.part = (float *)((uint8_t *)workspace + ws_data_off(p));
+            c.sp.cnt = (uint32_t *)(cnt + split_cnt_bytes(p));
+            c.sp.part = (float *)data;
         }
         // fp32 activations, bf16 math: with room after the partial tiles, x is
         // rounded to bf16 once into the workspace (the same rounding the
         // kernel applies when it stages fp32 rows) and the bf16 kernel runs
-        const int64_t xoff = ws_data_off(p) + round_up(c.part_bytes, 256), xcb = xconv_bytes(p, B);
-        if (workspace && xcb && (size_t)(xoff + xcb) <= ws_bytes) {
-            void *xb = (uint8_t *)workspace + xoff;
+        const int64_t xoff = round_up(c.part_bytes, 256), xcb = xconv_bytes(p, B);
+        if (cnt && xcb && xoff + xcb <= data_bytes) {
+            void *xb = data + xoff;
             e = launch_x_to_bf16((const float *)x, xb, B * p.K, st);
             if (e != hipSuccess)
                 return hip_fail(e, "qgemm_run: kernel launch");
@@ -789,6 +869,49 @@ int qgemm_run_ws(const qgemm_plan *plan, int64_t B, const void *w, const void *x
     if (e != hipSuccess)
         return hip_fail(e, "qgemm_run: kernel launch");
     return QGEMM_OK;
+}
+
+}  // namespace qg
+
+extern "C" {
+
+int qgemm_run_ws(const qgemm_plan *plan, int64_t B, const void *w, const void *x, void *y,
+                 void *workspace, size_t ws_bytes, void *stream)
+{
+    const int r = check_run(plan, B, w, x, y);
+    if (r != QGEMM_OK || B == 0)
+        return r;
+    if (workspace && ((uintptr_t)workspace & 255u))
+        return fail(QGEMM_EINVAL, "qgemm_run: workspace must be 256-byte aligned");
+    const int64_t off = ws_data_off(plan->p);
+    uint8_t *ws = (uint8_t *)workspace;
+    if (!ws || (int64_t)ws_bytes < off)
+        return run_with(plan, B, w, x, y, nullptr, nullptr, 0, (hipStream_t)stream);
+    return run_with(plan, B, w, x, y, ws, ws + off, (int64_t)ws_bytes - off, (hipStream_t)stream);
+}
+
+int qgemm_run_noalloc(const qgemm_plan *plan, int64_t B, const void *w, const void *x, void *y,
+                      void *stream)
+{
+    const int r = check_run(plan, B, w, x, y);
+    if (r != QGEMM_OK || B == 0)
+        return r;
+    const int64_t need = (int64_t)qgemm_workspace_bytes(plan, B);
+    const int64_t off = ws_data_off(plan->p);
+    if (need > 0 && (off > (int64_t)QGEMM_SCRATCH_COUNTER_BYTES ||
+                     need - off > (int64_t)(QGEMM_SCRATCH_BYTES - QGEMM_SCRATCH_COUNTER_BYTES)))
+        return fail(QGEMM_EINVAL,
+                    "qgemm_run_noalloc: this call needs %lld bytes of scratch (%lld of counters), above "
+                    "the static %lld (%lld); use qgemm_run_ws with a workspace or qgemm_run",
+                    (long long)need, (long long)off, (long long)QGEMM_SCRATCH_BYTES,
+                    (long long)QGEMM_SCRATCH_COUNTER_BYTES);
+    if (need == 0)
+        return run_with(plan, B, w, x, y, nullptr, nullptr, 0, (hipStream_t)stream);
+    uint8_t *sp = scratch_setup(current_device(), (hipStream_t)stream, false);
+    if (!sp)
+        return fail(QGEMM_EHIP, "qgemm_run_noalloc: static scratch unavailable on this device");
+    return run_with(plan, B, w, x, y, sp, sp + QGEMM_SCRATCH_COUNTER_BYTES,
+                    (int64_t)(QGEMM_SCRATCH_BYTES - QGEMM_SCRATCH_COUNTER_BYTES), (hipStream_t)stream);
 }
 
 int qgemm_run_grouped(const qgemm_plan *plan, int64_t E, int64_t T, const void *const *w_table,
