@@ -7,12 +7,16 @@ weight-stream GB/s = packed weight bytes per call / time per call.  One step
 is one qgemm_run.  The packed weights rotate over enough copies (> 1 GiB in
 total) that every call streams them from HBM, not from the 256 MB Infinity
 Cache.  Steps are replayed from a HIP graph so host launch cost is not timed.
+value is the median of 7 timed loops of at least max(--steps, 200) calls.
+The same loop over a plain read kernel of the same bytes gives the achieved
+bandwidth ceiling (roofline.ceiling_GBs, frac_of_ceiling), and the same call
+without a workspace (qgemm_run's unsplit route) is timed too.
 
 Extra keys carry the rest of the B sweep of that shape and the prefill
 workloads (Q8_0 FFN B = 2048, MXFP4 down projection, NVFP4 fused gate+up at
 B = 1 and 16 as well as 2048, FP8-weight attention projection, routed-expert
-fused gate+up),
-plus the roofline of the dominant kernel and the CPU oracle baseline.
+fused gate+up), the matrix-core roofline of the B = 2048 workloads
+(roofline_mfma), and the CPU oracle baseline on all cores and on one.
 
     python bench.py [--steps K] [--warmup W] [--headline-only] [--no-cpu-baseline]
 """
@@ -56,6 +60,72 @@ def log(msg):
 
 # GPU work run untimed before each timed loop (the clock's ramp after host-side set-up)
 WARM_MS = 20.0
+TRIALS = 7            # timed loops of the headline; value is their median
+MIN_LAUNCHES = 200    # calls per timed loop, at least
+
+
+class GraphTimer:
+    """Launches replayed from one HIP graph on a stream of their own, timed
+    with HIP events recorded on that stream.  `launches` is a list of
+    closures, each enqueueing one call on the current stream; the graph
+    holds them all (one per weight copy)."""
+
+    def __init__(self, launches, eager_first=1):
+        import torch
+
+        self.n = len(launches)
+        self.stream = torch.cuda.Stream()
+        self.untimed = 0
+        with torch.cuda.stream(self.stream):
+            for i in range(max(eager_first, self.n)):
+                launches[i % self.n]()
+        self.untimed += max(eager_first, self.n)
+        self.stream.synchronize()
+        self.g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.g, stream=self.stream):
+            for f in launches:
+                f()
+        self.warm()
+
+    def warm(self, warm_ms=WARM_MS):
+        """Untimed replays until about warm_ms of GPU work has run: the timed
+        loops then see the steady clock, not the ramp after host set-up."""
+        import torch
+
+        w0 = torch.cuda.Event(enable_timing=True)
+        w1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(self.stream):
+            w0.record(self.stream)
+            self.g.replay()
+            w1.record(self.stream)
+        w1.synchronize()
+        more = max(0, min(math.ceil(warm_ms / max(w0.elapsed_time(w1), 1e-3)) - 1, 100000))
+        with torch.cuda.stream(self.stream):
+            for _ in range(more):
+                self.g.replay()
+        self.stream.synchronize()
+        self.untimed += self.n * (1 + more)
+
+    def timed(self, launches):
+        """ms per call over at least `launches` calls (whole replays)."""
+        import torch
+
+        reps = max(1, math.ceil(launches / self.n))
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(self.stream):
+            start.record(self.stream)
+            for _ in range(reps):
+                self.g.replay()
+            end.record(self.stream)
+        end.synchronize()
+        return start.elapsed_time(end) / (reps * self.n), reps * self.n
+
+    def trials(self, ntrials, launches):
+        """Per-call ms of `ntrials` timed loops (sorted) and calls per loop."""
+        out = [self.timed(launches) for _ in range(ntrials)]
+        return sorted(t for t, _ in out), out[0][1]
 
 
 class Workload:
@@ -91,33 +161,27 @@ class Workload:
         log(f"[bench] {name} B={B} copies={copies} ready in {time.time() - t0:.1f}s "
             f"tier={self.plan.tier(B)}")
 
-    def flops(self):
-        return 2.0 * self.B * self.N * self.K
+    def launches(self, workspace="auto"):
+        return [(lambda w=w: self.plan.run(self.x, w, self.y, workspace=workspace)) for w in self.ws]
 
-    def io_bytes(self):
-        xb = self.x.numel() * self.x.element_size()
-        yb = self.y.numel() * self.y.element_size()
-        return self.wbytes + xb + yb
+    def timer(self, warmup=1, workspace="auto"):
+        t = GraphTimer(self.launches(workspace), eager_first=warmup)
+        self.untimed_calls = t.untimed
+        return t
 
-    def time_ms(self, steps, warmup, eager=False, warm_ms=WARM_MS):
-        """Average ms per call over `steps` calls replayed from a HIP graph
-        holding one call per weight copy (or launched one by one when
-        `eager`), bracketed by events on the stream the calls run on.  Before
-        the timed calls: `warmup` (at least one per weight copy) eager calls,
-        then untimed replays until about `warm_ms` of GPU work has run, so the
-        timed calls see the steady clock rather than the ramp after the host
-        set the workload up (`self.untimed_calls` counts them all)."""
+    def time_ms(self, steps, warmup, eager=False):
+        """ms per call over at least `steps` calls (whole replays of the
+        graph holding one call per weight copy, or eager launches)."""
         import torch
 
-        n = len(self.ws)
-        reps = max(1, math.ceil(steps / n))
-        stream = torch.cuda.Stream()
-        self.untimed_calls = max(warmup, n)
-        with torch.cuda.stream(stream):
-            for i in range(max(warmup, n)):
-                self.plan.run(self.x, self.ws[i % n], self.y)
-        stream.synchronize()
         if eager:
+            n = len(self.ws)
+            reps = max(1, math.ceil(steps / n))
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                for i in range(max(warmup, n)):
+                    self.plan.run(self.x, self.ws[i % n], self.y)
+            stream.synchronize()
             start = torch.cuda.Event(enable_timing=True)
             end = torch.cuda.Event(enable_timing=True)
             with torch.cuda.stream(stream):
@@ -126,38 +190,32 @@ class Workload:
                     self.plan.run(self.x, self.ws[i % n], self.y)
                 end.record(stream)
             end.synchronize()
+            self.untimed_calls = max(warmup, n)
             return start.elapsed_time(end) / (reps * n), reps * n
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for i in range(n):
-                self.plan.run(self.x, self.ws[i], self.y)
-        w0 = torch.cuda.Event(enable_timing=True)
-        w1 = torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(stream):
-            w0.record(stream)
-            g.replay()
-            w1.record(stream)
-        w1.synchronize()
-        more = math.ceil(warm_ms / max(w0.elapsed_time(w1), 1e-3)) - 1
-        with torch.cuda.stream(stream):
-            for _ in range(max(0, min(more, 100000))):
-                g.replay()
-        stream.synchronize()
-        self.untimed_calls += n * (1 + max(0, min(more, 100000)))
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        with torch.cuda.stream(stream):  # replays and events on one stream
-            start.record(stream)
-            for _ in range(reps):
-                g.replay()
-            end.record(stream)
-        end.synchronize()
-        torch.cuda.synchronize()
-        return start.elapsed_time(end) / (reps * n), reps * n
+        return self.timer(warmup).timed(steps)
+
+    def flops(self):
+        return 2.0 * self.B * self.N * self.K
+
+    def io_bytes(self):
+        xb = self.x.numel() * self.x.element_size()
+        yb = self.y.numel() * self.y.element_size()
+        return self.wbytes + xb + yb
 
     def free(self):
         self.ws = self.x = self.y = None
+
+
+def read_ceiling(wl, ntrials, launches):
+    """The plain read kernel over the same packed weight copies in the same
+    rotation (one launch per copy): per-call ms of each trial."""
+    import torch
+
+    import prefill_q8_mxfp4_amd as q
+
+    sink = torch.zeros(2048, dtype=torch.int32, device="cuda:0")
+    t = GraphTimer([(lambda w=w: q.read_bytes(w, sink)) for w in wl.ws])
+    return t.trials(ntrials, launches)
 
 
 def copies_for(wbytes):
@@ -174,9 +232,20 @@ def traffic_record(sha):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, budget_s=10.0):
-    """The fp64 oracle on the host cores, on whole headline calls repeated
-    until about `budget_s` seconds have passed (at least one call)."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, budget_s=10.0, one_thread_calls=1):
+    """The fp64 oracle on the host: whole headline calls on all the cores it
+    uses, repeated until about `budget_s` seconds have passed, then
+    `one_thread_calls` whole calls on one thread."""
     import oracle
 
     calls, t0 = 0, time.time()
@@ -187,10 +256,22 @@ def cpu_baseline(wl, budget_s=10.0):
         if dt >= budget_s or dt / calls * (calls + 1) > 3 * budget_s:
             break
     per = dt / calls
-    return {"value": round(wl.wbytes / per / 1e9, 6), "unit": "GB/s", "cores": oracle.threads(),
+    cores = oracle.threads()
+    oracle.set_threads(1)
+    try:
+        t1 = time.time()
+        for _ in range(one_thread_calls):
+            oracle.gemm(wl.w_logical, wl.x_host)
+        per1 = (time.time() - t1) / one_thread_calls
+    finally:
+        oracle.set_threads(cores)
+    return {"value": round(wl.wbytes / per / 1e9, 6), "unit": "GB/s", "cores": cores,
             "kind": "oracle", "seconds_per_call": round(per, 3),
-            "sample": f"{calls} whole headline call(s) of the fp64 oracle: q8_0 K=N=5120, "
-                      f"B={wl.B}, fp32 activations"}
+            "one_thread": {"value": round(wl.wbytes / per1 / 1e9, 6), "unit": "GB/s", "cores": 1,
+                           "seconds_per_call": round(per1, 3), "calls": one_thread_calls},
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "sample": f"{calls} whole headline call(s) of the fp64 oracle on {cores} threads, then "
+                      f"{one_thread_calls} on one thread: q8_0 K=N=5120, B={wl.B}, fp32 activations"}
 
 
 def copy_calibration(mib=512, reps=5):
@@ -308,21 +389,38 @@ def main():
         log(f"[bench] {args.steps} calls of {args.calls_of[0]} B={args.calls_of[1]} done")
         return
 
-    # ---- headline: q8_0 5120x5120, B = 16, fp32 activations
+    # ---- headline: q8_0 5120x5120, B = 16, fp32 activations.  value is the
+    # median of TRIALS timed loops of at least max(--steps, MIN_LAUNCHES)
+    # graph-replayed calls each (whole rotations of the weight copies).
     B = 16
     probe = q.weight_bytes("q8_0", 5120, 5120)
     wl = Workload("q8_0_5120x5120", B, copies=copies_for(probe))
-    ms, steps_done = wl.time_ms(args.steps, args.warmup, eager=args.eager)
+    launches = max(args.steps, MIN_LAUNCHES)
+    if args.eager:
+        per = sorted(wl.time_ms(launches, args.warmup, eager=True)[0] for _ in range(TRIALS))
+        steps_done = math.ceil(launches / len(wl.ws)) * len(wl.ws)
+    else:
+        timer = wl.timer(args.warmup)
+        per, steps_done = timer.trials(TRIALS, launches)
+    ms = per[TRIALS // 2]
+    untimed = wl.untimed_calls
     value = wl.wbytes / (ms * 1e-3) / 1e9
     achieved = wl.io_bytes() / (ms * 1e-3) / 1e9
+    # the plain read of the same bytes in the same rotation: the achieved ceiling
+    rc, _ = read_ceiling(wl, TRIALS, launches)
+    ceil_ms = rc[TRIALS // 2]
+    ceiling = wl.wbytes / (ceil_ms * 1e-3) / 1e9
+    # the same call without a workspace (qgemm_run: the unsplit route)
+    nws, _ = GraphTimer(wl.launches(workspace=None)).trials(3, launches)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": steps_done,
+        "trials": TRIALS,
         "warmup": args.warmup,
-        "untimed_calls": wl.untimed_calls,
+        "untimed_calls": untimed,
         "ms_per_step": round(ms, 6),
         "higher_is_better": True,
         "scaling": "weak",
@@ -336,13 +434,22 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_record(sha), "algorithmic_bytes": wl.io_bytes(),
+                     "ceiling_GBs": round(ceiling, 1),
+                     "frac_of_ceiling": round(value / ceiling, 4),
+                     "ceiling_kernel": "read_bytes_kernel (plain 16-byte-load read of the same "
+                                       "packed weight copies, same rotation)",
                      "kernel_src_sha": sha},
+        "headline_trials_us": {"n": TRIALS, "calls_per_trial": steps_done,
+                               "min": round(per[0] * 1e3, 3), "median": round(ms * 1e3, 3),
+                               "max": round(per[-1] * 1e3, 3)},
+        "read_ceiling_trials_us": {"n": TRIALS, "min": round(rc[0] * 1e3, 3),
+                                   "median": round(ceil_ms * 1e3, 3), "max": round(rc[-1] * 1e3, 3)},
+        "headline_no_workspace": {"us": round(nws[1] * 1e3, 3),
+                                  "weight_GBs": round(wl.wbytes / (nws[1] * 1e-3) / 1e9, 1),
+                                  "route": "qgemm_run without a workspace (no K split)"},
     }
-    log(f"[bench] headline {ms * 1e3:.2f} us/call  {value:.1f} GB/s weights")
-    # spread: 7 more trials of the same loop (the value above stays the timed K steps)
-    trials = sorted(wl.time_ms(max(50, args.steps // 8), 0, eager=args.eager)[0] * 1e3 for _ in range(7))
-    line["headline_trials_us"] = {"n": 7, "min": round(trials[0], 3), "median": round(trials[3], 3),
-                                  "max": round(trials[-1], 3)}
+    log(f"[bench] headline {ms * 1e3:.2f} us/call  {value:.1f} GB/s weights; plain read "
+        f"{ceil_ms * 1e3:.2f} us ({ceiling:.0f} GB/s); no workspace {nws[1] * 1e3:.2f} us")
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl)
@@ -352,7 +459,7 @@ def main():
         sweep = {}
         for b in (1, 4, 8, 16, 64, 65, 70, 76, 256):
             w = Workload("q8_0_5120x5120", b, copies=copies_for(probe) if b <= 16 else 4)
-            t, _ = w.time_ms(max(40, args.steps // 4), 5)
+            t, _ = w.time_ms(max(80, args.steps // 2), 5)
             sweep[str(b)] = {"us": round(t * 1e3, 2),
                              "weight_GBs": round(w.wbytes / (t * 1e-3) / 1e9, 1),
                              "hbm_frac": round(w.io_bytes() / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -369,7 +476,7 @@ def main():
                 # several calls per graph replay (distinct weight copies) so the
                 # replay overhead is spread as in the B sweep
                 w = Workload(name, b, copies=copies_for(nb) if b <= 16 else 4)
-                t, _ = w.time_ms(max(20, args.steps // 10) if b > 16 else max(40, args.steps // 4),
+                t, _ = w.time_ms(max(20, args.steps // 10) if b > 16 else max(80, args.steps // 2),
                                  3)
                 c = w.c
                 key = f"{name}:B={b}"
@@ -383,6 +490,16 @@ def main():
                 w.free()
                 torch.cuda.empty_cache()
         line["prefill"] = pre
+        # the matrix-core side of the metric: every B = 2048 workload against
+        # the dense bf16 peak (the largest, NVFP4 fused gate+up, as the object)
+        big = {k: v for k, v in pre.items() if k.endswith(":B=2048")}
+        key = "nvfp4_gate_up_34816x5120:B=2048"
+        if key in big:
+            r = big[key]
+            line["roofline_mfma"] = {"bound": "mfma", "achieved": r["TFLOPs"], "peak": BF16_PEAK_TFLOPS,
+                                     "unit": "TFLOP/s", "frac": r["mfma_frac"], "traffic": None,
+                                     "workload": key, "dtype": "bf16",
+                                     "all_B2048": {k: v["mfma_frac"] for k, v in big.items()}}
         line["routed_moe:nvfp4:512x(2x512)x2048:top10:tokens2048"] = bench_moe(args.steps)
 
     print(json.dumps(line), flush=True)

@@ -296,6 +296,14 @@ int qgemm_destroy(qgemm_plan *plan);
 int qgemm_dequantize(qgemm_format fmt, const void *w, float *w_out, int64_t N, int64_t K,
                      void *stream);
 
+/* Measurement aid, not part of the GEMM: read `bytes` (a positive multiple
+ * of 16) of device memory at buf (16-byte aligned) once, with the 16-byte
+ * loads the streaming kernel uses, over `wgs` workgroups of 256 threads
+ * (0 = 2048), and write one XOR-folded word per workgroup to sink (device,
+ * wgs words) so the loads are kept.  The plain read rate of the same bytes
+ * is the achieved-bandwidth ceiling the weight stream is compared with. */
+int qgemm_read_bytes(const void *buf, size_t bytes, uint32_t *sink, int wgs, void *stream);
+
 /* Text for a status code (static storage). */
 const char *qgemm_strerror(int status);
 

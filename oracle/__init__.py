@@ -67,6 +67,8 @@ def _load():
             f.argtypes = [arg]
         lib.oracle_threads.restype = i32
         lib.oracle_threads.argtypes = []
+        lib.oracle_set_threads.restype = None
+        lib.oracle_set_threads.argtypes = [i32]
         lib.oracle_dequant.restype = None
         lib.oracle_dequant.argtypes = [i32, vp, vp, vp, i64, i32, i64, i64, vp]
         lib.oracle_gemm.restype = None
@@ -128,6 +130,12 @@ def e4m3(b):
 def threads() -> int:
     """Threads the oracle's parallel loops use."""
     return int(_load().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads the oracle's parallel loops use from now on (timing only:
+    every output is one sequential sum, whatever the thread count)."""
+    _load().oracle_set_threads(int(n))
 
 
 def silu(t):

@@ -230,6 +230,14 @@ int oracle_threads(void)
     return n;
 }
 
+/* Threads the parallel loops use from now on (n >= 1); for the timing of
+ * the benchmark's one-thread baseline.  Results do not depend on it: every
+ * output is one sequential sum. */
+void oracle_set_threads(int n)
+{
+    omp_set_num_threads(n > 0 ? n : 1);
+}
+
 double oracle_silu(double t)
 {
     return t / (1.0 + exp(-t));

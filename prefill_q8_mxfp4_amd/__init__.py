@@ -38,7 +38,7 @@ EXPORTS = ("qgemm_weight_bytes", "qgemm_pack", "qgemm_create", "qgemm_run", "qge
            "qgemm_run_noalloc", "qgemm_run_grouped",
            "qgemm_workspace_bytes", "qgemm_plan_tier", "qgemm_init_device", "qgemm_xcd_local",
            "qgemm_device_status",
-           "qgemm_destroy", "qgemm_dequantize", "qgemm_strerror", "qgemm_last_error",
+           "qgemm_destroy", "qgemm_dequantize", "qgemm_read_bytes", "qgemm_strerror", "qgemm_last_error",
            "qgemm_version")
 DEV_XCD_MISMATCH = 0x1
 DEV_BAD_OFFSETS = 0x2
@@ -87,6 +87,8 @@ def lib():
     L.qgemm_destroy.argtypes = [vp]
     L.qgemm_dequantize.restype = i32
     L.qgemm_dequantize.argtypes = [i32, vp, vp, i64, i64, vp]
+    L.qgemm_read_bytes.restype = i32
+    L.qgemm_read_bytes.argtypes = [vp, sz, vp, i32, vp]
     L.qgemm_strerror.restype = ctypes.c_char_p
     L.qgemm_strerror.argtypes = [i32]
     L.qgemm_last_error.restype = ctypes.c_char_p
@@ -341,6 +343,17 @@ def dequantize(fmt: str, w, N: int, K: int, stream=None):
     _check(lib().qgemm_dequantize(FORMATS[fmt], _dev_ptr(w, "w"), _dev_ptr(out, "out"), N, K,
                                   _stream_ptr(stream)))
     return out
+
+
+def read_bytes(buf, sink, wgs: int = 0, nbytes: int | None = None, stream=None):
+    """qgemm_read_bytes: a plain 16-byte-load read of a device buffer (the
+    achieved-bandwidth ceiling of the weight stream); sink: int32 tensor of
+    at least wgs (default 2048) elements on the same device."""
+    n = buf.numel() * buf.element_size() if nbytes is None else nbytes
+    if sink.numel() < (wgs or 2048):
+        raise ValueError("sink too small")
+    _check(lib().qgemm_read_bytes(_dev_ptr(buf, "buf"), n, _dev_ptr(sink, "sink"), wgs,
+                                  _stream_ptr(stream)))
 
 
 def xcd_local() -> int:

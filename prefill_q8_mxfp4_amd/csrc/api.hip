@@ -963,6 +963,18 @@ int qgemm_run(const qgemm_plan *plan, int64_t B, const void *w, const void *x, v
     return qgemm_run_ws(plan, B, w, x, y, nullptr, 0, stream);
 }
 
+int qgemm_read_bytes(const void *buf, size_t bytes, uint32_t *sink, int wgs, void *stream)
+{
+    if (!buf || !sink || !aligned16(buf) || (bytes & 15u) || bytes == 0)
+        return fail(QGEMM_EINVAL, "qgemm_read_bytes: null, misaligned or empty buffer, or bytes %% 16");
+    if (wgs < 0 || wgs > (1 << 20))
+        return fail(QGEMM_EINVAL, "qgemm_read_bytes: wgs outside 0..2^20");
+    const hipError_t e = launch_read_bytes(buf, (int64_t)bytes, sink, wgs ? wgs : 2048, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "qgemm_read_bytes: kernel launch");
+    return QGEMM_OK;
+}
+
 int qgemm_dequantize(qgemm_format fmt, const void *w, float *w_out, int64_t N, int64_t K, void *stream)
 {
     Layout L;

@@ -458,5 +458,6 @@ hipError_t launch_grouped(const Problem &p, const KArgs &a, const Groups &g, int
 hipError_t launch_grouped_fp32(const Problem &p, const KArgs &a, const Groups &g, int BM, int64_t tiles,
                                hipStream_t st);
 hipError_t launch_dequant(int fmt, const KArgs &a, float *out, hipStream_t st);
+hipError_t launch_read_bytes(const void *buf, int64_t bytes, uint32_t *sink, int wgs, hipStream_t st);
 
 }  // namespace qg

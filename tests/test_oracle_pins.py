@@ -512,3 +512,19 @@ def test_rel_fro_groups_equals_rel_fro_per_group():
         sel = gi == g
         want = oracle.rel_fro(y[sel], ref[sel]) if sel.any() else math.nan
         assert _same(per[g], want) or per[g] == pytest.approx(want, rel=1e-12), g
+
+
+def test_thread_count_does_not_change_results():
+    """The one-thread timing leg computes the same outputs as all cores."""
+    rng = np.random.default_rng(13)
+    w = _rand_weights("q8_0", 64, 256, rng)
+    x = _rand_x("f32", 5, 256, rng)
+    n0 = oracle.threads()
+    full = oracle.gemm(w, x)
+    oracle.set_threads(1)
+    try:
+        assert oracle.threads() == 1
+        assert np.array_equal(oracle.gemm(w, x), full)
+    finally:
+        oracle.set_threads(n0)
+    assert oracle.threads() == n0
