@@ -356,6 +356,9 @@ def main():
                     help="launch calls one by one instead of replaying a HIP graph (profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 512 MiB copy (scales profiler byte counters)")
+    ap.add_argument("--profile-headline", action="store_true",
+                    help="time only the headline GEMM loop (no read ceiling, no no-workspace "
+                         "route, no CPU baseline): the program under the kernel-trace profile")
     ap.add_argument("--calls-of", nargs=2, metavar=("CONFIG", "B"),
                     help="only launch CONFIG at batch B eagerly --steps times, print nothing "
                          "else (a short program for counter passes)")
@@ -406,6 +409,11 @@ def main():
     untimed = wl.untimed_calls
     value = wl.wbytes / (ms * 1e-3) / 1e9
     achieved = wl.io_bytes() / (ms * 1e-3) / 1e9
+    if args.profile_headline:
+        print(json.dumps({"profile_headline_us": round(ms * 1e3, 3), "calls_per_trial": steps_done,
+                          "trials": TRIALS, "untimed_calls": untimed,
+                          "weight_GBs": round(value, 2), "kernel_src_sha": sha}), flush=True)
+        return
     # the plain read of the same bytes in the same rotation: the achieved ceiling
     rc, _ = read_ceiling(wl, TRIALS, launches)
     ceil_ms = rc[TRIALS // 2]

@@ -102,12 +102,20 @@ typedef enum qgemm_math {
 typedef enum qgemm_tier {
     QGEMM_TIER_SKINNY = 1, /* weights streamed once per 16..64 batch rows straight
                               into matrix-core operands; for small B */
-    QGEMM_TIER_TILED = 2   /* batch x weight tiles staged through LDS; for large B
+    QGEMM_TIER_TILED = 2,  /* batch x weight tiles staged through LDS; for large B
                               (B > 32 with bf16 math, B > 16 with fp32 math) */
+    QGEMM_TIER_GEMV = 3    /* B = 1, 2: one workgroup per 16-row tile over all of
+                              K, fp32 FMA on the vector ALUs, a fixed-order
+                              cross-lane sum; no K split and no workspace.  Only
+                              when forced (measured slower than the skinny tier's
+                              streaming kernel on MI355X); it needs the B
+                              activation rows, as fp32, to fit in 72 KB of LDS,
+                              and returns QGEMM_ENOTSUP for other calls */
 } qgemm_tier;
 
 #define QGEMM_FLAG_FORCE_SKINNY 0x1u
 #define QGEMM_FLAG_FORCE_TILED 0x2u
+#define QGEMM_FLAG_FORCE_GEMV 0x4u
 
 /* ---------------------------------------------------------------- layout
  * The packed device buffer that qgemm_pack writes and every kernel reads.
@@ -161,7 +169,7 @@ typedef struct qgemm_plan qgemm_plan;
  * dtype; math: see qgemm_math (QGEMM_MATH_FP32 needs act = QGEMM_F32; the
  * SwiGLU epilogue needs QGEMM_MATH_BF16, else QGEMM_ENOTSUP); flags:
  * 0 or one QGEMM_FLAG_FORCE_* bit (also settable with the environment
- * variable QGEMM_FORCE_TIER=skinny|tiled).  Host-only: allocates the small
+ * variable QGEMM_FORCE_TIER=skinny|tiled|gemv).  Host-only: allocates the small
  * plan object, makes no HIP call and works without a device.  Tuning
  * overrides in the environment (QGEMM_ST_*, QGEMM_SK_*, QGEMM_TI_*) are read
  * here, once.  *plan receives the handle. */

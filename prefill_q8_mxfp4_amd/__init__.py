@@ -28,9 +28,10 @@ FORMATS = {"q8_0": 0, "mxfp4": 1, "nvfp4": 2, "fp8": 3}
 DTYPES = {"f32": 0, "bf16": 1}
 EPILOGUES = {"none": 0, "swiglu": 1}
 MATHS = {"fp32": 0, "bf16": 1}
-TIERS = {1: "skinny", 2: "tiled"}
+TIERS = {1: "skinny", 2: "tiled", 3: "gemv"}
 FLAG_FORCE_SKINNY = 0x1
 FLAG_FORCE_TILED = 0x2
+FLAG_FORCE_GEMV = 0x4
 ALIGN = 256
 MAX_TENSORS = 60
 
@@ -209,6 +210,8 @@ class Plan:
             flags = FLAG_FORCE_SKINNY
         elif tier == "tiled":
             flags = FLAG_FORCE_TILED
+        elif tier == "gemv":
+            flags = FLAG_FORCE_GEMV
         elif tier is not None:
             raise ValueError(tier)
         self.fmt, self.N, self.K, self.act, self.out, self.epilogue, self.math = (

@@ -43,6 +43,8 @@ static void read_knobs(Knobs *k)
 {
     k->st_waves = env_int("QGEMM_ST_WAVES", 0);
     k->st_nph = env_int("QGEMM_ST_NPH", 0);
+    k->st_depth = env_int("QGEMM_ST_DEPTH", 0);
+    k->gv_maxb = env_int("QGEMM_GV_MAXB", -1);
     k->sk_stream = env_int("QGEMM_SK_STREAM", 1);
     k->sk_nt = env_int("QGEMM_SK_NT", 2);
     k->ti_bm = env_int("QGEMM_TI_BM", 0);
@@ -155,6 +157,30 @@ static int64_t ws_data_off(const Problem &p)
 static bool use_stream(const Problem &p, int64_t B)
 {
     return B <= ST_MAX_B && p.kn.sk_stream != 0;
+}
+
+// The GEMV kernel takes B = 1 and 2 when its activation rows fit in LDS
+// with room for two workgroups per CU (one workgroup per row tile, so a grid
+// above 256 tiles needs them resident two at a time).
+static const int GV_MAX_B = 2;
+static const int64_t GV_LDS_MAX = 72 * 1024;
+
+static bool gemv_fits(const Problem &p, int64_t B)
+{
+    return B <= GV_MAX_B && gemv_lds_bytes(p, B) <= GV_LDS_MAX;
+}
+
+// Automatic choice: off.  Measured on the box against the MFMA streaming
+// kernel (NT loads, pipelined): Q8_0 5120^2 B = 1 10.8 vs 10.2 us, B = 2
+// 14.2 vs 10.3; MXFP4 5120x17408 B = 1 22.0 vs 13.9; NVFP4 gate+up B = 1
+// 35.0 vs 28.9 (one workgroup per 16-row tile leaves 64 of 256 CUs with two
+// tiles at N = 5120, and fp32 FMAs make the FP4 formats VALU-bound).  The
+// tier stays available by force (QGEMM_FLAG_FORCE_GEMV) and QGEMM_GV_MAXB=1|2
+// turns the automatic choice on for measurements.
+static bool use_gemv(const Problem &p, int64_t B)
+{
+    const int maxb = p.kn.gv_maxb > 0 ? (p.kn.gv_maxb < GV_MAX_B ? p.kn.gv_maxb : GV_MAX_B) : 0;
+    return B <= maxb && gemv_fits(p, B);
 }
 
 // XCD dispatch probe.  The streaming kernel's XCD-local split exchange
@@ -330,6 +356,11 @@ static StCfg stream_cfg(const Problem &p, bool split)
     c.NPH = sh.NPH;
     c.Nh = p.epi == QGEMM_EPI_SWIGLU ? (int)(p.N / 2) : 0;
     c.KC = sh.W * sh.NPH;
+    // weight items a wave keeps in flight, fastest on the box per format:
+    // Q8_0 4, MXFP4 and FP8 3 (MXFP4 down projection B = 1: 16.6 -> 13.9 us
+    // against all at once), NVFP4 all at once (16)
+    c.depth = p.kn.st_depth ? p.kn.st_depth
+            : p.fmt == FMT_Q8 ? 4 : (p.fmt == FMT_MX || p.fmt == FMT_FP8) ? 3 : 16;
     c.kc = split ? c.KC : (S + c.KC - 1) / c.KC * c.KC;
     c.ksplit = (S + c.kc - 1) / c.kc;
     c.ngroups = (int)((p.L.RT + 7) / 8);
@@ -478,6 +509,8 @@ static int choose_tier(const qgemm_plan *plan, int64_t B)
     const Problem &p = plan->p;
     if (plan->forced_tier)
         return plan->forced_tier;
+    if (use_gemv(p, B))  // B = 1, 2: the GEMV kernel (no K split, no workspace)
+        return QGEMM_TIER_GEMV;
     if (p.math == QGEMM_MATH_FP32)  // the streaming kernel, else the faithful tiled variant
         return B <= ST_MAX_B ? QGEMM_TIER_SKINNY : QGEMM_TIER_TILED;
     if (p.epi == QGEMM_EPI_SWIGLU)  // fused gate+up: the streaming kernel or the tiled tier
@@ -643,17 +676,21 @@ int qgemm_create(qgemm_plan **plan, qgemm_format fmt, qgemm_dtype act, qgemm_dty
     if (math == QGEMM_MATH_FP32 && epi == QGEMM_EPI_SWIGLU)
         return fail(QGEMM_ENOTSUP, "qgemm_create: the fused gate+up epilogue computes in bf16 "
                                    "(QGEMM_MATH_BF16)");
-    if ((flags & ~(QGEMM_FLAG_FORCE_SKINNY | QGEMM_FLAG_FORCE_TILED)) ||
-        ((flags & QGEMM_FLAG_FORCE_SKINNY) && (flags & QGEMM_FLAG_FORCE_TILED)))
+    const uint32_t force = flags & (QGEMM_FLAG_FORCE_SKINNY | QGEMM_FLAG_FORCE_TILED | QGEMM_FLAG_FORCE_GEMV);
+    if ((flags & ~(QGEMM_FLAG_FORCE_SKINNY | QGEMM_FLAG_FORCE_TILED | QGEMM_FLAG_FORCE_GEMV)) ||
+        (force & (force - 1)))
         return fail(QGEMM_EINVAL, "qgemm_create: bad flags 0x%x", flags);
     int forced = (flags & QGEMM_FLAG_FORCE_SKINNY) ? QGEMM_TIER_SKINNY
-               : (flags & QGEMM_FLAG_FORCE_TILED) ? QGEMM_TIER_TILED : 0;
+               : (flags & QGEMM_FLAG_FORCE_TILED) ? QGEMM_TIER_TILED
+               : (flags & QGEMM_FLAG_FORCE_GEMV) ? QGEMM_TIER_GEMV : 0;
     if (!forced) {
         const char *e = getenv("QGEMM_FORCE_TIER");
         if (e && !strcmp(e, "skinny"))
             forced = QGEMM_TIER_SKINNY;
         else if (e && !strcmp(e, "tiled"))
             forced = QGEMM_TIER_TILED;
+        else if (e && !strcmp(e, "gemv"))
+            forced = QGEMM_TIER_GEMV;
     }
     qgemm_plan *p = new (std::nothrow) qgemm_plan;
     if (!p)
@@ -754,7 +791,10 @@ size_t qgemm_workspace_bytes(const qgemm_plan *plan, int64_t B)
 {
     if (!plan || plan->magic != PLAN_MAGIC || B <= 0 || B > (1ll << 30))
         return 0;
-    if (choose_tier(plan, B) != QGEMM_TIER_SKINNY) {
+    const int tier = choose_tier(plan, B);
+    if (tier == QGEMM_TIER_GEMV)
+        return 0;
+    if (tier != QGEMM_TIER_SKINNY) {
         const TiCfg c = tiled_cfg(plan->p, B, true);
         const int64_t extra = round_up(c.part_bytes, 256) + xconv_bytes(plan->p, B);
         return extra ? (size_t)(ws_data_off(plan->p) + extra) : 0;
@@ -801,7 +841,18 @@ static int run_with(const qgemm_plan *plan, int64_t B, const void *w, const void
         data_bytes = -1;
     const KArgs a = make_args(p, B, w, x, y);
     hipError_t e;
-    if (choose_tier(plan, B) == QGEMM_TIER_SKINNY) {
+    const int tier = choose_tier(plan, B);
+    if (tier == QGEMM_TIER_GEMV) {
+        if (!gemv_fits(p, B))
+            return fail(QGEMM_ENOTSUP, "qgemm_run: the GEMV tier takes B <= %d with B*K*4 <= %lld bytes "
+                                       "of activations (B=%lld, K=%lld)", GV_MAX_B, (long long)GV_LDS_MAX,
+                        (long long)B, (long long)p.K);
+        e = launch_gemv(p, a, st);
+        if (e != hipSuccess)
+            return hip_fail(e, "qgemm_run: kernel launch");
+        return QGEMM_OK;
+    }
+    if (tier == QGEMM_TIER_SKINNY) {
         if (p.epi == QGEMM_EPI_SWIGLU && !use_stream(p, B))
             return fail(QGEMM_ENOTSUP, "qgemm_run: the small-batch tier runs the fused gate+up epilogue "
                                        "for B <= %d only (B=%lld)", ST_MAX_B, (long long)B);
@@ -924,9 +975,9 @@ int qgemm_run_grouped(const qgemm_plan *plan, int64_t E, int64_t T, const void *
         return fail(QGEMM_EINVAL, "qgemm_run_grouped: E=%lld outside 1..2^16", (long long)E);
     if (T < 0 || T > (1ll << 30))
         return fail(QGEMM_EINVAL, "qgemm_run_grouped: T=%lld outside 0..2^30", (long long)T);
-    if (plan->forced_tier == QGEMM_TIER_SKINNY)
+    if (plan->forced_tier == QGEMM_TIER_SKINNY || plan->forced_tier == QGEMM_TIER_GEMV)
         return fail(QGEMM_ENOTSUP, "qgemm_run_grouped: routed experts run in the large-batch tier "
-                                   "(tier not forced to skinny)");
+                                   "(tier not forced to skinny or gemv)");
     if (T == 0)
         return QGEMM_OK;
     if (!w_table || !offsets || !x || !y)

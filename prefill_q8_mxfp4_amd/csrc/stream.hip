@@ -44,7 +44,7 @@
 
 namespace qg {
 
-template <int FMT, int ACT, int NTERM, int NPH, int OUTT, bool FULLK>
+template <int FMT, int ACT, int NTERM, int NPH, int OUTT, bool FULLK, int PDEPTH>
 __global__ __launch_bounds__(64 * st_max_waves(NPH)) void stream_kernel(KArgs a, SkinnyWs ws, int ngroups, int Nh)
 {
     constexpr int KS = slab_k(FMT);
@@ -146,40 +146,47 @@ __global__ __launch_bounds__(64 * st_max_waves(NPH)) void stream_kernel(KArgs a,
         // of them below the weights, making the first MFMA wait for every
         // weight byte of the wave.
         __builtin_amdgcn_sched_barrier(0);
+        // Weight and scale loads, one item per (phase, row tile): the first
+        // PD items now, then item i + PD just before item i is computed, so a
+        // wave's data arrive in the order it uses them and its decode and
+        // MFMA work overlaps the rest of the stream (PD >= NI: all at once).
+        constexpr int NI = NPH * ST_RG;
+        constexpr int PD = PDEPTH < NI ? PDEPTH : NI;
         u32x4 wr[NPH][ST_RG];
         uint32_t sr[NPH][ST_RG][2];
-#pragma unroll
-        for (int ph = 0; ph < NPH; ph++) {
+        auto issue = [&](int i) {
+            const int ph = i / ST_RG, g = i % ST_RG;
             const int s = c_beg + ph * W + wid;
             const int sc = min(s, a.S - 1);
             const bool live = s < s_end;
-#pragma unroll
-            for (int g = 0; g < ST_RG; g++) {
-                const int64_t rt = tile_of(g);
-                wr[ph][g] = bload16(make_rsrc(a.w + ((rt * a.S + sc) << 10), live ? 1024 : 0), wvoff, 0);
-                const __amdgpu_buffer_rsrc_t srs = make_rsrc(
-                    a.w + a.scale_off + (rt * a.S + sc) * (16 * SBYTES), live ? 16 * SBYTES : 0);
-                if constexpr (FMT == FMT_NV) {
-                    const u32x2 v = bload8(srs, svoff, 0);
-                    sr[ph][g][0] = v[0];
-                    sr[ph][g][1] = v[1];
-                } else {
-                    sr[ph][g][0] = bload4(srs, svoff, 0);
-                    sr[ph][g][1] = 0u;
-                }
+            const int64_t rt = tile_of(g);
+            wr[ph][g] = bload16_nt(make_rsrc(a.w + ((rt * a.S + sc) << 10), live ? 1024 : 0), wvoff, 0);
+            const __amdgpu_buffer_rsrc_t srs = make_rsrc(
+                a.w + a.scale_off + (rt * a.S + sc) * (16 * SBYTES), live ? 16 * SBYTES : 0);
+            if constexpr (FMT == FMT_NV) {
+                const u32x2 v = bload8_nt(srs, svoff, 0);
+                sr[ph][g][0] = v[0];
+                sr[ph][g][1] = v[1];
+            } else {
+                sr[ph][g][0] = bload4_nt(srs, svoff, 0);
+                sr[ph][g][1] = 0u;
             }
-        }
+        };
+#pragma unroll
+        for (int i = 0; i < PD; i++)
+            issue(i);
         __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll
         for (int ph = 0; ph < NPH; ph++) {
             const int s = c_beg + ph * W + wid;  // this wave's slab
-            if (s < s_end) {                     // uniform
-                // units past K (padding of the last slab) are left out
-                const int nu = FULLK ? U : min(U, (a.K - s * KS + 31) / 32);
+            const bool live = s < s_end;         // uniform
+            // units past K (padding of the last slab) are left out
+            const int nu = FULLK ? U : min(U, (a.K - s * KS + 31) / 32);
 
-                // ---- 2. activation operands, then one partial tile per row tile
-                bf16x8 A[U][NTA];
+            // ---- 2. activation operands, then one partial tile per row tile
+            bf16x8 A[U][NTA];
+            if (live) {
 #pragma unroll
                 for (int u = 0; u < U; u++) {
                     if constexpr (ACT == ACT_F32) {
@@ -197,8 +204,14 @@ __global__ __launch_bounds__(64 * st_max_waves(NPH)) void stream_kernel(KArgs a,
                         A[u][0] = __builtin_bit_cast(bf16x8, masked(xr[ph][u][0], xm[ph][u]));
                     }
                 }
+            }
 #pragma unroll
-                for (int g = 0; g < ST_RG; g++) {
+            for (int g = 0; g < ST_RG; g++) {
+                if (PD < NI && ph * ST_RG + g + PD < NI) {
+                    issue(ph * ST_RG + g + PD);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if (live) {
                     const u32x4 wc = wr[ph][g];
                     const uint32_t s0 = sr[ph][g][0], s1 = sr[ph][g][1];
                     f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -351,7 +364,7 @@ __global__ __launch_bounds__(64 * st_max_waves(NPH)) void stream_kernel(KArgs a,
         for (int i = 0; i < 4; i++) {
             const int b = 4 * gq + i;
             if (b < a.B)
-                store_out<OUTT>(a.y, (int64_t)b * Nh + col, silu(g0 * acc[i]) * (g1 * up[i]));
+                store_out_nt<OUTT>(a.y, (int64_t)b * Nh + col, silu(g0 * acc[i]) * (g1 * up[i]));
         }
         return;
     }
@@ -365,24 +378,39 @@ __global__ __launch_bounds__(64 * st_max_waves(NPH)) void stream_kernel(KArgs a,
     for (int i = 0; i < 4; i++) {
         const int b = 4 * gq + i;
         if (b < a.B)
-            store_out<OUTT>(a.y, (int64_t)b * a.N + n, gsc * acc[i]);
+            store_out_nt<OUTT>(a.y, (int64_t)b * a.N + n, gsc * acc[i]);
     }
 }
 
 // ------------------------------------------------------------------ host
 
-template <int FMT, int ACT, int NTERM, int OUTT, bool FULLK>
-static void launch_kf(const KArgs &a, const StCfg &c, const SkinnyWs &ws, hipStream_t st)
+template <int FMT, int ACT, int NTERM, int OUTT, bool FULLK, int PD>
+static void launch_kd(const KArgs &a, const StCfg &c, const SkinnyWs &ws, hipStream_t st)
 {
     const dim3 grid((unsigned)c.grid);
     const dim3 block((unsigned)(64 * c.W));
     const size_t lds = (size_t)c.W * ST_RG * 1024;
     if (c.NPH == 2)
-        hipLaunchKernelGGL((stream_kernel<FMT, ACT, NTERM, 2, OUTT, FULLK>), grid, block, lds, st, a, ws,
+        hipLaunchKernelGGL((stream_kernel<FMT, ACT, NTERM, 2, OUTT, FULLK, PD>), grid, block, lds, st, a, ws,
                            c.ngroups, c.Nh);
     else
-        hipLaunchKernelGGL((stream_kernel<FMT, ACT, NTERM, 1, OUTT, FULLK>), grid, block, lds, st, a, ws,
+        hipLaunchKernelGGL((stream_kernel<FMT, ACT, NTERM, 1, OUTT, FULLK, PD>), grid, block, lds, st, a, ws,
                            c.ngroups, c.Nh);
+}
+
+// prefetch depth in (phase, row tile) items; 16 covers every item of a chunk
+template <int FMT, int ACT, int NTERM, int OUTT, bool FULLK>
+static void launch_kf(const KArgs &a, const StCfg &c, const SkinnyWs &ws, hipStream_t st)
+{
+    if constexpr (NTERM != 1 && NTERM != 2) {
+        switch (c.depth) {
+        case 2: launch_kd<FMT, ACT, NTERM, OUTT, FULLK, 2>(a, c, ws, st); return;
+        case 3: launch_kd<FMT, ACT, NTERM, OUTT, FULLK, 3>(a, c, ws, st); return;
+        case 4: launch_kd<FMT, ACT, NTERM, OUTT, FULLK, 4>(a, c, ws, st); return;
+        default: break;
+        }
+    }
+    launch_kd<FMT, ACT, NTERM, OUTT, FULLK, 16>(a, c, ws, st);
 }
 
 // K a whole number of slabs: no unit or activation masking at all
@@ -402,8 +430,8 @@ static void launch_sf(const Problem &p, const KArgs &a, const StCfg &c, const Sk
 {
     const bool o32 = p.out == QGEMM_F32;
     if (p.act != QGEMM_F32) {
-        if (o32) launch_kc<FMT, ACT_BF16, 1, OUT_F32>(a, c, ws, st);
-        else launch_kc<FMT, ACT_BF16, 1, OUT_BF16>(a, c, ws, st);
+        if (o32) launch_kc<FMT, ACT_BF16, 0, OUT_F32>(a, c, ws, st);
+        else launch_kc<FMT, ACT_BF16, 0, OUT_BF16>(a, c, ws, st);
     } else if (nterm == 1) {
         if (o32) launch_kc<FMT, ACT_F32, 1, OUT_F32>(a, c, ws, st);
         else launch_kc<FMT, ACT_F32, 1, OUT_BF16>(a, c, ws, st);

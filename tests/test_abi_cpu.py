@@ -65,6 +65,8 @@ def _create(*args):
     ((0, 0, 0, 0, 0, 256, 512, 3), q.EINVAL),        # both tiers forced
     ((0, 0, 0, 0, 0, 256, 512, 0x10), q.EINVAL),     # unknown flag
     ((0, 0, 0, 0, 0, 256, 512, 2), q.OK),            # fp32 math in the tiled tier
+    ((0, 0, 0, 0, 0, 256, 512, 4), q.OK),            # the GEMV tier
+    ((0, 0, 0, 0, 0, 256, 512, 5), q.EINVAL),        # two tiers forced
     ((2, 1, 1, 1, 1, 64, 512, 1), q.OK),             # SwiGLU in the skinny tier (B <= 16)
     ((2, 0, 0, 1, 0, 64, 512, 0), q.ENOTSUP),        # SwiGLU with fp32 math
 ])
@@ -144,7 +146,9 @@ def test_tier_choice():
     assert p.tier(2048) == "tiled" and p.tier(17) == "tiled"
     assert p.tier(1) == "skinny" and p.tier(16) == "skinny"
     p = q.Plan("q8_0", 5120, 5120, act="f32", tier="skinny")
-    assert p.tier(256) == "skinny"
+    assert p.tier(1) == "skinny" and p.tier(256) == "skinny"
+    p = q.Plan("q8_0", 5120, 5120, act="f32", tier="gemv")
+    assert p.tier(1) == "gemv" and p.tier(300) == "gemv" and p.workspace_bytes(2) == 0
 
 
 def _split_part_bytes(plan, B, N):

@@ -156,9 +156,11 @@ def test_boundary_matrix_chunked_is_bitwise(q8_attn, tier):
 
 
 def test_deterministic_and_row_independent(q8_attn):
-    """Repeated calls agree bit for bit, and within the small-batch tiers a
+    """Repeated calls agree bit for bit, and within the small-batch tier a
     row's result does not depend on how many other rows share the call (the
-    summation order is fixed by N and K alone)."""
+    summation order is fixed by N and K alone; the streaming kernel for
+    B <= 16 and the skinny kernel above it share it up to 8 batch groups).
+    The GEMV tier has an order of its own, equally independent of B."""
     w, x, ref, wd = q8_attn
     plan = q.Plan("q8_0", 5120, 5120, act="f32", out="f32", math="fp32", tier="skinny")
     y16 = run(plan, x[:16], wd)
@@ -167,9 +169,13 @@ def test_deterministic_and_row_independent(q8_attn):
         yb = run(plan, x[:B], wd)
         n = min(B, 16)
         assert np.array_equal(yb[:n], y16[:n]), B
+    gv = q.Plan("q8_0", 5120, 5120, act="f32", out="f32", math="fp32", tier="gemv")
+    y2 = run(gv, x[:2], wd)
+    assert np.array_equal(y2, run(gv, x[:2], wd))
+    assert np.array_equal(run(gv, x[:1], wd), y2[:1])
 
 
-@pytest.mark.parametrize("B", (1, 16, 65, 256))
+@pytest.mark.parametrize("B", (3, 16, 65, 256))
 def test_split_k_and_unsplit_agree(q8_attn, B):
     """The K-split route (with a workspace) and the unsplit route both meet
     the fp32 bound, and the tile counters are re-armed after every call."""
@@ -249,7 +255,7 @@ def test_stream_split_exchange_modes_agree(fmt, n, k, act, epi, monkeypatch):
     coh = q.Plan(fmt, n, k, act=act, out="f32", math=math, epilogue=epi)   # device-coherent
     monkeypatch.delenv("QGEMM_ST_XLOCAL")
     q.device_status(clear=True)
-    for B in (1, 16):
+    for B in (3, 16):
         assert plan.tier(B) == "skinny"
         x = synth.gen_x_f32(B, k, seed=B) if act == "f32" else synth.gen_x_bf16(B, k, seed=B)
         ws = torch.zeros(plan.workspace_bytes(B), dtype=torch.uint8, device=_dev())
@@ -286,7 +292,7 @@ good = q.Plan("q8_0", 5120, 5120, act="f32", out="f32")
 os.environ["QGEMM_XCC_FAKE"] = "1"
 bad = q.Plan("q8_0", 5120, 5120, act="f32", out="f32")
 q.device_status(clear=True)
-for B in (1, 16):
+for B in (3, 16):
     x = torch.from_numpy(synth.gen_config_x("q8_0_5120x5120", B)).cuda()
     y0 = torch.full((B, 5120), float("nan"), device="cuda")
     y1 = torch.full((B, 5120), float("nan"), device="cuda")
@@ -848,7 +854,7 @@ def test_swiglu_streaming_small_batch(fmt):
     w = _gate_up(fmt, nh, k, 31)
     wd = w_dev(w)
     plan = q.Plan(fmt, 2 * nh, k, act="bf16", out="f32", epilogue="swiglu")
-    for B in (1, 7, 16):
+    for B in (1, 3, 7, 16):
         assert plan.tier(B) == "skinny"
         x = synth.gen_x_bf16(B, k, seed=B)
         ref = oracle.swiglu(w, x)
@@ -1076,3 +1082,88 @@ def test_grouped_bad_offsets_do_nothing_and_report(case):
     assert q.device_status() == 0
     ref = oracle.gemm_grouped(ws, good, x)
     assert oracle.rel_fro(host(y), ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "mxfp4", "nvfp4", "fp8"])
+@pytest.mark.parametrize("act,out", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
+def test_gemv_narrow_batches(fmt, act, out):
+    """B = 1 and 2 in the GEMV tier (forced: one workgroup per row tile over
+    all of K, fp32 FMA) in every format: K = 5120 (five slabs a wave) and 17408
+    (nine: the register ring turns over), a ragged N; against the oracle
+    element by element (component-wise bound: exact decoded weights, fp32
+    FMA accumulation) and row 0 bitwise the same at B = 1 and B = 2; no
+    workspace needed."""
+    for n, k in ((1000, 5120), (272, 17408)):
+        w = synth.gen_weights(fmt, n, k, seed=71)
+        xf = synth.gen_x_f32(2, k, seed=72)
+        x = xf if act == "f32" else synth.f32_to_bf16_bits(xf)
+        plan = q.Plan(fmt, n, k, act=act, out=out, tier="gemv")
+        ys = []
+        # two fp32 rows of K = 17408 exceed the kernel's LDS budget
+        for B in (1, 2) if 2 * k * 4 <= 72 * 1024 else (1,):
+            assert plan.tier(B) == "gemv" and plan.workspace_bytes(B) == 0
+            y = run(plan, x[:B], w_dev(w))
+            ref = oracle.gemm(w, x[:B])
+            bi = np.repeat(np.arange(B), n)
+            ni = np.tile(np.arange(n), B)
+            mag = oracle.gemm_abs_at(w, x[:B], bi, ni).reshape(B, n)
+            tol = TOL_FP32 if out == "f32" else TOL_BF16
+            assert oracle.rel_fro(y, ref) <= tol, (B, n, k)
+            if out == "f32":
+                _assert_componentwise(y, ref, mag, _nadds(k, 1), f"gemv {fmt} {act} B={B} K={k}")
+            ys.append(y)
+        if len(ys) == 2:
+            assert np.array_equal(ys[0], ys[1][:1])
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "mxfp4", "nvfp4"])
+def test_gemv_swiglu_and_graph_replay(fmt):
+    """Fused gate+up at B = 1 and 2 in the GEMV kernel (a workgroup owns a
+    gate tile and its up tile) against the oracle, and a captured graph of
+    it replayed bit-identically."""
+    nh, k = 1088, 5120
+    w = _gate_up(fmt, nh, k, 81)
+    wd = w_dev(w)
+    plan = q.Plan(fmt, 2 * nh, k, act="bf16", out="bf16", epilogue="swiglu", tier="gemv")
+    for B in (1, 2):
+        x = synth.gen_x_bf16(B, k, seed=82 + B)
+        y = run(plan, x, wd)
+        bi, ji, tid, nt = _tile_samples(B, nh, 83, tb=16, tn=16, per_tile=8)
+        ref = oracle.swiglu_at(w, x, bi, ji)
+        assert oracle.rel_fro(y[bi, ji], ref) <= TOL_BF16, B
+        _assert_tiles(y[bi, ji], ref, tid, nt, TOL_BF16, f"gemv swiglu {fmt} B={B} per tile")
+    xd = x_dev(x)
+    yg = y_new(plan, 2)
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        plan.run(xd, wd, yg)
+    st.synchronize()
+    want = host(yg)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        plan.run(xd, wd, yg)
+    for rep_ in range(3):
+        yg.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(yg), want), rep_
+
+
+def test_gemv_tier_forced_and_refused():
+    """A plan forced to the GEMV tier runs B = 1, 2 and refuses wider calls
+    and activation rows past its LDS budget with QGEMM_ENOTSUP; routed
+    experts refuse a plan forced to it."""
+    w = synth.gen_weights("q8_0", 256, 512, seed=91)
+    x = synth.gen_x_f32(3, 512, seed=92)
+    plan = q.Plan("q8_0", 256, 512, act="f32", out="f32", tier="gemv")
+    assert oracle.rel_fro(run(plan, x[:2], w_dev(w)), oracle.gemm(w, x[:2])) <= TOL_FP32
+    with pytest.raises(q.QgemmError) as e:
+        run(plan, x, w_dev(w))
+    assert e.value.status == q.ENOTSUP
+    big = q.Plan("mxfp4", 256, 32768, act="bf16", out="f32", tier="gemv")   # 128 KB of fp32 rows
+    xb = torch.zeros((1, 32768), dtype=torch.bfloat16, device=_dev())
+    wb = torch.zeros(q.weight_bytes("mxfp4", 256, 32768), dtype=torch.uint8, device=_dev())
+    with pytest.raises(q.QgemmError) as e:
+        big.run(xb, wb, y_new(big, 1))
+    assert e.value.status == q.ENOTSUP
