@@ -274,6 +274,34 @@ def cpu_baseline(wl, budget_s=10.0, one_thread_calls=1):
                       f"{one_thread_calls} on one thread: q8_0 K=N=5120, B={wl.B}, fp32 activations"}
 
 
+def next4_mfma_rates(iters=4096, reps=5):
+    """The int8-activation question for Q8_0 weights, measured: dense TOPS of
+    the matrix-core loops of qgemm_mfma_rate (median of `reps` launches,
+    each after a warm-up launch)."""
+    import torch
+
+    import prefill_q8_mxfp4_amd as q
+
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda:0")
+    out = {}
+    for mode, (name, kdeep) in q.MFMA_RATE_MODES.items():
+        q.mfma_rate(mode, iters, sink)
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            q.mfma_rate(mode, iters, sink)
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        t = sorted(ts)[reps // 2]
+        mfmas = 512 * 8 * iters * 8       # workgroups x waves x trips x chains
+        tops = mfmas * 2.0 * 16 * 16 * kdeep / t / 1e12
+        out[name] = {"TOPS": round(tops, 1), "ms": round(t * 1e3, 4)}
+    log(f"[bench] next4 matrix-core rates {out}")
+    return out
+
+
 def copy_calibration(mib=512, reps=5):
     """A plain device copy of known size, for scaling the HBM byte counters
     of a profiled run (FETCH_SIZE / WRITE_SIZE of this copy read mib MiB)."""
@@ -509,6 +537,7 @@ def main():
                                      "workload": key, "dtype": "bf16",
                                      "all_B2048": {k: v["mfma_frac"] for k, v in big.items()}}
         line["routed_moe:nvfp4:512x(2x512)x2048:top10:tokens2048"] = bench_moe(args.steps)
+        line["next4_int8_vs_bf16_mfma"] = next4_mfma_rates()
 
     print(json.dumps(line), flush=True)
 

@@ -39,7 +39,8 @@ EXPORTS = ("qgemm_weight_bytes", "qgemm_pack", "qgemm_create", "qgemm_run", "qge
            "qgemm_run_noalloc", "qgemm_run_grouped",
            "qgemm_workspace_bytes", "qgemm_plan_tier", "qgemm_init_device", "qgemm_xcd_local",
            "qgemm_device_status",
-           "qgemm_destroy", "qgemm_dequantize", "qgemm_read_bytes", "qgemm_strerror", "qgemm_last_error",
+           "qgemm_destroy", "qgemm_dequantize", "qgemm_read_bytes", "qgemm_mfma_rate", "qgemm_strerror",
+           "qgemm_last_error",
            "qgemm_version")
 DEV_XCD_MISMATCH = 0x1
 DEV_BAD_OFFSETS = 0x2
@@ -88,6 +89,8 @@ def lib():
     L.qgemm_destroy.argtypes = [vp]
     L.qgemm_dequantize.restype = i32
     L.qgemm_dequantize.argtypes = [i32, vp, vp, i64, i64, vp]
+    L.qgemm_mfma_rate.restype = i32
+    L.qgemm_mfma_rate.argtypes = [i32, i32, vp, vp]
     L.qgemm_read_bytes.restype = i32
     L.qgemm_read_bytes.argtypes = [vp, sz, vp, i32, vp]
     L.qgemm_strerror.restype = ctypes.c_char_p
@@ -357,6 +360,19 @@ def read_bytes(buf, sink, wgs: int = 0, nbytes: int | None = None, stream=None):
         raise ValueError("sink too small")
     _check(lib().qgemm_read_bytes(_dev_ptr(buf, "buf"), n, _dev_ptr(sink, "sink"), wgs,
                                   _stream_ptr(stream)))
+
+
+MFMA_RATE_MODES = {0: ("bf16 16x16x32", 32), 1: ("i8 16x16x32", 32), 2: ("i8 16x16x64", 64),
+                   3: ("i8 16x16x32 + per-32 scale (int8 tier loop)", 32),
+                   4: ("bf16 16x16x32 + per-32 scale FMA", 32)}
+
+
+def mfma_rate(mode: int, iters: int, sink, stream=None):
+    """qgemm_mfma_rate: one launch of the matrix-core loop `mode` (see
+    MFMA_RATE_MODES: name, K per MFMA); sink: int32 tensor of 4096 elements."""
+    if sink.numel() < 4096:
+        raise ValueError("sink too small")
+    _check(lib().qgemm_mfma_rate(mode, iters, _dev_ptr(sink, "sink"), _stream_ptr(stream)))
 
 
 def xcd_local() -> int:

@@ -500,5 +500,6 @@ hipError_t launch_grouped_fp32(const Problem &p, const KArgs &a, const Groups &g
                                hipStream_t st);
 hipError_t launch_dequant(int fmt, const KArgs &a, float *out, hipStream_t st);
 hipError_t launch_read_bytes(const void *buf, int64_t bytes, uint32_t *sink, int wgs, hipStream_t st);
+hipError_t launch_mfma_rate(int mode, int iters, uint32_t *sink, hipStream_t st);
 
 }  // namespace qg

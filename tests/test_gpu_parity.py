@@ -1167,3 +1167,32 @@ def test_gemv_tier_forced_and_refused():
     with pytest.raises(q.QgemmError) as e:
         big.run(xb, wb, y_new(big, 1))
     assert e.value.status == q.ENOTSUP
+
+
+# ------------------------------------------------------ measurement aids
+
+@pytest.mark.parametrize("nbytes,wgs", [(27852800, 0), (16 * 1000003, 300), (4096, 7)])
+def test_read_bytes_reads_every_byte_once(nbytes, wgs):
+    """The plain read kernel behind the bench's bandwidth ceiling: the XOR of
+    its per-workgroup words equals the XOR of every 32-bit word of the
+    buffer (each 16-byte chunk read exactly once)."""
+    rng = np.random.default_rng(nbytes % 1000)
+    host_words = rng.integers(0, 2 ** 32, nbytes // 4, dtype=np.uint32)
+    buf = torch.from_numpy(host_words.view(np.int32)).to(_dev())
+    n = wgs or 2048
+    sink = torch.zeros(n, dtype=torch.int32, device=_dev())
+    q.read_bytes(buf, sink, wgs=wgs)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(host_words)
+
+
+def test_mfma_rate_modes_run():
+    sink = torch.zeros(4096, dtype=torch.int32, device=_dev())
+    for mode in q.MFMA_RATE_MODES:
+        sink.zero_()
+        q.mfma_rate(mode, 8, sink)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(sink) > 0, mode
+    with pytest.raises(q.QgemmError):
+        q.mfma_rate(5, 8, sink)
