@@ -49,6 +49,7 @@ static void read_knobs(Knobs *k)
     k->sk_nt = env_int("QGEMM_SK_NT", 2);
     k->ti_bm = env_int("QGEMM_TI_BM", 0);
     k->ti_split = env_int("QGEMM_TI_SPLIT", 0);
+    k->ti_waves = env_int("QGEMM_TI_WAVES", 0);
     k->xlocal = env_int("QGEMM_ST_XLOCAL", -1) == 0 ? 0 : -1;
     k->fp32_terms = 3;
     k->xcc_fake = 0;
@@ -479,6 +480,7 @@ static TiCfg tiled_cfg(const Problem &p, int64_t B, bool split)
             c.BM = bm;
         }
     }
+    c.NW = faith ? 8 : (p.kn.ti_waves == 4 ? 4 : 8);
     c.mtiles = (int)((B + c.BM - 1) / c.BM);
     c.ntiles = ntiles;
     c.tiles = c.mtiles * c.ntiles;

@@ -347,6 +347,7 @@ struct Knobs {
     int sk_stream;         // 0: B <= 16 through the skinny kernel (QGEMM_SK_STREAM)
     int sk_nt;             // 1: one row tile per skinny wave (QGEMM_SK_NT)
     int ti_bm, ti_split;   // large-batch row-tile height, K splits (QGEMM_TI_BM, QGEMM_TI_SPLIT)
+    int ti_waves;          // large-batch waves per workgroup, 4 or 8 (QGEMM_TI_WAVES; 0 = default)
     int xlocal;            // -1 the probe decides, 0 device-coherent, 1 forced (debug)
     int fp32_terms;        // activation terms of fp32-faithful math (3; debug 1..3)
     int xcc_fake;          // debug: odd K splits report the next XCC to the placement check
@@ -473,11 +474,13 @@ struct TiSplit {
 
 struct TiCfg {
     int BM, mtiles, ntiles, tiles, wgs;
+    int NW;              // waves per workgroup: 8 (2 x 4), or 4 (2 x 2, bf16 math)
     TiSplit sp;
     int64_t part_bytes;  // workspace the split needs (0 without a split)
 };
 
 hipError_t launch_tiled(const Problem &p, const KArgs &a, const TiCfg &c, hipStream_t st);
+hipError_t launch_tiled_w4(const Problem &p, const KArgs &a, const TiCfg &c, hipStream_t st);
 hipError_t launch_tiled_fp32(const Problem &p, const KArgs &a, const TiCfg &c, hipStream_t st);
 // x[n] fp32 -> xb[n] bf16, round to nearest even (n a multiple of 8, both
 // 16-byte aligned).

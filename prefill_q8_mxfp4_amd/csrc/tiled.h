@@ -2,8 +2,12 @@
 // LDS-staged fragments.
 //
 // 8 waves (two per SIMD) arranged 2 (batch) x 4 (weight rows); each wave owns
-// BM/2 x 64 outputs as (BM/32) x 4 tiles of v_mfma_f32_16x16x32_bf16.  K
-// advances 64 per step:
+// BM/2 x 64 outputs as (BM/32) x 4 tiles of v_mfma_f32_16x16x32_bf16.  A
+// 4-wave form (NW = 4: one wave per SIMD, 2 x 2, each wave BM/2 x 128
+// outputs, its 256 accumulator registers in AGPRs) reads a third fewer LDS
+// fragment bytes per MFMA but hides less latency; it measured 4-15 % slower
+// at B = 2048 and is selected only by QGEMM_TI_WAVES=4.  K advances 64 per
+// step:
 //
 //  * activations: BM x 64 (fp32 input rounded to bf16 on the way);
 //  * weights: BN rows x 64, i.e. one Q8_0 slab or half an FP4 slab of each of
@@ -13,9 +17,9 @@
 //    MXFP4 instead stages the codes with their scale and decodes each
 //    fragment as it is read (half the LDS bytes, the same values).
 //
-// LDS holds both operands as 16-byte fragment entries [k-group][row], rows
-// padded by one entry so neither the stage writes nor the fragment reads
-// collide in banks; it is double-buffered.  Global loads go through buffer
+// LDS holds both operands as 16-byte fragment entries [k-group][row ^
+// k-group], a swizzle under which neither the stage writes nor the fragment
+// reads collide in banks; it is double-buffered.  Global loads go through buffer
 // resources (fixed per-lane offsets, the step in the scalar offset, zero
 // past the data) into register stages two steps ahead of their use (three or
 // four for routed experts), and the conversion and LDS stores of the next
@@ -44,25 +48,48 @@
 
 namespace qg {
 
-template <int FMT, int ACT, int OUTT, bool DUAL, int BM, bool GROUPED, bool FAITH>
-__global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles, TiSplit sp, Groups grp)
+// Output column (in the staged BN rows) of n-tile j of wave column wn, for
+// NW waves in 2 x NW/2 (SwiGLU: the first half of a wave's tiles are gate
+// columns, the second half the matching up columns BN/2 further on).
+template <bool DUAL, int NW>
+__device__ __forceinline__ int tiled_wcol(int wn, int j)
+{
+    constexpr int BN = 256, WCOLS = BN / (NW / 2), TN = WCOLS / 16;
+    if constexpr (DUAL)
+        return j < TN / 2 ? wn * (WCOLS / 2) + 16 * j : BN / 2 + wn * (WCOLS / 2) + 16 * (j - TN / 2);
+    else
+        return wn * WCOLS + 16 * j;
+}
+
+template <int FMT, int ACT, int OUTT, bool DUAL, int BM, bool GROUPED, bool FAITH, int NW = 8>
+__global__ __launch_bounds__(NW * 64) void tiled_kernel(KArgs a, int Nh, int mtiles, TiSplit sp, Groups grp)
 {
     constexpr int BN = 256;                    // staged weight rows
     constexpr int KT = 64;                     // K per step
     constexpr int KG = KT / 8;                 // 16-byte k-groups per step
-    constexpr int NTHR = 512;
-    constexpr int XP = BM + 1, WP = BN + 1;    // padded LDS row counts
+    constexpr int NTHR = NW * 64;
+    constexpr int XP = BM, WP = BN;            // LDS entries per k-group
     constexpr int TM = BM / 2 / 16;            // 16-row MFMA tiles per wave (batch)
-    constexpr int TN = 4;                      // 16-col MFMA tiles per wave (weights)
+    constexpr int TN = BN / (NW / 2) / 16;     // 16-col MFMA tiles per wave (weights)
+    static_assert(NW == 8 || (NW == 4 && !FAITH), "8 waves, or 4 for bf16 math");
     constexpr int CE = ACT == ACT_F32 ? 4 : 8; // activations per 16-byte load
     constexpr int XCH = BM * KT / CE / NTHR;   // activation loads per thread per step
-    constexpr int WCH = (BN / 16) * 64 / NTHR; // weight chunks per thread per step (2)
+    constexpr int WCH = (BN / 16) * 64 / NTHR; // weight chunks per thread per step (2 or 4)
+    constexpr int WCH2 = WCH / 2;              // chunks per half (gate / up) of the staged rows
     constexpr bool FP4 = FMT == FMT_MX || FMT == FMT_NV;  // 128-wide slabs, two steps each
     constexpr int NTA = FAITH && ACT == ACT_F32 ? 3 : 1;  // activation terms
     constexpr bool POST = FAITH && FMT != FMT_NV;         // block scale after the MFMA
     static_assert(XCH * NTHR * CE == BM * KT, "activation staging");
     static_assert(!FAITH || BM == 64 || BM == 96, "the faithful variant runs 64- or 96-row tiles");
 
+    // LDS entry of (k-group kg, row): rows XOR kg.  Fragment reads (16 rows of
+    // one k-group per 16 lanes) then cover all 64 banks without conflict, and
+    // so do the activation stage writes (8 k-groups of one row per 8 lanes),
+    // which a plain [kg][row] layout would put in one bank group (measured on
+    // gfx950: 4 and 13 cycles per wave-wide 16-byte read and write, against 8
+    // for the reads of a layout padded by one entry per k-group).
+    auto lx = [](int kg, int row) { return kg * XP + (row ^ kg); };
+    auto lw = [](int kg, int col) { return kg * WP + (col ^ kg); };
     __shared__ u32x4 xs[2][NTA][KG * XP];
     // MXFP4 (bf16 math) stages the packed codes instead of decoded bf16: each
     // entry is one lane's 8 codes of a fragment and its E8M0 scale as fp32
@@ -192,8 +219,10 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
     const int64_t sc_bytes = (int64_t)a.RT * a.S * SREC;
     const __amdgpu_buffer_rsrc_t xres =
         make_rsrc((const uint8_t *)a.x + (int64_t)b0 * a.K * ESZ, (int64_t)(a.B - b0) * a.K * ESZ);
-    // weight chunk i of a thread covers staged row tile c >> 6 with c = tid + 512 i:
-    // i = 0 the first BN/32 tiles, i = 1 the second (SwiGLU: gate, then up)
+    // weight chunk i of a thread covers staged row tile c >> 6 with c = tid +
+    // NTHR i: chunks i < WCH2 the first BN/32 tiles, the rest the second
+    // (SwiGLU: gate, then up); within a half, chunk i starts (i % WCH2) *
+    // NTHR/64 tiles on (in the scalar offset)
     const int64_t wb0 = (int64_t)gate_rt0 * a.S * 1024, wb1 = (int64_t)up_rt0 * a.S * 1024;
     const int64_t sb0 = (int64_t)gate_rt0 * a.S * SREC, sb1 = (int64_t)up_rt0 * a.S * SREC;
     const __amdgpu_buffer_rsrc_t wres[2] = {make_rsrc(a.w + wb0, code_bytes - wb0),
@@ -205,8 +234,9 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
     constexpr int XRI = NTHR / (KT / CE);
     const int xoff = ((tid / (KT / CE)) * a.K + (tid % (KT / CE)) * CE) * ESZ;
     const int xrow_bytes = XRI * a.K * ESZ;
-    const int woff = ((((tid >> 6) & (BN / 32 - 1)) * a.S) << 10) + (lane << 4);
-    const int soff = ((tid >> 6) & (BN / 32 - 1)) * a.S * SREC + (lane & 15) * scale_bytes_per_slab(FMT);
+    const int woff = (((tid >> 6) * a.S) << 10) + (lane << 4);
+    const int soff = (tid >> 6) * a.S * SREC + (lane & 15) * scale_bytes_per_slab(FMT);
+    const int wtile_step = (NTHR / 64) * a.S;  // slabs between chunk i and i + 1 of a half
     const bool ktail = a.K % KT != 0;  // the last step has columns past K
 
     // Register stages: PF slots, each one step's global loads; slot r is
@@ -225,20 +255,21 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
         const int ssc = s * SREC;
 #pragma unroll
         for (int i = 0; i < WCH; i++) {
+            const int h = i / WCH2, t = (i % WCH2) * wtile_step;  // half, slabs from its first tile
             if constexpr (FP4) {
-                const u32x2 v = bload8(wres[i], woff, (s << 10) + 8 * half);
+                const u32x2 v = bload8(wres[h], woff, ((s + t) << 10) + 8 * half);
                 wr[r][i][0] = v[0];
                 wr[r][i][1] = v[1];
             } else {
-                const u32x4 v = bload16(wres[i], woff, s << 10);
+                const u32x4 v = bload16(wres[h], woff, (s + t) << 10);
                 wr[r][i][0] = v[0]; wr[r][i][1] = v[1]; wr[r][i][2] = v[2]; wr[r][i][3] = v[3];
             }
             if constexpr (FMT == FMT_NV) {
-                const u32x2 v = bload8(sres[i], soff, ssc);
+                const u32x2 v = bload8(sres[h], soff, ssc + t * SREC);
                 sr[r][i][0] = v[0];
                 sr[r][i][1] = v[1];
             } else {
-                sr[r][i][0] = bload4(sres[i], soff, ssc);
+                sr[r][i][0] = bload4(sres[h], soff, ssc + t * SREC);
                 sr[r][i][1] = 0;
             }
         }
@@ -258,9 +289,15 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
         }
     };
     // One activation chunk (i < XCH) of the next stage into LDS buffer buf.
+    // The swizzle permutes only the low three bits of a row (or column), so
+    // every LDS access below is a per-lane base plus a compile-time offset.
+    // Activation chunk i of this thread: row tid / (KT/CE) + i * XRI, columns
+    // xkk .. xkk + CE - 1 of the step.
+    const int xkk = (tid % (KT / CE)) * CE;
+    const int xw0 = lx(xkk >> 3, tid / (KT / CE));
     auto xpiece = [&](int r, int buf, int i) {
-        const int c = tid + i * NTHR;
-        const int row = c / (KT / CE), kk = (c % (KT / CE)) * CE;
+        const int e = xw0 + i * XRI;
+        const int kk = xkk;
         const u32x4 v = xr[r][i];
         if constexpr (NTA > 1) {
             float f[4];
@@ -271,7 +308,7 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
 #pragma unroll
             for (int t = 0; t < NTA; t++) {
                 const u32x4 q = __builtin_bit_cast(u32x4, s.t[t]);
-                u32x2 *dst = (u32x2 *)&xs[buf][t][(kk >> 3) * XP + row] + ((kk & 7) >> 2);
+                u32x2 *dst = (u32x2 *)&xs[buf][t][e] + ((kk & 7) >> 2);
                 *dst = u32x2{q[0], q[1]};
             }
         } else if constexpr (ACT == ACT_F32) {
@@ -280,21 +317,23 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
             p0[1] = (__bf16)__uint_as_float(v[1]);
             p1[0] = (__bf16)__uint_as_float(v[2]);
             p1[1] = (__bf16)__uint_as_float(v[3]);
-            u32x2 *dst = (u32x2 *)&xs[buf][0][(kk >> 3) * XP + row] + ((kk & 7) >> 2);
+            u32x2 *dst = (u32x2 *)&xs[buf][0][e] + ((kk & 7) >> 2);
             *dst = u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
         } else {
-            xs[buf][0][(kk >> 3) * XP + row] = v;
+            xs[buf][0][e] = v;
         }
     };
     // One decoded weight unit (p < 2 * WCH: chunk p / 2, unit p % 2) of the
     // next stage (step `step`) into LDS buffer buf, block scale folded in.
+    // Weight unit ul of chunk i: k-group 4 ul + lane / 16 of staged column
+    // (tid / 64 + i NTHR / 64) * 16 + lane % 16.
+    const int ww0[2] = {lw(lane >> 4, (tid >> 6) * 16 + (lane & 15)), lw(4 + (lane >> 4), (tid >> 6) * 16 + (lane & 15))};
     auto wpiece = [&](int r, int buf, int step, int p) {
         const int i = p >> 1, ul = p & 1;
         const int half = FP4 ? step & 1 : 0;
-        const int c = tid + i * NTHR;
-        const int tr = c >> 6, L = c & 63;
-        const int col = tr * 16 + (L & 15);
-        const int g = L >> 4;
+        const int col = ((tid >> 6) + i * (NTHR / 64)) * 16 + (lane & 15);
+        const int g = lane >> 4;
+        const int e = ww0[ul] + i * (NTHR / 64) * 16;
         bf16x8 h;
         if constexpr (POST) {
             // exact codes; the block scale goes to LDS once per staged row
@@ -319,15 +358,18 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
         } else if constexpr (FMT == FMT_MX) {
             const int u = 2 * half + ul;
             const float d = e8m0_to_f32((sr[r][i][0] >> (8 * u)) & 0xFFu);
-            wsc[buf][(4 * ul + g) * WP + col] = u32x2{wr[r][i][ul], __float_as_uint(d)};
+            wsc[buf][e] = u32x2{wr[r][i][ul], __float_as_uint(d)};
             return;
         } else {
             const int u = 2 * half + ul;
             const int si = 2 * u + (g >> 1);
-            const uint32_t sb = (si < 4 ? sr[r][i][0] >> (8 * si) : sr[r][i][1] >> (8 * (si - 4))) & 0xFFu;
+            // byte si of the 8 scale bytes, by one 64-bit shift (a select of
+            // the dword turned into an indexed private array, i.e. scratch)
+            const uint64_t sc8 = ((uint64_t)sr[r][i][1] << 32) | sr[r][i][0];
+            const uint32_t sb = (uint32_t)(sc8 >> (8 * si)) & 0xFFu;
             h = fp4_to_bf16_mul(wr[r][i][ul], e4m3_to_f32(sb));
         }
-        ws[buf][(4 * ul + g) * WP + col] = __builtin_bit_cast(u32x4, h);
+        ws[buf][e] = __builtin_bit_cast(u32x4, h);
     };
     auto store_stage = [&](int r, int buf, int step) {
 #pragma unroll
@@ -338,14 +380,12 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
             wpiece(r, buf, step, p);
     };
 
-    // staged column of the wave's n-tile j (SwiGLU: tiles 0,1 gate, 2,3 the
-    // matching up columns)
-    auto wcol = [&](int j) {
-        if constexpr (DUAL)
-            return j < 2 ? wn * 32 + 16 * j : BN / 2 + wn * 32 + 16 * (j - 2);
-        else
-            return wn * 64 + 16 * j;
-    };
+    // staged column of the wave's n-tile j
+    auto wcol = [&](int j) { return tiled_wcol<DUAL, NW>(wn, j); };
+    // fragment reads of MFMA k-step kk: k-group 4 kk + lane / 16, row (or
+    // column) base + lane % 16 for a base that is a multiple of 16
+    const int xa[2] = {lx(lane >> 4, wm * (BM / 2) + (lane & 15)), lx(4 + (lane >> 4), wm * (BM / 2) + (lane & 15))};
+    const int wb[2] = {lw(lane >> 4, lane & 15), lw(4 + (lane >> 4), lane & 15)};
 
     f32x4 acc[TM][TN];
 #pragma unroll
@@ -353,6 +393,17 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
 #pragma unroll
         for (int j = 0; j < TN; j++)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (NW == 4) {
+        // 4 waves: the 256 (BM = 256) accumulator registers live in AGPRs for
+        // the whole kernel.  Binding them there once (an empty asm, no
+        // instruction) keeps the register allocator from splitting them
+        // between the two register files and copying them every step.
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+            for (int j = 0; j < TN; j++)
+                asm volatile("" : "+a"(acc[i][j]));
+    }
 
     auto load_xstage = [&](int r, int step) {
 #pragma unroll
@@ -380,8 +431,10 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
     // Past the last step the pieces repeat the last step's data into a
     // buffer no one reads.
     constexpr int NG = TM * NTA;  // MFMA groups per k-step
-    // The loop exists twice: with the K-tail masking (K not a multiple of the
-    // step) and without it, so the common case carries no masking work.
+    // With 8 waves the loop exists twice: with the K-tail masking (K not a
+    // multiple of the step) and without it, so the common case carries no
+    // masking work; with 4 waves once, masking behind a uniform branch (two
+    // copies of a loop carrying 256 accumulators defeat the allocator).
     auto main_loop = [&](auto masking) {
     for (int step0 = sb; step0 < se; step0 += PF) {
 #pragma unroll
@@ -395,21 +448,20 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
             tail_mask(r, nst);
 #pragma unroll
         for (int kk = 0; kk < 2; kk++) {        // two 32-wide MFMA k-steps
-            const int kg = 4 * kk + (lane >> 4);
             // A fragment q: batch tile q / NTA, term q % NTA
             auto afrag = [&](int q) {
                 return __builtin_bit_cast(
-                    bf16x8, xs[buf][q % NTA][kg * XP + wm * (BM / 2) + 16 * (q / NTA) + (lane & 15)]);
+                    bf16x8, xs[buf][q % NTA][xa[kk] + 16 * (q / NTA)]);
             };
             bf16x8 bw[TN];
             float bsc[TN];  // block scale of each n-tile's column (POST)
 #pragma unroll
             for (int j = 0; j < TN; j++) {
                 if constexpr (CMX) {
-                    const u32x2 e = wsc[buf][kg * WP + wcol(j) + (lane & 15)];
+                    const u32x2 e = wsc[buf][wb[kk] + wcol(j)];
                     bw[j] = fp4_to_bf16(e[0], __uint_as_float(e[1]));
                 } else {
-                    bw[j] = __builtin_bit_cast(bf16x8, ws[buf][kg * WP + wcol(j) + (lane & 15)]);
+                    bw[j] = __builtin_bit_cast(bf16x8, ws[buf][wb[kk] + wcol(j)]);
                 }
                 if constexpr (POST)
                     bsc[j] = ss[(buf * 2 + kk) * BN + wcol(j) + (lane & 15)];
@@ -459,7 +511,7 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
     }
     }
     };
-    if (ktail)
+    if (NW == 4 || ktail)
         main_loop(std::true_type{});
     else
         main_loop(std::false_type{});
@@ -483,7 +535,7 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
     // ---- epilogue (lane holds rows 4*(lane/16)+e of each 16x16 tile, column lane%16)
 #pragma unroll
     for (int j = 0; j < (DUAL ? TN / 2 : TN); j++) {
-        const int col = n0 + (DUAL ? wn * 32 + 16 * j : wn * 64 + 16 * j) + (lane & 15);
+        const int col = n0 + wcol(j) + (lane & 15);
         if (col >= (DUAL ? Nh : a.N))
             continue;
         float g0 = 1.f, g1 = 1.f;
@@ -501,7 +553,7 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
                     continue;
                 if constexpr (DUAL) {
                     const float G = g0 * acc[i][j][e];
-                    const float U = g1 * acc[i][j + 2][e];
+                    const float U = g1 * acc[i][j + TN / 2][e];
                     store_out<OUTT>(a.y, (int64_t)b * Nh + col, silu(G) * U);
                 } else {
                     store_out<OUTT>(a.y, (int64_t)b * a.N + col, g0 * acc[i][j][e]);
@@ -514,10 +566,10 @@ __global__ __launch_bounds__(512) void tiled_kernel(KArgs a, int Nh, int mtiles,
 // tiled_kernel epilogue.  The partial layout is the one tiled_kernel writes:
 // [split tile][piece][MFMA tile i * TN + j][thread][4], one thread of this
 // kernel per (split tile, i, j-pair, thread of the tiled workgroup).
-template <int FMT, int OUTT, bool DUAL, int BM>
+template <int FMT, int OUTT, bool DUAL, int BM, int NW>
 __global__ __launch_bounds__(256) void tiled_reduce(KArgs a, int Nh, int mtiles, TiSplit sp, int nsplit)
 {
-    constexpr int NTHR = 512, TM = BM / 2 / 16, TN = 4;
+    constexpr int NTHR = NW * 64, TM = BM / 2 / 16, TN = 256 / (NW / 2) / 16;
     constexpr int JN = DUAL ? TN / 2 : TN;      // output column tiles per wave
     const int64_t per_piece = (int64_t)NTHR * TM * TN;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -545,7 +597,7 @@ __global__ __launch_bounds__(256) void tiled_reduce(KArgs a, int Nh, int mtiles,
             const int k = min(k0 + u, sp.S - 1);
             t0[u] = src[k * per_piece + (i * TN + jj) * NTHR];
             if constexpr (DUAL)
-                t1[u] = src[k * per_piece + (i * TN + jj + 2) * NTHR];
+                t1[u] = src[k * per_piece + (i * TN + jj + TN / 2) * NTHR];
         }
 #pragma unroll
         for (int u = 0; u < 8; u++) {
@@ -557,7 +609,7 @@ __global__ __launch_bounds__(256) void tiled_reduce(KArgs a, int Nh, int mtiles,
             }
         }
     }
-    const int col = n0 + (DUAL ? wn * 32 + 16 * jj : wn * 64 + 16 * jj) + (lane & 15);
+    const int col = n0 + tiled_wcol<DUAL, NW>(wn, jj) + (lane & 15);
     if (col >= (DUAL ? Nh : a.N))
         return;
     float g0 = 1.f, g1 = 1.f;
@@ -580,17 +632,18 @@ __global__ __launch_bounds__(256) void tiled_reduce(KArgs a, int Nh, int mtiles,
 
 // ------------------------------------------------------------------ host
 
-template <int FMT, int ACT, int OUTT, bool DUAL, int BM, bool FAITH>
+template <int FMT, int ACT, int OUTT, bool DUAL, int BM, bool FAITH, int NW = 8>
 static void launch_tiled_bm(const KArgs &a, const TiCfg &c, hipStream_t st, int Nh)
 {
+    constexpr int TN = 256 / (NW / 2) / 16;
     const int nsplit = c.tiles - c.sp.full;
     const Groups none = {nullptr, nullptr, 0, 0};
-    hipLaunchKernelGGL((tiled_kernel<FMT, ACT, OUTT, DUAL, BM, false, FAITH>), dim3((unsigned)c.wgs), dim3(512),
-                       0, st, a, Nh, c.mtiles, c.sp, none);
+    hipLaunchKernelGGL((tiled_kernel<FMT, ACT, OUTT, DUAL, BM, false, FAITH, NW>), dim3((unsigned)c.wgs),
+                       dim3(NW * 64), 0, st, a, Nh, c.mtiles, c.sp, none);
     if (c.sp.S > 1) {
-        const int64_t n = (int64_t)nsplit * (BM / 32) * (DUAL ? 2 : 4) * 512;
-        hipLaunchKernelGGL((tiled_reduce<FMT, OUTT, DUAL, BM>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                           st, a, Nh, c.mtiles, c.sp, nsplit);
+        const int64_t n = (int64_t)nsplit * (BM / 32) * (DUAL ? TN / 2 : TN) * NW * 64;
+        hipLaunchKernelGGL((tiled_reduce<FMT, OUTT, DUAL, BM, NW>), dim3((unsigned)((n + 255) / 256)), dim3(256),
+                           0, st, a, Nh, c.mtiles, c.sp, nsplit);
     }
 }
 
@@ -607,7 +660,9 @@ static void launch_grouped_bm(const KArgs &a, const Groups &g, int64_t tiles, hi
 
 // One (format, math) pair: the activation, output and epilogue variants.
 // bf16 math runs 128- or 256-row tiles, fp32-faithful math 64-row tiles.
-template <int FMT, bool FAITH>
+// NW: waves per workgroup of the plain GEMM (routed experts and the
+// fp32-faithful variant always run 8; they are instantiated with NW = 8 only).
+template <int FMT, bool FAITH, int NW>
 static void launch_tiled_f(const Problem &p, const KArgs &a, const TiCfg *c, hipStream_t st, const Groups *g,
                            int BM, int64_t gtiles)
 {
@@ -619,10 +674,14 @@ static void launch_tiled_f(const Problem &p, const KArgs &a, const TiCfg *c, hip
         constexpr bool D = decltype(du)::value;
         auto bm = [&](auto bmv) {
             constexpr int M = decltype(bmv)::value;
-            if (g)
-                launch_grouped_bm<FMT, A, O, D, M, FAITH>(a, *g, gtiles, st, Nh);
-            else
-                launch_tiled_bm<FMT, A, O, D, M, FAITH>(a, *c, st, Nh);
+            if constexpr (NW == 8) {
+                if (g)
+                    launch_grouped_bm<FMT, A, O, D, M, FAITH>(a, *g, gtiles, st, Nh);
+                else
+                    launch_tiled_bm<FMT, A, O, D, M, FAITH>(a, *c, st, Nh);
+            } else {
+                launch_tiled_bm<FMT, A, O, D, M, FAITH, NW>(a, *c, st, Nh);
+            }
         };
         if constexpr (FAITH) {
             // 64-row tiles, or 96 for B in (64, 96] (plain GEMM only)
@@ -630,9 +689,10 @@ static void launch_tiled_f(const Problem &p, const KArgs &a, const TiCfg *c, hip
                 launch_tiled_bm<FMT, A, O, D, 96, FAITH>(a, *c, st, Nh);
             else
                 bm(std::integral_constant<int, 64>{});
-        } else if (g && BM == 64) {
+        } else if (NW == 8 && g && BM == 64) {
             // routed experts with few rows each
-            launch_grouped_bm<FMT, A, O, D, 64, FAITH>(a, *g, gtiles, st, Nh);
+            if constexpr (NW == 8)
+                launch_grouped_bm<FMT, A, O, D, 64, FAITH>(a, *g, gtiles, st, Nh);
         } else if (BM == 128) {
             bm(std::integral_constant<int, 128>{});
         } else {
@@ -658,15 +718,15 @@ static void launch_tiled_f(const Problem &p, const KArgs &a, const TiCfg *c, hip
 
 // Every format of one math mode (c: the plain GEMM's shape; g: routed
 // experts instead, BM-row tiles, gtiles row tiles).
-template <bool FAITH>
+template <bool FAITH, int NW = 8>
 static hipError_t launch_tiled_math(const Problem &p, const KArgs &a, const TiCfg *c, const Groups *g, int BM,
                                     int64_t gtiles, hipStream_t st)
 {
     switch (p.fmt) {
-    case FMT_Q8: launch_tiled_f<FMT_Q8, FAITH>(p, a, c, st, g, BM, gtiles); break;
-    case FMT_MX: launch_tiled_f<FMT_MX, FAITH>(p, a, c, st, g, BM, gtiles); break;
-    case FMT_FP8: launch_tiled_f<FMT_FP8, FAITH>(p, a, c, st, g, BM, gtiles); break;
-    default: launch_tiled_f<FMT_NV, FAITH>(p, a, c, st, g, BM, gtiles); break;
+    case FMT_Q8: launch_tiled_f<FMT_Q8, FAITH, NW>(p, a, c, st, g, BM, gtiles); break;
+    case FMT_MX: launch_tiled_f<FMT_MX, FAITH, NW>(p, a, c, st, g, BM, gtiles); break;
+    case FMT_FP8: launch_tiled_f<FMT_FP8, FAITH, NW>(p, a, c, st, g, BM, gtiles); break;
+    default: launch_tiled_f<FMT_NV, FAITH, NW>(p, a, c, st, g, BM, gtiles); break;
     }
     return hipGetLastError();
 }

@@ -34,6 +34,8 @@ hipError_t launch_tiled(const Problem &p, const KArgs &a, const TiCfg &c, hipStr
 {
     if (p.math == QGEMM_MATH_FP32)
         return launch_tiled_fp32(p, a, c, st);
+    if (c.NW == 4)
+        return launch_tiled_w4(p, a, c, st);
     return launch_tiled_math<false>(p, a, &c, nullptr, c.BM, 0, st);
 }
 
