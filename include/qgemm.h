@@ -202,16 +202,32 @@ int qgemm_run(const qgemm_plan *plan, int64_t B, const void *w, const void *x, v
  *            offsets[E] = T (the caller sorts the routed rows by expert);
  *            1 <= E <= 2^16;
  *   x: [T][K] routed activation rows; y: [T][N] (or [T][N/2] with SwiGLU).
- * Experts with no rows cost only a scan.  One launch of the large-batch
- * kernel, unsplit, so each expert's rows are bitwise those of a qgemm_run of
- * that expert in the large-batch tier without a workspace.  Either math
- * mode; a plan forced to the small-batch tier returns QGEMM_ENOTSUP.  T = 0 returns QGEMM_OK and enqueues nothing.
+ * Experts with no rows cost only a scan.  One launch, on one of two routes
+ * (qgemm_grouped_tier tells which):
+ *   QGEMM_TIER_SKINNY: bf16 math with fewer than 64 rows per expert on
+ *     average (T < 64 E) and under 2^31 bytes of activations, or a plan
+ *     forced to the small-batch tier (bf16 math): each expert's weights are streamed once for all of its rows, in
+ *     the small-batch tier's summation order, so each expert's rows are
+ *     bitwise those of qgemm_run of that expert in the small-batch tier
+ *     without a workspace (a row's result does not depend on the other rows;
+ *     with SwiGLU, calls of at most 16 rows);
+ *   QGEMM_TIER_TILED: otherwise (fp32-faithful math, more rows per expert,
+ *     or a plan forced to the large-batch tier): the large-batch kernel,
+ *     unsplit, so each expert's rows are bitwise those of qgemm_run of that
+ *     expert in the large-batch tier without a workspace.
+ * A plan forced to the GEMV tier, or to the small-batch tier with fp32 math,
+ * returns QGEMM_ENOTSUP.  T = 0 returns QGEMM_OK and enqueues nothing.
  * The offsets are read and checked on the device: when they break a rule
  * above, the kernel reads and writes nothing outside the offsets array and
  * the table and sets QGEMM_DEV_BAD_OFFSETS in the device status word (y is
  * left unwritten; qgemm_device_status reports it). */
 int qgemm_run_grouped(const qgemm_plan *plan, int64_t E, int64_t T, const void *const *w_table,
                       const int32_t *offsets, const void *x, void *y, void *stream);
+
+/* The route qgemm_run_grouped takes for E experts and T rows
+ * (QGEMM_TIER_SKINNY or QGEMM_TIER_TILED, as described there), or 0 for a bad
+ * plan or sizes, or a plan with no routed-expert route.  Host only. */
+int qgemm_grouped_tier(const qgemm_plan *plan, int64_t E, int64_t T);
 
 /* Bytes of device workspace with which qgemm_run_ws may split K across
  * workgroups for this plan and B (0 when the chosen tier does not use one). */

@@ -36,7 +36,7 @@ ALIGN = 256
 MAX_TENSORS = 60
 
 EXPORTS = ("qgemm_weight_bytes", "qgemm_pack", "qgemm_create", "qgemm_run", "qgemm_run_ws",
-           "qgemm_run_noalloc", "qgemm_run_grouped",
+           "qgemm_run_noalloc", "qgemm_run_grouped", "qgemm_grouped_tier",
            "qgemm_workspace_bytes", "qgemm_plan_tier", "qgemm_init_device", "qgemm_xcd_local",
            "qgemm_device_status",
            "qgemm_destroy", "qgemm_dequantize", "qgemm_read_bytes", "qgemm_mfma_rate", "qgemm_strerror",
@@ -81,6 +81,8 @@ def lib():
     L.qgemm_run_noalloc.argtypes = [vp, i64, vp, vp, vp, vp]
     L.qgemm_run_grouped.restype = i32
     L.qgemm_run_grouped.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
+    L.qgemm_grouped_tier.restype = i32
+    L.qgemm_grouped_tier.argtypes = [vp, i64, i64]
     L.qgemm_workspace_bytes.restype = sz
     L.qgemm_workspace_bytes.argtypes = [vp, i64]
     L.qgemm_plan_tier.restype = i32
@@ -230,6 +232,12 @@ class Plan:
 
     def tier(self, B: int) -> str:
         return TIERS.get(lib().qgemm_plan_tier(self._h, B), "invalid")
+
+    def grouped_tier(self, E: int, T: int) -> str:
+        """The route run_grouped takes for E experts and T rows: "skinny" (the
+        small-batch order, bf16 math with few rows per expert), "tiled", or
+        "invalid" (no route for this plan)."""
+        return TIERS.get(lib().qgemm_grouped_tier(self._h, E, T), "invalid")
 
     def workspace_bytes(self, B: int) -> int:
         return int(lib().qgemm_workspace_bytes(self._h, B))

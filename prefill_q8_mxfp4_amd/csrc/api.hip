@@ -967,6 +967,32 @@ int qgemm_run_noalloc(const qgemm_plan *plan, int64_t B, const void *w, const vo
                     (int64_t)(QGEMM_SCRATCH_BYTES - QGEMM_SCRATCH_COUNTER_BYTES), (hipStream_t)stream);
 }
 
+// Route of a routed-expert call: bf16 math with fewer than 64 rows per
+// expert on average takes the streaming kernel over (expert, row-tile group)
+// work items (the small-batch tier's order); otherwise, or for a plan forced
+// to the large-batch tier, the large-batch kernel.  0: not runnable.
+static int grouped_tier(const qgemm_plan *plan, int64_t E, int64_t T)
+{
+    const Problem &p = plan->p;
+    if (plan->forced_tier == QGEMM_TIER_GEMV)
+        return 0;
+    const int64_t xsz = p.act == QGEMM_F32 ? 4 : 2;
+    const bool small_ok = p.math == QGEMM_MATH_BF16 && T * p.K * xsz < (1ll << 31) &&
+                          E * moe_groups(p) <= 0x7FFFFFFFll && moe_groups_per_wg(p, E) >= 1;
+    if (plan->forced_tier == QGEMM_TIER_SKINNY)
+        return small_ok ? QGEMM_TIER_SKINNY : 0;
+    if (plan->forced_tier == QGEMM_TIER_TILED)
+        return QGEMM_TIER_TILED;
+    return small_ok && T < 64 * E ? QGEMM_TIER_SKINNY : QGEMM_TIER_TILED;
+}
+
+int qgemm_grouped_tier(const qgemm_plan *plan, int64_t E, int64_t T)
+{
+    if (!plan || plan->magic != PLAN_MAGIC || E < 1 || E > (1 << 16) || T < 0 || T > (1ll << 30))
+        return 0;
+    return grouped_tier(plan, E, T);
+}
+
 int qgemm_run_grouped(const qgemm_plan *plan, int64_t E, int64_t T, const void *const *w_table,
                       const int32_t *offsets, const void *x, void *y, void *stream)
 {
@@ -977,9 +1003,10 @@ int qgemm_run_grouped(const qgemm_plan *plan, int64_t E, int64_t T, const void *
         return fail(QGEMM_EINVAL, "qgemm_run_grouped: E=%lld outside 1..2^16", (long long)E);
     if (T < 0 || T > (1ll << 30))
         return fail(QGEMM_EINVAL, "qgemm_run_grouped: T=%lld outside 0..2^30", (long long)T);
-    if (plan->forced_tier == QGEMM_TIER_SKINNY || plan->forced_tier == QGEMM_TIER_GEMV)
-        return fail(QGEMM_ENOTSUP, "qgemm_run_grouped: routed experts run in the large-batch tier "
-                                   "(tier not forced to skinny or gemv)");
+    const int tier = grouped_tier(plan, E, T);
+    if (!tier)
+        return fail(QGEMM_ENOTSUP, "qgemm_run_grouped: a plan forced to the GEMV tier, or to the small-batch "
+                                   "tier with fp32 math or T*K beyond 2^31 bytes, has no routed-expert route");
     if (T == 0)
         return QGEMM_OK;
     if (!w_table || !offsets || !x || !y)
@@ -990,6 +1017,21 @@ int qgemm_run_grouped(const qgemm_plan *plan, int64_t E, int64_t T, const void *
     if (T * p.K > (1ll << 31) - 1 || T * ncols > (1ll << 31) - 1)
         return fail(QGEMM_EINVAL, "qgemm_run_grouped: T*K or T*N above 2^31 elements");
     KArgs a = make_args(p, T, nullptr, x, y);
+    if (tier == QGEMM_TIER_SKINNY) {
+        Groups g;
+        g.wtab = (const uint8_t *const *)w_table;
+        g.off = offsets;
+        g.E = (int)E;
+        g.T = (int)T;
+        g.ntiles = moe_groups(p);
+        g.status = status_word(current_device());
+        if (!g.status)
+            return fail(QGEMM_EHIP, "qgemm_run_grouped: no device status word");
+        const hipError_t e = launch_moe(p, a, g, (hipStream_t)stream);
+        if (e != hipSuccess)
+            return hip_fail(e, "qgemm_run_grouped: kernel launch");
+        return QGEMM_OK;
+    }
     // BM by the mean rows per expert; an upper bound on the experts' row tiles
     // (each expert adds at most one partial tile, and at most T experts have rows)
     const int BM = p.math == QGEMM_MATH_FP32 ? 64 : T / E >= 192 ? 256 : T / E >= 64 ? 128 : 64;

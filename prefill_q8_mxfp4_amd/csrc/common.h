@@ -501,6 +501,11 @@ hipError_t launch_grouped(const Problem &p, const KArgs &a, const Groups &g, int
                           hipStream_t st);
 hipError_t launch_grouped_fp32(const Problem &p, const KArgs &a, const Groups &g, int BM, int64_t tiles,
                                hipStream_t st);
+// Routed experts with few rows each, bf16 math: one workgroup per (expert,
+// row-tile group), moe_groups(p) groups per expert (moe.hip).
+hipError_t launch_moe(const Problem &p, const KArgs &a, const Groups &g, hipStream_t st);
+int moe_groups(const Problem &p);
+int moe_groups_per_wg(const Problem &p, int64_t E);
 hipError_t launch_dequant(int fmt, const KArgs &a, float *out, hipStream_t st);
 hipError_t launch_read_bytes(const void *buf, int64_t bytes, uint32_t *sink, int wgs, hipStream_t st);
 hipError_t launch_mfma_rate(int mode, int iters, uint32_t *sink, hipStream_t st);

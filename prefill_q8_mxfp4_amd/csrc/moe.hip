@@ -1,0 +1,434 @@
+// Routed experts with few rows each (bf16 math): every expert's packed
+// weights streamed once from HBM straight into MFMA operands, as in the
+// small-batch tier, for all of that expert's rows at once.
+//
+// A workgroup is 4 waves and owns one expert and a run of its row-tile
+// groups: a group is 4 * NTG output row tiles (with SwiGLU, NTG gate tiles
+// per wave and the NTG matching up tiles, so SiLU(G) * U is formed in the
+// lane that holds both).  An expert's groups are split over a few
+// workgroups with consecutive ids on one XCD, so the expert's activation rows
+// are read from that XCD's L2.  A workgroup walks its (group, pass) items in order and
+// loads each item's first activation stage and weight slabs while the item
+// before it finishes.
+//
+//  * The expert's rows are taken 16 * MB at a time (one pass for up to 64
+//    rows).  Their activations are staged in LDS KCH slabs at a time (two
+//    stages, the next one loaded while the current one is used), already
+//    in MFMA fragment order (16-byte entry [slab][16-row group][unit][lane]),
+//    rounded to bf16 on the way for fp32 input, zero past the last row and
+//    past K; only the 16-row groups that hold rows are staged (all MB are
+//    multiplied: fewer branches and registers than skipping the empty ones).
+//  * Each lane's 16-byte chunk of a weight slab is its B operand, decoded in
+//    registers; waves keep D slabs of their row tiles in flight through the
+//    LDS stages (loads of dead slabs go through empty buffer resources).
+//  * Summation order, the small-batch tier's: per (slab, row tile) its units
+//    in order into a partial from zero (Q8_0 / MXFP4 / FP8 block scales
+//    applied to the block's fp32 partial, NVFP4's E4M3 scale folded into the
+//    operand), partials added to the running tile in slab order.  A row's
+//    result therefore does not depend on the other rows, and each expert's
+//    rows are bitwise those of an unsplit small-batch call of that expert.
+//
+// The offsets are checked by every workgroup before any load that uses them
+// (offsets[0] = 0, non-decreasing, offsets[E] = T): when they break a rule no
+// workgroup does any work and workgroup 0 sets DEV_BAD_OFFSETS.
+#include "common.h"
+
+namespace qg {
+
+constexpr int MOE_MB = 4;        // 16-row groups per pass
+constexpr int MOE_KCH = 1;       // slabs of activations per LDS stage (two stages in LDS)
+constexpr int MOE_D = 2;         // weight slabs in flight per wave (measured: deeper is slower)
+constexpr int MOE_NTG = 2;       // output row tiles per wave
+constexpr int MOE_NTG_DUAL = 1;  // with SwiGLU: gate tiles per wave (and as many up tiles)
+
+template <int FMT, int ACT, int OUTT, bool DUAL, int NTG, bool FULLK>
+__global__ __launch_bounds__(256, 2) void moe_kernel(KArgs a, Groups grp, int Nh, int ngroups, int gpw)
+{
+    constexpr int KS = slab_k(FMT);
+    constexpr int U = KS / 32;                 // 32-wide units per slab
+    constexpr int MB = MOE_MB, KCH = MOE_KCH, D = MOE_D;
+    constexpr int WT = DUAL ? 2 * NTG : NTG;   // row tiles per wave
+    constexpr int XSZ = ACT == ACT_F32 ? 4 : 2;
+    constexpr int SBYTES = scale_bytes_per_slab(FMT);
+    constexpr int SLAB_E = MB * U * 64;        // LDS entries per staged slab
+    constexpr int NXF = (KCH * MB * U + 3) / 4;  // activation fragments per wave and stage
+    constexpr bool POST = FMT != FMT_NV;
+
+    __shared__ u32x4 xs[2 * KCH * SLAB_E];  // two stages
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15, gq = lane >> 4;
+
+    // ---- this workgroup's expert and row-tile groups [g_beg, g_end):
+    // consecutive ids (one expert's groups) on one XCD
+    int t;
+    {
+        const int nwg = gridDim.x, per = (nwg + 7) / 8;
+        const int xcd = blockIdx.x % 8, loc = blockIdx.x / 8;
+        const int full = nwg % 8 == 0 ? 8 : nwg % 8;
+        t = xcd < full ? xcd * per + loc : full * per + (xcd - full) * (per - 1) + loc;
+    }
+    const int nsplit = (ngroups + gpw - 1) / gpw;
+    const int e = t / nsplit;
+    const int g_beg = t % nsplit * gpw, g_end = min(ngroups, g_beg + gpw);
+
+    // ---- offsets check (all of them, before any use; this expert's own
+    // offsets and weights pointer are loaded in the same round)
+    int bad = 0;
+    for (int e2 = tid; e2 < grp.E; e2 += 256) {
+        const int lo2 = grp.off[e2], hi2 = grp.off[e2 + 1];
+        bad |= (hi2 < lo2) | (e2 == 0 && lo2 != 0) | (e2 == grp.E - 1 && hi2 != grp.T);
+    }
+    const int lo = grp.off[e];
+    const int rows = grp.off[e + 1] - lo;
+    a.w = grp.wtab[e];
+    if (__syncthreads_or(bad)) {
+        if (blockIdx.x == 0 && tid == 0)
+            __hip_atomic_fetch_or(grp.status, DEV_BAD_OFFSETS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;  // uniform
+    }
+    if (rows <= 0 || g_beg >= g_end)
+        return;  // uniform
+    const int ncols = DUAL ? Nh : a.N;
+    const uint8_t *xe = (const uint8_t *)a.x + (int64_t)lo * a.K * XSZ;
+    void *ye = (uint8_t *)a.y + (int64_t)lo * ncols * (OUTT == OUT_F32 ? 4 : 2);
+    const __amdgpu_buffer_rsrc_t xres = make_rsrc(xe, (int64_t)rows * a.K * XSZ);
+    const uint32_t nvsh = 8 * (gq >> 1);  // NVFP4: this lane's scale byte within a unit's pair
+
+    // Work items: (row-tile group g, pass b0 over 16 * MB rows), g major.  An
+    // item's first activation stage and first D weight slabs are loaded while
+    // the item before it finishes, so a workgroup pays the load latency once.
+    const int npass = (rows + 16 * MB - 1) / (16 * MB);
+    const int nitems = (g_end - g_beg) * npass;
+    const int nst = (a.S + KCH - 1) / KCH;     // activation stages per item
+    const int Sp = (a.S + D - 1) / D * D;      // slabs walked per item (whole ring turns)
+
+    // first output row tile of this wave in item it's group (with SwiGLU the
+    // up tiles are Nh/16 further on); tiles past the last compute on a copy of
+    // it and are never stored
+    auto t0_of = [&](int it) { return ((g_beg + it / npass) * 4 + wid) * NTG; };
+    auto b0_of = [&](int it) { return it % npass * 16 * MB; };
+    auto tile_of = [&](int t0, int j) -> int64_t {
+        const int rt = DUAL ? (j < NTG ? t0 + j : Nh / 16 + t0 + j - NTG) : t0 + j;
+        return min(rt, a.RT - 1);
+    };
+
+    // ---- weight ring: slot j holds slab j mod D of the walk
+    u32x4 wr[D][WT];
+    uint32_t sr[D][WT][2];
+    auto wload = [&](int j, int t0, int s) {  // slot j <- slab s of the tiles from t0 (none past the last)
+        const bool live = s < a.S;
+        const int sc = min(s, a.S - 1);
+#pragma unroll
+        for (int q = 0; q < WT; q++) {
+            const int64_t rt = tile_of(t0, q);
+            wr[j][q] = bload16_nt(make_rsrc(a.w + ((rt * a.S + sc) << 10), live ? 1024 : 0), lane << 4, 0);
+            const __amdgpu_buffer_rsrc_t srs =
+                make_rsrc(a.w + a.scale_off + (rt * a.S + sc) * (16 * SBYTES), live ? 16 * SBYTES : 0);
+            if constexpr (FMT == FMT_NV) {
+                const u32x2 v = bload8_nt(srs, r * SBYTES, 0);
+                sr[j][q][0] = v[0];
+                sr[j][q][1] = v[1];
+            } else {
+                sr[j][q][0] = bload4_nt(srs, r * SBYTES, 0);
+                sr[j][q][1] = 0u;
+            }
+        }
+    };
+
+    // ---- activation stages.  Fragment (slab sl of the stage, group mb, unit
+    // u) is one 1 KB block of LDS entries, lane l holding row 16 mb + l % 16,
+    // columns 8 (l / 16) .. + 7 of the unit.  Wave w loads fragments w, w + 4,
+    // ... (indices past the last repeat it: the same bytes to the same place,
+    // no branch).  Stage c + 1 is loaded at the start of stage c, before the
+    // weight loads issued while stage c is computed, so waiting for it never
+    // waits for weight loads issued after it; it is stored at the start of
+    // stage c + 1 into the buffer stage c - 1 used (every wave passed the
+    // barrier that opened stage c after finishing stage c - 1).
+    u32x4 xv0[NXF], xv1[NXF];
+    auto xfrag = [&](int b0, int nfr, int c, int i, int &dst, int &row, int &k) {
+        const int f = min(wid + 4 * i, nfr - 1);
+        const int per = nfr / KCH;  // fragments per slab
+        const int sl = f / per, rem = f % per;
+        const int mb = rem / U, u = rem % U;
+        row = b0 + 16 * mb + r;
+        k = (c * KCH + sl) * KS + 32 * u + 8 * gq;
+        dst = (c & 1) * (KCH * SLAB_E) + ((sl * MB + mb) * U + u) * 64 + lane;
+    };
+    auto nfr_of = [&](int b0) { return KCH * min(MB, (rows - b0 + 15) / 16) * U; };
+    auto xload = [&](int it, int c) {  // stage c of item it into registers
+        const int b0 = b0_of(it), nfr = nfr_of(b0);
+#pragma unroll
+        for (int i = 0; i < NXF; i++) {
+            int dst, row, k;
+            xfrag(b0, nfr, c, i, dst, row, k);
+            const int vo = (min(row, rows - 1) * a.K + min(k, a.K - 8)) * XSZ;
+            xv0[i] = bload16(xres, vo, 0);
+            if constexpr (ACT == ACT_F32)
+                xv1[i] = bload16(xres, vo + 16, 0);
+        }
+    };
+    auto xstore = [&](int it, int c) {  // the registers of stage c of item it into its LDS buffer
+        const int b0 = b0_of(it), nfr = nfr_of(b0);
+#pragma unroll
+        for (int i = 0; i < NXF; i++) {
+            int dst, row, k;
+            xfrag(b0, nfr, c, i, dst, row, k);
+            const uint32_t m = keep_mask(row < rows && k < a.K);  // K % 16 == 0: 8 columns all in or out
+            u32x4 v;
+            if constexpr (ACT == ACT_F32) {
+                float fv[8];
+#pragma unroll
+                for (int e2 = 0; e2 < 4; e2++) {
+                    fv[e2] = __uint_as_float(xv0[i][e2] & m);
+                    fv[4 + e2] = __uint_as_float(xv1[i][e2] & m);
+                }
+                v = __builtin_bit_cast(u32x4, split_f32<1, 8>(fv).t[0]);
+            } else {
+                v = masked(xv0[i], m);
+            }
+            xs[dst] = v;
+        }
+    };
+
+    // ---- the first item's first stage and ring
+    xload(0, 0);
+#pragma unroll
+    for (int j = 0; j < D; j++)
+        wload(j, t0_of(0), j);
+    xstore(0, 0);
+    __syncthreads();
+    if (nst > 1)
+        xload(0, 1);
+    else if (nitems > 1)
+        xload(1, 0);
+
+    for (int it = 0; it < nitems; it++) {
+        const int t0 = t0_of(it), b0 = b0_of(it);
+        const bool more = it + 1 < nitems;
+        const int t0n = more ? t0_of(it + 1) : t0;
+        // NVFP4 tensor scales of this item's columns, loaded now, used at the end
+        float g0 = 1.f, g1 = 1.f;
+        if constexpr (FMT == FMT_NV) {
+            const int col = min(t0 * 16 + r, ncols - 1);  // clamped only for tiles never stored
+            g0 = tensor_scale(a, col);
+            if constexpr (DUAL)
+                g1 = tensor_scale(a, Nh + col);
+        }
+        f32x4 acc[MB][WT];
+#pragma unroll
+        for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+            for (int q = 0; q < WT; q++)
+                acc[mb][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        for (int s0 = 0; s0 < Sp; s0 += D) {
+#pragma unroll
+            for (int j = 0; j < D; j++) {
+                const int s = s0 + j;
+                if (s > 0 && s < a.S && s % KCH == 0) {  // stage s / KCH begins (uniform)
+                    const int c = s / KCH;
+                    xstore(it, c);
+                    __syncthreads();
+                    if (c + 1 < nst)
+                        xload(it, c + 1);
+                    else if (more)
+                        xload(it + 1, 0);
+                }
+                u32x4 wc[WT];
+                uint32_t sc[WT][2];
+#pragma unroll
+                for (int q = 0; q < WT; q++) {
+                    wc[q] = wr[j][q];
+                    sc[q][0] = sr[j][q][0];
+                    sc[q][1] = sr[j][q][1];
+                }
+                // refill: this item's slab s + D, else the next item's slab
+                // s + D - Sp (slot j keeps slab j mod D), else nothing
+                if (s + D < a.S)
+                    wload(j, t0, s + D);
+                else
+                    wload(j, t0n, more && s + D >= Sp ? s + D - Sp : a.S);
+                if (s >= a.S)
+                    continue;  // past the last slab (uniform)
+                const u32x4 *slab = xs + ((s / KCH) & 1) * (KCH * SLAB_E) + (s % KCH) * SLAB_E;
+                // units within K (all of them when K is a whole number of
+                // slabs: no per-unit branch, so one slab's decode and MFMAs
+                // form one block the compiler can interleave)
+                const int nu = FULLK ? U : min(U, (a.K - s * KS + 31) / 32);
+                // per (row tile, group) a partial from zero over the units in
+                // order; every group is multiplied (groups past the rows hold
+                // stale entries; their outputs are never stored)
+                f32x4 part[WT][MB];
+#pragma unroll
+                for (int q = 0; q < WT; q++)
+#pragma unroll
+                    for (int mb = 0; mb < MB; mb++)
+                        part[q][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                // activation fragments one unit ahead of their MFMAs
+                bf16x8 A2[2][MB];
+#pragma unroll
+                for (int mb = 0; mb < MB; mb++)
+                    A2[0][mb] = __builtin_bit_cast(bf16x8, slab[(mb * U) * 64 + lane]);
+#pragma unroll
+                for (int u = 0; u < U; u++) {
+                    if (u + 1 < U) {
+#pragma unroll
+                        for (int mb = 0; mb < MB; mb++)
+                            A2[(u + 1) & 1][mb] = __builtin_bit_cast(bf16x8, slab[(mb * U + u + 1) * 64 + lane]);
+                    }
+                    if (!FULLK && u >= nu)
+                        continue;  // uniform
+                    const bf16x8 *A = A2[u & 1];
+#pragma unroll
+                    for (int q = 0; q < WT; q++) {
+                        bf16x8 Bw;
+                        float ps = 1.f;
+                        if constexpr (FMT == FMT_Q8) {
+                            Bw = q8_to_bf16(wc[q][2 * u], wc[q][2 * u + 1]);
+                            ps = fp16_bits_to_f32((sc[q][0] >> (16 * u)) & 0xFFFFu);
+                        } else if constexpr (FMT == FMT_FP8) {
+                            Bw = fp8_to_bf16(wc[q][2 * u], wc[q][2 * u + 1]);
+                            ps = __uint_as_float(sc[q][0]);
+                        } else if constexpr (FMT == FMT_MX) {
+                            Bw = fp4_to_bf16(wc[q][u], 1.0f);
+                            ps = e8m0_to_f32((sc[q][0] >> (8 * u)) & 0xFFu);
+                        } else {
+                            const uint32_t sv = (u < 2 ? sc[q][0] : sc[q][1]) >> nvsh;
+                            const float bs = (u & 1) ? e4m3_byte_to_f32<2>(sv) : e4m3_byte_to_f32<0>(sv);
+                            Bw = fp4_to_bf16_mul(wc[q][u], bs);
+                        }
+#pragma unroll
+                        for (int mb = 0; mb < MB; mb++) {
+                            if constexpr (POST) {
+                                const f32x4 tq = mfma(A[mb], Bw, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                                for (int i = 0; i < 4; i++)
+                                    part[q][mb][i] = __builtin_fmaf(ps, tq[i], part[q][mb][i]);
+                            } else {
+                                part[q][mb] = mfma(A[mb], Bw, part[q][mb]);
+                            }
+                        }
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < WT; q++)
+#pragma unroll
+                    for (int mb = 0; mb < MB; mb++) {
+                        acc[mb][q][0] += part[q][mb][0];
+                        acc[mb][q][1] += part[q][mb][1];
+                        acc[mb][q][2] += part[q][mb][2];
+                        acc[mb][q][3] += part[q][mb][3];
+                    }
+            }
+        }
+
+        // ---- epilogue (lane holds rows 4 gq + i of column r of each tile)
+        const int nmb = min(MB, (rows - b0 + 15) / 16);
+#pragma unroll
+        for (int q = 0; q < (DUAL ? NTG : WT); q++) {
+            const int col = (t0 + q) * 16 + r;
+            if (col >= ncols)
+                continue;
+            float h0 = g0, h1 = g1;
+            if constexpr (FMT == FMT_NV) {
+                if (q > 0) {  // tensor scales of the further tiles (NTG > 1)
+                    h0 = tensor_scale(a, col);
+                    if constexpr (DUAL)
+                        h1 = tensor_scale(a, Nh + col);
+                }
+            }
+#pragma unroll
+            for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int b = b0 + 16 * mb + 4 * gq + i;
+                    if (mb >= nmb || b >= rows)
+                        continue;
+                    if constexpr (DUAL)
+                        store_out_nt<OUTT>(ye, (int64_t)b * Nh + col,
+                                           silu(h0 * acc[mb][q][i]) * (h1 * acc[mb][q + NTG][i]));
+                    else
+                        store_out_nt<OUTT>(ye, (int64_t)b * a.N + col, h0 * acc[mb][q][i]);
+                }
+        }
+
+        if (!more)
+            break;
+        // ---- the next item's first stage (its loads were issued during
+        // this item) into buffer 0, once every wave is done with this item
+        __syncthreads();
+        xstore(it + 1, 0);
+        __syncthreads();
+        if (nst > 1)
+            xload(it + 1, 1);
+        else if (it + 2 < nitems)
+            xload(it + 2, 0);
+    }
+}
+
+// ------------------------------------------------------------------ host
+
+// Row-tile groups per expert (workgroups per expert).
+int moe_groups(const Problem &p)
+{
+    const bool dual = p.epi == QGEMM_EPI_SWIGLU;
+    const int64_t out_tiles = dual ? p.N / 2 / 16 : (p.N + 15) / 16;
+    const int per = 4 * (dual ? MOE_NTG_DUAL : MOE_NTG);
+    return (int)((out_tiles + per - 1) / per);
+}
+
+// Groups per workgroup: enough workgroups for about four rounds of two per
+// CU (whole experts per workgroup would leave the kernel waiting for the
+// experts with the most rows), each taking a run of one expert's groups.
+int moe_groups_per_wg(const Problem &p, int64_t E)
+{
+    const int ng = moe_groups(p);
+    const int64_t want = 2048;  // workgroups
+    const int64_t split = E >= want ? 1 : (want + E - 1) / E;
+    const int64_t gpw = (ng + (split < ng ? split : ng) - 1) / (split < ng ? split : ng);
+    return (int)gpw;
+}
+
+template <int FMT, int ACT, int OUTT, bool DUAL>
+static void launch_m(const KArgs &a, const Groups &g, int Nh, int ngroups, int gpw, hipStream_t st)
+{
+    constexpr int NTG = DUAL ? MOE_NTG_DUAL : MOE_NTG;
+    const dim3 grid((unsigned)((int64_t)g.E * ((ngroups + gpw - 1) / gpw)));
+    if (a.K % slab_k(FMT) == 0)
+        hipLaunchKernelGGL((moe_kernel<FMT, ACT, OUTT, DUAL, NTG, true>), grid, dim3(256), 0, st, a, g, Nh, ngroups,
+                           gpw);
+    else
+        hipLaunchKernelGGL((moe_kernel<FMT, ACT, OUTT, DUAL, NTG, false>), grid, dim3(256), 0, st, a, g, Nh, ngroups,
+                           gpw);
+}
+
+template <int FMT>
+static void launch_mf(const Problem &p, const KArgs &a, const Groups &g, hipStream_t st)
+{
+    const bool f32 = p.act == QGEMM_F32, o32 = p.out == QGEMM_F32;
+    const bool dual = p.epi == QGEMM_EPI_SWIGLU;
+    const int Nh = (int)(p.N / 2);
+    const int ng = moe_groups(p), gw = moe_groups_per_wg(p, g.E);
+    if (f32) {
+        if (o32) { if (dual) launch_m<FMT, ACT_F32, OUT_F32, true>(a, g, Nh, ng, gw, st); else launch_m<FMT, ACT_F32, OUT_F32, false>(a, g, Nh, ng, gw, st); }
+        else { if (dual) launch_m<FMT, ACT_F32, OUT_BF16, true>(a, g, Nh, ng, gw, st); else launch_m<FMT, ACT_F32, OUT_BF16, false>(a, g, Nh, ng, gw, st); }
+    } else {
+        if (o32) { if (dual) launch_m<FMT, ACT_BF16, OUT_F32, true>(a, g, Nh, ng, gw, st); else launch_m<FMT, ACT_BF16, OUT_F32, false>(a, g, Nh, ng, gw, st); }
+        else { if (dual) launch_m<FMT, ACT_BF16, OUT_BF16, true>(a, g, Nh, ng, gw, st); else launch_m<FMT, ACT_BF16, OUT_BF16, false>(a, g, Nh, ng, gw, st); }
+    }
+}
+
+hipError_t launch_moe(const Problem &p, const KArgs &a, const Groups &g, hipStream_t st)
+{
+    switch (p.fmt) {
+    case FMT_Q8: launch_mf<FMT_Q8>(p, a, g, st); break;
+    case FMT_MX: launch_mf<FMT_MX>(p, a, g, st); break;
+    case FMT_FP8: launch_mf<FMT_FP8>(p, a, g, st); break;
+    default: launch_mf<FMT_NV>(p, a, g, st); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace qg

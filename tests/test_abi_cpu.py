@@ -319,6 +319,32 @@ def test_grouped_argument_checks():
     assert L.qgemm_run_grouped(h, 4, 0, None, None, None, None, None) == q.OK
     assert L.qgemm_run_grouped(h, 4, 10, fake, None, fake, fake, None) == q.EINVAL   # null offsets
     L.qgemm_destroy(h)
-    assert L.qgemm_create(ctypes.byref(h), 2, 1, 0, 0, 1, 256, 512, 1) == q.OK        # forced skinny
+    assert L.qgemm_create(ctypes.byref(h), 2, 0, 0, 0, 0, 256, 512, 1) == q.OK        # skinny, fp32 math
     assert L.qgemm_run_grouped(h, 4, 10, fake, fake, fake, fake, None) == q.ENOTSUP
     L.qgemm_destroy(h)
+    assert L.qgemm_create(ctypes.byref(h), 2, 1, 0, 0, 1, 256, 512, 4) == q.OK        # forced GEMV
+    assert L.qgemm_run_grouped(h, 4, 10, fake, fake, fake, fake, None) == q.ENOTSUP
+    L.qgemm_destroy(h)
+
+
+def test_grouped_route_choice():
+    """qgemm_grouped_tier (host only): bf16 math with fewer than 64 rows per
+    expert on average streams the experts (small-batch route), otherwise the
+    large-batch kernel; forced tiers and fp32 math as documented."""
+    cases = [  # (act, math, flags, E, T) -> tier
+        ((1, 1, 0, 512, 20480), "skinny"),   # the benchmark's routed MoE: 40 rows per expert
+        ((1, 1, 0, 4, 255), "skinny"),
+        ((1, 1, 0, 4, 256), "tiled"),        # 64 rows per expert
+        ((0, 1, 0, 4, 10), "skinny"),        # fp32 activations, bf16 math
+        ((0, 0, 0, 4, 10), "tiled"),         # fp32-faithful math
+        ((1, 1, 2, 4, 10), "tiled"),         # forced large-batch
+        ((1, 1, 1, 4, 1000), "skinny"),      # forced small-batch, bf16 math
+        ((0, 0, 1, 4, 10), "invalid"),       # forced small-batch, fp32 math
+        ((1, 1, 4, 4, 10), "invalid"),       # forced GEMV
+        ((1, 1, 0, 0, 10), "invalid"),       # E = 0
+    ]
+    for (act, math, flags, E, T), want in cases:
+        plan = q.Plan("nvfp4", 256, 512, act="f32" if act == 0 else "bf16",
+                      math="fp32" if math == 0 else "bf16",
+                      tier={0: None, 1: "skinny", 2: "tiled", 4: "gemv"}[flags])
+        assert plan.grouped_tier(E, T) == want, (act, math, flags, E, T)

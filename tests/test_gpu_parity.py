@@ -889,7 +889,29 @@ def test_swiglu_forced_skinny_above_16_is_not_supported():
 
 # ------------------------------------------------------------ routed experts
 
-def _grouped_case(fmt, act, out, epi, E, n, k, offsets, seed, math="bf16"):
+def _solo_rows(plan, tier, x_rows, buf):
+    """One expert's rows as the routed call computes them: qgemm_run of that
+    expert alone, without a workspace, in the route's tier (the small-batch
+    route in calls of at most 16 rows: a row's result there does not depend
+    on the other rows, and a SwiGLU plan forced to that tier takes B <= 16)."""
+    solo = q.Plan(plan.fmt, plan.N, plan.K, act=plan.act, out=plan.out, epilogue=plan.epilogue,
+                  math=plan.math, tier=tier)
+    if tier == "tiled":
+        return run(solo, x_rows, buf, workspace=None)
+    return np.concatenate([run(solo, x_rows[i:i + 16], buf, workspace=None)
+                           for i in range(0, x_rows.shape[0], 16)])
+
+
+def _assert_experts_bitwise(plan, offsets, x, bufs, y, tier):
+    for e in range(len(offsets) - 1):
+        r0, r1 = offsets[e], offsets[e + 1]
+        if r1 > r0:
+            ye = _solo_rows(plan, tier, x[r0:r1], bufs[e])
+            assert np.array_equal(ye.astype(np.float32).view(np.uint32),
+                                  y[r0:r1].astype(np.float32).view(np.uint32)), (tier, e)
+
+
+def _grouped_case(fmt, act, out, epi, E, n, k, offsets, seed, math="bf16", tier=None):
     ws = [synth.gen_expert_weights(fmt, n, k, e, seed=seed, swiglu=epi == "swiglu") for e in range(E)]
     T = int(offsets[-1])
     xf = synth.gen_x_f32(T, k, seed=seed + 1)
@@ -897,7 +919,7 @@ def _grouped_case(fmt, act, out, epi, E, n, k, offsets, seed, math="bf16"):
     bufs = [w_dev(w) for w in ws]
     table = torch.tensor([b.data_ptr() for b in bufs], dtype=torch.int64, device=_dev())
     off = torch.from_numpy(np.asarray(offsets, dtype=np.int32)).to(_dev())
-    plan = q.Plan(fmt, n, k, act=act, out=out, epilogue=epi, math=math)
+    plan = q.Plan(fmt, n, k, act=act, out=out, epilogue=epi, math=math, tier=tier)
     y = y_new(plan, T)
     plan.run_grouped(x_dev(x), table, off, y)
     torch.cuda.synchronize()
@@ -908,25 +930,45 @@ def _grouped_case(fmt, act, out, epi, E, n, k, offsets, seed, math="bf16"):
                                              ("mxfp4", "bf16", "f32", "none"),
                                              ("q8_0", "f32", "f32", "none"),
                                              ("fp8", "bf16", "f32", "swiglu")])
-def test_grouped_matches_oracle_and_per_expert_calls(fmt, act, out, epi):
-    """Routed experts in one launch: each expert's rows match the fp64 oracle
-    and, bit for bit, a large-batch call of that expert alone (empty experts,
-    one-row experts and an expert spanning three row tiles included)."""
+@pytest.mark.parametrize("tier", ["tiled", "skinny"])
+def test_grouped_matches_oracle_and_per_expert_calls(fmt, act, out, epi, tier):
+    """Routed experts in one launch, on both routes (forced: the large-batch
+    kernel, and the streaming kernel over (expert, row-tile group) items):
+    each expert's rows match the fp64 oracle and, bit for bit, calls of that
+    expert alone in the route's tier (empty experts, one-row experts, an
+    expert of 300 rows, i.e. five passes of 64 rows, and ragged ones)."""
     n, k = 256, 512
     rows = [5, 0, 1, 300, 17, 0, 128, 129, 2, 40]
     offsets = np.concatenate([[0], np.cumsum(rows)])
     E = len(rows)
-    ws, bufs, x, y, plan = _grouped_case(fmt, act, out, epi, E, n, k, offsets, seed=3)
+    ws, bufs, x, y, plan = _grouped_case(fmt, act, out, epi, E, n, k, offsets, seed=3, tier=tier)
+    assert plan.grouped_tier(E, int(offsets[-1])) == tier
     ref = oracle.gemm_grouped(ws, offsets, x, swiglu_epi=epi == "swiglu")
     err = oracle.rel_fro(y, ref)
-    print(f"grouped {fmt} {epi} rel_fro={err:.3e}")
+    print(f"grouped {tier} {fmt} {epi} rel_fro={err:.3e}")
     assert err <= TOL_BF16
-    solo = q.Plan(fmt, n, k, act=act, out=out, epilogue=epi, math="bf16", tier="tiled")
-    for e in range(E):
-        r0, r1 = offsets[e], offsets[e + 1]
-        if r1 > r0:
-            ye = run(solo, x[r0:r1], bufs[e], workspace=None)
-            assert np.array_equal(ye.view(np.uint64), y[r0:r1].view(np.uint64)), e
+    _assert_experts_bitwise(plan, offsets, x, bufs, y, tier)
+
+
+@pytest.mark.parametrize("fmt,epi", [("nvfp4", "swiglu"), ("mxfp4", "none"), ("q8_0", "swiglu"),
+                                     ("fp8", "none")])
+def test_grouped_streaming_route_k_tails_and_wide_rows(fmt, epi):
+    """The streaming route with K not a multiple of the slab (K = 1056: the
+    last slab has padding units; NVFP4 also K = 1040, half a unit), more
+    output tiles than one workgroup covers (N = 608, a partial group) and
+    automatic routing (T < 64 E): oracle bound and per-expert bitwise."""
+    ks = (1056, 1040) if fmt == "nvfp4" else (1056,)
+    for k in ks:
+        n = 608
+        rows = [33, 1, 0, 64, 65, 16, 0, 7]
+        offsets = np.concatenate([[0], np.cumsum(rows)])
+        E = len(rows)
+        ws, bufs, x, y, plan = _grouped_case(fmt, "bf16", "f32", epi, E, n, k, offsets, seed=11)
+        assert plan.grouped_tier(E, int(offsets[-1])) == "skinny"
+        err = oracle.rel_fro(y, oracle.gemm_grouped(ws, offsets, x, swiglu_epi=epi == "swiglu"))
+        print(f"grouped streaming {fmt} {epi} K={k} rel_fro={err:.3e}")
+        assert err <= TOL_BF16
+        _assert_experts_bitwise(plan, offsets, x, bufs, y, "skinny")
 
 
 @pytest.mark.parametrize("fmt", ["q8_0", "mxfp4", "nvfp4", "fp8"])
@@ -942,12 +984,8 @@ def test_grouped_fp32_math(fmt):
     err = oracle.rel_fro(y, oracle.gemm_grouped(ws, offsets, x))
     print(f"grouped fp32 {fmt} rel_fro={err:.3e}")
     assert err <= TOL_FP32
-    solo = q.Plan(fmt, n, k, act="f32", out="f32", math="fp32", tier="tiled")
-    for e in range(E):
-        r0, r1 = offsets[e], offsets[e + 1]
-        if r1 > r0:
-            ye = run(solo, x[r0:r1], bufs[e], workspace=None)
-            assert np.array_equal(ye.view(np.uint64), y[r0:r1].view(np.uint64)), e
+    assert plan.grouped_tier(E, int(offsets[-1])) == "tiled"
+    _assert_experts_bitwise(plan, offsets, x, bufs, y, "tiled")
 
 
 def test_grouped_graph_capture_replays():
@@ -990,8 +1028,8 @@ def test_grouped_single_expert_and_empty():
     n, k = 128, 256
     offsets = np.array([0, 77])
     ws, bufs, x, y, plan = _grouped_case("nvfp4", "bf16", "f32", "none", 1, n, k, offsets, seed=7)
-    solo = q.Plan("nvfp4", n, k, act="bf16", out="f32", tier="tiled")
-    assert np.array_equal(run(solo, x, bufs[0], workspace=None), y)
+    assert plan.grouped_tier(1, 77) == "tiled"  # 77 rows per expert: the large-batch route
+    _assert_experts_bitwise(plan, offsets, x, bufs, y, "tiled")
     # T = 0: nothing enqueued, OK returned
     table = torch.tensor([bufs[0].data_ptr()], dtype=torch.int64, device=_dev())
     off = torch.zeros(2, dtype=torch.int32, device=_dev())
@@ -1005,8 +1043,9 @@ def test_grouped_benched_moe_shape():
     2 x 512 gate+up rows, K = 2048, top-10 routing of 2048 tokens (20,480
     rows; eight generated experts copied into 512 buffers, as the benchmark
     does).  Every (expert, 128-column) output tile within the bf16 bound on
-    at least 64 oracle samples, and every expert's rows bitwise those of an
-    unsplit large-batch call of that expert alone."""
+    at least 64 oracle samples, and every expert's rows bitwise those of
+    calls of that expert alone in the route's tier (the streaming route:
+    40 rows per expert on average)."""
     E, topk, tokens, nh, K = 512, 10, 2048, 512, 2048
     distinct = [synth.gen_expert_weights("nvfp4", 2 * nh, K, e, swiglu=True) for e in range(8)]
     packed = [w_dev(w) for w in distinct]
@@ -1017,6 +1056,7 @@ def test_grouped_benched_moe_shape():
     assert T == tokens * topk
     x = synth.gen_x_bf16(tokens, K)[tok]
     plan = q.Plan("nvfp4", 2 * nh, K, act="bf16", out="bf16", epilogue="swiglu")
+    assert plan.grouped_tier(E, T) == "skinny"
     y = y_new(plan, T)
     plan.run_grouped(x_dev(x), table, torch.from_numpy(offsets.astype(np.int32)).to(_dev()), y)
     torch.cuda.synchronize()
@@ -1040,16 +1080,16 @@ def test_grouped_benched_moe_shape():
     print(f"routed moe 512 experts rel_fro(sampled)={err:.3e}")
     assert err <= TOL_BF16
     _assert_tiles(y[bi, ji], ref, tid, live.size * ct, TOL_BF16, "routed moe per (expert, tile)")
-    solo = q.Plan("nvfp4", 2 * nh, K, act="bf16", out="bf16", epilogue="swiglu", tier="tiled")
-    yb = y.astype(np.float32).view(np.uint32)
     for e in live:
         r0, r1 = offsets[e], offsets[e + 1]
-        ye = run(solo, x[r0:r1], bufs[e], workspace=None)
-        assert np.array_equal(ye.astype(np.float32).view(np.uint32), yb[r0:r1]), e
+        ye = _solo_rows(plan, "skinny", x[r0:r1], bufs[e])
+        assert np.array_equal(ye.astype(np.float32).view(np.uint32),
+                              y[r0:r1].astype(np.float32).view(np.uint32)), e
 
 
 @pytest.mark.parametrize("case", ["decreasing", "first_not_zero", "last_not_T", "negative"])
-def test_grouped_bad_offsets_do_nothing_and_report(case):
+@pytest.mark.parametrize("tier", ["tiled", "skinny"])
+def test_grouped_bad_offsets_do_nothing_and_report(case, tier):
     """Offsets that break their rules (non-decreasing, offsets[0] = 0,
     offsets[E] = T): the launch writes nothing (y keeps its NaN fill) and
     sets QGEMM_DEV_BAD_OFFSETS; good offsets afterwards run normally and set
@@ -1072,7 +1112,8 @@ def test_grouped_bad_offsets_do_nothing_and_report(case):
     table = torch.tensor([b.data_ptr() for b in bufs], dtype=torch.int64, device=_dev())
     x = synth.gen_x_bf16(T, k, seed=10)
     xd = x_dev(x)
-    plan = q.Plan("mxfp4", n, k, act="bf16", out="f32")
+    plan = q.Plan("mxfp4", n, k, act="bf16", out="f32", tier=tier)
+    assert plan.grouped_tier(len(rows), T) == tier
     q.device_status(clear=True)
     y = y_new(plan, T)
     plan.run_grouped(xd, table, torch.from_numpy(bad).to(_dev()), y)
