@@ -7,20 +7,21 @@
 // per wave and the NTG matching up tiles, so SiLU(G) * U is formed in the
 // lane that holds both).  An expert's groups are split over a few
 // workgroups with consecutive ids on one XCD, so the expert's activation rows
-// are read from that XCD's L2.  A workgroup walks its (group, pass) items in order and
-// loads each item's first activation stage and weight slabs while the item
-// before it finishes.
+// are read from that XCD's L2.  A workgroup walks the slabs of its (group,
+// pass) items as one sequence, loading D slabs ahead across item boundaries.
 //
 //  * The expert's rows are taken 16 * MB at a time (one pass for up to 64
-//    rows).  Their activations are staged in LDS KCH slabs at a time (two
-//    stages, the next one loaded while the current one is used), already
-//    in MFMA fragment order (16-byte entry [slab][16-row group][unit][lane]),
-//    rounded to bf16 on the way for fp32 input, zero past the last row and
-//    past K; only the 16-row groups that hold rows are staged (all MB are
-//    multiplied: fewer branches and registers than skipping the empty ones).
+//    rows).  Each slab's activations are loaded into registers together with
+//    its weights, written into one of two LDS stages one step before they
+//    are used, in MFMA fragment order (16-byte entry [16-row group][unit]
+//    [lane]), zero past the last row and past K, fp32 rounded to bf16; only
+//    the 16-row groups that hold rows are loaded (all MB are multiplied:
+//    fewer branches and registers than skipping the empty ones).  The
+//    measured alternative, gfx950's direct loads into LDS, lets the compiler
+//    order every fragment read after the newest such load, which serialises
+//    the walk.
 //  * Each lane's 16-byte chunk of a weight slab is its B operand, decoded in
-//    registers; waves keep D slabs of their row tiles in flight through the
-//    LDS stages (loads of dead slabs go through empty buffer resources).
+//    registers (loads of dead slabs go through empty buffer resources).
 //  * Summation order, the small-batch tier's: per (slab, row tile) its units
 //    in order into a partial from zero (Q8_0 / MXFP4 / FP8 block scales
 //    applied to the block's fp32 partial, NVFP4's E4M3 scale folded into the
@@ -36,25 +37,25 @@
 namespace qg {
 
 constexpr int MOE_MB = 4;        // 16-row groups per pass
-constexpr int MOE_KCH = 1;       // slabs of activations per LDS stage (two stages in LDS)
-constexpr int MOE_D = 2;         // weight slabs in flight per wave (measured: deeper is slower)
+constexpr int MOE_D = 2;         // slabs (weights and activations) in flight per wave
 constexpr int MOE_NTG = 2;       // output row tiles per wave
 constexpr int MOE_NTG_DUAL = 1;  // with SwiGLU: gate tiles per wave (and as many up tiles)
 
 template <int FMT, int ACT, int OUTT, bool DUAL, int NTG, bool FULLK>
-__global__ __launch_bounds__(256, 2) void moe_kernel(KArgs a, Groups grp, int Nh, int ngroups, int gpw)
+__global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void moe_kernel(KArgs a, Groups grp, int Nh, int ngroups, int gpw)
 {
     constexpr int KS = slab_k(FMT);
     constexpr int U = KS / 32;                 // 32-wide units per slab
-    constexpr int MB = MOE_MB, KCH = MOE_KCH, D = MOE_D;
+    constexpr int MB = MOE_MB, D = MOE_D;
     constexpr int WT = DUAL ? 2 * NTG : NTG;   // row tiles per wave
     constexpr int XSZ = ACT == ACT_F32 ? 4 : 2;
     constexpr int SBYTES = scale_bytes_per_slab(FMT);
     constexpr int SLAB_E = MB * U * 64;        // LDS entries per staged slab
-    constexpr int NXF = (KCH * MB * U + 3) / 4;  // activation fragments per wave and stage
+    constexpr int NXF = (MB * U + 3) / 4;      // activation fragments per wave and slab
     constexpr bool POST = FMT != FMT_NV;
 
-    __shared__ u32x4 xs[2 * KCH * SLAB_E];  // two stages
+    __shared__ u32x4 xs[2 * SLAB_E];  // two activation stages of one slab
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -96,12 +97,11 @@ __global__ __launch_bounds__(256, 2) void moe_kernel(KArgs a, Groups grp, int Nh
     const __amdgpu_buffer_rsrc_t xres = make_rsrc(xe, (int64_t)rows * a.K * XSZ);
     const uint32_t nvsh = 8 * (gq >> 1);  // NVFP4: this lane's scale byte within a unit's pair
 
-    // Work items: (row-tile group g, pass b0 over 16 * MB rows), g major.  An
-    // item's first activation stage and first D weight slabs are loaded while
-    // the item before it finishes, so a workgroup pays the load latency once.
+    // Work items: (row-tile group g, pass b0 over 16 * MB rows), g major; the
+    // walk over their slabs does not stop between items, so a workgroup pays
+    // the load latency once.
     const int npass = (rows + 16 * MB - 1) / (16 * MB);
     const int nitems = (g_end - g_beg) * npass;
-    const int nst = (a.S + KCH - 1) / KCH;     // activation stages per item
     const int Sp = (a.S + D - 1) / D * D;      // slabs walked per item (whole ring turns)
 
     // first output row tile of this wave in item it's group (with SwiGLU the
@@ -137,77 +137,82 @@ __global__ __launch_bounds__(256, 2) void moe_kernel(KArgs a, Groups grp, int Nh
         }
     };
 
-    // ---- activation stages.  Fragment (slab sl of the stage, group mb, unit
-    // u) is one 1 KB block of LDS entries, lane l holding row 16 mb + l % 16,
-    // columns 8 (l / 16) .. + 7 of the unit.  Wave w loads fragments w, w + 4,
+    // ---- activation slabs.  Fragment (16-row group mb, unit u) of a slab is
+    // one 1 KB block of LDS entries, lane l holding row 16 mb + l % 16,
+    // columns 8 (l / 16) .. + 7 of the unit; wave w loads fragments w, w + 4,
     // ... (indices past the last repeat it: the same bytes to the same place,
-    // no branch).  Stage c + 1 is loaded at the start of stage c, before the
-    // weight loads issued while stage c is computed, so waiting for it never
-    // waits for weight loads issued after it; it is stored at the start of
-    // stage c + 1 into the buffer stage c - 1 used (every wave passed the
-    // barrier that opened stage c after finishing stage c - 1).
-    u32x4 xv0[NXF], xv1[NXF];
-    auto xfrag = [&](int b0, int nfr, int c, int i, int &dst, int &row, int &k) {
+    // no branch).  Position p of the walk is slab p % Sp of item p / Sp; its
+    // activations go into register slot p % D and its weights into ring slot
+    // p % D at step p - D, activations first, so waiting for them never waits
+    // for a later weight load.  At step p - 1 they are written (masked past
+    // the rows and past K, fp32 rounded to bf16) into LDS stage p % 2, which
+    // the barrier opening step p makes visible; the same barrier frees stage
+    // (p + 1) % 2, read at step p - 1.  Positions past the last item or slab
+    // load nothing but zeros (empty resources, offsets past the end).
+    u32x4 xv0[D][NXF], xv1[D][NXF];
+    auto xfrag = [&](int b0, int i, int s2, int &mb, int &u, int &row, int &k) {
+        const int nfr = U * min(MB, (rows - b0 + 15) / 16);  // fragments of a slab
         const int f = min(wid + 4 * i, nfr - 1);
-        const int per = nfr / KCH;  // fragments per slab
-        const int sl = f / per, rem = f % per;
-        const int mb = rem / U, u = rem % U;
+        mb = f / U;
+        u = f % U;
         row = b0 + 16 * mb + r;
-        k = (c * KCH + sl) * KS + 32 * u + 8 * gq;
-        dst = (c & 1) * (KCH * SLAB_E) + ((sl * MB + mb) * U + u) * 64 + lane;
+        k = s2 * KS + 32 * u + 8 * gq;
     };
-    auto nfr_of = [&](int b0) { return KCH * min(MB, (rows - b0 + 15) / 16) * U; };
-    auto xload = [&](int it, int c) {  // stage c of item it into registers
-        const int b0 = b0_of(it), nfr = nfr_of(b0);
+    auto xld = [&](int slot, int p) {  // activations of position p into slot
+        const int it2 = p / Sp, s2 = p % Sp;
+        const bool live = it2 < nitems && s2 < a.S;
+        const int b0 = b0_of(min(it2, nitems - 1));
 #pragma unroll
         for (int i = 0; i < NXF; i++) {
-            int dst, row, k;
-            xfrag(b0, nfr, c, i, dst, row, k);
-            const int vo = (min(row, rows - 1) * a.K + min(k, a.K - 8)) * XSZ;
-            xv0[i] = bload16(xres, vo, 0);
+            int mb, u, row, k;
+            xfrag(b0, i, s2, mb, u, row, k);
+            const int vo = live && row < rows && k < a.K ? (row * a.K + k) * XSZ : 0x7FFFFFE0;
+            xv0[slot][i] = bload16(xres, vo, 0);
             if constexpr (ACT == ACT_F32)
-                xv1[i] = bload16(xres, vo + 16, 0);
+                xv1[slot][i] = bload16(xres, vo + 16, 0);
         }
     };
-    auto xstore = [&](int it, int c) {  // the registers of stage c of item it into its LDS buffer
-        const int b0 = b0_of(it), nfr = nfr_of(b0);
+    auto xst = [&](int slot, int p) {  // slot (position p) into LDS stage p % 2
+        const int it2 = p / Sp, s2 = p % Sp;
+        const int b0 = b0_of(min(it2, nitems - 1));
+        u32x4 *st = xs + (p & 1) * SLAB_E;
 #pragma unroll
         for (int i = 0; i < NXF; i++) {
-            int dst, row, k;
-            xfrag(b0, nfr, c, i, dst, row, k);
-            const uint32_t m = keep_mask(row < rows && k < a.K);  // K % 16 == 0: 8 columns all in or out
+            int mb, u, row, k;
+            xfrag(b0, i, s2, mb, u, row, k);
             u32x4 v;
             if constexpr (ACT == ACT_F32) {
                 float fv[8];
 #pragma unroll
                 for (int e2 = 0; e2 < 4; e2++) {
-                    fv[e2] = __uint_as_float(xv0[i][e2] & m);
-                    fv[4 + e2] = __uint_as_float(xv1[i][e2] & m);
+                    fv[e2] = __uint_as_float(xv0[slot][i][e2]);
+                    fv[4 + e2] = __uint_as_float(xv1[slot][i][e2]);
                 }
                 v = __builtin_bit_cast(u32x4, split_f32<1, 8>(fv).t[0]);
             } else {
-                v = masked(xv0[i], m);
+                v = xv0[slot][i];
             }
-            xs[dst] = v;
+            st[(mb * U + u) * 64 + lane] = v;
         }
     };
+    // weights of position p into ring slot j (tiles of p's item)
+    auto wld = [&](int j, int p) {
+        const int it2 = p / Sp, s2 = p % Sp;
+        const bool live = it2 < nitems;
+        wload(j, t0_of(live ? it2 : nitems - 1), live ? s2 : a.S);
+    };
 
-    // ---- the first item's first stage and ring
-    xload(0, 0);
+    // ---- the first D positions, and position 0 into LDS stage 0
 #pragma unroll
-    for (int j = 0; j < D; j++)
-        wload(j, t0_of(0), j);
-    xstore(0, 0);
-    __syncthreads();
-    if (nst > 1)
-        xload(0, 1);
-    else if (nitems > 1)
-        xload(1, 0);
+    for (int j = 0; j < D; j++) {
+        xld(j, j);
+        __builtin_amdgcn_sched_barrier(0);
+        wld(j, j);
+    }
+    xst(0, 0);
 
     for (int it = 0; it < nitems; it++) {
         const int t0 = t0_of(it), b0 = b0_of(it);
-        const bool more = it + 1 < nitems;
-        const int t0n = more ? t0_of(it + 1) : t0;
         // NVFP4 tensor scales of this item's columns, loaded now, used at the end
         float g0 = 1.f, g1 = 1.f;
         if constexpr (FMT == FMT_NV) {
@@ -227,15 +232,14 @@ __global__ __launch_bounds__(256, 2) void moe_kernel(KArgs a, Groups grp, int Nh
 #pragma unroll
             for (int j = 0; j < D; j++) {
                 const int s = s0 + j;
-                if (s > 0 && s < a.S && s % KCH == 0) {  // stage s / KCH begins (uniform)
-                    const int c = s / KCH;
-                    xstore(it, c);
-                    __syncthreads();
-                    if (c + 1 < nst)
-                        xload(it, c + 1);
-                    else if (more)
-                        xload(it + 1, 0);
-                }
+                const int p = it * Sp + s;
+                __syncthreads();
+                // The next position's activations, into the other stage.  Only
+                // the weight loads of that position (2 WT) were issued after
+                // them; the explicit wait says so (the compiler, left alone,
+                // drains every load here).
+                __builtin_amdgcn_s_waitcnt(0xF70 | (2 * WT));  // vmcnt(2 WT), expcnt and lgkmcnt untouched
+                xst((j + 1) % D, p + 1);
                 u32x4 wc[WT];
                 uint32_t sc[WT][2];
 #pragma unroll
@@ -244,18 +248,16 @@ __global__ __launch_bounds__(256, 2) void moe_kernel(KArgs a, Groups grp, int Nh
                     sc[q][0] = sr[j][q][0];
                     sc[q][1] = sr[j][q][1];
                 }
-                // refill: this item's slab s + D, else the next item's slab
-                // s + D - Sp (slot j keeps slab j mod D), else nothing
-                if (s + D < a.S)
-                    wload(j, t0, s + D);
-                else
-                    wload(j, t0n, more && s + D >= Sp ? s + D - Sp : a.S);
-                if (s >= a.S)
-                    continue;  // past the last slab (uniform)
-                const u32x4 *slab = xs + ((s / KCH) & 1) * (KCH * SLAB_E) + (s % KCH) * SLAB_E;
-                // units within K (all of them when K is a whole number of
-                // slabs: no per-unit branch, so one slab's decode and MFMAs
-                // form one block the compiler can interleave)
+                xld(j, p + D);
+                __builtin_amdgcn_sched_barrier(0);
+                wld(j, p + D);
+                __builtin_amdgcn_sched_barrier(0);
+                if (!FULLK && s >= a.S)
+                    continue;  // padding of the walk (uniform)
+                const u32x4 *slab = xs + (p & 1) * SLAB_E;
+                // units within K (FULLK: K is a whole number of slabs and of
+                // ring turns, so no unit or padding branch, and one step's
+                // loads, decode and MFMAs form one block)
                 const int nu = FULLK ? U : min(U, (a.K - s * KS + 31) / 32);
                 // per (row tile, group) a partial from zero over the units in
                 // order; every group is multiplied (groups past the rows hold
@@ -354,17 +356,6 @@ __global__ __launch_bounds__(256, 2) void moe_kernel(KArgs a, Groups grp, int Nh
                 }
         }
 
-        if (!more)
-            break;
-        // ---- the next item's first stage (its loads were issued during
-        // this item) into buffer 0, once every wave is done with this item
-        __syncthreads();
-        xstore(it + 1, 0);
-        __syncthreads();
-        if (nst > 1)
-            xload(it + 1, 1);
-        else if (it + 2 < nitems)
-            xload(it + 2, 0);
     }
 }
 
@@ -396,7 +387,7 @@ static void launch_m(const KArgs &a, const Groups &g, int Nh, int ngroups, int g
 {
     constexpr int NTG = DUAL ? MOE_NTG_DUAL : MOE_NTG;
     const dim3 grid((unsigned)((int64_t)g.E * ((ngroups + gpw - 1) / gpw)));
-    if (a.K % slab_k(FMT) == 0)
+    if (a.K % slab_k(FMT) == 0 && a.S % MOE_D == 0)  // no unit masking, no padding slabs
         hipLaunchKernelGGL((moe_kernel<FMT, ACT, OUTT, DUAL, NTG, true>), grid, dim3(256), 0, st, a, g, Nh, ngroups,
                            gpw);
     else
