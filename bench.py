@@ -368,7 +368,9 @@ def bench_moe(steps):
     wbytes = sum(b.numel() for b in bufs)
     rec = {"us": round(ms * 1e3, 2), "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-           "weight_GBs": round(wbytes / (ms * 1e-3) / 1e9, 1), "rows": T, "experts": E, "top_k": topk}
+           "weight_GBs": round(wbytes / (ms * 1e-3) / 1e9, 1),
+           "hbm_frac": round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "route": plan.grouped_tier(E, T), "rows": T, "experts": E, "top_k": topk}
     log(f"[bench] moe {rec}")
     return rec
 

@@ -17,6 +17,9 @@
 //           accumulator (4 cvt, 4 mul, 4 fma per lane): the int8 tier's loop
 //   mode 4  mode 0 from a zero accumulator plus a per-block fp32 scale FMA
 //           (4 fma per lane): the block-scale pattern of the fp32-faithful path
+// (modes 3 and 4 give every chain and trip its own operand, one XOR each: a
+// product from a zero accumulator with loop-invariant operands would be
+// hoisted out of the loop, and equal ones merged)
 //
 // Operands are derived from the thread id and a seed so nothing folds; each
 // wave writes one word to sink.  Throughput = MFMAs x 2 x 16 x 16 x K / time.
@@ -54,12 +57,15 @@ __global__ __launch_bounds__(512) void mfma_rate_kernel(int iters, uint32_t seed
             } else if constexpr (MODE == 2) {
                 iacc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a8, a8, iacc[j], 0, 0, 0);
             } else if constexpr (MODE == 3) {
-                const i32x4 t = __builtin_amdgcn_mfma_i32_16x16x32_i8(a4, a4, i32x4{0, 0, 0, 0}, 0, 0, 0);
+                // operands differ per trip (one XOR a trip), so the product
+                // from a zero accumulator cannot be hoisted out of the loop
+                const i32x4 t = __builtin_amdgcn_mfma_i32_16x16x32_i8(a4 ^ (long)(it * NC + j), a4, i32x4{0, 0, 0, 0}, 0, 0, 0);
 #pragma unroll
                 for (int e = 0; e < 4; e++)
                     acc[j][e] = __builtin_fmaf(dw * dx[e], (float)t[e], acc[j][e]);
             } else {
-                const f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, ab, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                const bf16x8 abi = __builtin_bit_cast(bf16x8, bits ^ (uint32_t)((it * NC + j) & 0x003F003F));
+                const f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abi, ab, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
                 for (int e = 0; e < 4; e++)
                     acc[j][e] = __builtin_fmaf(dw, t[e], acc[j][e]);

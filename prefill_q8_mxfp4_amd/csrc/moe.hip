@@ -40,9 +40,10 @@ constexpr int MOE_MB = 4;        // 16-row groups per pass
 constexpr int MOE_D = 2;         // slabs (weights and activations) in flight per wave
 constexpr int MOE_NTG = 2;       // output row tiles per wave
 constexpr int MOE_NTG_DUAL = 1;  // with SwiGLU: gate tiles per wave (and as many up tiles)
+constexpr int MOE_W = 4;         // waves per workgroup (8, with half the activation staging, measured slower)
 
 template <int FMT, int ACT, int OUTT, bool DUAL, int NTG, bool FULLK>
-__global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64 * MOE_W, 8 / MOE_W) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void moe_kernel(KArgs a, Groups grp, int Nh, int ngroups, int gpw)
 {
     constexpr int KS = slab_k(FMT);
@@ -52,7 +53,7 @@ void moe_kernel(KArgs a, Groups grp, int Nh, int ngroups, int gpw)
     constexpr int XSZ = ACT == ACT_F32 ? 4 : 2;
     constexpr int SBYTES = scale_bytes_per_slab(FMT);
     constexpr int SLAB_E = MB * U * 64;        // LDS entries per staged slab
-    constexpr int NXF = (MB * U + 3) / 4;      // activation fragments per wave and slab
+    constexpr int NXF = (MB * U + MOE_W - 1) / MOE_W;  // activation fragments per wave and slab
     constexpr bool POST = FMT != FMT_NV;
 
     __shared__ u32x4 xs[2 * SLAB_E];  // two activation stages of one slab
@@ -77,7 +78,7 @@ void moe_kernel(KArgs a, Groups grp, int Nh, int ngroups, int gpw)
     // ---- offsets check (all of them, before any use; this expert's own
     // offsets and weights pointer are loaded in the same round)
     int bad = 0;
-    for (int e2 = tid; e2 < grp.E; e2 += 256) {
+    for (int e2 = tid; e2 < grp.E; e2 += 64 * MOE_W) {
         const int lo2 = grp.off[e2], hi2 = grp.off[e2 + 1];
         bad |= (hi2 < lo2) | (e2 == 0 && lo2 != 0) | (e2 == grp.E - 1 && hi2 != grp.T);
     }
@@ -107,7 +108,7 @@ void moe_kernel(KArgs a, Groups grp, int Nh, int ngroups, int gpw)
     // first output row tile of this wave in item it's group (with SwiGLU the
     // up tiles are Nh/16 further on); tiles past the last compute on a copy of
     // it and are never stored
-    auto t0_of = [&](int it) { return ((g_beg + it / npass) * 4 + wid) * NTG; };
+    auto t0_of = [&](int it) { return ((g_beg + it / npass) * MOE_W + wid) * NTG; };
     auto b0_of = [&](int it) { return it % npass * 16 * MB; };
     auto tile_of = [&](int t0, int j) -> int64_t {
         const int rt = DUAL ? (j < NTG ? t0 + j : Nh / 16 + t0 + j - NTG) : t0 + j;
@@ -152,7 +153,7 @@ void moe_kernel(KArgs a, Groups grp, int Nh, int ngroups, int gpw)
     u32x4 xv0[D][NXF], xv1[D][NXF];
     auto xfrag = [&](int b0, int i, int s2, int &mb, int &u, int &row, int &k) {
         const int nfr = U * min(MB, (rows - b0 + 15) / 16);  // fragments of a slab
-        const int f = min(wid + 4 * i, nfr - 1);
+        const int f = min(wid + MOE_W * i, nfr - 1);
         mb = f / U;
         u = f % U;
         row = b0 + 16 * mb + r;
@@ -366,7 +367,7 @@ int moe_groups(const Problem &p)
 {
     const bool dual = p.epi == QGEMM_EPI_SWIGLU;
     const int64_t out_tiles = dual ? p.N / 2 / 16 : (p.N + 15) / 16;
-    const int per = 4 * (dual ? MOE_NTG_DUAL : MOE_NTG);
+    const int per = MOE_W * (dual ? MOE_NTG_DUAL : MOE_NTG);
     return (int)((out_tiles + per - 1) / per);
 }
 
@@ -388,10 +389,10 @@ static void launch_m(const KArgs &a, const Groups &g, int Nh, int ngroups, int g
     constexpr int NTG = DUAL ? MOE_NTG_DUAL : MOE_NTG;
     const dim3 grid((unsigned)((int64_t)g.E * ((ngroups + gpw - 1) / gpw)));
     if (a.K % slab_k(FMT) == 0 && a.S % MOE_D == 0)  // no unit masking, no padding slabs
-        hipLaunchKernelGGL((moe_kernel<FMT, ACT, OUTT, DUAL, NTG, true>), grid, dim3(256), 0, st, a, g, Nh, ngroups,
+        hipLaunchKernelGGL((moe_kernel<FMT, ACT, OUTT, DUAL, NTG, true>), grid, dim3(64 * MOE_W), 0, st, a, g, Nh, ngroups,
                            gpw);
     else
-        hipLaunchKernelGGL((moe_kernel<FMT, ACT, OUTT, DUAL, NTG, false>), grid, dim3(256), 0, st, a, g, Nh, ngroups,
+        hipLaunchKernelGGL((moe_kernel<FMT, ACT, OUTT, DUAL, NTG, false>), grid, dim3(64 * MOE_W), 0, st, a, g, Nh, ngroups,
                            gpw);
 }
 
