@@ -315,7 +315,10 @@ def copy_calibration(mib=512, reps=5):
     log(f"[bench] copy calibration: {reps} copies of {mib} MiB")
 
 
-def bench_moe(steps):
+MOE_SHAPE = (512, 10, 2048, 512, 2048)  # experts, top-k, tokens, gate (= up) rows, K
+
+
+def moe_inputs():
     """Routed-expert NVFP4 fused gate+up at the scale of the Atlas issue's
     validation plan (512 experts, top-10, 2048 tokens).  The pages give no
     expert dimensions; K = 2048 and 2 x 512 gate/up rows stand in.  Eight
@@ -327,7 +330,7 @@ def bench_moe(steps):
     import prefill_q8_mxfp4_amd as q
     import synth
 
-    E, topk, tokens, nh, K = 512, 10, 2048, 512, 2048
+    E, topk, tokens, nh, K = MOE_SHAPE
     dev = torch.device("cuda:0")
     t0 = time.time()
     distinct = [torch.from_numpy(q.pack_logical(synth.gen_expert_weights("nvfp4", 2 * nh, K, e, swiglu=True)))
@@ -341,6 +344,15 @@ def bench_moe(steps):
     plan = q.Plan("nvfp4", 2 * nh, K, act="bf16", out="bf16", epilogue="swiglu")
     y = torch.empty((T, nh), dtype=torch.bfloat16, device=dev)
     log(f"[bench] moe ready in {time.time() - t0:.1f}s")
+    return plan, x, table, off, y, bufs, T
+
+
+def bench_moe(steps):
+    """The routed-expert workload of moe_inputs(), graph-replayed."""
+    import torch
+
+    E, topk, tokens, nh, K = MOE_SHAPE
+    plan, x, table, off, y, bufs, T = moe_inputs()
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         for _ in range(3):
@@ -391,7 +403,9 @@ def main():
                          "route, no CPU baseline): the program under the kernel-trace profile")
     ap.add_argument("--calls-of", nargs=2, metavar=("CONFIG", "B"),
                     help="only launch CONFIG at batch B eagerly --steps times, print nothing "
-                         "else (a short program for counter passes)")
+                         "else (a short program for counter passes); CONFIG routed_moe (B "
+                         "ignored) launches the routed-expert workload, mfma_rate the "
+                         "matrix-core rate kernel")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path; "
@@ -408,6 +422,20 @@ def main():
     sha = kernel_src_sha()
     if args.copy_calibration:
         copy_calibration()
+    if args.calls_of and args.calls_of[0] == "mfma_rate":
+        sink = torch.zeros(4096, dtype=torch.int32, device="cuda:0")
+        for _ in range(3 + args.steps):  # mode 0: chained bf16 MFMAs, the matrix cores' own rate
+            q.mfma_rate(0, 4096, sink)
+        torch.cuda.synchronize()
+        log(f"[bench] {args.steps} calls of the MFMA rate kernel done")
+        return
+    if args.calls_of and args.calls_of[0] == "routed_moe":
+        plan, x, table, off, y, bufs, T = moe_inputs()
+        for _ in range(20 + args.steps):  # the first 20 warm the clock
+            plan.run_grouped(x, table, off, y)
+        torch.cuda.synchronize()
+        log(f"[bench] {args.steps} calls of routed_moe done")
+        return
     if args.calls_of:
         w = Workload(args.calls_of[0], int(args.calls_of[1]))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
