@@ -17,9 +17,6 @@
 //           accumulator (4 cvt, 4 mul, 4 fma per lane): the int8 tier's loop
 //   mode 4  mode 0 from a zero accumulator plus a per-block fp32 scale FMA
 //           (4 fma per lane): the block-scale pattern of the fp32-faithful path
-// (modes 3 and 4 give every chain and trip its own operand, one XOR each: a
-// product from a zero accumulator with loop-invariant operands would be
-// hoisted out of the loop, and equal ones merged)
 //
 // Operands are derived from the thread id and a seed so nothing folds; each
 // wave writes one word to sink.  Throughput = MFMAs x 2 x 16 x 16 x K / time.
@@ -47,7 +44,19 @@ __global__ __launch_bounds__(512) void mfma_rate_kernel(int iters, uint32_t seed
     }
     float dw = __uint_as_float(0x3F800000u | (v & 0xFFFu));
     f32x4 dx = f32x4{1.f, 1.5f, 2.f, 2.5f};
+    // modes 3 and 4: each chain its own B operand, and an A operand that
+    // changes every trip (one XOR a trip for all chains), so the products
+    // from a zero accumulator are neither hoisted out of the loop nor merged
+    bf16x8 bb[NC];
+    long b8[NC];
+#pragma unroll
+    for (int j = 0; j < NC; j++) {
+        bb[j] = __builtin_bit_cast(bf16x8, bits ^ (uint32_t)(0x00010001u * (j + 1)));
+        b8[j] = a4 ^ (long)(0x0101010101010101ll * (j + 1));
+    }
     for (int it = 0; it < iters; it++) {
+        const long a4t = a4 ^ (long)it;
+        const bf16x8 abt = __builtin_bit_cast(bf16x8, bits ^ (uint32_t)(it & 0x003F003F));
 #pragma unroll
         for (int j = 0; j < NC; j++) {
             if constexpr (MODE == 0) {
@@ -59,13 +68,12 @@ __global__ __launch_bounds__(512) void mfma_rate_kernel(int iters, uint32_t seed
             } else if constexpr (MODE == 3) {
                 // operands differ per trip (one XOR a trip), so the product
                 // from a zero accumulator cannot be hoisted out of the loop
-                const i32x4 t = __builtin_amdgcn_mfma_i32_16x16x32_i8(a4 ^ (long)(it * NC + j), a4, i32x4{0, 0, 0, 0}, 0, 0, 0);
+                const i32x4 t = __builtin_amdgcn_mfma_i32_16x16x32_i8(a4t, b8[j], i32x4{0, 0, 0, 0}, 0, 0, 0);
 #pragma unroll
                 for (int e = 0; e < 4; e++)
                     acc[j][e] = __builtin_fmaf(dw * dx[e], (float)t[e], acc[j][e]);
             } else {
-                const bf16x8 abi = __builtin_bit_cast(bf16x8, bits ^ (uint32_t)((it * NC + j) & 0x003F003F));
-                const f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abi, ab, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                const f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abt, bb[j], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
                 for (int e = 0; e < 4; e++)
                     acc[j][e] = __builtin_fmaf(dw, t[e], acc[j][e]);
