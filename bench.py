@@ -274,17 +274,19 @@ def cpu_baseline(wl, budget_s=10.0, one_thread_calls=1):
                       f"{one_thread_calls} on one thread: q8_0 K=N=5120, B={wl.B}, fp32 activations"}
 
 
-def next4_mfma_rates(iters=4096, reps=5):
-    """The int8-activation question for Q8_0 weights, measured: dense TOPS of
-    the matrix-core loops of qgemm_mfma_rate (median of `reps` launches,
-    each after a warm-up launch)."""
+def next4_mfma_rates(modes=(0, 1, 2, 3, 4), iters=4096, reps=5):
+    """Dense TOPS of the matrix-core loops of qgemm_mfma_rate (median of
+    `reps` launches, each after a warm-up launch): modes 0-4 answer the
+    int8-activation question for Q8_0 weights, modes 5-7 time the hardware
+    block-scaled route for the MX formats."""
     import torch
 
     import prefill_q8_mxfp4_amd as q
 
     sink = torch.zeros(4096, dtype=torch.int32, device="cuda:0")
     out = {}
-    for mode, (name, kdeep) in q.MFMA_RATE_MODES.items():
+    for mode in modes:
+        name, kdeep = q.MFMA_RATE_MODES[mode]
         q.mfma_rate(mode, iters, sink)
         ts = []
         for _ in range(reps):
@@ -298,8 +300,29 @@ def next4_mfma_rates(iters=4096, reps=5):
         mfmas = 512 * 8 * iters * 8       # workgroups x waves x trips x chains
         tops = mfmas * 2.0 * 16 * 16 * kdeep / t / 1e12
         out[name] = {"TOPS": round(tops, 1), "ms": round(t * 1e3, 4)}
-    log(f"[bench] next4 matrix-core rates {out}")
+    log(f"[bench] matrix-core rates {out}")
     return out
+
+
+def pages_context(pre, sweep):
+    """The pages' own figures for this path, on their own hardware, next to
+    the nearest figure measured here (context, not a target)."""
+    nv = pre.get("nvfp4_gate_up_34816x5120:B=2048", {}).get("TFLOPs")
+    b1 = sweep.get(1, sweep.get("1", {})).get("weight_GBs")
+    # hipfire issue, "Model": the 27B MQ3 trunk file is 12,618,796,032 bytes;
+    # at one token per full read of it, 22.8 tok/s streams about 288 GB/s
+    mq3_bytes = 12_618_796_032
+    return {
+        "nvfp4_prefill_gemm": {
+            "pages_TFLOPs": 16.0, "pages_hw": "gfx1151 (Strix Halo iGPU), w4a16 GEMM, 27B FFN, 2048-token chunks",
+            "source": "Atlas issue, 'Kernel ranking: Strix long prefill is GEMM-efficiency-bound'",
+            "here_TFLOPs": nv, "here": "NVFP4 fused gate+up 2x17408x5120, B=2048"},
+        "ar_decode_27b": {
+            "pages_tok_s": 22.8, "pages_hw": "RX 9060 XT (gfx1200), 27B MQ3 trunk, single stream",
+            "source": "hipfire issue, 'Baseline: AR is healthy' and 'Model'",
+            "pages_implied_weight_GBs": round(mq3_bytes * 22.8 / 1e9, 1),
+            "here_weight_GBs": b1, "here": "Q8_0 5120x5120, B=1 weight stream"},
+    }
 
 
 def copy_calibration(mib=512, reps=5):
@@ -568,6 +591,8 @@ def main():
                                      "all_B2048": {k: v["mfma_frac"] for k, v in big.items()}}
         line["routed_moe:nvfp4:512x(2x512)x2048:top10:tokens2048"] = bench_moe(args.steps)
         line["next4_int8_vs_bf16_mfma"] = next4_mfma_rates()
+        line["mx_scaled_mfma_rates"] = next4_mfma_rates((0, 5, 6, 7))
+        line["pages_context"] = pages_context(pre, sweep)
 
     print(json.dumps(line), flush=True)
 

@@ -331,12 +331,16 @@ int qgemm_read_bytes(const void *buf, size_t bytes, uint32_t *sink, int wgs, voi
 /* Measurement aid, not part of the GEMM: one launch of a matrix-core loop
  * (512 workgroups of 8 waves, each wave `iters` trips of eight independent
  * accumulator chains) that shows whether an int8-activation tier could beat
- * the bf16 tier for Q8_0 weights, whose scales change every 32 weights:
+ * the bf16 tier for Q8_0 weights, whose scales change every 32 weights, and
+ * what the hardware block-scaled route would give the MX formats:
  *   0 v_mfma_f32_16x16x32_bf16; 1 v_mfma_i32_16x16x32_i8 (one 32-wide block
  *   per MFMA); 2 v_mfma_i32_16x16x64_i8 (two blocks, no per-block scale);
  *   3 mode 1 plus each block's int32 -> fp32 conversion and scale product
  *   d_w * d_x into an fp32 accumulator; 4 mode 0 plus a per-block fp32 scale
- *   FMA.  sink: device, 4096 words.  The caller times the launch. */
+ *   FMA; 5 v_mfma_scale_f32_16x16x128_f8f6f4 with E4M3 A and E2M1 B (E8M0
+ *   scale per row and 32-wide block on each side); 6 the same with E2M1 on
+ *   both sides; 7 the same with E4M3 on both sides.  mode outside 0..7 ->
+ *   QGEMM_EINVAL.  sink: device, 4096 words.  The caller times the launch. */
 int qgemm_mfma_rate(int mode, int iters, uint32_t *sink, void *stream);
 
 /* Text for a status code (static storage). */

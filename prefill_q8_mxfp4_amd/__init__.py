@@ -372,7 +372,9 @@ def read_bytes(buf, sink, wgs: int = 0, nbytes: int | None = None, stream=None):
 
 MFMA_RATE_MODES = {0: ("bf16 16x16x32", 32), 1: ("i8 16x16x32", 32), 2: ("i8 16x16x64", 64),
                    3: ("i8 16x16x32 + per-32 scale (int8 tier loop)", 32),
-                   4: ("bf16 16x16x32 + per-32 scale FMA", 32)}
+                   4: ("bf16 16x16x32 + per-32 scale FMA", 32),
+                   5: ("scaled 16x16x128 e4m3 x e2m1", 128), 6: ("scaled 16x16x128 e2m1 x e2m1", 128),
+                   7: ("scaled 16x16x128 e4m3 x e4m3", 128)}
 
 
 def mfma_rate(mode: int, iters: int, sink, stream=None):

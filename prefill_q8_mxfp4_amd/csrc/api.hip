@@ -1072,8 +1072,8 @@ int qgemm_read_bytes(const void *buf, size_t bytes, uint32_t *sink, int wgs, voi
 
 int qgemm_mfma_rate(int mode, int iters, uint32_t *sink, void *stream)
 {
-    if (mode < 0 || mode > 4 || iters < 1 || iters > (1 << 24) || !sink)
-        return fail(QGEMM_EINVAL, "qgemm_mfma_rate: mode 0..4, iters 1..2^24, sink not null");
+    if (mode < 0 || mode > 7 || iters < 1 || iters > (1 << 24) || !sink)
+        return fail(QGEMM_EINVAL, "qgemm_mfma_rate: mode 0..7, iters 1..2^24, sink not null");
     const hipError_t e = launch_mfma_rate(mode, iters, sink, (hipStream_t)stream);
     if (e != hipSuccess)
         return hip_fail(e, "qgemm_mfma_rate: kernel launch");

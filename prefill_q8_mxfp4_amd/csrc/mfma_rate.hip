@@ -18,6 +18,15 @@
 //   mode 4  mode 0 from a zero accumulator plus a per-block fp32 scale FMA
 //           (4 fma per lane): the block-scale pattern of the fp32-faithful path
 //
+// and the block-scaled matrix-core route for the MX formats (one E8M0 scale
+// per operand row and 32-wide block, applied by the hardware), K = 128 per
+// instruction:
+//
+//   mode 5  v_mfma_scale_f32_16x16x128_f8f6f4, A E4M3, B E2M1 (MXFP4 weights
+//           against fp8 activations)
+//   mode 6  the same, A and B E2M1 (fp4 activations)
+//   mode 7  the same, A and B E4M3 (FP8 weights against fp8 activations)
+//
 // Operands are derived from the thread id and a seed so nothing folds; each
 // wave writes one word to sink.  Throughput = MFMAs x 2 x 16 x 16 x K / time.
 #include "common.h"
@@ -25,6 +34,7 @@
 namespace qg {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 template <int MODE>
 __global__ __launch_bounds__(512) void mfma_rate_kernel(int iters, uint32_t seed, uint32_t *sink)
@@ -54,6 +64,12 @@ __global__ __launch_bounds__(512) void mfma_rate_kernel(int iters, uint32_t seed
         bb[j] = __builtin_bit_cast(bf16x8, bits ^ (uint32_t)(0x00010001u * (j + 1)));
         b8[j] = a4 ^ (long)(0x0101010101010101ll * (j + 1));
     }
+    // modes 5-7: 32 fp8 codes (or 32 fp4 codes in the low four words) per
+    // lane, without the E4M3 NaN pattern; E8M0 scales near 1
+    const uint32_t m8 = 0x3B3B3B3Bu;
+    const i32x8 q8 = i32x8{(int)(v & m8), (int)((v * 3u) & m8), (int)((v * 5u) & m8), (int)((v * 7u) & m8),
+                           (int)((v * 9u) & m8), (int)((v * 11u) & m8), (int)((v * 13u) & m8), (int)((v * 15u) & m8)};
+    const int sa = 125 + (int)(v & 3u), sb = 126 + (int)((v >> 2) & 1u);
     for (int it = 0; it < iters; it++) {
         const long a4t = a4 ^ (long)it;
         const bf16x8 abt = __builtin_bit_cast(bf16x8, bits ^ (uint32_t)(it & 0x003F003F));
@@ -72,6 +88,12 @@ __global__ __launch_bounds__(512) void mfma_rate_kernel(int iters, uint32_t seed
 #pragma unroll
                 for (int e = 0; e < 4; e++)
                     acc[j][e] = __builtin_fmaf(dw * dx[e], (float)t[e], acc[j][e]);
+            } else if constexpr (MODE == 5) {
+                acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q8, q8, acc[j], 0, 4, 0, sa, 0, sb);
+            } else if constexpr (MODE == 6) {
+                acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q8, q8, acc[j], 4, 4, 0, sa, 0, sb);
+            } else if constexpr (MODE == 7) {
+                acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q8, q8, acc[j], 0, 0, 0, sa, 0, sb);
             } else {
                 const f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abt, bb[j], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
@@ -99,7 +121,10 @@ hipError_t launch_mfma_rate(int mode, int iters, uint32_t *sink, hipStream_t st)
     case 1: hipLaunchKernelGGL(mfma_rate_kernel<1>, grid, block, 0, st, iters, 12345u, sink); break;
     case 2: hipLaunchKernelGGL(mfma_rate_kernel<2>, grid, block, 0, st, iters, 12345u, sink); break;
     case 3: hipLaunchKernelGGL(mfma_rate_kernel<3>, grid, block, 0, st, iters, 12345u, sink); break;
-    default: hipLaunchKernelGGL(mfma_rate_kernel<4>, grid, block, 0, st, iters, 12345u, sink); break;
+    case 4: hipLaunchKernelGGL(mfma_rate_kernel<4>, grid, block, 0, st, iters, 12345u, sink); break;
+    case 5: hipLaunchKernelGGL(mfma_rate_kernel<5>, grid, block, 0, st, iters, 12345u, sink); break;
+    case 6: hipLaunchKernelGGL(mfma_rate_kernel<6>, grid, block, 0, st, iters, 12345u, sink); break;
+    default: hipLaunchKernelGGL(mfma_rate_kernel<7>, grid, block, 0, st, iters, 12345u, sink); break;
     }
     return hipGetLastError();
 }

@@ -403,6 +403,35 @@ def test_one_hot_tiled_rounds_decoded_weights_once(fmt):
     assert np.array_equal(y, ref.astype(np.float64))
 
 
+@pytest.mark.parametrize("fmt,epi,n,k,B", [
+    ("q8_0", "none", 768, 1056, 300),      # K tail, 3 x 3 tiles: a split partial round
+    ("mxfp4", "none", 512, 2048, 2048),    # 256-row tiles, whole rounds
+    ("nvfp4", "swiglu", 2 * 384, 1024, 200),
+    ("fp8", "none", 640, 1024, 77),        # ragged weight tile and batch tile
+])
+def test_tiled_four_wave_form_is_bitwise_the_eight_wave_form(fmt, epi, n, k, B, monkeypatch):
+    """The large-batch kernel with one wave per SIMD (QGEMM_TI_WAVES=4: 2 x 2
+    waves, accumulators in AGPRs) runs the same tiles, K steps and split
+    pieces in the same order as the default 8-wave form, so its output is
+    bitwise the same; both meet the oracle's bf16-math bound."""
+    if epi == "swiglu":
+        w = _gate_up(fmt, n // 2, k, 43)
+    else:
+        w = synth.quantize(fmt, synth.normal_f32(43, synth.SID_W, n, k, 0.02))
+    wd = w_dev(w)
+    x = synth.gen_x_bf16(B, k, seed=5)
+    out = "bf16" if epi == "swiglu" else "f32"
+    p8 = q.Plan(fmt, n, k, act="bf16", out=out, math="bf16", epilogue=epi, tier="tiled")
+    monkeypatch.setenv("QGEMM_TI_WAVES", "4")   # read at plan creation
+    p4 = q.Plan(fmt, n, k, act="bf16", out=out, math="bf16", epilogue=epi, tier="tiled")
+    monkeypatch.delenv("QGEMM_TI_WAVES")
+    y8 = run(p8, x, wd)
+    y4 = run(p4, x, wd)
+    assert np.array_equal(y4, y8), (fmt, np.nanmax(np.abs(y4 - y8)))
+    ref = oracle.swiglu(w, x) if epi == "swiglu" else oracle.gemm(w, x)
+    assert oracle.rel_fro(y8, ref) <= TOL_BF16
+
+
 @pytest.mark.parametrize("tier,math", [("skinny", "fp32"), ("tiled", "bf16"), ("tiled", "fp32")])
 def test_closed_form_constant_is_exact(tier, math):
     """Constant q = 3, d = 2^-7, x = 0.5 over K = 5120: every output is
@@ -1236,4 +1265,4 @@ def test_mfma_rate_modes_run():
         torch.cuda.synchronize()
         assert torch.count_nonzero(sink) > 0, mode
     with pytest.raises(q.QgemmError):
-        q.mfma_rate(5, 8, sink)
+        q.mfma_rate(8, 8, sink)
