@@ -171,16 +171,20 @@ static bool gemv_fits(const Problem &p, int64_t B)
     return B <= GV_MAX_B && gemv_lds_bytes(p, B) <= GV_LDS_MAX;
 }
 
-// Automatic choice: off.  Measured on the box against the MFMA streaming
-// kernel (NT loads, pipelined): Q8_0 5120^2 B = 1 10.8 vs 10.2 us, B = 2
-// 14.2 vs 10.3; MXFP4 5120x17408 B = 1 22.0 vs 13.9; NVFP4 gate+up B = 1
-// 35.0 vs 28.9 (one workgroup per 16-row tile leaves 64 of 256 CUs with two
-// tiles at N = 5120, and fp32 FMAs make the FP4 formats VALU-bound).  The
-// tier stays available by force (QGEMM_FLAG_FORCE_GEMV) and QGEMM_GV_MAXB=1|2
-// turns the automatic choice on for measurements.
+// Automatic choice: B = 1 for Q8_0 and FP8 weights without the fused
+// epilogue.  Measured on the box against the MFMA streaming kernel, with 8
+// waves per GEMV workgroup (several resident per CU, so the CUs that hold a
+// tile more than others keep HBM busy): Q8_0 5120^2 B = 1 9.37 vs 10.19 us,
+// FP8 8.95 vs 9.85; at B = 2 the streaming kernel wins (Q8_0 11.24 vs 10.19),
+// and for MXFP4 5120x17408 B = 1 (16.8 vs 14.0: fp32 FMAs make the FP4
+// formats VALU-bound).  QGEMM_GV_MAXB=0|1|2 overrides the rule (0: never).
 static bool use_gemv(const Problem &p, int64_t B)
 {
-    const int maxb = p.kn.gv_maxb > 0 ? (p.kn.gv_maxb < GV_MAX_B ? p.kn.gv_maxb : GV_MAX_B) : 0;
+    int maxb;
+    if (p.kn.gv_maxb >= 0)
+        maxb = p.kn.gv_maxb < GV_MAX_B ? p.kn.gv_maxb : GV_MAX_B;
+    else
+        maxb = (p.fmt == FMT_Q8 || p.fmt == FMT_FP8) && p.epi != QGEMM_EPI_SWIGLU ? 1 : 0;
     return B <= maxb && gemv_fits(p, B);
 }
 

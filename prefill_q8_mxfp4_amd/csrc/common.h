@@ -343,7 +343,7 @@ __device__ __forceinline__ void store_out_nt(void *y, int64_t idx, float v)
 struct Knobs {
     int st_waves, st_nph;  // streaming-kernel shape (QGEMM_ST_WAVES, QGEMM_ST_NPH)
     int st_depth;          // streaming kernel's load depth in row tiles (QGEMM_ST_DEPTH)
-    int gv_maxb;           // largest B sent to the GEMV kernel (QGEMM_GV_MAXB; 0 = none)
+    int gv_maxb;           // largest B sent to the GEMV kernel (QGEMM_GV_MAXB; 0 = none, -1 = the default rule)
     int sk_stream;         // 0: B <= 16 through the skinny kernel (QGEMM_SK_STREAM)
     int sk_nt;             // 1: one row tile per skinny wave (QGEMM_SK_NT)
     int ti_bm, ti_split;   // large-batch row-tile height, K splits (QGEMM_TI_BM, QGEMM_TI_SPLIT)

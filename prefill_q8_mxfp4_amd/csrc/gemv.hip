@@ -266,7 +266,11 @@ static void launch_gf(const Problem &p, const KArgs &a, int W, int Nh, hipStream
     }
 }
 
-int gemv_waves(const Problem &p) { return (int)(p.L.S < GV_MAXW ? p.L.S : GV_MAXW); }
+// 8 waves: a workgroup small enough that several are resident on a CU (16
+// waves, one workgroup per CU, measured 10.8 against 9.4 us on Q8_0 5120^2
+// at B = 1; 4 waves 9.1 there but 18.5 against 16.8 on MXFP4 5120x17408)
+constexpr int GV_W = 8;
+int gemv_waves(const Problem &p) { return (int)(p.L.S < GV_W ? p.L.S : GV_W); }
 
 int64_t gemv_lds_bytes(const Problem &p, int64_t B) { return B * p.L.S * p.L.KS * 4; }
 

@@ -149,6 +149,13 @@ def test_tier_choice():
     assert p.tier(1) == "skinny" and p.tier(256) == "skinny"
     p = q.Plan("q8_0", 5120, 5120, act="f32", tier="gemv")
     assert p.tier(1) == "gemv" and p.tier(300) == "gemv" and p.workspace_bytes(2) == 0
+    # automatic: the GEMV kernel for B = 1 with Q8_0 and FP8 weights (no fused
+    # epilogue), the streaming kernel from B = 2
+    for fmt, act in (("q8_0", "f32"), ("fp8", "bf16")):
+        p = q.Plan(fmt, 5120, 5120, act=act)
+        assert p.tier(1) == "gemv" and p.tier(2) == "skinny" and p.workspace_bytes(1) == 0
+    p = q.Plan("q8_0", 2 * 512, 5120, act="bf16", epilogue="swiglu")
+    assert p.tier(1) == "skinny"
 
 
 def _split_part_bytes(plan, B, N):
