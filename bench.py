@@ -304,6 +304,50 @@ def next4_mfma_rates(modes=(0, 1, 2, 3, 4), iters=4096, reps=5):
     return out
 
 
+def torch_bf16_gemm_rates(reps=10):
+    """Context for the large-batch rates: torch's own bf16 GEMM (the vendor
+    library) on the same shapes with plain bf16 weights and no decode, the
+    weights stored [K][N] ("nn") and [N][K] ("nt", as this library stores
+    them), timed with events after about 100 ms of untimed calls (median of
+    `reps` timed calls per shape and layout)."""
+    import torch
+
+    shapes = [("2048x17408x5120", 2048, 17408, 5120), ("2048x5120x17408", 2048, 5120, 17408),
+              ("2048x34816x5120", 2048, 34816, 5120), ("2048x5120x5120", 2048, 5120, 5120),
+              ("256x5120x17408", 256, 5120, 17408), ("8192x8192x8192", 8192, 8192, 8192)]
+    g = torch.Generator(device="cuda:0").manual_seed(0)
+    out = {}
+    for name, B, N, K in shapes:
+        x = torch.randn(B, K, device="cuda:0", dtype=torch.bfloat16, generator=g)
+        y = torch.empty(B, N, device="cuda:0", dtype=torch.bfloat16)
+        flop = 2.0 * B * N * K
+        n_warm = max(3, int(0.1 / (flop / 1.0e15)))
+        rec = {}
+        for lay in ("nn", "nt"):
+            w = torch.randn((K, N) if lay == "nn" else (N, K), device="cuda:0", dtype=torch.bfloat16,
+                            generator=g)
+            wop = w if lay == "nn" else w.t()  # 2-D product: the transposed view is the "nt" layout
+            for _ in range(n_warm):
+                torch.matmul(x, wop, out=y)
+            ts = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                torch.matmul(x, wop, out=y)
+                e1.record()
+                e1.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e-3)
+            t = sorted(ts)[reps // 2]
+            rec[lay] = {"us": round(t * 1e6, 2), "TFLOPs": round(flop / t / 1e12, 1)}
+            del w, wop
+        best = max(rec.values(), key=lambda r: r["TFLOPs"])
+        out[name] = dict(rec, best_frac_bf16_peak=round(best["TFLOPs"] / BF16_PEAK_TFLOPS, 4))
+        del x, y
+        torch.cuda.empty_cache()
+    log(f"[bench] torch bf16 GEMM {out}")
+    return out
+
+
 def pages_context(pre, sweep):
     """The pages' own figures for this path, on their own hardware, next to
     the nearest figure measured here (context, not a target)."""
@@ -593,6 +637,7 @@ def main():
         line["next4_int8_vs_bf16_mfma"] = next4_mfma_rates()
         line["mx_scaled_mfma_rates"] = next4_mfma_rates((0, 5, 6, 7))
         line["pages_context"] = pages_context(pre, sweep)
+        line["context_torch_bf16_gemm"] = torch_bf16_gemm_rates()
 
     print(json.dumps(line), flush=True)
 
