@@ -171,21 +171,24 @@ static bool gemv_fits(const Problem &p, int64_t B)
     return B <= GV_MAX_B && gemv_lds_bytes(p, B) <= GV_LDS_MAX;
 }
 
-// Automatic choice: B = 1 for Q8_0 and FP8 weights without the fused
-// epilogue.  Measured on the box against the MFMA streaming kernel, with 8
-// waves per GEMV workgroup (several resident per CU, so the CUs that hold a
-// tile more than others keep HBM busy): Q8_0 5120^2 B = 1 9.37 vs 10.19 us,
-// FP8 8.95 vs 9.85; at B = 2 the streaming kernel wins (Q8_0 11.24 vs 10.19),
-// and for MXFP4 5120x17408 B = 1 (16.8 vs 14.0: fp32 FMAs make the FP4
-// formats VALU-bound).  QGEMM_GV_MAXB=0|1|2 overrides the rule (0: never).
+// Automatic choice: B = 1 when the activation row takes at most 32 KB of
+// LDS (K <= 8192), so that four or more GEMV workgroups of 8 waves fit on a
+// CU and the CUs that hold a tile more than others keep HBM busy.  Measured
+// on the box against the MFMA streaming kernel: Q8_0 5120^2 B = 1 9.37 vs
+// 10.19 us, FP8 5120^2 8.95 vs 9.85, NVFP4 gate+up 2x17408x5120 23.7 vs
+// 29.0; MXFP4 5120x17408 (K = 17408, 70 KB of LDS) 16.8 vs 14.0; at B = 2
+// the streaming kernel wins everywhere (Q8_0 11.2 vs 10.2, FP8 10.6 vs 9.9,
+// NVFP4 gate+up 32.5 vs 29.3).  QGEMM_GV_MAXB=0|1|2 overrides the rule
+// (0: never).
+static const int64_t GV_AUTO_LDS = 32 * 1024;
+
 static bool use_gemv(const Problem &p, int64_t B)
 {
-    int maxb;
-    if (p.kn.gv_maxb >= 0)
-        maxb = p.kn.gv_maxb < GV_MAX_B ? p.kn.gv_maxb : GV_MAX_B;
-    else
-        maxb = (p.fmt == FMT_Q8 || p.fmt == FMT_FP8) && p.epi != QGEMM_EPI_SWIGLU ? 1 : 0;
-    return B <= maxb && gemv_fits(p, B);
+    if (p.kn.gv_maxb >= 0) {
+        const int maxb = p.kn.gv_maxb < GV_MAX_B ? p.kn.gv_maxb : GV_MAX_B;
+        return B <= maxb && gemv_fits(p, B);
+    }
+    return B == 1 && gemv_lds_bytes(p, 1) <= GV_AUTO_LDS;
 }
 
 // XCD dispatch probe.  The streaming kernel's XCD-local split exchange

@@ -144,18 +144,18 @@ def test_tier_choice():
     assert p.tier(32) == "skinny" and p.tier(33) == "tiled"  # bf16 math: tiled from B = 33
     p = q.Plan("nvfp4", 2 * 17408, 5120, act="bf16", out="bf16", epilogue="swiglu")
     assert p.tier(2048) == "tiled" and p.tier(17) == "tiled"
-    assert p.tier(1) == "skinny" and p.tier(16) == "skinny"
+    assert p.tier(1) == "gemv" and p.tier(2) == "skinny" and p.tier(16) == "skinny"
     p = q.Plan("q8_0", 5120, 5120, act="f32", tier="skinny")
     assert p.tier(1) == "skinny" and p.tier(256) == "skinny"
     p = q.Plan("q8_0", 5120, 5120, act="f32", tier="gemv")
     assert p.tier(1) == "gemv" and p.tier(300) == "gemv" and p.workspace_bytes(2) == 0
-    # automatic: the GEMV kernel for B = 1 with Q8_0 and FP8 weights (no fused
-    # epilogue), the streaming kernel from B = 2
-    for fmt, act in (("q8_0", "f32"), ("fp8", "bf16")):
-        p = q.Plan(fmt, 5120, 5120, act=act)
+    # automatic: the GEMV kernel for B = 1 when one activation row fits in
+    # 32 KB of LDS (K <= 8192), the streaming kernel from B = 2
+    for fmt, act in (("q8_0", "f32"), ("fp8", "bf16"), ("mxfp4", "bf16"), ("nvfp4", "f32")):
+        p = q.Plan(fmt, 5120, 8192, act=act)
         assert p.tier(1) == "gemv" and p.tier(2) == "skinny" and p.workspace_bytes(1) == 0
-    p = q.Plan("q8_0", 2 * 512, 5120, act="bf16", epilogue="swiglu")
-    assert p.tier(1) == "skinny"
+        p = q.Plan(fmt, 5120, 8448, act=act)
+        assert p.tier(1) == "skinny"
 
 
 def _split_part_bytes(plan, B, N):

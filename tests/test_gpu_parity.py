@@ -882,7 +882,7 @@ def test_swiglu_streaming_small_batch(fmt):
     nh, k = 320, 1024
     w = _gate_up(fmt, nh, k, 31)
     wd = w_dev(w)
-    plan = q.Plan(fmt, 2 * nh, k, act="bf16", out="f32", epilogue="swiglu")
+    plan = q.Plan(fmt, 2 * nh, k, act="bf16", out="f32", epilogue="swiglu", tier="skinny")
     for B in (1, 3, 7, 16):
         assert plan.tier(B) == "skinny"
         x = synth.gen_x_bf16(B, k, seed=B)
