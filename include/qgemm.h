@@ -106,11 +106,13 @@ typedef enum qgemm_tier {
                               (B > 32 with bf16 math, B > 16 with fp32 math) */
     QGEMM_TIER_GEMV = 3    /* B = 1, 2: one workgroup per 16-row tile over all of
                               K, fp32 FMA on the vector ALUs, a fixed-order
-                              cross-lane sum; no K split and no workspace.  Only
-                              when forced (measured slower than the skinny tier's
-                              streaming kernel on MI355X); it needs the B
-                              activation rows, as fp32, to fit in 72 KB of LDS,
-                              and returns QGEMM_ENOTSUP for other calls */
+                              cross-lane sum; no K split and no workspace.
+                              Chosen automatically for B = 1 when the row, as
+                              fp32, takes at most 32 KB (K <= 8192; measured
+                              faster than the streaming kernel there on
+                              MI355X), else only when forced; a forced call
+                              needs the B rows, as fp32, to fit in 72 KB of
+                              LDS, and returns QGEMM_ENOTSUP otherwise */
 } qgemm_tier;
 
 #define QGEMM_FLAG_FORCE_SKINNY 0x1u
