@@ -308,7 +308,7 @@ def torch_bf16_gemm_rates(reps=10):
     """Context for the large-batch rates: torch's own bf16 GEMM (the vendor
     library) on the same shapes with plain bf16 weights and no decode, the
     weights stored [K][N] ("nn") and [N][K] ("nt", as this library stores
-    them), timed with events after about 100 ms of untimed calls (median of
+    them), timed with events after about 50 ms of untimed calls (median of
     `reps` timed calls per shape and layout)."""
     import torch
 
@@ -321,7 +321,7 @@ def torch_bf16_gemm_rates(reps=10):
         x = torch.randn(B, K, device="cuda:0", dtype=torch.bfloat16, generator=g)
         y = torch.empty(B, N, device="cuda:0", dtype=torch.bfloat16)
         flop = 2.0 * B * N * K
-        n_warm = max(3, int(0.1 / (flop / 1.0e15)))
+        n_warm = max(3, int(0.05 / (flop / 1.0e15)))
         rec = {}
         for lay in ("nn", "nt"):
             w = torch.randn((K, N) if lay == "nn" else (N, K), device="cuda:0", dtype=torch.bfloat16,
