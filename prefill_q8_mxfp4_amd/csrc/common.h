@@ -252,6 +252,11 @@ __device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, int voff, i
 // data a call reads exactly once (the small-batch weight stream): measured on
 // the box, the headline's weight loads alone run 0.5 us faster with it.
 constexpr int CP_NT = 2;
+// Scope bits of the same field for plain loads of data other workgroups
+// stored with scoped stores: SC0 as the compiler sets for workgroup-scope
+// atomics (served by the XCD's L2), SC1 for device scope.
+constexpr int CP_SC0 = 1;
+constexpr int CP_SC1 = 16;
 
 __device__ __forceinline__ u32x4 bload16_nt(__amdgpu_buffer_rsrc_t r, int voff, int soff)
 {
@@ -346,6 +351,7 @@ struct Knobs {
     int gv_maxb;           // largest B sent to the GEMV kernel (QGEMM_GV_MAXB; 0 = none, -1 = the default rule)
     int sk_stream;         // 0: B <= 16 through the skinny kernel (QGEMM_SK_STREAM)
     int sk_nt;             // 1: one row tile per skinny wave (QGEMM_SK_NT)
+    int vf;                // 0: no verify kernel for fp32-faithful 16 < B <= 80 (QGEMM_VF)
     int ti_bm, ti_split;   // large-batch row-tile height, K splits (QGEMM_TI_BM, QGEMM_TI_SPLIT)
     int ti_waves;          // large-batch waves per workgroup, 4 or 8 (QGEMM_TI_WAVES; 0 = default)
     int xlocal;            // -1 the probe decides, 0 device-coherent, 1 forced (debug)
@@ -463,6 +469,12 @@ hipError_t launch_skinny(const Problem &p, const KArgs &a, const SkCfg &c, const
                          int nterm, hipStream_t st);
 hipError_t launch_stream(const Problem &p, const KArgs &a, const StCfg &c, const SkinnyWs &ws,
                          int nterm, hipStream_t st);
+// fp32-faithful math with 16 < B <= VF_MAX_B and K a whole number of slabs:
+// the streaming kernel's row groups and K splits (StCfg) with all batch rows
+// per workgroup (verify.hip); partial tiles [ksplit][ngroups * 8][MB][64][4].
+constexpr int VF_MAX_B = 80;
+int verify_mb(int64_t B);
+hipError_t launch_verify(const Problem &p, const KArgs &a, const StCfg &c, const SkinnyWs &ws, hipStream_t st);
 // Large-batch tier shape: BM x 256 tiles; the first `full` tiles run whole,
 // the rest are split along K into S pieces each (one workgroup per piece),
 // with partial tiles in `part` and one counter per split tile in `cnt`.

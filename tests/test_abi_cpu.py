@@ -129,8 +129,10 @@ def test_run_validation_before_any_hip_call():
     assert L.qgemm_run(None, 4, p16, p16, p16, None) == q.EINVAL
     assert L.qgemm_run(h, 1 << 31, p16, p16, p16, None) == q.EINVAL
     assert L.qgemm_plan_tier(h, 16) == 1
-    assert L.qgemm_plan_tier(h, 17) == 2      # fp32 math above the streaming kernel's 16 rows:
-    assert L.qgemm_plan_tier(h, 256) == 2     # the faithful variant of the large-batch tier
+    assert L.qgemm_plan_tier(h, 17) == 1      # fp32 math up to 80 rows: the verify kernel
+    assert L.qgemm_plan_tier(h, 80) == 1
+    assert L.qgemm_plan_tier(h, 81) == 2      # above: the faithful variant of the large-batch tier
+    assert L.qgemm_plan_tier(h, 256) == 2
     assert L.qgemm_plan_tier(h, 2048) == 2
     assert L.qgemm_plan_tier(h, -1) == 0
     if not _has_device():
@@ -183,9 +185,35 @@ def test_large_batch_shape_choices(fmt, N, K, act, B, bm, s, rem):
     measured shapes (each the fastest of the forced choices on the box),
     read back through the workspace size: rem tiles x s pieces x bm x 256
     fp32 partials."""
-    plan = q.Plan(fmt, N, K, act=act, out="f32")
+    # fp32-faithful math at B <= 80 runs the verify kernel by default; the
+    # tiled tier is forced there to read its cost model
+    faithful_small = act == "f32" and B <= 80
+    plan = q.Plan(fmt, N, K, act=act, out="f32", tier="tiled" if faithful_small else None)
     assert plan.tier(B) == "tiled"
     assert _split_part_bytes(plan, B, N) == rem * s * bm * 256 * 4
+
+
+@pytest.mark.parametrize("fmt,K", [("q8_0", 5120), ("fp8", 5120), ("mxfp4", 17408), ("nvfp4", 5120)])
+def test_verify_kernel_choice_and_workspace(fmt, K):
+    """fp32-faithful math at 16 < B <= 80 takes the verify kernel (small-batch
+    tier): the streaming kernel's row groups of 8 row tiles and K splits,
+    partial tiles for every 16-row batch group.  Below 17 rows the streaming
+    kernel, above 80 the faithful tiled variant; bf16 math, the fused
+    epilogue and K not a whole number of slabs never take it."""
+    N = 5120
+    p = q.Plan(fmt, N, K, act="f32", out="f32", math="fp32")
+    rt = N // 16
+    cnt = -(-(8 * ((rt + 3) // 4) * 4) // 256) * 256 + 1024
+    stream_part = p.workspace_bytes(16) - cnt        # ksplit x groups x 8 KB
+    assert stream_part > 0 and stream_part % (-(-rt // 8) * 8 * 1024) == 0
+    for B in (17, 32, 33, 64, 65, 70, 76, 80):
+        assert p.tier(B) == "skinny", B
+        mb = -(-B // 16)
+        assert p.workspace_bytes(B) - cnt == stream_part * mb, B
+    assert p.tier(81) == "tiled"
+    assert q.Plan(fmt, N, K, act="f32", out="f32", math="bf16").tier(64) == "tiled"
+    slab = 64 if fmt in ("q8_0", "fp8") else 128
+    assert q.Plan(fmt, N, K + 32 if K % slab else K - 32, act="f32", math="fp32").tier(64) == "tiled"
 
 
 def test_weight_bytes_match_format_density():

@@ -136,6 +136,38 @@ def test_q8_0_5120_sweep_fp32(q8_attn, B):
                           _nadds(5120, 3), f"q8_0 5120 B={B}")
 
 
+@pytest.mark.parametrize("fmt,n,k", [("q8_0", 272, 2560), ("fp8", 208, 1536), ("mxfp4", 144, 2560),
+                                     ("nvfp4", 200, 1536)])
+def test_verify_kernel_rows_match_streaming_and_oracle(fmt, n, k):
+    """fp32-faithful math at 16 < B <= 80 (the verify kernel, the MTP verify
+    widths of the hipfire issue): every 16-row slice of a call is bitwise the
+    streaming kernel's result on those rows alone (same row groups, K splits
+    and summation order), with the K split and without a workspace, and every
+    output meets the component-wise bound of exact products against the
+    oracle.  Ragged row groups (N not a multiple of 128) included."""
+    w = synth.gen_weights(fmt, n, k, seed=41)
+    wd = w_dev(w)
+    plan = q.Plan(fmt, n, k, act="f32", out="f32", math="fp32")
+    xf = synth.gen_x_f32(80, k, seed=42)
+    ref = oracle.gemm(w, xf)
+    stream = {}
+    for r0 in range(0, 80, 16):
+        for wsp in ("auto", None):
+            stream[r0, wsp] = run(plan, xf[r0:r0 + 16], wd, workspace=wsp)
+    for B in (17, 31, 48, 64, 65, 76, 80):
+        assert plan.tier(B) == "skinny"
+        for wsp in ("auto", None):
+            y = run(plan, xf[:B], wd, workspace=wsp)
+            for r0 in range(0, B, 16):
+                rows = min(16, B - r0)
+                assert np.array_equal(y[r0:r0 + rows], stream[r0, wsp][:rows]), (B, wsp, r0)
+        bi = np.repeat(np.arange(B), n)
+        ni = np.tile(np.arange(n), B)
+        mag = oracle.gemm_abs_at(w, xf[:B], bi, ni).reshape(B, n)
+        _assert_componentwise(y, ref[:B], 1.01 * mag, _nadds(k, 3), f"{fmt} {n}x{k} B={B} verify")
+        assert oracle.rel_fro(y, ref[:B]) <= TOL_FP32
+
+
 @pytest.mark.parametrize("tier", ["skinny", "tiled"])
 def test_boundary_matrix_chunked_is_bitwise(q8_attn, tier):
     """hipfire PR 'fix(mtp): chunk scalar Q8 batched GEMM above 64 rows',
@@ -255,7 +287,7 @@ def test_stream_split_exchange_modes_agree(fmt, n, k, act, epi, monkeypatch):
     coh = q.Plan(fmt, n, k, act=act, out="f32", math=math, epilogue=epi)   # device-coherent
     monkeypatch.delenv("QGEMM_ST_XLOCAL")
     q.device_status(clear=True)
-    for B in (3, 16):
+    for B in (3, 16) + ((70,) if math == "fp32" else ()):  # 70: the verify kernel
         assert plan.tier(B) == "skinny"
         x = synth.gen_x_f32(B, k, seed=B) if act == "f32" else synth.gen_x_bf16(B, k, seed=B)
         ws = torch.zeros(plan.workspace_bytes(B), dtype=torch.uint8, device=_dev())
@@ -292,7 +324,7 @@ good = q.Plan("q8_0", 5120, 5120, act="f32", out="f32")
 os.environ["QGEMM_XCC_FAKE"] = "1"
 bad = q.Plan("q8_0", 5120, 5120, act="f32", out="f32")
 q.device_status(clear=True)
-for B in (3, 16):
+for B in (3, 16, 70):
     x = torch.from_numpy(synth.gen_config_x("q8_0_5120x5120", B)).cuda()
     y0 = torch.full((B, 5120), float("nan"), device="cuda")
     y1 = torch.full((B, 5120), float("nan"), device="cuda")
@@ -495,6 +527,7 @@ def test_fp32_activations_rounded_once_in_the_workspace(fmt):
 
 
 @pytest.mark.parametrize("fmt,act,math,B", [("q8_0", "f32", "fp32", 16),     # streaming, K split
+                                           ("q8_0", "f32", "fp32", 70),     # verify kernel, K split
                                            ("mxfp4", "bf16", "bf16", 40),   # skinny
                                            ("q8_0", "f32", "fp32", 100),    # fp32-faithful tiled
                                            ("nvfp4", "bf16", "bf16", 300),  # tiled, K split + reduce
