@@ -44,9 +44,13 @@ __host__ __device__ constexpr int vf_depth(int fmt, int mb)
 {
     return (slab_k(fmt) == 64 ? 8 : 4) / (mb <= 3 ? 1 : 2);
 }
-// Activation slabs in flight per staging wave: slab s + VF_NSET is issued
-// when slab s + 1 is staged.
+// Steps of activations in flight per staging wave: step t + VF_NSET is
+// issued when step t + 1 is staged.
 constexpr int VF_NSET = 2;
+// Slabs per step (one barrier each): two of 64 columns up to 64 rows (half
+// the barriers: B = 64 24.1 -> 23.3 us on the box), else one (at 80 rows
+// the ring would then hold only two steps: B = 65-80 ran 3-4 % slower).
+__host__ __device__ constexpr int vf_sps(int fmt, int mb) { return slab_k(fmt) == 64 && mb <= 4 ? 2 : 1; }
 
 // Splits of a chunk whose partial tiles the last workgroup loads together.
 constexpr int VF_RCH = 8;
@@ -94,7 +98,8 @@ __global__ __launch_bounds__(512) void verify_kernel(KArgs a, SkinnyWs ws, int n
     constexpr int U = KS / 32;                   // 32-wide units per slab
     constexpr int NTA = 3;                       // bf16 terms per fp32 activation
     constexpr int NT = VF_NT, D = vf_depth(FMT, MB), NSET = VF_NSET;
-    static_assert(D % NSET == 0, "sets and buffers known at compile time");
+    constexpr int SPS = vf_sps(FMT, MB), DS = D / SPS;  // slabs per step, steps of weights in flight
+    static_assert(D % SPS == 0 && DS % NSET == 0 && DS % 2 == 0, "sets and buffers known at compile time");
     constexpr bool POST = FMT != FMT_NV;         // block scale after the MFMA
     constexpr int SBYTES = FMT == FMT_NV ? 8 : 4;  // scale bytes per row and slab
     constexpr int CPR = KS / 4;                  // 16-byte fp32 chunks per row and slab
@@ -103,7 +108,7 @@ __global__ __launch_bounds__(512) void verify_kernel(KArgs a, SkinnyWs ws, int n
     constexpr int TSTR = MB * U * 64;            // entries per term
     constexpr int SLAB_E = NTA * TSTR;           // 16-byte entries per staged slab
 
-    __shared__ u32x4 xs[2][SLAB_E];              // [buffer][term][mb][unit][64]
+    __shared__ u32x4 xs[2][SPS * SLAB_E];        // [buffer][slab of the step][term][mb][unit][64]
     __shared__ int s_is_last;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -151,25 +156,30 @@ __global__ __launch_bounds__(512) void verify_kernel(KArgs a, SkinnyWs ws, int n
         xvo[i] = ((16 * mb + b) * a.K + 32 * u + 8 * g8 + 4 * h) * 4;
         xeo[i] = 2 * ((mb * U + u) * 64 + g8 * 16 + b) + h;  // 8-byte slot of term 0
     }
-    u32x4 xr[NSET][XPT];  // slab s in set (s - s_beg) % NSET
+    u32x4 xr[NSET][SPS][XPT];  // step t (its first slab s_beg + t * SPS) in set t % NSET
     auto xload = [&](int set, int s) {
 #pragma unroll
-        for (int i = 0; i < XPT; i++)
-            xr[set][i] = bload16(xres, xvo[i], s * KS * 4);
+        for (int sl = 0; sl < SPS; sl++)
+#pragma unroll
+            for (int i = 0; i < XPT; i++)
+                xr[set][sl][i] = bload16(xres, xvo[i], min(s + sl, s_last) * KS * 4);
     };
     auto xstore = [&](int set, u32x4 *buf) {
-        u32x2 *b2 = (u32x2 *)buf;
 #pragma unroll
-        for (int i = 0; i < XPT; i++) {
-            float v[4];
+        for (int sl = 0; sl < SPS; sl++) {
+            u32x2 *b2 = (u32x2 *)(buf + sl * SLAB_E);
 #pragma unroll
-            for (int e = 0; e < 4; e++)
-                v[e] = __uint_as_float(xr[set][i][e]);
-            const Split<NTA> sp = split_f32<NTA, 4>(v);
+            for (int i = 0; i < XPT; i++) {
+                float v[4];
 #pragma unroll
-            for (int t = 0; t < NTA; t++) {
-                const u32x4 q = __builtin_bit_cast(u32x4, sp.t[t]);  // elements 0..3 hold the values
-                b2[xeo[i] + 2 * t * TSTR] = u32x2{q[0], q[1]};
+                for (int e = 0; e < 4; e++)
+                    v[e] = __uint_as_float(xr[set][sl][i][e]);
+                const Split<NTA> sp = split_f32<NTA, 4>(v);
+#pragma unroll
+                for (int t = 0; t < NTA; t++) {
+                    const u32x4 q = __builtin_bit_cast(u32x4, sp.t[t]);  // elements 0..3 hold the values
+                    b2[xeo[i] + 2 * t * TSTR] = u32x2{q[0], q[1]};
+                }
             }
         }
     };
@@ -276,33 +286,34 @@ __global__ __launch_bounds__(512) void verify_kernel(KArgs a, SkinnyWs ws, int n
             }
     };
 
-    // ---- the two roles, each in a loop of its own with one barrier per
-    // slab (the same count in both).  Step s: compute waves compute slab s
-    // from its LDS buffer and the ring slot holding its weights, then refill
-    // that slot with slab s + D; staging waves split slab s + 1 into the other
-    // buffer and issue the loads of slab s + 1 + NSET into the register set
-    // that freed.  D is a multiple of NSET (and even), so buffers and sets
-    // are known at compile time.  Each
+    // ---- the two roles, each in a loop of its own with one barrier per step
+    // of SPS slabs (the same count in both).  Step t: compute waves compute
+    // its slabs (in slab order) from its LDS buffer and the ring slots
+    // holding their weights, then refill those slots with the slabs D
+    // further on; staging waves split step t + 1 into the other buffer and
+    // issue the loads of step t + 1 + NSET into the register set that freed.
+    // The steps of a ring turn are unrolled and DS is a multiple of NSET and
+    // of 2, so slots, sets and buffers are known at compile time.  Each
     // prologue leaves the same loads in flight as a step does, so the
-    // compiler's waits need no drain on entry.  Both loops run whole groups
-    // of D steps; past the range the staging repeats the last slab into a
-    // buffer nobody reads and the compute waves only keep the barrier count.
-    // (One loop with a branch per role, or early exits from the unrolled
-    // steps, made the compiler merge or copy load results, draining every
-    // load at every step.)
+    // compiler's waits need no drain on entry.  Both loops run whole ring
+    // turns; past the range the staging repeats the last slab into a buffer
+    // nobody reads and the compute waves only keep the barrier count.  (One
+    // loop with a branch per role, or early exits from the unrolled steps,
+    // made the compiler merge or copy load results, draining every load at
+    // every step.)
+    const int nsteps = (s_end - s_beg + SPS - 1) / SPS;
     if (stager) {
 #pragma unroll
         for (int k = 0; k < NSET; k++)
-            xload(k, min(s_beg + k, s_last));
+            xload(k, s_beg + k * SPS);
         xstore(0, xs[0]);
-        xload(0, min(s_beg + NSET, s_last));
+        xload(0, s_beg + NSET * SPS);
         __syncthreads();
-        for (int s0 = s_beg; s0 < s_end; s0 += D) {
+        for (int t0 = 0; t0 < nsteps; t0 += DS) {
 #pragma unroll
-            for (int j = 0; j < D; j++) {
-                const int s = s0 + j;
+            for (int j = 0; j < DS; j++) {
                 xstore((j + 1) % NSET, xs[(j + 1) & 1]);
-                xload((j + 1) % NSET, min(s + 1 + NSET, s_last));
+                xload((j + 1) % NSET, s_beg + (t0 + j + 1 + NSET) * SPS);
                 __syncthreads();
             }
         }
@@ -311,16 +322,21 @@ __global__ __launch_bounds__(512) void verify_kernel(KArgs a, SkinnyWs ws, int n
         for (int j = 0; j < D; j++)
             wload(j, s_beg + j);
         __syncthreads();
-        for (int s0 = s_beg; s0 < s_end; s0 += D) {
+        for (int t0 = 0; t0 < nsteps; t0 += DS) {
 #pragma unroll
-            for (int j = 0; j < D; j++) {
-                const int s = s0 + j;
-                if (s < s_end)  // uniform; padding steps only keep the barrier count
-                    compute(xs[j & 1], wr[j], sr[j]);
-                // refill the slot after its last use, so the new slab loads
-                // into the same registers and nothing is copied at the back
-                // edge (a copy would wait for every load in flight)
-                wload(j, s + D);
+            for (int j = 0; j < DS; j++) {
+#pragma unroll
+                for (int sl = 0; sl < SPS; sl++) {
+                    const int s = s_beg + (t0 + j) * SPS + sl;
+                    if (s < s_end)  // uniform; padding only keeps the barrier count
+                        compute(xs[j & 1] + sl * SLAB_E, wr[j * SPS + sl], sr[j * SPS + sl]);
+                }
+                // refill the slots after their last use, so the new slabs
+                // load into the same registers and nothing is copied at the
+                // back edge (a copy would wait for every load in flight)
+#pragma unroll
+                for (int sl = 0; sl < SPS; sl++)
+                    wload(j * SPS + sl, s_beg + (t0 + j) * SPS + sl + D);
                 __syncthreads();
             }
         }
