@@ -421,32 +421,35 @@ struct StCfg {
 };
 
 // Last workgroup of a K split: sum the ksplit partial tiles of `tile` in
-// split order (its own partial `own` in place ks), loading up to 8 partials
-// at a time so their latencies overlap.  SCOPE is the scope the partials
-// were stored with (see SkinnyWs::xlocal).
+// split order (its own partial `own` in place ks).  A lane's 16 bytes of a
+// partial are one load carrying the cache-scope bits of the stores (SCOPE:
+// workgroup, served by the XCD's L2, or device), only the other splits are
+// loaded, and the loads of up to 8 splits are issued before the first add.
 template <int SCOPE>
 __device__ __forceinline__ f32x4 reduce_partials_s(const uint64_t *part, int ksplit, int ks, int64_t tiles,
                                                    int64_t tile, int lane, f32x4 own)
 {
+    constexpr int AUX = SCOPE == __HIP_MEMORY_SCOPE_WORKGROUP ? CP_SC0 : CP_SC1;
+    const int64_t tbytes = tiles * 1024;
+    const int voff = (int)(tile * 1024) + lane * 16;
     f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int k0 = 0; k0 < ksplit; k0 += 8) {
-        uint64_t lo[8], hi[8];
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const int kk = min(k0 + j, ksplit - 1);
-            const uint64_t *src = part + (((int64_t)kk * tiles + tile) * 64 + lane) * 2;
-            lo[j] = __hip_atomic_load(src, __ATOMIC_RELAXED, SCOPE);
-            hi[j] = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, SCOPE);
-        }
+        f32x4 v[8];
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             const int kk = k0 + j;
-            if (kk >= ksplit)
-                break;
-            const f32x4 v = kk == ks ? own
-                                     : __builtin_bit_cast(f32x4, u32x4{(uint32_t)lo[j], (uint32_t)(lo[j] >> 32),
-                                                                       (uint32_t)hi[j], (uint32_t)(hi[j] >> 32)});
-            sum[0] += v[0]; sum[1] += v[1]; sum[2] += v[2]; sum[3] += v[3];
+            if (kk < ksplit && kk != ks) {  // uniform
+                const __amdgpu_buffer_rsrc_t r = make_rsrc((const uint8_t *)part + kk * tbytes, tbytes);
+                v[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, AUX));
+            } else {
+                v[j] = own;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            if (k0 + j >= ksplit)
+                break;  // uniform
+            sum[0] += v[j][0]; sum[1] += v[j][1]; sum[2] += v[j][2]; sum[3] += v[j][3];
         }
     }
     return sum;
