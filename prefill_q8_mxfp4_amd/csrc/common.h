@@ -420,6 +420,19 @@ struct StCfg {
     int64_t cnt_bytes, part_bytes;
 };
 
+// A K split's partial tile `tile` of split ks, a lane's 16 bytes in one
+// store carrying the cache-scope bits of a scoped store at SCOPE (workgroup:
+// kept in the XCD's L2; device: written through to the point of coherence).
+template <int SCOPE>
+__device__ __forceinline__ void publish_partial(uint64_t *part, int ks, int64_t tiles, int64_t tile, int lane,
+                                                f32x4 v)
+{
+    constexpr int AUX = SCOPE == __HIP_MEMORY_SCOPE_WORKGROUP ? CP_SC0 : CP_SC1;
+    const int64_t tbytes = tiles * 1024;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc((uint8_t *)part + ks * tbytes, tbytes);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)(tile * 1024) + lane * 16, 0, AUX);
+}
+
 // Last workgroup of a K split: sum the ksplit partial tiles of `tile` in
 // split order (its own partial `own` in place ks).  A lane's 16 bytes of a
 // partial are one load carrying the cache-scope bits of the stores (SCOPE:

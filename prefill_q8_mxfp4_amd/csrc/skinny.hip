@@ -261,12 +261,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(KArgs a, SkinnyWs ws)
         for (int mb = 0; mb < MB; mb++)
 #pragma unroll
             for (int nt = 0; nt < NT; nt++) {
-                uint64_t *dst = part + (((int64_t)ks * tiles + tbase + mb * NT + nt) * 64 + lane) * 2;
-                const u32x4 v = __builtin_bit_cast(u32x4, acc[mb][nt]);
-                __hip_atomic_store(dst, (uint64_t)v[0] | ((uint64_t)v[1] << 32), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(dst + 1, (uint64_t)v[2] | ((uint64_t)v[3] << 32), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+                publish_partial<__HIP_MEMORY_SCOPE_AGENT>(part, ks, tiles, tbase + mb * NT + nt, lane, acc[mb][nt]);
             }
         __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are acknowledged
         __syncthreads();

@@ -291,17 +291,10 @@ __global__ __launch_bounds__(64 * st_max_waves(NPH)) void stream_kernel(KArgs a,
         const int64_t tile = (int64_t)grp * ST_RG + wid;
         uint64_t *part = (uint64_t *)ws.part;
         if (wid < ST_RG) {
-            uint64_t *dst = part + (((int64_t)ks * tiles + tile) * 64 + lane) * 2;
-            const u32x4 v = __builtin_bit_cast(u32x4, acc);
-            const uint64_t v0 = (uint64_t)v[0] | ((uint64_t)v[1] << 32);
-            const uint64_t v1 = (uint64_t)v[2] | ((uint64_t)v[3] << 32);
-            if (ws.xlocal) {  // every reader of these lines runs on this XCD
-                __hip_atomic_store(dst, v0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                __hip_atomic_store(dst + 1, v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            } else {
-                __hip_atomic_store(dst, v0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(dst + 1, v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+            if (ws.xlocal)  // every reader of these lines runs on this XCD
+                publish_partial<__HIP_MEMORY_SCOPE_WORKGROUP>(part, ks, tiles, tile, lane, acc);
+            else
+                publish_partial<__HIP_MEMORY_SCOPE_AGENT>(part, ks, tiles, tile, lane, acc);
         }
         __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are acknowledged
         __syncthreads();
