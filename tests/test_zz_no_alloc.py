@@ -49,7 +49,7 @@ def _bits(t):
 
 @pytest.mark.parametrize("name,Bs,tol", [
     ("q8_0_5120x5120", (16, 4), 1e-5),              # streaming kernel, K split
-    ("q8_0_5120x5120", (256, 70), 1e-5),            # fp32-faithful tiled, K split + reduce
+    ("q8_0_5120x5120", (256, 70), 1e-5),            # fp32-faithful tiled (split + reduce), then the verify kernel
     ("nvfp4_gate_up_34816x5120", (16, 1), 1e-2),    # streaming fused gate+up, 272 row groups
     ("mxfp4_down_5120x17408", (256, 33), 1e-2),     # tiled bf16, split pieces
     ("q8_0_ffn_17408x5120", (64, 17), 1e-2),        # x rounded to bf16 in the scratch
