@@ -22,8 +22,9 @@ LIB = os.path.join(HERE, "libqgemm.so")
 LIB_DEBUG = os.path.join(HERE, "libqgemm_debug.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 UNITS = ("api.hip", "skinny.hip", "stream.hip", "tiled.hip", "tiled_w4.hip", "tiled_fp32.hip", "dequant.hip",
-         "readbw.hip", "gemv.hip", "mfma_rate.hip", "moe.hip", "verify.hip")
-HEADERS = ("common.h", "layout.h", "tiled.h")
+         "readbw.hip", "gemv.hip", "mfma_rate.hip", "moe.hip", "verify.hip",
+         "verify_bf16.hip")
+HEADERS = ("common.h", "layout.h", "tiled.h", "verify.h", "verify_launch.h")
 
 FLAGS = [
     "--offload-arch=gfx950",

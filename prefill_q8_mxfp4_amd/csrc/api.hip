@@ -48,6 +48,7 @@ static void read_knobs(Knobs *k)
     k->sk_stream = env_int("QGEMM_SK_STREAM", 1);
     k->sk_nt = env_int("QGEMM_SK_NT", 2);
     k->vf = env_int("QGEMM_VF", 1);
+    k->vf_bf16_maxb = env_int("QGEMM_VF_BF16_MAXB", VF_BF16_MAXB);
     k->ti_bm = env_int("QGEMM_TI_BM", 0);
     k->ti_split = env_int("QGEMM_TI_SPLIT", 0);
     k->ti_waves = env_int("QGEMM_TI_WAVES", 0);
@@ -161,15 +162,22 @@ static bool use_stream(const Problem &p, int64_t B)
     return B <= ST_MAX_B && p.kn.sk_stream != 0;
 }
 
-// fp32-faithful math at 16 < B <= 80 (the MTP verify widths), no fused
-// epilogue, K a whole number of slabs: the verify kernel, one pass over the
-// weights for all batch rows in the streaming kernel's summation order.
+// 16 < B <= 80 (the MTP verify widths), no fused epilogue, K a whole number
+// of slabs: the verify kernel, one pass over the weights for all batch rows
+// in the streaming kernel's summation order; fp32-faithful math (three
+// terms) up to 80 rows, bf16 math up to QGEMM_VF_BF16_MAXB rows.
 // QGEMM_VF=0 turns it off (the skinny kernel, or the tiled tier by default).
+static int plan_nterm(const Problem &p) { return p.math == QGEMM_MATH_BF16 ? 1 : p.kn.fp32_terms; }
+
 static bool use_verify(const Problem &p, int64_t B, int nterm)
 {
-    return p.kn.vf != 0 && p.math == QGEMM_MATH_FP32 && p.act == QGEMM_F32 && nterm == 3 &&
-           p.epi != QGEMM_EPI_SWIGLU && B > ST_MAX_B && B <= VF_MAX_B && p.K % slab_k(p.fmt) == 0 &&
-           (p.L.RT + 7) / 8 * 8 * (VF_MAX_B / 16) * 1024 < (1ll << 31);  // a split's partials: 32-bit offsets
+    if (p.kn.vf == 0 || p.epi == QGEMM_EPI_SWIGLU || B <= ST_MAX_B || B > VF_MAX_B ||
+        p.K % slab_k(p.fmt) != 0 ||
+        (p.L.RT + 7) / 8 * 8 * (VF_MAX_B / 16) * 1024 >= (1ll << 31))  // a split's partials: 32-bit offsets
+        return false;
+    if (p.math == QGEMM_MATH_FP32)
+        return p.act == QGEMM_F32 && nterm == 3;
+    return nterm == 1 && B <= p.kn.vf_bf16_maxb;
 }
 
 // The GEMV kernel takes B = 1 and 2 when its activation rows fit in LDS
@@ -521,7 +529,7 @@ static int64_t skinny_ws_bytes(const Problem &p, int64_t B)
         const StCfg c = stream_cfg(p, true);
         return c.cnt_bytes + c.part_bytes;
     }
-    if (use_verify(p, B, p.kn.fp32_terms)) {
+    if (use_verify(p, B, plan_nterm(p))) {
         const StCfg c = stream_cfg(p, true);
         return c.ksplit > 1 ? c.cnt_bytes + c.part_bytes * verify_mb(B) : 0;
     }
@@ -537,9 +545,11 @@ static int choose_tier(const qgemm_plan *plan, int64_t B)
     if (use_gemv(p, B))  // B = 1, 2: the GEMV kernel (no K split, no workspace)
         return QGEMM_TIER_GEMV;
     if (p.math == QGEMM_MATH_FP32)  // the streaming and verify kernels, else the faithful tiled variant
-        return B <= ST_MAX_B || use_verify(p, B, p.kn.fp32_terms) ? QGEMM_TIER_SKINNY : QGEMM_TIER_TILED;
+        return B <= ST_MAX_B || use_verify(p, B, plan_nterm(p)) ? QGEMM_TIER_SKINNY : QGEMM_TIER_TILED;
     if (p.epi == QGEMM_EPI_SWIGLU)  // fused gate+up: the streaming kernel or the tiled tier
         return B <= ST_MAX_B ? QGEMM_TIER_SKINNY : QGEMM_TIER_TILED;
+    if (use_verify(p, B, 1))
+        return QGEMM_TIER_SKINNY;
     // bf16 math: the skinny kernel's cost grows per 16-row group, the tiled
     // kernel's 128-row tile costs about the same from B = 17 to 128; measured
     // on the box the tiled tier wins from B = 48 in every format (and at 32 for
@@ -881,7 +891,7 @@ static int run_with(const qgemm_plan *plan, int64_t B, const void *w, const void
         if (p.epi == QGEMM_EPI_SWIGLU && !use_stream(p, B))
             return fail(QGEMM_ENOTSUP, "qgemm_run: the small-batch tier runs the fused gate+up epilogue "
                                        "for B <= %d only (B=%lld)", ST_MAX_B, (long long)B);
-        const int nterm = p.math == QGEMM_MATH_BF16 ? 1 : p.kn.fp32_terms;
+        const int nterm = plan_nterm(p);
         const int64_t need = skinny_ws_bytes(p, B);
         const bool split = cnt != nullptr && (need == 0 || need - ws_data_off(p) <= data_bytes);
         const bool vf = use_verify(p, B, nterm);
@@ -896,7 +906,7 @@ static int run_with(const qgemm_plan *plan, int64_t B, const void *w, const void
             ws.xlocal = c.xlocal;
             ws.xcc_fake = p.kn.xcc_fake;
             ws.status = c.xlocal ? status_word(current_device()) : nullptr;
-            e = vf ? launch_verify(p, a, c, ws, st) : launch_stream(p, a, c, ws, nterm, st);
+            e = vf ? launch_verify(p, a, c, ws, nterm, st) : launch_stream(p, a, c, ws, nterm, st);
             if (e != hipSuccess)
                 return hip_fail(e, "qgemm_run: kernel launch");
             return QGEMM_OK;

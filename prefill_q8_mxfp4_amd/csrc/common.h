@@ -352,6 +352,7 @@ struct Knobs {
     int sk_stream;         // 0: B <= 16 through the skinny kernel (QGEMM_SK_STREAM)
     int sk_nt;             // 1: one row tile per skinny wave (QGEMM_SK_NT)
     int vf;                // 0: no verify kernel for fp32-faithful 16 < B <= 80 (QGEMM_VF)
+    int vf_bf16_maxb;      // largest B of bf16 math the verify kernel takes (QGEMM_VF_BF16_MAXB)
     int ti_bm, ti_split;   // large-batch row-tile height, K splits (QGEMM_TI_BM, QGEMM_TI_SPLIT)
     int ti_waves;          // large-batch waves per workgroup, 4 or 8 (QGEMM_TI_WAVES; 0 = default)
     int xlocal;            // -1 the probe decides, 0 device-coherent, 1 forced (debug)
@@ -485,12 +486,16 @@ hipError_t launch_skinny(const Problem &p, const KArgs &a, const SkCfg &c, const
                          int nterm, hipStream_t st);
 hipError_t launch_stream(const Problem &p, const KArgs &a, const StCfg &c, const SkinnyWs &ws,
                          int nterm, hipStream_t st);
-// fp32-faithful math with 16 < B <= VF_MAX_B and K a whole number of slabs:
-// the streaming kernel's row groups and K splits (StCfg) with all batch rows
-// per workgroup (verify.hip); partial tiles [ksplit][ngroups * 8][MB][64][4].
+// 16 < B <= VF_MAX_B and K a whole number of slabs: the streaming kernel's
+// row groups and K splits (StCfg) with all batch rows per workgroup (verify.h);
+// partial tiles [ksplit][ngroups * 8][MB][64][4].  nterm: 3 (fp32-faithful,
+// fp32 activations) or 1 (bf16 math).
 constexpr int VF_MAX_B = 80;
+constexpr int VF_BF16_MAXB = 80;  // bf16 math: the default of Knobs::vf_bf16_maxb
 int verify_mb(int64_t B);
-hipError_t launch_verify(const Problem &p, const KArgs &a, const StCfg &c, const SkinnyWs &ws, hipStream_t st);
+hipError_t launch_verify(const Problem &p, const KArgs &a, const StCfg &c, const SkinnyWs &ws, int nterm,
+                         hipStream_t st);
+hipError_t launch_verify_bf16(const Problem &p, const KArgs &a, const StCfg &c, const SkinnyWs &ws, hipStream_t st);
 // Large-batch tier shape: BM x 256 tiles; the first `full` tiles run whole,
 // the rest are split along K into S pieces each (one workgroup per piece),
 // with partial tiles in `part` and one counter per split tile in `cnt`.

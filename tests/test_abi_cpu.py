@@ -143,7 +143,9 @@ def test_run_validation_before_any_hip_call():
 def test_tier_choice():
     p = q.Plan("mxfp4", 5120, 17408, act="bf16")
     assert p.tier(1) == "skinny" and p.tier(16) == "skinny" and p.tier(2048) == "tiled"
-    assert p.tier(32) == "skinny" and p.tier(33) == "tiled"  # bf16 math: tiled from B = 33
+    # bf16 math: the verify kernel up to 80 rows (K a whole number of slabs), tiled above
+    assert p.tier(32) == "skinny" and p.tier(80) == "skinny" and p.tier(81) == "tiled"
+    assert q.Plan("mxfp4", 5120, 17408 - 32, act="bf16").tier(33) == "tiled"  # skinny kernel to 32
     p = q.Plan("nvfp4", 2 * 17408, 5120, act="bf16", out="bf16", epilogue="swiglu")
     assert p.tier(2048) == "tiled" and p.tier(17) == "tiled"
     assert p.tier(1) == "gemv" and p.tier(2) == "skinny" and p.tier(16) == "skinny"
@@ -198,8 +200,9 @@ def test_verify_kernel_choice_and_workspace(fmt, K):
     """fp32-faithful math at 16 < B <= 80 takes the verify kernel (small-batch
     tier): the streaming kernel's row groups of 8 row tiles and K splits,
     partial tiles for every 16-row batch group.  Below 17 rows the streaming
-    kernel, above 80 the faithful tiled variant; bf16 math, the fused
-    epilogue and K not a whole number of slabs never take it."""
+    kernel, above 80 the faithful tiled variant; bf16 math takes it over the
+    same widths; the fused epilogue and K not a whole number of slabs never
+    take it."""
     N = 5120
     p = q.Plan(fmt, N, K, act="f32", out="f32", math="fp32")
     rt = N // 16
@@ -211,7 +214,8 @@ def test_verify_kernel_choice_and_workspace(fmt, K):
         mb = -(-B // 16)
         assert p.workspace_bytes(B) - cnt == stream_part * mb, B
     assert p.tier(81) == "tiled"
-    assert q.Plan(fmt, N, K, act="f32", out="f32", math="bf16").tier(64) == "tiled"
+    assert q.Plan(fmt, N, K, act="f32", out="f32", math="bf16").tier(64) == "skinny"  # bf16 math too
+    assert q.Plan(fmt, N, K, act="f32", out="f32", math="bf16").tier(81) == "tiled"
     slab = 64 if fmt in ("q8_0", "fp8") else 128
     assert q.Plan(fmt, N, K + 32 if K % slab else K - 32, act="f32", math="fp32").tier(64) == "tiled"
 

@@ -168,6 +168,34 @@ def test_verify_kernel_rows_match_streaming_and_oracle(fmt, n, k):
         assert oracle.rel_fro(y, ref[:B]) <= TOL_FP32
 
 
+@pytest.mark.parametrize("fmt,n,k,act", [("q8_0", 272, 2560, "f32"), ("fp8", 208, 1536, "bf16"),
+                                         ("mxfp4", 144, 2560, "bf16"), ("nvfp4", 200, 1536, "f32")])
+def test_verify_kernel_bf16_math_rows_match_streaming(fmt, n, k, act):
+    """bf16 math at 16 < B <= 80 through the verify kernel (bf16 activations
+    as they are, fp32 ones rounded to bf16 once): every 16-row slice bitwise
+    the streaming kernel's result on those rows alone, with and without the
+    K split, and within the bf16 tolerance of the oracle."""
+    w = synth.gen_weights(fmt, n, k, seed=43)
+    wd = w_dev(w)
+    plan = q.Plan(fmt, n, k, act=act, out="f32", math="bf16")
+    xf = synth.gen_x_f32(80, k, seed=44)
+    x = xf if act == "f32" else synth.f32_to_bf16_bits(xf)
+    ref = oracle.gemm(w, x)
+    stream = {}
+    for r0 in range(0, 80, 16):
+        for wsp in ("auto", None):
+            stream[r0, wsp] = run(plan, x[r0:r0 + 16], wd, workspace=wsp)
+    for B in (17, 40, 64, 70, 80):
+        if plan.tier(B) != "skinny":
+            continue  # widths the default route sends to the tiled tier
+        for wsp in ("auto", None):
+            y = run(plan, x[:B], wd, workspace=wsp)
+            for r0 in range(0, B, 16):
+                rows = min(16, B - r0)
+                assert np.array_equal(y[r0:r0 + rows], stream[r0, wsp][:rows]), (B, wsp, r0)
+            assert oracle.rel_fro(y, ref[:B]) <= TOL_BF16, (B, wsp)
+
+
 @pytest.mark.parametrize("tier", ["skinny", "tiled"])
 def test_boundary_matrix_chunked_is_bitwise(q8_attn, tier):
     """hipfire PR 'fix(mtp): chunk scalar Q8 batched GEMM above 64 rows',
