@@ -101,10 +101,10 @@ typedef enum qgemm_math {
 /* Tiers (how a call maps onto kernels); qgemm_create flags may force one. */
 typedef enum qgemm_tier {
     QGEMM_TIER_SKINNY = 1, /* weights streamed once per 16..80 batch rows straight
-                              into matrix-core operands; for small B (bf16 math
-                              B <= 32; fp32 math B <= 80 when K is a whole
-                              number of slabs and there is no fused epilogue,
-                              else B <= 16).  fp32 math keeps one summation
+                              into matrix-core operands; for small B (B <= 80
+                              when K is a whole number of slabs and there is
+                              no fused epilogue; else B <= 16, or B <= 32 with
+                              bf16 math).  Each math mode keeps one summation
                               order per output across the tier, so a batch
                               row's result does not depend on B there */
     QGEMM_TIER_TILED = 2,  /* batch x weight tiles staged through LDS; for large B
