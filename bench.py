@@ -454,6 +454,52 @@ def bench_moe(steps):
     return rec
 
 
+# The verify kernel (16 < B <= 80) against the routes it replaced (the
+# skinny kernel to B = 32 with bf16 math, the tiled tier above; QGEMM_VF=0,
+# read when a plan is created), alternating on one box: (config, math, widths).
+VERIFY_COMPARE = (
+    ("q8_0_5120x5120", None, (17, 32, 48, 64, 65, 70, 76, 80)),   # fp32-faithful
+    ("q8_0_5120x5120", "bf16", (17, 24, 32, 40, 48, 64, 80)),      # fp32 x, bf16 math
+    ("fp8_5120x5120", None, (17, 24, 32, 40, 48, 64, 80)),
+    ("mxfp4_down_5120x17408", None, (17, 24, 32, 40, 48, 64, 80)),
+)
+
+
+def verify_compare():
+    """µs per call of each VERIFY_COMPARE width with the verify kernel and
+    with QGEMM_VF=0 (graph-replayed, rotating weight copies, median of 5
+    loops of at least 200 calls), one JSON line."""
+    import statistics
+
+    import torch
+
+    import prefill_q8_mxfp4_amd as q
+    import synth
+
+    out = {}
+    for name, mm, widths in VERIFY_COMPARE:
+        key = name + (":" + mm if mm else "")
+        c = synth.CONFIGS[name]
+        copies = copies_for(q.weight_bytes(c["fmt"], c["N"], c["K"]))
+        out[key] = {}
+        for B in widths:
+            rec = {}
+            for vf in ("1", "0"):
+                os.environ["QGEMM_VF"] = vf
+                wl = Workload(name, B, copies=copies, math_mode=mm)
+                t = wl.timer()
+                tr, _ = t.trials(5, MIN_LAUNCHES)
+                rec["verify" if vf == "1" else "before"] = {"us": round(statistics.median(tr) * 1e3, 2),
+                                                            "tier": wl.plan.tier(B)}
+                wl.free()
+                del t
+                torch.cuda.empty_cache()
+            os.environ.pop("QGEMM_VF", None)
+            out[key][B] = rec
+            log(f"[bench] verify compare {key} B={B} {rec}")
+    print(json.dumps({"verify_compare_us": out}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -473,6 +519,9 @@ def main():
                          "else (a short program for counter passes); CONFIG routed_moe (B "
                          "ignored) launches the routed-expert workload, mfma_rate the "
                          "matrix-core rate kernel")
+    ap.add_argument("--verify-compare", action="store_true",
+                    help="only time the verify kernel's widths against the routes it replaced "
+                         "(QGEMM_VF=0) and print that table as one JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path; "
@@ -489,6 +538,9 @@ def main():
     sha = kernel_src_sha()
     if args.copy_calibration:
         copy_calibration()
+    if args.verify_compare:
+        verify_compare()
+        return
     if args.calls_of and args.calls_of[0] == "mfma_rate":
         sink = torch.zeros(4096, dtype=torch.int32, device="cuda:0")
         for _ in range(3 + args.steps):  # mode 0: chained bf16 MFMAs, the matrix cores' own rate
