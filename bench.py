@@ -462,6 +462,7 @@ VERIFY_COMPARE = (
     ("q8_0_5120x5120", "bf16", (17, 24, 32, 40, 48, 64, 80)),      # fp32 x, bf16 math
     ("fp8_5120x5120", None, (17, 24, 32, 40, 48, 64, 80)),
     ("mxfp4_down_5120x17408", None, (17, 24, 32, 40, 48, 64, 80)),
+    ("nvfp4_gate_up_34816x5120", None, (17, 32, 48, 64, 80)),      # fused gate+up
 )
 
 

@@ -49,6 +49,7 @@ static void read_knobs(Knobs *k)
     k->sk_nt = env_int("QGEMM_SK_NT", 2);
     k->vf = env_int("QGEMM_VF", 1);
     k->vf_bf16_maxb = env_int("QGEMM_VF_BF16_MAXB", VF_BF16_MAXB);
+    k->vf_swiglu_maxb = env_int("QGEMM_VF_SWIGLU_MAXB", VF_SWIGLU_MAXB);
     k->ti_bm = env_int("QGEMM_TI_BM", 0);
     k->ti_split = env_int("QGEMM_TI_SPLIT", 0);
     k->ti_waves = env_int("QGEMM_TI_WAVES", 0);
@@ -162,16 +163,19 @@ static bool use_stream(const Problem &p, int64_t B)
     return B <= ST_MAX_B && p.kn.sk_stream != 0;
 }
 
-// 16 < B <= 80 (the MTP verify widths), no fused epilogue, K a whole number
-// of slabs: the verify kernel, one pass over the weights for all batch rows
-// in the streaming kernel's summation order; fp32-faithful math (three
-// terms) up to 80 rows, bf16 math up to QGEMM_VF_BF16_MAXB rows.
-// QGEMM_VF=0 turns it off (the skinny kernel, or the tiled tier by default).
+// 16 < B <= 80 (the MTP verify widths), K a whole number of slabs: the
+// verify kernel, one pass over the weights for all batch rows in the
+// streaming kernel's summation order; fp32-faithful math (three terms) up to
+// 80 rows, bf16 math up to QGEMM_VF_BF16_MAXB rows (80), the fused gate+up
+// epilogue up to QGEMM_VF_SWIGLU_MAXB (48: NVFP4 gate+up 2x17408x5120 ran
+// 39.8 / 55.3 us at B = 17 / 48 against the tiled tier's 64.2 / 66.3, but
+// 69.9 / 86.9 at 64 / 80 against 68.4 / 72.0).  QGEMM_VF=0 turns it off (the
+// skinny kernel, or the tiled tier by default).
 static int plan_nterm(const Problem &p) { return p.math == QGEMM_MATH_BF16 ? 1 : p.kn.fp32_terms; }
 
 static bool use_verify(const Problem &p, int64_t B, int nterm)
 {
-    if (p.kn.vf == 0 || p.epi == QGEMM_EPI_SWIGLU || B <= ST_MAX_B || B > VF_MAX_B ||
+    if (p.kn.vf == 0 || (p.epi == QGEMM_EPI_SWIGLU && B > p.kn.vf_swiglu_maxb) || B <= ST_MAX_B || B > VF_MAX_B ||
         p.K % slab_k(p.fmt) != 0 ||
         (p.L.RT + 7) / 8 * 8 * (VF_MAX_B / 16) * 1024 >= (1ll << 31))  // a split's partials: 32-bit offsets
         return false;
@@ -546,8 +550,8 @@ static int choose_tier(const qgemm_plan *plan, int64_t B)
         return QGEMM_TIER_GEMV;
     if (p.math == QGEMM_MATH_FP32)  // the streaming and verify kernels, else the faithful tiled variant
         return B <= ST_MAX_B || use_verify(p, B, plan_nterm(p)) ? QGEMM_TIER_SKINNY : QGEMM_TIER_TILED;
-    if (p.epi == QGEMM_EPI_SWIGLU)  // fused gate+up: the streaming kernel or the tiled tier
-        return B <= ST_MAX_B ? QGEMM_TIER_SKINNY : QGEMM_TIER_TILED;
+    if (p.epi == QGEMM_EPI_SWIGLU)  // fused gate+up: the streaming or verify kernel, or the tiled tier
+        return B <= ST_MAX_B || use_verify(p, B, 1) ? QGEMM_TIER_SKINNY : QGEMM_TIER_TILED;
     if (use_verify(p, B, 1))
         return QGEMM_TIER_SKINNY;
     // bf16 math: the skinny kernel's cost grows per 16-row group, the tiled
@@ -888,9 +892,11 @@ static int run_with(const qgemm_plan *plan, int64_t B, const void *w, const void
         return QGEMM_OK;
     }
     if (tier == QGEMM_TIER_SKINNY) {
-        if (p.epi == QGEMM_EPI_SWIGLU && !use_stream(p, B))
+        if (p.epi == QGEMM_EPI_SWIGLU && !use_stream(p, B) && !use_verify(p, B, plan_nterm(p)))
             return fail(QGEMM_ENOTSUP, "qgemm_run: the small-batch tier runs the fused gate+up epilogue "
-                                       "for B <= %d only (B=%lld)", ST_MAX_B, (long long)B);
+                                       "for B <= %d, or B <= %d with K a whole number of slabs (B=%lld)",
+                        ST_MAX_B, p.kn.vf_swiglu_maxb < VF_MAX_B ? p.kn.vf_swiglu_maxb : VF_MAX_B,
+                        (long long)B);
         const int nterm = plan_nterm(p);
         const int64_t need = skinny_ws_bytes(p, B);
         const bool split = cnt != nullptr && (need == 0 || need - ws_data_off(p) <= data_bytes);

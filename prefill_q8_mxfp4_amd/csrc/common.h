@@ -353,6 +353,7 @@ struct Knobs {
     int sk_nt;             // 1: one row tile per skinny wave (QGEMM_SK_NT)
     int vf;                // 0: no verify kernel for fp32-faithful 16 < B <= 80 (QGEMM_VF)
     int vf_bf16_maxb;      // largest B of bf16 math the verify kernel takes (QGEMM_VF_BF16_MAXB)
+    int vf_swiglu_maxb;    // largest B the fused gate+up epilogue takes the verify kernel at (QGEMM_VF_SWIGLU_MAXB)
     int ti_bm, ti_split;   // large-batch row-tile height, K splits (QGEMM_TI_BM, QGEMM_TI_SPLIT)
     int ti_waves;          // large-batch waves per workgroup, 4 or 8 (QGEMM_TI_WAVES; 0 = default)
     int xlocal;            // -1 the probe decides, 0 device-coherent, 1 forced (debug)
@@ -492,6 +493,7 @@ hipError_t launch_stream(const Problem &p, const KArgs &a, const StCfg &c, const
 // fp32 activations) or 1 (bf16 math).
 constexpr int VF_MAX_B = 80;
 constexpr int VF_BF16_MAXB = 80;  // bf16 math: the default of Knobs::vf_bf16_maxb
+constexpr int VF_SWIGLU_MAXB = 48;  // fused gate+up: the default of Knobs::vf_swiglu_maxb
 int verify_mb(int64_t B);
 hipError_t launch_verify(const Problem &p, const KArgs &a, const StCfg &c, const SkinnyWs &ws, int nterm,
                          hipStream_t st);

@@ -96,7 +96,7 @@ __device__ __forceinline__ void vf_sum_splits(const uint8_t *part, int ksplit, i
 }
 
 template <int FMT, int MB, int OUTT, int NTA, int ACT>
-__global__ __launch_bounds__(512) void verify_kernel(KArgs a, SkinnyWs ws, int ngroups)
+__global__ __launch_bounds__(512) void verify_kernel(KArgs a, SkinnyWs ws, int ngroups, int Nh)
 {
     static_assert(NTA == 1 || (NTA == 3 && ACT == ACT_F32), "three terms of fp32 input, or one");
     constexpr int KS = slab_k(FMT);
@@ -140,7 +140,13 @@ __global__ __launch_bounds__(512) void verify_kernel(KArgs a, SkinnyWs ws, int n
         ks = t / ngroups;
         grp = t % ngroups;
     }
-    const int rt0 = grp * ST_RG + (wid & 3) * NT;  // a compute wave's first row tile
+    // The group's 8 tile slots: 8 consecutive row tiles, or with SwiGLU
+    // (Nh > 0) 4 gate tiles and the 4 matching up tiles Nh/16 further on.
+    // A compute wave holds slots 2w, 2w + 1, or with SwiGLU gate slot w and
+    // its up slot 4 + w, so G and U of an output column meet in one lane.
+    static_assert(NT == 2, "two tile slots per compute wave");
+    auto slot_of = [&](int t) { return Nh ? (wid & 3) + 4 * t : (wid & 3) * NT + t; };
+    auto row_of = [&](int g) { return Nh ? (g < 4 ? grp * 4 + g : Nh / 16 + grp * 4 + g - 4) : grp * ST_RG + g; };
     const int s_beg = ks * ws.kc;
     const int s_end = min(a.S, s_beg + ws.kc);
     const int s_last = s_end - 1;
@@ -216,7 +222,7 @@ __global__ __launch_bounds__(512) void verify_kernel(KArgs a, SkinnyWs ws, int n
         const int sc = min(s, s_last);
 #pragma unroll
         for (int t = 0; t < NT; t++) {
-            const int64_t rt = min(rt0 + t, a.RT - 1);
+            const int64_t rt = min(row_of(slot_of(t)), a.RT - 1);
             wr[j][t] = bload16_nt(make_rsrc(a.w + ((rt * a.S + sc) << 10), live ? 1024 : 0), wvoff, 0);
             const __amdgpu_buffer_rsrc_t srs = make_rsrc(
                 a.w + a.scale_off + (rt * a.S + sc) * (16 * SBYTES), live ? 16 * SBYTES : 0);
@@ -385,6 +391,27 @@ __global__ __launch_bounds__(512) void verify_kernel(KArgs a, SkinnyWs ws, int n
             }
     };
 
+    // SwiGLU: store SiLU(G) * U of gate tile gt (lane: batch rows
+    // 16*mb + 4*gq + i of column r), y being [B][Nh].
+    auto store_swiglu = [&](int gt, const f32x4 (&G)[MB], const f32x4 (&Up)[MB]) {
+        const int col = gt * 16 + r;
+        if (col >= Nh)
+            return;
+        float g0 = 1.f, g1 = 1.f;
+        if constexpr (FMT == FMT_NV) {
+            g0 = tensor_scale(a, col);
+            g1 = tensor_scale(a, Nh + col);
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int b = 16 * mb + 4 * gq + i;
+                if (b < a.B)
+                    store_out_nt<OUTT>(a.y, (int64_t)b * Nh + col, silu(g0 * G[mb][i]) * (g1 * Up[mb][i]));
+            }
+    };
+
     // ---- K split: publish the partial tiles; the last workgroup of the
     // group adds them in split order
     if (ws.ksplit > 1) {
@@ -396,7 +423,7 @@ __global__ __launch_bounds__(512) void verify_kernel(KArgs a, SkinnyWs ws, int n
             for (int mb = 0; mb < MB; mb++) {
                 if (stager)
                     break;  // uniform
-                const int64_t tile = ((int64_t)grp * ST_RG + (wid & 3) * NT + t) * MB + mb;
+                const int64_t tile = ((int64_t)grp * ST_RG + slot_of(t)) * MB + mb;
                 if (ws.xlocal)  // every reader of these lines runs on this XCD
                     publish_partial<__HIP_MEMORY_SCOPE_WORKGROUP>(part, ks, tiles, tile, lane, acc[t][mb]);
                 else
@@ -436,25 +463,42 @@ __global__ __launch_bounds__(512) void verify_kernel(KArgs a, SkinnyWs ws, int n
         // lane's 16 bytes of a partial tile are one load, with the cache
         // scope of the stores (workgroup: this XCD's L2; else device), and
         // every load of a chunk of splits is issued before the first add.
+        // With SwiGLU, waves 0..3 each add gate slot w and up slot 4 + w.
         const int64_t tbytes = tiles * 1024;
-        const int tvo = (int)((((int64_t)grp * ST_RG + wid) * MB) * 1024) + lane * 16;
-        f32x4 sum[MB];
-        if (ws.xlocal)
-            vf_sum_splits<CP_SC0, MB>((const uint8_t *)ws.part, ws.ksplit, tbytes, tvo, sum);
-        else
-            vf_sum_splits<CP_SC1, MB>((const uint8_t *)ws.part, ws.ksplit, tbytes, tvo, sum);
         if (tid == 0)
             __hip_atomic_store(&ws.cnt[grp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        store_tile(grp * ST_RG + wid, sum);
+        auto sum_slot = [&](int g, f32x4 (&sum)[MB]) {
+            const int tvo = (int)((((int64_t)grp * ST_RG + g) * MB) * 1024) + lane * 16;
+            if (ws.xlocal)
+                vf_sum_splits<CP_SC0, MB>((const uint8_t *)ws.part, ws.ksplit, tbytes, tvo, sum);
+            else
+                vf_sum_splits<CP_SC1, MB>((const uint8_t *)ws.part, ws.ksplit, tbytes, tvo, sum);
+        };
+        f32x4 sum[MB];
+        if (Nh) {
+            if (wid >= 4)
+                return;  // uniform per wave; no barrier follows
+            f32x4 up[MB];
+            sum_slot(wid, sum);
+            sum_slot(4 + wid, up);
+            store_swiglu(grp * 4 + wid, sum, up);
+            return;
+        }
+        sum_slot(wid, sum);
+        store_tile(row_of(wid), sum);
         return;
     }
 
-    // ---- unsplit: each compute wave stores its two row tiles
+    // ---- unsplit: each compute wave stores its two tile slots
     if (stager)
         return;  // uniform
+    if (Nh) {
+        store_swiglu(grp * 4 + (wid & 3), acc[0], acc[1]);
+        return;
+    }
 #pragma unroll
     for (int t = 0; t < NT; t++)
-        store_tile(rt0 + t, acc[t]);
+        store_tile(row_of(slot_of(t)), acc[t]);
 }
 
 }  // namespace qg

@@ -11,10 +11,10 @@ static void launch_vm(const Problem &p, const KArgs &a, const StCfg &c, const Sk
 {
     if (p.out == QGEMM_F32)
         hipLaunchKernelGGL((verify_kernel<FMT, MB, OUT_F32, NTA, ACT>), dim3((unsigned)c.grid), dim3(512), 0, st,
-                           a, ws, c.ngroups);
+                           a, ws, c.ngroups, c.Nh);
     else
         hipLaunchKernelGGL((verify_kernel<FMT, MB, OUT_BF16, NTA, ACT>), dim3((unsigned)c.grid), dim3(512), 0, st,
-                           a, ws, c.ngroups);
+                           a, ws, c.ngroups, c.Nh);
 }
 
 template <int FMT, int NTA, int ACT>

@@ -147,7 +147,9 @@ def test_tier_choice():
     assert p.tier(32) == "skinny" and p.tier(80) == "skinny" and p.tier(81) == "tiled"
     assert q.Plan("mxfp4", 5120, 17408 - 32, act="bf16").tier(33) == "tiled"  # skinny kernel to 32
     p = q.Plan("nvfp4", 2 * 17408, 5120, act="bf16", out="bf16", epilogue="swiglu")
-    assert p.tier(2048) == "tiled" and p.tier(17) == "tiled"
+    # fused gate+up: the verify kernel to 48 rows, then the tiled tier
+    assert p.tier(2048) == "tiled" and p.tier(17) == "skinny" and p.tier(48) == "skinny"
+    assert p.tier(49) == "tiled"
     assert p.tier(1) == "gemv" and p.tier(2) == "skinny" and p.tier(16) == "skinny"
     p = q.Plan("q8_0", 5120, 5120, act="f32", tier="skinny")
     assert p.tier(1) == "skinny" and p.tier(256) == "skinny"

@@ -196,6 +196,34 @@ def test_verify_kernel_bf16_math_rows_match_streaming(fmt, n, k, act):
             assert oracle.rel_fro(y, ref[:B]) <= TOL_BF16, (B, wsp)
 
 
+@pytest.mark.parametrize("fmt,nh,k,act", [("nvfp4", 1040, 2048, "bf16"), ("mxfp4", 528, 1536, "f32"),
+                                          ("q8_0", 272, 1024, "bf16")])
+def test_verify_kernel_swiglu_rows_match_streaming(fmt, nh, k, act):
+    """The fused gate+up epilogue at 16 < B <= 48 through the verify kernel:
+    every 16-row slice of SiLU(G)*U bitwise the streaming kernel's on those
+    rows alone (ragged gate-tile groups included), with and without the K
+    split, and within the SwiGLU tolerance of the oracle."""
+    w = _gate_up(fmt, nh, k, 45)
+    wd = w_dev(w)
+    plan = q.Plan(fmt, 2 * nh, k, act=act, out="f32", epilogue="swiglu", math="bf16")
+    xf = synth.gen_x_f32(80, k, seed=46)
+    x = xf if act == "f32" else synth.f32_to_bf16_bits(xf)
+    ref = oracle.swiglu(w, x)
+    stream = {}
+    for r0 in range(0, 80, 16):
+        for wsp in ("auto", None):
+            stream[r0, wsp] = run(plan, x[r0:r0 + 16], wd, workspace=wsp)
+    for B in (17, 33, 48):  # above 48 rows the fused epilogue takes the tiled tier
+        assert plan.tier(B) == "skinny"
+        for wsp in ("auto", None):
+            y = run(plan, x[:B], wd, workspace=wsp)
+            for r0 in range(0, B, 16):
+                rows = min(16, B - r0)
+                assert np.array_equal(y[r0:r0 + rows], stream[r0, wsp][:rows]), (B, wsp, r0)
+            # bf16 x: exact products, fp32 sums only; fp32 x: rounded to bf16 once
+            assert oracle.rel_fro(y, ref[:B]) <= (1e-4 if act == "bf16" else TOL_BF16), (B, wsp)
+
+
 @pytest.mark.parametrize("tier", ["skinny", "tiled"])
 def test_boundary_matrix_chunked_is_bitwise(q8_attn, tier):
     """hipfire PR 'fix(mtp): chunk scalar Q8 batched GEMM above 64 rows',
@@ -968,12 +996,22 @@ def test_swiglu_streaming_gate_up_shape_b16():
     assert err <= TOL_BF16, err
 
 
-def test_swiglu_forced_skinny_above_16_is_not_supported():
-    plan = q.Plan("nvfp4", 128, 256, act="bf16", out="f32", epilogue="swiglu", tier="skinny")
-    x = synth.gen_x_bf16(17, 256)
+def test_swiglu_forced_skinny_limits():
+    """A SwiGLU plan forced to the small-batch tier runs B <= 48 when K is a
+    whole number of slabs (the verify kernel above 16 rows) and refuses wider
+    calls, or B > 16 with a partial last slab, with QGEMM_ENOTSUP."""
     w = _gate_up("nvfp4", 64, 256, 3)
+    plan = q.Plan("nvfp4", 128, 256, act="bf16", out="f32", epilogue="swiglu", tier="skinny")
+    x = synth.gen_x_bf16(49, 256)
+    y = run(plan, x[:48], w_dev(w))
+    assert oracle.rel_fro(y, oracle.swiglu(w, x[:48])) <= 1e-4
     with pytest.raises(q.QgemmError) as e:
         run(plan, x, w_dev(w))
+    assert e.value.status == q.ENOTSUP
+    w = _gate_up("nvfp4", 64, 144, 3)
+    plan = q.Plan("nvfp4", 128, 144, act="bf16", out="f32", epilogue="swiglu", tier="skinny")
+    with pytest.raises(q.QgemmError) as e:
+        run(plan, synth.gen_x_bf16(17, 144), w_dev(w))
     assert e.value.status == q.ENOTSUP
 
 
