@@ -102,8 +102,8 @@ typedef enum qgemm_math {
 typedef enum qgemm_tier {
     QGEMM_TIER_SKINNY = 1, /* weights streamed once per 16..80 batch rows straight
                               into matrix-core operands; for small B (B <= 80
-                              when K is a whole number of slabs and there is
-                              no fused epilogue; else B <= 16, or B <= 32 with
+                              when K is a whole number of slabs, B <= 48 with
+                              the fused epilogue; else B <= 16, or B <= 32 with
                               bf16 math).  Each math mode keeps one summation
                               order per output across the tier, so a batch
                               row's result does not depend on B there */
