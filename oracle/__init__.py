@@ -14,7 +14,7 @@ What it computes (plain definitions, see qgemm_oracle.c for the decoders):
   Halo: prefill 2.4x gap + DP4A verify tiers for K=5..9", section
   "Kernel-level root cause of the gfx1151 NVFP4 prefill gap", Fix); FP8
   ``s * E4M3(c)`` with one fp32 scale per row and 128-wide K block (the same
-  issue's FP8-weight projection GEMM; the block rule is this build's reading).
+  issue's FP8-weight projection GEMM; the pages do not fix the block width, 128 is a reading).
 * fused gate+up: ``out[b][j] = SiLU(G) * U`` with G from row j and U from row
   Nh + j (Atlas issue, "What's the job?" asks for the fused gate+up
   dual-accumulator GEMM; the workload names SiLU(gate)*up).

@@ -198,7 +198,7 @@ static bool gemv_fits(const Problem &p, int64_t B)
 // Automatic choice: B = 1 when the activation row takes at most 32 KB of
 // LDS (K <= 8192), so that four or more GEMV workgroups of 8 waves fit on a
 // CU and the CUs that hold a tile more than others keep HBM busy.  Measured
-// on the box against the MFMA streaming kernel: Q8_0 5120^2 B = 1 9.37 vs
+// on MI355X against the MFMA streaming kernel: Q8_0 5120^2 B = 1 9.37 vs
 // 10.19 us, FP8 5120^2 8.95 vs 9.85, NVFP4 gate+up 2x17408x5120 23.7 vs
 // 29.0; MXFP4 5120x17408 (K = 17408, 70 KB of LDS) 16.8 vs 14.0; at B = 2
 // the streaming kernel wins everywhere (Q8_0 11.2 vs 10.2, FP8 10.6 vs 9.9,
@@ -388,7 +388,7 @@ static StCfg stream_cfg(const Problem &p, bool split)
     c.NPH = sh.NPH;
     c.Nh = p.epi == QGEMM_EPI_SWIGLU ? (int)(p.N / 2) : 0;
     c.KC = sh.W * sh.NPH;
-    // weight items a wave keeps in flight, fastest on the box per format:
+    // weight items a wave keeps in flight, fastest on MI355X per format:
     // Q8_0 4, MXFP4 and FP8 3 (MXFP4 down projection B = 1: 16.6 -> 13.9 us
     // against all at once), NVFP4 all at once (16)
     c.depth = p.kn.st_depth ? p.kn.st_depth
@@ -556,8 +556,8 @@ static int choose_tier(const qgemm_plan *plan, int64_t B)
         return QGEMM_TIER_SKINNY;
     // bf16 math: the skinny kernel's cost grows per 16-row group, the tiled
     // kernel's 128-row tile costs about the same from B = 17 to 128; measured
-    // on the box the tiled tier wins from B = 48 in every format (and at 32 for
-    // MXFP4 and Q8_0)
+    // on MI355X the tiled tier wins from B = 48 in every format (and at 32 for
+    // MXFP4 and Q8_0).  Both give way to the verify kernel where it applies.
     return B <= 32 ? QGEMM_TIER_SKINNY : QGEMM_TIER_TILED;
 }
 

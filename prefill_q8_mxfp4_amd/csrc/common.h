@@ -250,7 +250,7 @@ __device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, int voff, i
 
 // The same loads with the nontemporal cache policy (gfx950 CPol NT = 2), for
 // data a call reads exactly once (the small-batch weight stream): measured on
-// the box, the headline's weight loads alone run 0.5 us faster with it.
+// MI355X, Q8_0 5120^2 weight loads alone at B = 16 run 0.5 us faster with it.
 constexpr int CP_NT = 2;
 // Scope bits of the same field for plain loads of data other workgroups
 // stored with scoped stores: SC0 as the compiler sets for workgroup-scope

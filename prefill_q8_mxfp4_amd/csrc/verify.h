@@ -9,10 +9,11 @@
 // split (the same slab ranges), so every output is summed in exactly the
 // streaming kernel's order and a batch row's result does not depend on B
 // across the small-batch tier.  It is 8 waves in two roles, one of each per
-// SIMD, meeting at one barrier per slab:
+// SIMD, meeting at one barrier per step of one or two slabs:
 //
-//  * compute waves 0..3: wave w computes row tiles 2w and 2w + 1 over the
-//    whole slab range.  Its weights arrive straight into registers as MFMA B
+//  * compute waves 0..3: wave w computes row tiles 2w and 2w + 1 (with the
+//    fused gate+up epilogue, gate tile w and its up tile) over the whole slab
+//    range.  Its weights arrive straight into registers as MFMA B
 //    operands (a lane's 16-byte chunk of a slab is its operand; see
 //    layout.h), D slabs ahead, through nontemporal buffer loads (past the
 //    range through an empty resource: zeros, no traffic).  Only weight loads
@@ -24,16 +25,17 @@
 //    16-byte entries), the step before they are used.  The split runs on the
 //    vector ALUs while the compute wave of the same SIMD issues MFMAs.
 //  * per 32-wide unit: both tiles' codes decoded once, then for each batch
-//    group the three terms' MFMAs into a block partial from zero and the
+//    group the NTA terms' MFMAs into a block partial from zero and the
 //    Q8_0 / MXFP4 / FP8 block scale multiplied into the slab partial (NVFP4:
 //    scale folded into the exact operand); slab partials added to the running
 //    tile in slab order.
 //
 // With fp32-faithful math the products are exact (bf16 terms of fp32 x times
-// exact codes), so only the fp32 accumulation rounds.  K splits meet as in the streaming kernel:
-// partial tiles through the XCD's L2 when the dispatcher keeps a row group's
-// splits on one XCD (checked every launch), else device-coherent, added in
-// split order by the last workgroup of the group.
+// exact codes), so only the fp32 accumulation rounds.  K splits meet as in
+// the streaming kernel: partial tiles through the XCD's L2 when the
+// dispatcher keeps a row group's splits on one XCD (checked every launch),
+// else device-coherent, added in split order by the last workgroup of the
+// group, all 8 of its waves sharing the adds.
 #pragma once
 
 #include "common.h"
@@ -52,7 +54,7 @@ __host__ __device__ constexpr int vf_depth(int fmt, int mb)
 // issued when step t + 1 is staged.
 constexpr int VF_NSET = 2;
 // Slabs per step (one barrier each): two of 64 columns up to 64 rows (half
-// the barriers: B = 64 24.1 -> 23.3 us on the box), else one (at 80 rows
+// the barriers: Q8_0 5120^2 B = 64 24.1 -> 23.3 us on MI355X), else one (at 80 rows
 // the ring would then hold only two steps: B = 65-80 ran 3-4 % slower).
 __host__ __device__ constexpr int vf_sps(int fmt, int mb) { return slab_k(fmt) == 64 && mb <= 4 ? 2 : 1; }
 

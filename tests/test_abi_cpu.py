@@ -186,7 +186,7 @@ def _split_part_bytes(plan, B, N):
 ])
 def test_large_batch_shape_choices(fmt, N, K, act, B, bm, s, rem):
     """The large-batch cost model's row-tile height and split count on the
-    measured shapes (each the fastest of the forced choices on the box),
+    measured shapes (each the fastest of the forced choices on MI355X),
     read back through the workspace size: rem tiles x s pieces x bm x 256
     fp32 partials."""
     # fp32-faithful math at B <= 80 runs the verify kernel by default; the
