@@ -776,6 +776,8 @@ def _library_ref(w, x, swiglu=False, magnitude=False):
 
 
 @pytest.mark.parametrize("act,math,B", [("f32", "fp32", 4),     # streaming
+                                         ("f32", "fp32", 70),    # verify kernel, hundreds of K splits
+                                         ("bf16", "bf16", 48),   # verify kernel, bf16 math
                                          ("f32", "fp32", 100),   # fp32-faithful tiled, 96-row tiles
                                          ("bf16", "bf16", 300)])  # tiled, 128-row tiles
 def test_largest_k(act, math, B):
